@@ -1,0 +1,240 @@
+"""Plain, slow CPU oracle of the MiniMax Sparse Attention (MSA) forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package's smoke check and the
+benchmark's CPU-baseline leg may import or run this module; the library and
+its Python binding never do.  It shares no code with the HIP path.
+
+Sources (the pages this follows; cited by title and section):
+  [HA]  hyper.ai paper page 2606.13392, "MiniMax Sparse Attention" summary,
+        sections 核心贡献 (Contributions) and 方法 (Method).
+  [TG]  Telegram review, channel quant_prune_distill, post 751, sections
+        "Метод" (Method) and "Эксперименты" (Experiments).
+  [HN]  hamidun.com news "MiniMax выпустила MSA …", section "Как устроен MSA".
+
+What is computed (everything in float64 from the bf16 input values, which
+are exact in float64):
+  index_scores   s[j] = idx_q[t,g] . idx_k[j]  for visible keys j <= t
+                 (a raw, pre-softmax dot product)            [HA 方法; TG Метод]
+  block_max      S[b] = max of s over the aligned block b (tokens [bB, (b+1)B)),
+                 clipped to j <= t                            [HA 方法; TG Метод]
+  select_blocks  the local block L(t) = floor(t/B) is always kept; the other
+                 min(k, L(t)+1) - 1 blocks are the highest S among blocks
+                 0..L(t)-1, equal scores broken by the lower block index;
+                 output ascending, padded with -1             [HA 方法, 核心贡献; TG Метод]
+  attention_row  exact softmax attention of each query head h of group
+                 g = floor(h / R) over the keys of the selected blocks that
+                 are <= t, scale 1/sqrt(d)                    [HA 方法; HN]
+  decode_row     the same for the one new token at position len-1 of a cache
+
+Readings where the pages are silent (the plainest reading the rest supports):
+  - no scale or activation on the index score; a positive scale would not
+    change the selection anyway;
+  - blocks are aligned at token 0; the last one may be partial;
+  - the local block is the aligned block holding the query and counts inside k;
+  - ties between equal block maxima go to the lower block index;
+  - query head h belongs to group floor(h / R), R = Hq / G;
+  - a decode cache of length len holds the new token at position len - 1.
+Parity of this module is pinned by tests/test_oracle_pins.py (dense
+equivalence through torch's SDPA, closed-form selections, exhaustive subset
+enumeration, invariants, special inputs, the 16 x 128 = 2048-token budget).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    """torch tensor (any float dtype, any device) or array -> float64 ndarray."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        import torch  # local: only to convert bf16 tensors
+        x = x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def local_block(t: int, B: int) -> int:
+    """The aligned block holding position t [HA 方法: the block containing the
+    current query position is always included]."""
+    return t // B
+
+
+def index_scores(idx_q_tg: np.ndarray, idx_k: np.ndarray, t: int) -> np.ndarray:
+    """Pre-softmax index scores of one (token, group) row against the visible
+    keys 0..t: one index-query head per group, one index-key head shared by
+    the layer, plain dot product [TG Метод; HA 方法]."""
+    return idx_k[: t + 1] @ idx_q_tg
+
+
+def block_max(scores: np.ndarray, t: int, B: int) -> np.ndarray:
+    """Block Max Pooling: the maximum token score in each aligned block of the
+    visible range, blocks 0..L(t) [HA 核心贡献, 方法; TG Метод]."""
+    L = local_block(t, B)
+    out = np.empty(L + 1, dtype=np.float64)
+    for b in range(L + 1):
+        lo, hi = b * B, min((b + 1) * B, t + 1)
+        out[b] = scores[lo:hi].max()
+    return out
+
+
+def select_blocks(S: np.ndarray, t: int, B: int, k: int) -> np.ndarray:
+    """Top-k block selection with the forced local block.
+
+    m = min(k, L+1) blocks are kept: the local block L and the m-1 highest of
+    the candidate blocks 0..L-1, ordered by score (descending) then block id
+    (ascending).  Returned ascending and padded with -1 to length k
+    [HA 方法: top-k per query group, local block always included; TG Метод]."""
+    L = local_block(t, B)
+    m = min(k, L + 1)
+    cand = np.arange(L)
+    order = np.lexsort((cand, -S[:L]))  # primary: -score, secondary: block id
+    chosen = np.concatenate([cand[order[: m - 1]], [L]]).astype(np.int64)
+    chosen.sort()
+    out = np.full(k, -1, dtype=np.int64)
+    out[:m] = chosen
+    return out
+
+
+def selected_tokens(sel: np.ndarray, t: int, B: int) -> np.ndarray:
+    """Key positions covered by the selected blocks, clipped to j <= t."""
+    toks = []
+    for b in sel:
+        if b < 0:
+            continue
+        toks.append(np.arange(b * B, min((b + 1) * B, t + 1)))
+    return np.concatenate(toks) if toks else np.zeros(0, dtype=np.int64)
+
+
+def attention_row(q_t: np.ndarray, K: np.ndarray, V: np.ndarray, toks: np.ndarray,
+                  scale: float):
+    """Exact softmax attention of query rows q_t [R, d] over the gathered
+    keys/values K[toks], V[toks] ([n, d]) [HA 方法: standard scaled dot-product
+    attention over the Key/Value vectors gathered from the selected blocks].
+    Returns (o [R, d], lse [R]) with lse = ln sum_j exp(x_j)."""
+    Kg, Vg = K[toks], V[toks]
+    x = scale * (q_t @ Kg.T)                      # [R, n]
+    mx = x.max(axis=1, keepdims=True)
+    w = np.exp(x - mx)
+    den = w.sum(axis=1, keepdims=True)
+    o = (w @ Vg) / den
+    lse = (mx + np.log(den))[:, 0]
+    return o, lse
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def prefill(q, k, v, idx_q, idx_k, B: int, topk: int, scale: float | None = None,
+            rows=None, dense: bool = False, block_idx=None):
+    """MSA prefill over a batch.
+
+    q [b,T,Hq,d], k/v [b,T,G,d], idx_q [b,T,G,di], idx_k [b,T,di] (any float
+    type; converted to float64).  rows: iterable of (batch, t) to compute, or
+    None for all.  dense: select every visible block (index branch skipped).
+    block_idx: optional given selection [b,T,G,topk] (main branch only).
+
+    Returns dict with 'out' {(s,t): [Hq,d]}, 'lse' {(s,t): [Hq]},
+    'block_idx' {(s,t): [G,topk]} (None in dense mode) for the rows computed,
+    plus 'S' {(s,t): list of per-group block-max arrays}.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    idx_q, idx_k = _f64(idx_q), _f64(idx_k)
+    nbatch, T, Hq, d = q.shape
+    G = k.shape[2]
+    R = Hq // G
+    if scale is None:
+        scale = default_scale(d)
+    if rows is None:
+        rows = [(s, t) for s in range(nbatch) for t in range(T)]
+    given = None if block_idx is None else np.asarray(_f64(block_idx), dtype=np.int64)
+    res = {"out": {}, "lse": {}, "block_idx": {} if not dense else None, "S": {}}
+    for s, t in rows:
+        o_t = np.empty((Hq, d))
+        lse_t = np.empty(Hq)
+        sel_t = np.full((G, topk), -1, dtype=np.int64)
+        S_t = []
+        for g in range(G):
+            if dense:
+                sel = np.arange(local_block(t, B) + 1)
+            elif given is not None:
+                sel = given[s, t, g]
+            else:
+                sc = index_scores(idx_q[s, t, g], idx_k[s], t)
+                Sg = block_max(sc, t, B)
+                S_t.append(Sg)
+                sel = select_blocks(Sg, t, B, topk)
+            if not dense:
+                sel_t[g] = sel
+            toks = selected_tokens(sel, t, B)
+            heads = slice(g * R, (g + 1) * R)
+            o, lse = attention_row(q[s, t, heads], k[s, :, g], v[s, :, g], toks, scale)
+            o_t[heads] = o
+            lse_t[heads] = lse
+        res["out"][(s, t)] = o_t
+        res["lse"][(s, t)] = lse_t
+        if not dense:
+            res["block_idx"][(s, t)] = sel_t
+        res["S"][(s, t)] = S_t
+    return res
+
+
+def decode(q, k_cache, v_cache, idx_q, idx_k_cache, cache_lens, B: int, topk: int,
+           scale: float | None = None, dense: bool = False, block_idx=None):
+    """One decode step per sequence: the new token sits at position len-1 of
+    its cache and runs the same index branch and main branch against cache
+    positions 0..len-1 [HA 方法; the pages' decode speed-up at 1M context].
+
+    q [b,Hq,d], k/v_cache [b,L,G,d], idx_q [b,G,di], idx_k_cache [b,L,di],
+    cache_lens [b].  Returns dict with 'out' [b,Hq,d], 'lse' [b,Hq],
+    'block_idx' [b,G,topk] (None in dense mode), 'S' list per sequence."""
+    q, k_cache, v_cache = _f64(q), _f64(k_cache), _f64(v_cache)
+    idx_q, idx_k_cache = _f64(idx_q), _f64(idx_k_cache)
+    lens = [int(x) for x in (cache_lens.tolist() if hasattr(cache_lens, "tolist") else cache_lens)]
+    nbatch, Hq, d = q.shape
+    G = k_cache.shape[2]
+    R = Hq // G
+    if scale is None:
+        scale = default_scale(d)
+    given = None if block_idx is None else np.asarray(_f64(block_idx), dtype=np.int64)
+    out = np.empty((nbatch, Hq, d))
+    lse = np.empty((nbatch, Hq))
+    sel_all = np.full((nbatch, G, topk), -1, dtype=np.int64)
+    S_all = []
+    for s in range(nbatch):
+        t = lens[s] - 1
+        S_s = []
+        for g in range(G):
+            if dense:
+                sel = np.arange(local_block(t, B) + 1)
+            elif given is not None:
+                sel = given[s, g]
+            else:
+                sc = index_scores(idx_q[s, g], idx_k_cache[s], t)
+                Sg = block_max(sc, t, B)
+                S_s.append(Sg)
+                sel = select_blocks(Sg, t, B, topk)
+                sel_all[s, g] = sel
+            toks = selected_tokens(sel, t, B)
+            heads = slice(g * R, (g + 1) * R)
+            o, l = attention_row(q[s, heads], k_cache[s, :, g], v_cache[s, :, g], toks, scale)
+            out[s, heads] = o
+            lse[s, heads] = l
+        S_all.append(S_s)
+    return {"out": out, "lse": lse, "block_idx": None if dense else sel_all, "S": S_all}
+
+
+def near_tie(S_g: np.ndarray, t: int, B: int, k: int, rel: float = 1e-3) -> bool:
+    """True when the selection of this (token, group) row is decided by a
+    near-tie: the last selected non-local candidate and the first unselected
+    one (in the oracle's score order) differ by less than rel relative."""
+    L = local_block(t, B)
+    m = min(k, L + 1)
+    if m - 1 == 0 or m - 1 >= L:
+        return False          # nothing chosen among candidates, or all of them
+    cand = np.arange(L)
+    order = np.lexsort((cand, -S_g[:L]))
+    sc = S_g[:L][order]
+    a, b = sc[m - 2], sc[m - 1]
+    return abs(a - b) < rel * max(abs(a), abs(b), 1e-30)

@@ -1,0 +1,334 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a library
+routine on a case that reduces to it (torch's scaled_dot_product_attention),
+closed-form selections, exhaustive enumeration by brute force, invariants,
+special inputs with known outputs, or a number the pages print.  Chosen so that
+a plausible slip in the oracle (a dropped term, a wrong sign or index, an
+off-by-one block edge, a transposed operand, a wrong head-to-group map) fails
+at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from block_sparse_long_02_amd import inputs
+from oracle import msa_oracle as orc
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _np(x):
+    return x.to(torch.float64).numpy()
+
+
+def _run_all(inp, B, k, **kw):
+    return orc.prefill(inp.q, inp.k, inp.v, inp.idx_q, inp.idx_k, B, k, **kw)
+
+
+def _stack(res, key, nbatch, T):
+    return np.stack([np.stack([res[key][(s, t)] for t in range(T)]) for s in range(nbatch)])
+
+
+# --------------------------------------------------------------------------
+# P1: k >= number of visible blocks  =>  dense causal GQA attention.
+# The reference is torch's SDPA (causal, GQA, default 1/sqrt(d) scale) in fp64.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("T,Hq,G,d,B", [(96, 4, 2, 16, 16), (130, 6, 3, 8, 32), (64, 4, 1, 128, 32)])
+def test_dense_equivalence_sdpa(T, Hq, G, d, B):
+    inp = inputs.make_prefill(T, Hq, G, d, 8, batch=2, seed=3)
+    nb = (T + B - 1) // B
+    res = _run_all(inp, B, nb + 2)
+    out = _stack(res, "out", 2, T)
+    lse = _stack(res, "lse", 2, T)
+    q = inp.q.to(torch.float64).transpose(1, 2)
+    k = inp.k.to(torch.float64).transpose(1, 2)
+    v = inp.v.to(torch.float64).transpose(1, 2)
+    ref = F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=True)
+    np.testing.assert_allclose(out, _np(ref.transpose(1, 2)), rtol=0, atol=1e-12)
+    # lse through torch.logsumexp over causally masked logits
+    R = Hq // G
+    kk = k.repeat_interleave(R, dim=1)
+    x = (q @ kk.transpose(-1, -2)) / math.sqrt(d)
+    mask = torch.ones(T, T, dtype=torch.bool).tril()
+    x = x.masked_fill(~mask, float("-inf"))
+    ref_lse = torch.logsumexp(x, dim=-1).transpose(1, 2)
+    np.testing.assert_allclose(lse, _np(ref_lse), rtol=0, atol=1e-11)
+    # dense mode of the oracle is the same thing
+    resd = _run_all(inp, B, 1, dense=True)
+    np.testing.assert_allclose(_stack(resd, "out", 2, T), out, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P2: k = 1  =>  causal attention restricted to the aligned local block
+# (block-diagonal causal mask through SDPA's attn_mask).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("T,B", [(100, 16), (128, 32)])
+def test_k1_block_diagonal(T, B):
+    Hq, G, d = 4, 2, 16
+    inp = inputs.make_prefill(T, Hq, G, d, 8, seed=5)
+    res = _run_all(inp, B, 1)
+    out = _stack(res, "out", 1, T)
+    i = torch.arange(T)
+    mask = (i[:, None] >= i[None, :]) & ((i[:, None] // B) == (i[None, :] // B))
+    q = inp.q.to(torch.float64).transpose(1, 2)
+    k = inp.k.to(torch.float64).transpose(1, 2)
+    v = inp.v.to(torch.float64).transpose(1, 2)
+    ref = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, enable_gqa=True)
+    np.testing.assert_allclose(out, _np(ref.transpose(1, 2)), rtol=0, atol=1e-12)
+    for t in range(T):
+        for g in range(G):
+            sel = res["block_idx"][(0, t)][g]
+            assert sel[0] == t // B and sel.shape == (1,)
+
+
+# --------------------------------------------------------------------------
+# P3: exhaustive enumeration on tiny integer inputs.  Scores and block maxima
+# are recomputed here by explicit integer loops; the chosen set must be the
+# max-sum subset of size m-1 among blocks 0..L-1, ties resolved to the
+# lexicographically smallest ascending tuple (which equals "lower block index
+# wins" for a total order), plus the local block.
+# --------------------------------------------------------------------------
+def _brute_block_max(iq, ik, t, B):
+    L = t // B
+    out = []
+    for b in range(L + 1):
+        best = None
+        for j in range(b * B, min((b + 1) * B, t + 1)):
+            s = 0
+            for c in range(len(iq)):
+                s += int(iq[c]) * int(ik[j][c])
+            best = s if best is None or s > best else best
+        out.append(best)
+    return out
+
+
+@pytest.mark.parametrize("k", [1, 2, 4, 6])
+def test_exhaustive_enumeration(k):
+    T, B, G, di = 160, 10, 2, 6
+    inp = inputs.make_prefill(T, 2 * G, G, 8, di, seed=11 + k, idx_mode="integer")
+    res = _run_all(inp, B, k)
+    iq = inp.idx_q.to(torch.int64).numpy()
+    ik = inp.idx_k.to(torch.int64).numpy()
+    n_ties = 0
+    for t in range(0, T, 3):
+        for g in range(G):
+            S = _brute_block_max(iq[0, t, g], ik[0], t, B)
+            L = t // B
+            m = min(k, L + 1)
+            best, best_sum = None, None
+            for comb in itertools.combinations(range(L), m - 1):  # lexicographic order
+                sm = sum(S[b] for b in comb)
+                if best_sum is None or sm > best_sum:
+                    best, best_sum = comb, sm
+            expect = sorted(list(best) + [L]) + [-1] * (k - m)
+            got = res["block_idx"][(0, t)][g].tolist()
+            assert got == expect, (t, g, S, got, expect)
+            if L > m - 1 >= 1 and sorted(S[:L], reverse=True)[m - 2] == sorted(S[:L], reverse=True)[m - 1]:
+                n_ties += 1
+            np.testing.assert_array_equal(res["S"][(0, t)][g], np.array(S, dtype=np.float64))
+    assert k == 1 or n_ties > 0  # the integer inputs do exercise the tie rule
+
+
+# --------------------------------------------------------------------------
+# Closed-form selections: idx_q = e0 and idx_k[j] = f(j) e0 make s[t,g,j] = f(j).
+# --------------------------------------------------------------------------
+def _closed_form_inputs(T, f, G=2, di=4):
+    iq = torch.zeros(1, T, G, di)
+    iq[..., 0] = 1.0
+    ik = torch.zeros(1, T, di)
+    ik[0, :, 0] = torch.tensor([float(f(j)) for j in range(T)])
+    base = inputs.make_prefill(T, G, G, 8, di, seed=1)
+    return inputs.PrefillInputs(base.q, base.k, base.v, iq.to(torch.bfloat16), ik.to(torch.bfloat16))
+
+
+def test_closed_form_selection():
+    T, B, k = 200, 16, 5
+    for f, rule in [
+        (lambda j: j, "latest"),        # ascending scores: highest blocks below L
+        (lambda j: -j, "earliest"),     # descending scores: blocks 0..m-2
+        (lambda j: 0, "earliest"),      # all equal: lower index wins
+    ]:
+        inp = _closed_form_inputs(T, f)
+        res = _run_all(inp, B, k)
+        for t in range(T):
+            L = t // B
+            m = min(k, L + 1)
+            if rule == "latest":
+                exp = list(range(L - (m - 1), L + 1))
+            else:
+                exp = list(range(m - 1)) + [L]
+            exp = exp + [-1] * (k - m)
+            for g in range(2):
+                assert res["block_idx"][(0, t)][g].tolist() == exp, (rule, t)
+
+
+@pytest.mark.parametrize("pos", ["first", "last"])
+def test_block_edges(pos):
+    # A single spike at the first / last token of block b must select block b
+    # (an off-by-one block partition would credit a neighbour instead).
+    T, B, k = 160, 16, 2
+    for b in range(0, 8):
+        j0 = b * B if pos == "first" else b * B + B - 1
+        inp = _closed_form_inputs(T, lambda j: 5 if j == j0 else 0)
+        res = _run_all(inp, B, k, rows=[(0, T - 1)])
+        sel = res["block_idx"][(0, T - 1)][0].tolist()
+        assert sel == [b, (T - 1) // B], (pos, b, sel)
+
+
+# --------------------------------------------------------------------------
+# P4 invariants and P5 nesting on Gaussian and integer inputs.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["gaussian", "integer"])
+def test_invariants_and_nesting(mode):
+    T, B, G = 300, 16, 3
+    inp = inputs.make_prefill(T, G, G, 8, 8, seed=21, idx_mode=mode)
+    nb = (T + B - 1) // B
+    sels = {}
+    for k in range(1, nb + 2):
+        res = _run_all(inp, B, k, rows=[(0, t) for t in range(0, T, 7)])
+        sels[k] = res["block_idx"]
+        for (s, t), sel in res["block_idx"].items():
+            L = t // B
+            m = min(k, L + 1)
+            for g in range(G):
+                row = sel[g]
+                assert row.shape == (k,)
+                live = row[:m]
+                assert L in live
+                assert (row[m:] == -1).all()
+                assert (live >= 0).all() and (live <= L).all()
+                assert (np.diff(live) > 0).all()
+    for k in range(1, nb + 1):
+        for key in sels[k]:
+            for g in range(G):
+                a = set(sels[k][key][g].tolist()) - {-1}
+                b = set(sels[k + 1][key][g].tolist()) - {-1}
+                assert a <= b, (k, key, g)
+
+
+# --------------------------------------------------------------------------
+# P6 special inputs.
+# --------------------------------------------------------------------------
+def test_zero_query_gives_mean_of_selected_values():
+    T, Hq, G, d, B, k = 150, 6, 3, 16, 16, 3
+    inp = inputs.make_prefill(T, Hq, G, d, 8, seed=7)
+    inp.q.zero_()
+    res = _run_all(inp, B, k)
+    v = inp.v.to(torch.float64).numpy()
+    R = Hq // G
+    for t in range(T):
+        for g in range(G):
+            sel = res["block_idx"][(0, t)][g]
+            acc = np.zeros(d)
+            n = 0
+            for b in sel:
+                if b < 0:
+                    continue
+                for j in range(b * B, b * B + B):
+                    if j <= t:
+                        acc += v[0, j, g]
+                        n += 1
+            for r in range(R):
+                np.testing.assert_allclose(res["out"][(0, t)][g * R + r], acc / n, rtol=0, atol=1e-12)
+                # lse of all-zero logits is ln(n)
+                assert abs(res["lse"][(0, t)][g * R + r] - math.log(n)) < 1e-12
+
+
+def test_constant_values_per_group_pin_head_to_group_map():
+    T, Hq, G, d, B, k = 90, 8, 4, 16, 16, 2
+    inp = inputs.make_prefill(T, Hq, G, d, 8, seed=9)
+    consts = torch.tensor([1.5, -2.0, 0.25, 3.0])
+    inp.v.copy_(consts.view(1, 1, G, 1).expand_as(inp.v).to(torch.bfloat16))
+    res = _run_all(inp, B, k)
+    R = Hq // G
+    for t in range(T):
+        for h in range(Hq):
+            np.testing.assert_allclose(res["out"][(0, t)][h], float(consts[h // R]), rtol=0, atol=1e-12)
+
+
+def test_output_in_convex_hull_of_selected_values():
+    T, Hq, G, d, B, k = 128, 4, 2, 16, 16, 3
+    inp = inputs.make_prefill(T, Hq, G, d, 8, seed=13)
+    res = _run_all(inp, B, k)
+    v = inp.v.to(torch.float64).numpy()
+    R = Hq // G
+    for t in range(T):
+        for g in range(G):
+            toks = orc.selected_tokens(res["block_idx"][(0, t)][g], t, B)
+            lo, hi = v[0, toks, g].min(0), v[0, toks, g].max(0)
+            for r in range(R):
+                o = res["out"][(0, t)][g * R + r]
+                assert (o >= lo - 1e-12).all() and (o <= hi + 1e-12).all()
+
+
+# --------------------------------------------------------------------------
+# P7 decode equals the prefill row.
+# --------------------------------------------------------------------------
+def test_decode_equals_prefill_row():
+    T, Hq, G, d, di, B, k = 200, 4, 2, 16, 8, 16, 4
+    inp = inputs.make_prefill(T, Hq, G, d, di, batch=3, seed=17)
+    lens = [200, 57, 16]
+    # caches hold the full tensors; decode position = len-1
+    q_dec = torch.stack([inp.q[s, lens[s] - 1] for s in range(3)])
+    iq_dec = torch.stack([inp.idx_q[s, lens[s] - 1] for s in range(3)])
+    dres = orc.decode(q_dec, inp.k, inp.v, iq_dec, inp.idx_k, lens, B, k)
+    pres = _run_all(inp, B, k, rows=[(s, lens[s] - 1) for s in range(3)])
+    for s in range(3):
+        t = lens[s] - 1
+        np.testing.assert_array_equal(dres["block_idx"][s], pres["block_idx"][(s, t)])
+        np.testing.assert_allclose(dres["out"][s], pres["out"][(s, t)], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dres["lse"][s], pres["lse"][(s, t)], rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# P8 needle invariant (separable preset): every row's non-local selections
+# contain min(k-1, visible non-local needles) needle blocks.
+# --------------------------------------------------------------------------
+def test_needles_are_found():
+    T, G, di, B, k = 4096, 2, 128, 32, 6
+    inp = inputs.make_prefill(T, G, G, 8, di, seed=23, block_size=B, needles=10)
+    needles = set(inp.meta["needle_blocks"].tolist())
+    rows = [(0, t) for t in range(0, T, 37)] + [(0, T - 1)]
+    res = _run_all(inp, B, k, rows=rows)
+    hit_rows = 0
+    for (s, t), sel in res["block_idx"].items():
+        L = t // B
+        vis = len([b for b in needles if b < L])
+        for g in range(G):
+            nonlocal_sel = [b for b in sel[g].tolist() if 0 <= b < L]
+            got = len([b for b in nonlocal_sel if b in needles])
+            assert got == min(min(k, L + 1) - 1, vis), (t, g)
+            hit_rows += vis > 0
+    assert hit_rows > 0
+
+
+# --------------------------------------------------------------------------
+# The pages' printed budget: 16 blocks of 128 tokens = 2048 attended tokens.
+# --------------------------------------------------------------------------
+def test_attention_budget_golden():
+    with open(os.path.join(HERE, "golden", "attention_budget.json")) as f:
+        gold = json.load(f)
+    B, k = gold["block_size"], gold["topk"]
+    for L in [k - 1, k, 40]:
+        t_last = (L + 1) * B - 1
+        sel = orc.select_blocks(np.random.default_rng(0).standard_normal(L + 1), t_last, B, k)
+        assert len(orc.selected_tokens(sel, t_last, B)) == gold["attended_tokens"]
+        t_first = L * B
+        sel = orc.select_blocks(np.random.default_rng(1).standard_normal(L + 1), t_first, B, k)
+        assert len(orc.selected_tokens(sel, t_first, B)) == (k - 1) * B + 1
+
+
+def test_near_tie_helper():
+    B, k = 4, 3
+    t = 5 * B  # L = 5, candidates 0..4, m-1 = 2 chosen
+    S = np.array([10.0, 9.0, 8.0, 7.0, 1.0, 0.0])
+    assert not orc.near_tie(S, t, B, k)
+    S2 = np.array([10.0, 8.0, 8.0 * (1 - 1e-4), 7.0, 1.0, 0.0])
+    assert orc.near_tie(S2, t, B, k)
