@@ -1,0 +1,410 @@
+// C ABI of libmsa (declared in include/msa.h): host-side validation,
+// workspace planning, the query-chunk loop and stream-ordered launches.
+// Every argument check happens here, before any work is enqueued; no C++
+// exception crosses the ABI.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "msa.h"
+#include "msa_internal.h"
+
+namespace {
+
+thread_local char g_hip_err[256] = "";
+
+constexpr size_t kAlignWs = 256;
+// Default upper bound of the prefill workspace (per call).  Query chunks are
+// sized so that the block-score table and the block-major partials of one
+// chunk fit in it; MI355X has 288 GB of HBM per GPU.
+constexpr size_t kDefaultPrefillBudget = 32ull << 30;
+constexpr long kMaxInt32 = 2147483647L;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Layout {
+  size_t total = 0;
+  size_t add(size_t bytes) {
+    const size_t off = total;
+    total += round_up(bytes, kAlignWs);
+    return off;
+  }
+};
+
+int check_dims(const msa_dims* d, bool decode) {
+  if (d == nullptr) return MSA_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->seqlen < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->topk < 1)
+    return MSA_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return MSA_ERR_INVALID_ARG;
+  if (d->reserved != 0 || d->query_chunk < 0) return MSA_ERR_INVALID_ARG;
+  if (!isfinite(d->softmax_scale)) return MSA_ERR_INVALID_ARG;
+  const uint32_t known = MSA_DENSE | MSA_GIVEN_INDICES;
+  if ((d->flags & ~known) != 0) return MSA_ERR_INVALID_ARG;
+  if ((d->flags & MSA_DENSE) && (d->flags & MSA_GIVEN_INDICES)) return MSA_ERR_INVALID_ARG;
+  if (d->head_dim != 128) return MSA_ERR_UNSUPPORTED;
+  if (d->index_dim != 64 && d->index_dim != 128) return MSA_ERR_UNSUPPORTED;
+  if (d->block_size != 32 && d->block_size != 64 && d->block_size != 128) return MSA_ERR_UNSUPPORTED;
+  const int R = d->num_q_heads / d->num_kv_heads;
+  if (R > (decode ? 16 : msa::kAttnRows)) return MSA_ERR_UNSUPPORTED;
+  if (!decode && d->query_chunk > 0 && d->query_chunk % d->block_size != 0) return MSA_ERR_INVALID_ARG;
+  return MSA_OK;
+}
+
+float log2_scale(const msa_dims* d) {
+  const float sc = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
+  return sc * 1.4426950408889634f;
+}
+
+// ---------------------------------------------------------------------------
+// Prefill / index_topk plan
+// ---------------------------------------------------------------------------
+struct PrefillPlan {
+  int nb = 0, KS = 0, R = 0, mt = 0;
+  int Tc = 0, nchunks = 0;
+  int s_stride_max = 0;
+  long max_work = 0;
+  bool with_scores = false, with_main = false;
+  size_t off_S = 0, off_bidx = 0, off_cnt = 0, off_offs = 0, off_epos = 0, off_entries = 0,
+         off_work = 0, off_nwork = 0, off_pO = 0, off_pS = 0;
+  size_t total = 0;
+};
+
+size_t per_token_bytes(const msa_dims* d, const PrefillPlan& p) {
+  const size_t G = (size_t)d->num_kv_heads;
+  size_t b = 0;
+  if (p.with_scores) b += G * (size_t)p.s_stride_max * 4 + G * (size_t)d->topk * 4;
+  if (p.with_main) b += G * (size_t)p.KS * (4 + 4 + (size_t)p.R * (128 * 4 + 4));
+  return b;
+}
+
+int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
+  int st = check_dims(d, false);
+  if (st != MSA_OK) return st;
+  if (index_only && d->flags != 0) return MSA_ERR_INVALID_ARG;
+  const int T = d->seqlen, B = d->block_size, G = d->num_kv_heads;
+  p->nb = (T + B - 1) / B;
+  p->KS = d->topk < p->nb ? d->topk : p->nb;
+  p->R = d->num_q_heads / G;
+  p->mt = msa::kAttnRows / p->R;
+  p->with_scores = index_only || (d->flags == 0);
+  p->with_main = !index_only && !(d->flags & MSA_DENSE);
+  const int Lmax = (T - 1) / B;
+  p->s_stride_max = (int)round_up((size_t)(Lmax > 1 ? Lmax : 1), 4);
+  if (!p->with_scores && !p->with_main) {  // dense prefill needs no workspace
+    p->Tc = T;
+    p->nchunks = 1;
+    p->total = 0;
+    return MSA_OK;
+  }
+  const size_t ptb = per_token_bytes(d, *p) * (size_t)d->batch;
+  long tc_max;
+  if (d->query_chunk > 0) {
+    tc_max = d->query_chunk;
+  } else {
+    tc_max = (long)(kDefaultPrefillBudget / (ptb ? ptb : 1));
+    tc_max = tc_max / B * B;
+    if (tc_max < B) tc_max = B;
+  }
+  // keep per-chunk entry counts and indices inside int32
+  const long per_tok_entries = (long)d->batch * G * p->KS;
+  if (p->with_main) {
+    const long lim = (kMaxInt32 / 2) / (per_tok_entries ? per_tok_entries : 1);
+    if (tc_max > lim) tc_max = lim / B * B;
+    if (tc_max < B) return MSA_ERR_UNSUPPORTED;
+  }
+  if (tc_max >= T) {
+    p->Tc = T;
+    p->nchunks = 1;
+  } else {
+    const long nch = (T + tc_max - 1) / tc_max;
+    long tc = (T + nch - 1) / nch;
+    tc = (long)round_up((size_t)tc, (size_t)B);
+    if (tc > tc_max) tc = tc_max;
+    p->Tc = (int)tc;
+    p->nchunks = (int)((T + tc - 1) / tc);
+  }
+  Layout L;
+  const size_t nb_ = (size_t)d->batch, Tc = (size_t)p->Tc, G_ = (size_t)G;
+  if (p->with_scores) {
+    p->off_S = L.add(nb_ * Tc * G_ * (size_t)p->s_stride_max * 4);
+    p->off_bidx = L.add(nb_ * Tc * G_ * (size_t)d->topk * 4);
+  }
+  if (p->with_main) {
+    const size_t nlists = nb_ * G_ * (size_t)p->nb;
+    const size_t emax = nb_ * Tc * G_ * (size_t)p->KS;
+    p->max_work = (long)((emax + p->mt - 1) / p->mt + nlists);
+    p->off_cnt = L.add(nlists * 4);
+    p->off_offs = L.add(nlists * 4);
+    p->off_epos = L.add(emax * 4);
+    p->off_entries = L.add(emax * 4);
+    p->off_work = L.add((size_t)p->max_work * 8);
+    p->off_nwork = L.add(4);
+    p->off_pO = L.add(emax * (size_t)p->R * 128 * 4);
+    p->off_pS = L.add(emax * (size_t)p->R * 4);
+  }
+  p->total = L.total;
+  return MSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Decode plan
+// ---------------------------------------------------------------------------
+struct DecodePlan {
+  int nbmax = 0, R = 0, s_stride = 0, nsplit = 0, bps = 0;
+  bool with_scores = false;
+  size_t off_S = 0, off_bidx = 0, off_pO = 0, off_pS = 0, total = 0;
+};
+
+int make_decode_plan(const msa_dims* d, DecodePlan* p) {
+  int st = check_dims(d, true);
+  if (st != MSA_OK) return st;
+  const int B = d->block_size, G = d->num_kv_heads;
+  p->nbmax = (d->seqlen + B - 1) / B;
+  p->R = d->num_q_heads / G;
+  p->s_stride = (int)round_up((size_t)p->nbmax, 4);
+  p->with_scores = (d->flags == 0);
+  if (d->flags & MSA_DENSE) {
+    p->bps = 2048 / B;  // 2048 keys per work item
+    p->nsplit = (p->nbmax + p->bps - 1) / p->bps;
+  } else if (d->flags & MSA_GIVEN_INDICES) {
+    p->nsplit = d->topk;
+  } else {
+    p->nsplit = d->topk < p->nbmax ? d->topk : p->nbmax;
+  }
+  Layout L;
+  const size_t nb_ = (size_t)d->batch, G_ = (size_t)G;
+  if (p->with_scores) {
+    p->off_S = L.add(nb_ * G_ * (size_t)p->s_stride * 4);
+    p->off_bidx = L.add(nb_ * G_ * (size_t)d->topk * 4);
+  }
+  p->off_pO = L.add(nb_ * G_ * (size_t)p->nsplit * p->R * 128 * 4);
+  p->off_pS = L.add(nb_ * G_ * (size_t)p->nsplit * p->R * 4);
+  p->total = L.total;
+  return MSA_OK;
+}
+
+bool misaligned(const void* ptr, size_t a) { return ptr != nullptr && ((uintptr_t)ptr % a) != 0; }
+
+int hip_fail(hipError_t e) {
+  snprintf(g_hip_err, sizeof(g_hip_err), "%s (%d)", hipGetErrorString(e), (int)e);
+  return MSA_ERR_HIP;
+}
+
+int check_workspace(size_t need, const void* ws, size_t ws_bytes) {
+  if (need == 0) return MSA_OK;
+  if (ws == nullptr) return MSA_ERR_INVALID_ARG;
+  if (misaligned(ws, kAlignWs)) return MSA_ERR_ALIGNMENT;
+  if (ws_bytes < need) return MSA_ERR_WORKSPACE;
+  return MSA_OK;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// Index Branch for one chunk: scores + top-k into (bidx, rows, t_off).
+hipError_t run_index_chunk(const msa_dims* d, const PrefillPlan& p, const void* idx_q,
+                           const void* idx_k, void* ws, int t0, int tc, int32_t* bidx, long bidx_rows,
+                           int t_off, hipStream_t st) {
+  const int B = d->block_size;
+  const int Lc = (t0 + tc - 1) / B;
+  const int s_stride = (int)round_up((size_t)(Lc > 1 ? Lc : 1), 4);
+  float* S = at<float>(ws, p.off_S);
+  hipError_t e = msa::launch_index_blockmax_prefill(
+      static_cast<const uint16_t*>(idx_q), static_cast<const uint16_t*>(idx_k), S, d->batch,
+      d->seqlen, d->num_kv_heads, d->index_dim, B, t0, tc, s_stride, st);
+  if (e != hipSuccess) return e;
+  return msa::launch_topk_prefill(S, s_stride, bidx, bidx_rows, t_off, d->batch, d->num_kv_heads, B,
+                                  d->topk, t0, tc, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int msa_abi_version(void) { return 1; }
+
+const char* msa_status_string(int status) {
+  switch (status) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG: null pointer, non-positive size, Hq % G != 0 or bad flags";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED: head_dim, index_dim, block_size or heads per group not supported";
+    case MSA_ERR_ALIGNMENT: return "MSA_ERR_ALIGNMENT: tensor or workspace pointer misaligned";
+    case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE: workspace smaller than msa_workspace_bytes()";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP: a HIP launch failed (see msa_last_hip_error)";
+    default: return "unknown msa status";
+  }
+}
+
+const char* msa_last_hip_error(void) { return g_hip_err; }
+
+size_t msa_workspace_bytes(int op, const msa_dims* dims) {
+  if (op == MSA_OP_INDEX_TOPK || op == MSA_OP_PREFILL) {
+    PrefillPlan p;
+    if (make_prefill_plan(dims, op == MSA_OP_INDEX_TOPK, &p) != MSA_OK) return (size_t)-1;
+    return p.total;
+  }
+  if (op == MSA_OP_DECODE) {
+    DecodePlan p;
+    if (make_decode_plan(dims, &p) != MSA_OK) return (size_t)-1;
+    return p.total;
+  }
+  return (size_t)-1;
+}
+
+int msa_index_topk(const msa_dims* dims, const void* idx_q, const void* idx_k, int32_t* block_idx,
+                   void* workspace, size_t workspace_bytes, void* hip_stream) {
+  PrefillPlan p;
+  int st = make_prefill_plan(dims, true, &p);
+  if (st != MSA_OK) return st;
+  if (idx_q == nullptr || idx_k == nullptr || block_idx == nullptr) return MSA_ERR_INVALID_ARG;
+  if (misaligned(idx_q, 16) || misaligned(idx_k, 16) || misaligned(block_idx, 4)) return MSA_ERR_ALIGNMENT;
+  if ((st = check_workspace(p.total, workspace, workspace_bytes)) != MSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  for (int c = 0; c < p.nchunks; ++c) {
+    const int t0 = c * p.Tc;
+    const int tc = (dims->seqlen - t0) < p.Tc ? dims->seqlen - t0 : p.Tc;
+    hipError_t e = run_index_chunk(dims, p, idx_q, idx_k, workspace, t0, tc, block_idx, dims->seqlen, 0, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return MSA_OK;
+}
+
+int msa_prefill(const msa_dims* dims, const void* q, const void* k, const void* v, const void* idx_q,
+                const void* idx_k, void* out, float* lse, int32_t* block_idx, void* workspace,
+                size_t workspace_bytes, void* hip_stream) {
+  PrefillPlan p;
+  int st = make_prefill_plan(dims, false, &p);
+  if (st != MSA_OK) return st;
+  const bool dense = dims->flags & MSA_DENSE, given = dims->flags & MSA_GIVEN_INDICES;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return MSA_ERR_INVALID_ARG;
+  if (!dense && !given && (idx_q == nullptr || idx_k == nullptr)) return MSA_ERR_INVALID_ARG;
+  if (dense && block_idx != nullptr) return MSA_ERR_INVALID_ARG;
+  if (given && block_idx == nullptr) return MSA_ERR_INVALID_ARG;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
+      misaligned(idx_q, 16) || misaligned(idx_k, 16) || misaligned(lse, 4) || misaligned(block_idx, 4))
+    return MSA_ERR_ALIGNMENT;
+  if ((st = check_workspace(p.total, workspace, workspace_bytes)) != MSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+
+  msa::PrefillMainArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.batch = dims->batch;
+  a.T = dims->seqlen;
+  a.Hq = dims->num_q_heads;
+  a.G = dims->num_kv_heads;
+  a.B = dims->block_size;
+  a.topk = dims->topk;
+  a.KS = p.KS;
+  a.nbl = p.nb;
+  a.scale_log2 = log2_scale(dims);
+
+  if (dense) {
+    a.t0 = 0;
+    a.tc = dims->seqlen;
+    hipError_t e = msa::launch_prefill_main_dense(a, s);
+    return e == hipSuccess ? MSA_OK : hip_fail(e);
+  }
+  a.cnt = at<int32_t>(workspace, p.off_cnt);
+  a.offs = at<int32_t>(workspace, p.off_offs);
+  a.epos = at<int32_t>(workspace, p.off_epos);
+  a.entries = at<int32_t>(workspace, p.off_entries);
+  a.work = at<int2>(workspace, p.off_work);
+  a.n_work = at<int32_t>(workspace, p.off_nwork);
+  a.pO = at<float>(workspace, p.off_pO);
+  a.pS = at<float>(workspace, p.off_pS);
+
+  for (int c = 0; c < p.nchunks; ++c) {
+    const int t0 = c * p.Tc;
+    const int tc = (dims->seqlen - t0) < p.Tc ? dims->seqlen - t0 : p.Tc;
+    int32_t* bidx;
+    long rows;
+    int t_off;
+    if (block_idx != nullptr) {
+      bidx = block_idx;
+      rows = dims->seqlen;
+      t_off = 0;
+    } else {
+      bidx = at<int32_t>(workspace, p.off_bidx);
+      rows = p.Tc;
+      t_off = t0;
+    }
+    if (!given) {
+      hipError_t e = run_index_chunk(dims, p, idx_q, idx_k, workspace, t0, tc, bidx, rows, t_off, s);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    a.bidx = bidx;
+    a.bidx_rows = rows;
+    a.bidx_t_off = t_off;
+    a.t0 = t0;
+    a.tc = tc;
+    const long emax = (long)dims->batch * tc * dims->num_kv_heads * p.KS;
+    a.max_work = (emax + p.mt - 1) / p.mt + (long)dims->batch * dims->num_kv_heads * p.nb;
+    hipError_t e = msa::launch_prefill_main_sparse(a, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return MSA_OK;
+}
+
+int msa_decode(const msa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+               const void* idx_q, const void* idx_k_cache, const int32_t* cache_lens, void* out,
+               float* lse, int32_t* block_idx, void* workspace, size_t workspace_bytes,
+               void* hip_stream) {
+  DecodePlan p;
+  int st = make_decode_plan(dims, &p);
+  if (st != MSA_OK) return st;
+  const bool dense = dims->flags & MSA_DENSE, given = dims->flags & MSA_GIVEN_INDICES;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || cache_lens == nullptr || out == nullptr)
+    return MSA_ERR_INVALID_ARG;
+  if (!dense && !given && (idx_q == nullptr || idx_k_cache == nullptr)) return MSA_ERR_INVALID_ARG;
+  if (dense && block_idx != nullptr) return MSA_ERR_INVALID_ARG;
+  if (given && block_idx == nullptr) return MSA_ERR_INVALID_ARG;
+  if (misaligned(q, 16) || misaligned(k_cache, 16) || misaligned(v_cache, 16) || misaligned(out, 16) ||
+      misaligned(idx_q, 16) || misaligned(idx_k_cache, 16) || misaligned(cache_lens, 4) ||
+      misaligned(lse, 4) || misaligned(block_idx, 4))
+    return MSA_ERR_ALIGNMENT;
+  if ((st = check_workspace(p.total, workspace, workspace_bytes)) != MSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+
+  int32_t* bidx = block_idx;
+  if (!dense && !given) {
+    if (bidx == nullptr) bidx = at<int32_t>(workspace, p.off_bidx);
+    float* S = at<float>(workspace, p.off_S);
+    hipError_t e = msa::launch_index_blockmax_decode(
+        static_cast<const uint16_t*>(idx_q), static_cast<const uint16_t*>(idx_k_cache), cache_lens, S,
+        dims->batch, dims->seqlen, dims->num_kv_heads, dims->index_dim, dims->block_size, p.s_stride, s);
+    if (e != hipSuccess) return hip_fail(e);
+    e = msa::launch_topk_decode(S, p.s_stride, bidx, cache_lens, dims->seqlen, dims->batch,
+                                dims->num_kv_heads, dims->block_size, dims->topk, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  msa::DecodeMainArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.lens = cache_lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.bidx = bidx;
+  a.batch = dims->batch;
+  a.Lmax = dims->seqlen;
+  a.Hq = dims->num_q_heads;
+  a.G = dims->num_kv_heads;
+  a.B = dims->block_size;
+  a.topk = dims->topk;
+  a.dense = dense;
+  a.nsplit = p.nsplit;
+  a.blocks_per_split = p.bps;
+  a.scale_log2 = log2_scale(dims);
+  a.pO = at<float>(workspace, p.off_pO);
+  a.pS = at<float>(workspace, p.off_pS);
+  hipError_t e = msa::launch_decode_main(a, s);
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
+}  // extern "C"

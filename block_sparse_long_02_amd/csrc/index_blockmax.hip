@@ -1,0 +1,169 @@
+// Index Branch of MSA on gfx950: fused index scoring + Block-Max pooling.
+//
+// Definition [hyper.ai paper page 2606.13392, 方法 (Method); Telegram review
+// quant_prune_distill post 751, "Метод"]: every (query token t, GQA group g)
+// row scores each visible key j with the raw dot product
+// idx_q[t,g] . idx_k[j] (one index-key head per layer, shared by all groups),
+// and the scores are max-pooled over aligned blocks of B keys.
+//
+// Only blocks 0..L(t)-1 are produced: the local block L(t) is always kept by
+// the selection and its score is never compared, and every earlier block is
+// fully visible (all its keys are < L(t)*B <= t), so no causal mask is needed.
+// The T x T score matrix is never stored: each 32x32 MFMA tile of scores is
+// max-reduced in registers and only one float per (row, block) leaves the CU.
+//
+// Prefill kernel layout: a workgroup owns 256 consecutive (t, g) rows (4 waves
+// x 2 column tiles of 32 rows, idx_q kept in registers as the MFMA B operand)
+// and streams idx_k one block at a time through double-buffered LDS as the A
+// operand, so each idx_k byte fetched feeds 256 rows (256 flop/B against L2).
+// Workgroups are issued longest-first (latest tokens have the most blocks).
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+namespace {
+
+constexpr int kIdxRows = 256;   // rows per workgroup
+
+template <int DI, int B>
+__global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
+    const bf16_t* __restrict__ idx_q, const bf16_t* __restrict__ idx_k, float* __restrict__ S,
+    int T, int G, int t0, int tc, int s_stride, int n_tiles) {
+  constexpr int KPAD = DI + 8;            // LDS row stride (bf16): +16 B against bank conflicts
+  constexpr int KSTEPS = DI / 16;         // MFMA k-steps per 32x32 tile
+  constexpr int CPR = DI / 8;             // 16-byte chunks per idx_k row
+  constexpr int NCH = B * CPR;            // 16-byte chunks per block
+  constexpr int MAXCH = (NCH + 255) / 256;  // staging chunks per thread
+  __shared__ __attribute__((aligned(16))) bf16_t kbuf[2][B * KPAD];
+
+  const int s = blockIdx.y;
+  const int tile = n_tiles - 1 - (int)blockIdx.x;
+  const int rows_chunk = tc * G;
+  const int r0 = tile * kIdxRows;
+  const int r_last = min(r0 + kIdxRows, rows_chunk) - 1;
+  const int nblk = (t0 + r_last / G) / B;  // candidate blocks needed by the last row
+  if (nblk <= 0) return;                   // uniform across the workgroup
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+
+  // B operands: idx_q rows of this wave's two 32-row column tiles.
+  bf16x8 qop[2][KSTEPS];
+  int row_idx[2];
+  bool row_ok[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = r0 + wave * 64 + nt * 32 + col;
+    row_idx[nt] = r;
+    row_ok[nt] = r < rows_chunk;
+    const bf16_t* qp = idx_q + ((size_t)s * T * G + (size_t)t0 * G + (size_t)r) * DI;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      qop[nt][ks] = row_ok[nt] ? load_bf16x8(qp + 16 * ks + 8 * half) : zero_bf16x8();
+  }
+
+  const bf16_t* kseq = idx_k + (size_t)s * T * DI;
+
+  // Staging: each thread moves up to MAXCH 16-byte chunks of a B x DI block.
+  u32x4 stg[MAXCH];
+#define MSA_IDX_GLOAD(BLK)                                                               \
+  {                                                                                      \
+    const u32x4* src_ = reinterpret_cast<const u32x4*>(kseq + (size_t)(BLK) * B * DI);   \
+    _Pragma("unroll") for (int i = 0; i < MAXCH; ++i) {                                  \
+      const int c_ = tid + i * 256;                                                      \
+      if (NCH % 256 == 0 || c_ < NCH) stg[i] = src_[c_];                                                   \
+    }                                                                                    \
+  }
+#define MSA_IDX_LSTORE(BUF)                                                              \
+  {                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < MAXCH; ++i) {                                  \
+      const int c_ = tid + i * 256;                                                      \
+      if (NCH % 256 == 0 || c_ < NCH)                                                    \
+        *reinterpret_cast<u32x4*>(&kbuf[BUF][(c_ / CPR) * KPAD + (c_ % CPR) * 8]) = stg[i]; \
+    }                                                                                    \
+  }
+
+  MSA_IDX_GLOAD(0);
+  MSA_IDX_LSTORE(0);
+  __syncthreads();
+
+  f32x4 sb[2];
+  sb[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  sb[1] = sb[0];
+  constexpr int ktiles = B / 32;
+
+  for (int b = 0; b < nblk; ++b) {
+    const int cur = b & 1;
+    if (b + 1 < nblk) MSA_IDX_GLOAD(b + 1);
+
+    float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < ktiles; ++kt) {
+      f32x16 acc0 = {}, acc1 = {};
+      const bf16_t* arow = &kbuf[cur][(kt * 32 + col) * KPAD + 8 * half];
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 16 * ks);
+        acc0 = mfma32x32x16(a, qop[0][ks], acc0);
+        acc1 = mfma32x32x16(a, qop[1][ks], acc1);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        mx0 = fmaxf(mx0, acc0[i]);
+        mx1 = fmaxf(mx1, acc1[i]);
+      }
+    }
+    mx0 = fmaxf(mx0, __shfl_xor(mx0, 32, kWave));
+    mx1 = fmaxf(mx1, __shfl_xor(mx1, 32, kWave));
+
+    const int slot = b & 3;
+    if (slot == 0) { sb[0][0] = mx0; sb[1][0] = mx1; }
+    else if (slot == 1) { sb[0][1] = mx0; sb[1][1] = mx1; }
+    else if (slot == 2) { sb[0][2] = mx0; sb[1][2] = mx1; }
+    else { sb[0][3] = mx0; sb[1][3] = mx1; }
+    if (slot == 3 || b == nblk - 1) {
+      if (half == 0) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          if (row_ok[nt]) {
+            float* dst = S + ((size_t)s * rows_chunk + (size_t)row_idx[nt]) * s_stride + (b & ~3);
+            *reinterpret_cast<f32x4*>(dst) = sb[nt];
+          }
+        }
+      }
+    }
+
+    if (b + 1 < nblk) MSA_IDX_LSTORE(cur ^ 1);
+    __syncthreads();
+  }
+#undef MSA_IDX_GLOAD
+#undef MSA_IDX_LSTORE
+}
+
+}  // namespace
+
+hipError_t launch_index_blockmax_prefill(const uint16_t* idx_q, const uint16_t* idx_k, float* S,
+                                         int batch, int T, int G, int di, int B, int t0, int tc,
+                                         int s_stride, hipStream_t st) {
+  const long rows = (long)tc * G;
+  const int n_tiles = (int)((rows + kIdxRows - 1) / kIdxRows);
+  dim3 grid(n_tiles, batch);
+#define MSA_IDX_LAUNCH(DI_, B_)                                                                   \
+  index_blockmax_prefill_kernel<DI_, B_><<<grid, 256, 0, st>>>(idx_q, idx_k, S, T, G, t0, tc,     \
+                                                               s_stride, n_tiles)
+  if (di == 128) {
+    if (B == 128) MSA_IDX_LAUNCH(128, 128);
+    else if (B == 64) MSA_IDX_LAUNCH(128, 64);
+    else MSA_IDX_LAUNCH(128, 32);
+  } else {
+    if (B == 128) MSA_IDX_LAUNCH(64, 128);
+    else if (B == 64) MSA_IDX_LAUNCH(64, 64);
+    else MSA_IDX_LAUNCH(64, 32);
+  }
+#undef MSA_IDX_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace msa

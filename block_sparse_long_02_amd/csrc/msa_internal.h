@@ -1,0 +1,84 @@
+// Host-side launchers of the libmsa kernels (internal; not part of the C ABI).
+// Every launcher enqueues on `st` and returns hipGetLastError() of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+// Tokens (query rows) handled by one workgroup of the attention kernels:
+// 4 waves x 32 rows = 128 (token, head) rows; tokens per tile = 128 / R.
+constexpr int kAttnRows = 128;
+
+hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t value, hipStream_t st);
+
+// ---- Index Branch, prefill: scores + Block-Max for query tokens [t0, t0+tc) ----
+// S is [batch][tc*G][s_stride] fp32; row (t-t0)*G+g holds blocks 0..L(t)-1.
+hipError_t launch_index_blockmax_prefill(const uint16_t* idx_q, const uint16_t* idx_k, float* S,
+                                         int batch, int T, int G, int di, int B, int t0, int tc,
+                                         int s_stride, hipStream_t st);
+
+// ---- Top-k with the forced local block ----
+// prefill rows: (s, t in [t0, t0+tc), g); output row address
+//   bidx + ((s*bidx_rows + (t - bidx_t_off))*G + g)*k
+hipError_t launch_topk_prefill(const float* S, int s_stride, int32_t* bidx, long bidx_rows,
+                               int bidx_t_off, int batch, int G, int B, int k, int t0, int tc,
+                               hipStream_t st);
+// decode rows: (s, g); query position cache_lens[s]-1; output bidx + (s*G+g)*k
+hipError_t launch_topk_decode(const float* S, int s_stride, int32_t* bidx, const int32_t* lens,
+                              int Lmax, int batch, int G, int B, int k, hipStream_t st);
+
+// ---- Main Branch, prefill ----
+struct PrefillMainArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  float* lse;             // may be null
+  const int32_t* bidx;    // selection rows (see launch_topk_prefill addressing)
+  long bidx_rows;
+  int bidx_t_off;
+  int batch, T, Hq, G, B, topk;
+  int t0, tc;             // query chunk
+  int KS;                 // partial slots per (token, group) = min(topk, nb)
+  int nbl;                // block lists per (batch, group) = nb
+  float scale_log2;       // softmax_scale * log2(e)
+  // workspace
+  int32_t* cnt;           // [batch*G*nbl]
+  int32_t* offs;          // [batch*G*nbl]
+  int32_t* epos;          // [batch*tc*G*KS]
+  int32_t* entries;       // [batch*tc*G*KS]
+  int2* work;             // [max_work]
+  int32_t* n_work;        // [1]
+  long max_work;
+  float* pO;              // [batch*tc*G*KS*R*128]
+  float* pS;              // [batch*tc*G*KS*R]
+};
+hipError_t launch_prefill_main_sparse(const PrefillMainArgs& a, hipStream_t st);
+hipError_t launch_prefill_main_dense(const PrefillMainArgs& a, hipStream_t st);
+
+// ---- Decode ----
+hipError_t launch_index_blockmax_decode(const uint16_t* idx_q, const uint16_t* idx_k,
+                                        const int32_t* lens, float* S, int batch, int Lmax, int G,
+                                        int di, int B, int s_stride, hipStream_t st);
+struct DecodeMainArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* lens;
+  uint16_t* out;
+  float* lse;
+  const int32_t* bidx;    // [batch][G][topk] (sparse / given)
+  int batch, Lmax, Hq, G, B, topk;
+  bool dense;
+  int nsplit;             // work items per (s, g)
+  int blocks_per_split;   // dense: consecutive blocks per work item
+  float scale_log2;
+  float* pO;              // [batch*G*nsplit*R*128]
+  float* pS;              // [batch*G*nsplit*R]
+};
+hipError_t launch_decode_main(const DecodeMainArgs& a, hipStream_t st);
+
+}  // namespace msa

@@ -1,0 +1,552 @@
+// Main Branch of MSA on gfx950: exact softmax GQA attention restricted to the
+// selected blocks [hyper.ai paper page 2606.13392, 方法 (Method): attention is
+// limited to the tokens of the selected blocks, computed as standard scaled
+// dot-product attention over their gathered keys and values; hamidun.com news
+// "MiniMax выпустила MSA", "Как устроен MSA": the main branch is exact].
+//
+// Work split (an MI355X design choice, in the spirit of the pages' KV-outer
+// kernel, 核心贡献 / Contributions):
+//  * non-local selected blocks (b < L(t)) are processed block-major: for every
+//    (sequence, group, block) a list of the (token, slot) pairs that chose it
+//    is built by a counting sort; a workgroup loads one K/V block into LDS
+//    once and serves up to 128 (token, head) query rows of that list with
+//    MFMA, writing a normalised partial output and its log-sum-exp per row.
+//    K/V bytes are thereby shared across query tokens as well as across the R
+//    heads of a group; no causal mask is needed since b < L(t) lies wholly
+//    before t.
+//  * the local block L(t) is processed query-major (flash attention over the
+//    keys [L(t)*B, t] with the causal mask), and the same kernel then merges
+//    the row's partials in fixed slot order -- no atomics touch any value, so
+//    outputs are bitwise reproducible.
+//  * dense mode (every visible block) runs the query-major kernel over keys
+//    [0, t] with online softmax.
+//
+// Numerics: bf16 x bf16 products, fp32 accumulation, softmax in fp32 in the
+// base-2 domain (logit * scale * log2 e), probabilities rounded to bf16 for
+// the P.V product, output rounded to bf16 (nearest even).
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+namespace {
+
+constexpr int D = 128;          // head_dim
+constexpr int KROW = D + 8;     // LDS row stride of K tiles (bf16)
+
+// ---------------------------------------------------------------------------
+// LDS staging helpers (256 threads).
+// K tile: rows [key][D] -> Ks[key*KROW + d]
+// V tile: transposed -> Vt[d*VROW + key], so that a lane can fetch 4
+// consecutive keys of one d with one 8-byte read (PV operand layout).
+// Keys >= nvalid are zero-filled.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void stage_k(bf16_t* Ks, const bf16_t* __restrict__ kbase, size_t kstride,
+                                        int nkeys, int nvalid, int tid) {
+  const int nch = nkeys * (D / 8);
+  for (int c = tid; c < nch; c += 256) {
+    const int key = c >> 4, part = c & 15;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (key < nvalid) val = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * kstride + part * 8);
+    *reinterpret_cast<u32x4*>(Ks + key * KROW + part * 8) = val;
+  }
+}
+
+__device__ __forceinline__ void stage_vt(bf16_t* Vt, int vrow, const bf16_t* __restrict__ vbase,
+                                         size_t vstride, int nkeys, int nvalid, int tid) {
+  // unit = 4 keys x 4 d; 32 units per 4-key group
+  const int nunits = (nkeys / 4) * (D / 4);
+  for (int u = tid; u < nunits; u += 256) {
+    const int k4 = u >> 5, dq = u & 31;
+    u32x2 r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = k4 * 4 + i;
+      r[i] = u32x2{0u, 0u};
+      if (key < nvalid) r[i] = *reinterpret_cast<const u32x2*>(vbase + (size_t)key * vstride + dq * 4);
+    }
+    // 4x4 transpose of 16-bit lanes: o[j] = (r0[j], r1[j], r2[j], r3[j])
+    u32x2 o[4];
+    o[0] = u32x2{(r[0][0] & 0xffffu) | (r[1][0] << 16), (r[2][0] & 0xffffu) | (r[3][0] << 16)};
+    o[1] = u32x2{(r[0][0] >> 16) | (r[1][0] & 0xffff0000u), (r[2][0] >> 16) | (r[3][0] & 0xffff0000u)};
+    o[2] = u32x2{(r[0][1] & 0xffffu) | (r[1][1] << 16), (r[2][1] & 0xffffu) | (r[3][1] << 16)};
+    o[3] = u32x2{(r[0][1] >> 16) | (r[1][1] & 0xffff0000u), (r[2][1] >> 16) | (r[3][1] & 0xffff0000u)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x2*>(Vt + (dq * 4 + j) * vrow + k4 * 4) = o[j];
+  }
+}
+
+// S^T tile (32 keys x 32 query rows) = K[32 x D] . Q^T, A operand from LDS.
+__device__ __forceinline__ f32x16 qk_tile(const bf16_t* Ks, int key0, const bf16x8* qop, int col,
+                                          int half) {
+  f32x16 acc = {};
+  const bf16_t* arow = Ks + (key0 + col) * KROW + 8 * half;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    acc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(arow + 16 * ks), qop[ks], acc);
+  return acc;
+}
+
+// O^T[d-tile] += V^T[32 d x 16 keys] . P^T, for the 16-key slice starting at key0.
+__device__ __forceinline__ f32x16 pv_step(const bf16_t* Vt, int vrow, int dt, int key0, bf16x8 p,
+                                          f32x16 acc, int col, int half) {
+  const bf16_t* vr = Vt + (dt * 32 + col) * vrow + key0 + 4 * half;
+  const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
+  const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
+  return mfma32x32x16(join_bf16x4(lo, hi), p, acc);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& a, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)a[base + e];
+  return r;
+}
+
+__device__ __forceinline__ void load_q(bf16x8* qop, const bf16_t* qp, bool ok, int half) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qop[ks] = ok ? load_bf16x8(qp + 16 * ks + 8 * half) : zero_bf16x8();
+}
+
+// ---------------------------------------------------------------------------
+// Block lists: counting sort of the (token, slot) pairs by (s, g, block).
+// Entry of a row = tl * KS + rank, rank = position among the row's valid
+// non-local entries (so partial storage needs only KS = min(k, nb) slots).
+// ---------------------------------------------------------------------------
+__global__ void fill_i32_kernel(int32_t* p, size_t n, int32_t v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+__global__ void lists_count_kernel(PrefillMainArgs a) {
+  const long n_rows = (long)a.batch * a.tc * a.G;
+  const long row = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= n_rows) return;
+  const long per_b = (long)a.tc * a.G;
+  const int s = (int)(row / per_b);
+  const int tl = (int)((row % per_b) / a.G);
+  const int g = (int)(row % a.G);
+  const int t = a.t0 + tl;
+  const int L = t / a.B;
+  const int32_t* br = a.bidx + ((size_t)((long)s * a.bidx_rows + (t - a.bidx_t_off)) * a.G + g) * a.topk;
+  int rank = 0;
+  for (int j = 0; j < a.topk && rank < a.KS; ++j) {
+    const int e = br[j];
+    if (e >= 0 && e < L) {
+      const size_t lid = ((size_t)s * a.G + g) * a.nbl + e;
+      a.epos[(size_t)row * a.KS + rank] = atomicAdd(&a.cnt[lid], 1);
+      ++rank;
+    }
+  }
+}
+
+// Single workgroup: exclusive scans of list sizes and of list tiles; writes
+// the flat work list (list id, tile index) and its length.
+__global__ __launch_bounds__(1024) void lists_scan_kernel(const int32_t* __restrict__ cnt,
+                                                          int32_t* __restrict__ offs, int2* __restrict__ work,
+                                                          int32_t* __restrict__ n_work, long nlists,
+                                                          int mt) {
+  __shared__ long s_e[1024];
+  __shared__ long s_t[1024];
+  const int tid = threadIdx.x;
+  long carry_e = 0, carry_t = 0;
+  for (long base = 0; base < nlists; base += 1024) {
+    const long i = base + tid;
+    const int c = i < nlists ? cnt[i] : 0;
+    const long tiles = (c + mt - 1) / mt;
+    s_e[tid] = c;
+    s_t[tid] = tiles;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      long ve = 0, vt = 0;
+      if (tid >= off) { ve = s_e[tid - off]; vt = s_t[tid - off]; }
+      __syncthreads();
+      s_e[tid] += ve;
+      s_t[tid] += vt;
+      __syncthreads();
+    }
+    const long ex_e = s_e[tid] - c, ex_t = s_t[tid] - tiles;
+    if (i < nlists) {
+      offs[i] = (int32_t)(carry_e + ex_e);
+      const long w0 = carry_t + ex_t;
+      for (long j = 0; j < tiles; ++j) work[w0 + j] = make_int2((int)i, (int)j);
+    }
+    carry_e += s_e[1023];
+    carry_t += s_t[1023];
+    __syncthreads();
+  }
+  if (tid == 0) n_work[0] = (int32_t)carry_t;
+}
+
+__global__ void lists_scatter_kernel(PrefillMainArgs a) {
+  const long n_rows = (long)a.batch * a.tc * a.G;
+  const long row = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= n_rows) return;
+  const long per_b = (long)a.tc * a.G;
+  const int s = (int)(row / per_b);
+  const int tl = (int)((row % per_b) / a.G);
+  const int g = (int)(row % a.G);
+  const int t = a.t0 + tl;
+  const int L = t / a.B;
+  const int32_t* br = a.bidx + ((size_t)((long)s * a.bidx_rows + (t - a.bidx_t_off)) * a.G + g) * a.topk;
+  int rank = 0;
+  for (int j = 0; j < a.topk && rank < a.KS; ++j) {
+    const int e = br[j];
+    if (e >= 0 && e < L) {
+      const size_t lid = ((size_t)s * a.G + g) * a.nbl + e;
+      a.entries[(size_t)a.offs[lid] + a.epos[(size_t)row * a.KS + rank]] = tl * a.KS + rank;
+      ++rank;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block-major kernel: one (s, g, block, tile of up to 128/R tokens) per
+// workgroup.  Writes, per (token, head) row, the normalised partial output
+// (fp32, natural d order) and lse2 = max*c + log2(sum) (base-2 domain).
+// ---------------------------------------------------------------------------
+template <int BS>
+__global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
+  constexpr int VROW = BS + 4;
+  constexpr int KT = BS / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[BS * KROW];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[D * VROW];
+
+  const int w = blockIdx.x;
+  if (w >= a.n_work[0]) return;
+  const int2 wk = a.work[w];
+  const long lid = wk.x;
+  const int b = (int)(lid % a.nbl);
+  const long sg = lid / a.nbl;
+  const int g = (int)(sg % a.G);
+  const int s = (int)(sg / a.G);
+  const int R = a.Hq / a.G;
+  const int mt = kAttnRows / R;
+  const int count = a.cnt[lid];
+  const int e0 = wk.y * mt;
+  const int ne = min(mt, count - e0);
+  const int off = a.offs[lid];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+
+  const size_t kvstride = (size_t)a.G * D;
+  const size_t kvoff = ((size_t)s * a.T + (size_t)b * a.B) * kvstride + (size_t)g * D;
+  stage_k(Ks, a.k + kvoff, kvstride, BS, BS, tid);
+  stage_vt(Vt, VROW, a.v + kvoff, kvstride, BS, BS, tid);
+
+  const int row = wave * 32 + col;
+  const int e = row / R, r = row % R;
+  const bool valid = e < ne;
+  int tl = 0, rank = 0;
+  if (valid) {
+    const int ent = a.entries[(size_t)off + e0 + e];
+    tl = ent / a.KS;
+    rank = ent % a.KS;
+  }
+  const int t = a.t0 + tl;
+  const int h = g * R + r;
+  bf16x8 qop[D / 16];
+  load_q(qop, a.q + (((size_t)s * a.T + t) * a.Hq + h) * D, valid, half);
+  __syncthreads();
+
+  f32x16 sacc[KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) sacc[kt] = qk_tile(Ks, kt * 32, qop, col, half);
+
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  const float c = a.scale_log2;
+  const float mc = mx * c;
+  float l = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(sacc[kt][i] * c - mc);
+      sacc[kt][i] = p;
+      l += p;
+    }
+  l += __shfl_xor(l, 32, kWave);
+
+  bf16x8 pop[KT][2];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    pop[kt][0] = to_bf16x8(sacc[kt], 0);
+    pop[kt][1] = to_bf16x8(sacc[kt], 8);
+  }
+  f32x16 oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    oacc[dt] = f32x16{};
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      oacc[dt] = pv_step(Vt, VROW, dt, kt * 32, pop[kt][0], oacc[dt], col, half);
+      oacc[dt] = pv_step(Vt, VROW, dt, kt * 32 + 16, pop[kt][1], oacc[dt], col, half);
+    }
+  }
+
+  if (valid) {
+    const float inv = 1.0f / l;
+    const size_t prow = ((((size_t)s * a.tc + tl) * a.G + g) * a.KS + rank) * R + r;
+    float* dst = a.pO + prow * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 vv = make_float4(oacc[dt][4 * i4] * inv, oacc[dt][4 * i4 + 1] * inv,
+                                      oacc[dt][4 * i4 + 2] * inv, oacc[dt][4 * i4 + 3] * inv);
+        *reinterpret_cast<float4*>(dst + dt * 32 + i4 * 8 + 4 * half) = vv;
+      }
+    if (half == 0) a.pS[prow] = mc + __log2f(l);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Query-major kernel: a workgroup owns up to 128/R consecutive tokens of one
+// (s, g) with all R heads of the group and runs online-softmax attention over
+// key tiles of KTILE keys in [k_lo, t_last], masking per row to
+// [lo(t), t] with lo(t) = L(t)*B (sparse: the local block) or 0 (dense).
+// Sparse mode then merges the partials of the row's non-local blocks.
+// ---------------------------------------------------------------------------
+template <bool DENSE>
+__global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) {
+  constexpr int KTILE = 64;
+  constexpr int VROW = KTILE + 4;
+  constexpr int KT = KTILE / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[KTILE * KROW];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[D * VROW];
+
+  const int R = a.Hq / a.G;
+  const int mt = kAttnRows / R;
+  const int g = blockIdx.y, s = blockIdx.z;
+  const int tl0 = blockIdx.x * mt;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int row = wave * 32 + col;
+  const int e = row / R, r = row % R;
+  const int tl = tl0 + e;
+  const bool valid = e < mt && tl < a.tc;
+  const int t = a.t0 + min(tl, a.tc - 1);
+  const int h = g * R + r;
+  const int L = t / a.B;
+
+  // the row's own key window
+  int lo = DENSE ? 0 : L * a.B;
+  bool has_local = true;
+  const int32_t* br = nullptr;
+  if (!DENSE) {
+    br = a.bidx + ((size_t)((long)s * a.bidx_rows + (t - a.bidx_t_off)) * a.G + g) * a.topk;
+    // given selections may omit the local block
+    has_local = false;
+    for (int j = 0; j < a.topk; ++j)
+      if (br[j] == L) { has_local = true; break; }
+  }
+  const int hi = (valid && has_local) ? t : lo - 1;  // empty window when not attended
+
+  const int t_first = a.t0 + tl0;
+  const int t_last = a.t0 + min(tl0 + mt, a.tc) - 1;
+  const int k_lo = DENSE ? 0 : (t_first / a.B) * a.B;
+  const int k_hi = t_last;
+
+  bf16x8 qop[D / 16];
+  load_q(qop, a.q + (((size_t)s * a.T + t) * a.Hq + h) * D, valid, half);
+
+  const size_t kvstride = (size_t)a.G * D;
+  const bf16_t* kseq = a.k + (size_t)s * a.T * kvstride + (size_t)g * D;
+  const bf16_t* vseq = a.v + (size_t)s * a.T * kvstride + (size_t)g * D;
+  const float c = a.scale_log2;
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
+
+  for (int kb = k_lo; kb <= k_hi; kb += KTILE) {
+    const int nvalid = min(KTILE, k_hi + 1 - kb);
+    __syncthreads();
+    stage_k(Ks, kseq + (size_t)kb * kvstride, kvstride, KTILE, nvalid, tid);
+    stage_vt(Vt, VROW, vseq + (size_t)kb * kvstride, kvstride, KTILE, nvalid, tid);
+    __syncthreads();
+
+    f32x16 sacc[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) sacc[kt] = qk_tile(Ks, kt * 32, qop, col, half);
+    float tmx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = kb + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        const bool ok = j >= lo && j <= hi;
+        sacc[kt][i] = ok ? sacc[kt][i] : -INFINITY;
+        tmx = fmaxf(tmx, sacc[kt][i]);
+      }
+    tmx = fmaxf(tmx, __shfl_xor(tmx, 32, kWave));
+    const float m_new = fmaxf(m, tmx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f((m - m_use) * c);
+    const float muc = m_use * c;
+    float ps = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sacc[kt][i] * c - muc);
+        sacc[kt][i] = p;
+        ps += p;
+      }
+    ps += __shfl_xor(ps, 32, kWave);
+    l = l * alpha + ps;
+    m = m_new;
+    bf16x8 pop[KT][2];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      pop[kt][0] = to_bf16x8(sacc[kt], 0);
+      pop[kt][1] = to_bf16x8(sacc[kt], 8);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        oacc[dt] = pv_step(Vt, VROW, dt, kt * 32, pop[kt][0], oacc[dt], col, half);
+        oacc[dt] = pv_step(Vt, VROW, dt, kt * 32 + 16, pop[kt][1], oacc[dt], col, half);
+      }
+    }
+  }
+  if (!valid) return;
+
+  // lse2 of the local window (base-2 domain); -inf when nothing was attended
+  const float lse2_loc = (l > 0.f) ? m * c + __log2f(l) : -INFINITY;
+  float M2 = lse2_loc;
+  float scale_loc = (l > 0.f) ? 1.0f / l : 0.f;  // oacc is unnormalised
+  float o[4][16];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = oacc[dt][i];
+
+  float sumw = 0.f;
+  if (!DENSE) {
+    const size_t prow0 = (((size_t)s * a.tc + tl) * a.G + g) * a.KS;
+    const int R_ = R;
+    // pass 1: the merged maximum
+    int rank = 0;
+    for (int j = 0; j < a.topk && rank < a.KS; ++j) {
+      const int eb = br[j];
+      if (eb >= 0 && eb < L) {
+        M2 = fmaxf(M2, a.pS[(prow0 + rank) * R_ + r]);
+        ++rank;
+      }
+    }
+    const float M2u = (M2 == -INFINITY) ? 0.f : M2;
+    const float wl = (l > 0.f) ? __builtin_amdgcn_exp2f(lse2_loc - M2u) : 0.f;
+    sumw = wl;
+    const float f = wl * scale_loc;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= f;
+    // pass 2: weighted partials, in slot order
+    rank = 0;
+    for (int j = 0; j < a.topk && rank < a.KS; ++j) {
+      const int eb = br[j];
+      if (eb >= 0 && eb < L) {
+        const size_t prow = (prow0 + rank) * R_ + r;
+        const float wj = __builtin_amdgcn_exp2f(a.pS[prow] - M2u);
+        sumw += wj;
+        const float* src = a.pO + prow * D;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const float4 pv = *reinterpret_cast<const float4*>(src + dt * 32 + i4 * 8 + 4 * half);
+            o[dt][4 * i4] += wj * pv.x;
+            o[dt][4 * i4 + 1] += wj * pv.y;
+            o[dt][4 * i4 + 2] += wj * pv.z;
+            o[dt][4 * i4 + 3] += wj * pv.w;
+          }
+        ++rank;
+      }
+    }
+    M2 = M2u;
+  } else {
+    sumw = (l > 0.f) ? 1.f : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= scale_loc;
+    M2 = lse2_loc;
+  }
+
+  const float invw = (sumw > 0.f) ? 1.0f / sumw : 0.f;
+  bf16_t* dst = a.out + (((size_t)s * a.T + t) * a.Hq + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      bf16x4 v4;
+      v4[0] = (__bf16)(o[dt][4 * i4] * invw);
+      v4[1] = (__bf16)(o[dt][4 * i4 + 1] * invw);
+      v4[2] = (__bf16)(o[dt][4 * i4 + 2] * invw);
+      v4[3] = (__bf16)(o[dt][4 * i4 + 3] * invw);
+      *reinterpret_cast<bf16x4*>(dst + dt * 32 + i4 * 8 + 4 * half) = v4;
+    }
+  if (a.lse != nullptr && half == 0) {
+    const float lse2 = (sumw > 0.f) ? M2 + __log2f(sumw) : -INFINITY;
+    a.lse[((size_t)s * a.T + t) * a.Hq + h] = lse2 * kLn2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t value, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  fill_i32_kernel<<<dim3((unsigned)blocks), 256, 0, st>>>(p, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_main_sparse(const PrefillMainArgs& a, hipStream_t st) {
+  const long nlists = (long)a.batch * a.G * a.nbl;
+  hipError_t err = launch_fill_i32(a.cnt, (size_t)nlists, 0, st);
+  if (err != hipSuccess) return err;
+  const long n_rows = (long)a.batch * a.tc * a.G;
+  const unsigned rgrid = (unsigned)((n_rows + 255) / 256);
+  lists_count_kernel<<<rgrid, 256, 0, st>>>(a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int R = a.Hq / a.G;
+  const int mt = kAttnRows / R;
+  lists_scan_kernel<<<1, 1024, 0, st>>>(a.cnt, a.offs, a.work, a.n_work, nlists, mt);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  lists_scatter_kernel<<<rgrid, 256, 0, st>>>(a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (a.max_work > 0) {
+    const dim3 grid((unsigned)a.max_work);
+    if (a.B == 128) kv_outer_kernel<128><<<grid, 256, 0, st>>>(a);
+    else if (a.B == 64) kv_outer_kernel<64><<<grid, 256, 0, st>>>(a);
+    else kv_outer_kernel<32><<<grid, 256, 0, st>>>(a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  const dim3 qgrid((unsigned)((a.tc + mt - 1) / mt), a.G, a.batch);
+  query_major_kernel<false><<<qgrid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_main_dense(const PrefillMainArgs& a, hipStream_t st) {
+  const int R = a.Hq / a.G;
+  const int mt = kAttnRows / R;
+  const dim3 qgrid((unsigned)((a.tc + mt - 1) / mt), a.G, a.batch);
+  query_major_kernel<true><<<qgrid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,159 @@
+/*
+ * msa.h -- C ABI of libmsa.so, the MI355X (gfx950) forward path of MiniMax
+ * Sparse Attention (MSA).
+ *
+ * What the calls compute (sources cited by page title and section):
+ *  - Index Branch [hyper.ai paper page 2606.13392, 方法 (Method); Telegram
+ *    review quant_prune_distill post 751, "Метод"]: one index-query head per
+ *    GQA group and one index-key head per layer give raw dot-product scores
+ *    s[t,g,j] = idx_q[t,g] . idx_k[j] for every visible key j <= t; the scores
+ *    are max-pooled over aligned blocks of block_size tokens; per (query
+ *    token, group) the topk blocks with the largest maxima are kept, the block
+ *    holding the query (L(t) = t / block_size) always being one of them.
+ *    Equal maxima go to the lower block index.  block_idx rows list the kept
+ *    blocks in ascending order and are padded with -1 to length topk
+ *    (exactly min(topk, L(t)+1) entries are valid).
+ *  - Main Branch [same page, 方法; hamidun.com news "MiniMax выпустила MSA",
+ *    "Как устроен MSA"]: exact softmax attention of every query head h over
+ *    the keys of the kept blocks of its group g = h / (Hq/G), restricted to
+ *    keys j <= t, with scale softmax_scale (1/sqrt(head_dim) by default).
+ *  - Prefill and decode [hyper.ai page, 一句话总结 (summary): prefill and
+ *    decode speed-ups at 1M context].
+ *
+ * Conventions shared by every call:
+ *  - Tensor pointers are DEVICE pointers owned by the caller, row-major and
+ *    contiguous (innermost dimension last).  bf16 tensors are IEEE bfloat16
+ *    bit patterns (uint16) and must be 16-byte aligned; int32 and fp32
+ *    tensors must be 4-byte aligned.  The library never allocates or frees
+ *    device memory and keeps no state between calls.
+ *  - The caller supplies a device workspace of at least
+ *    msa_workspace_bytes(op, dims) bytes (256-byte aligned); its contents on
+ *    entry do not matter and are clobbered.
+ *  - Every call validates all arguments on the host before enqueueing any
+ *    work and returns a status; on a non-zero status nothing was enqueued
+ *    (except MSA_ERR_HIP, where earlier launches of the same call may have
+ *    been enqueued).  On MSA_OK the work is enqueued on hip_stream (a
+ *    hipStream_t; NULL = the default stream) and the call returns without
+ *    waiting.  Outputs are bitwise reproducible run to run.
+ *  - Calls on different streams with disjoint workspaces may run
+ *    concurrently; calls sharing a workspace must be ordered by the caller.
+ *  - Inputs must be finite; NaN or Inf inputs give unspecified outputs.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define MSA_OK 0
+#define MSA_ERR_INVALID_ARG 1  /* null pointer, non-positive size, Hq % G != 0, bad flag mix */
+#define MSA_ERR_UNSUPPORTED 2  /* head_dim != 128, index_dim not in {64,128}, block_size not in
+                                  {32,64,128}, or Hq/G above 128 (prefill) / 16 (decode) */
+#define MSA_ERR_ALIGNMENT 3    /* a tensor pointer misaligned (see above), or workspace not 256-byte aligned */
+#define MSA_ERR_WORKSPACE 4    /* workspace_bytes < msa_workspace_bytes(op, dims) */
+#define MSA_ERR_HIP 5          /* a HIP launch failed; see msa_status_string / msa_last_hip_error */
+
+/* ---- dims.flags ---- */
+/* Main branch over ALL visible blocks (full causal attention, the dense
+   baseline); the index branch is skipped.  block_idx must be NULL. */
+#define MSA_DENSE 0x1u
+/* block_idx is an INPUT: the main branch attends to the given blocks and the
+   index branch is skipped.  Entries outside [0, L(t)] (e.g. -1) are ignored;
+   valid entries of a row must be distinct. */
+#define MSA_GIVEN_INDICES 0x2u
+
+/* ---- operations for msa_workspace_bytes ---- */
+#define MSA_OP_INDEX_TOPK 0
+#define MSA_OP_PREFILL 1
+#define MSA_OP_DECODE 2
+
+typedef struct msa_dims {
+  int32_t batch;         /* sequences, >= 1 */
+  int32_t seqlen;        /* prefill: T (queries == keys); decode: cache capacity Lmax */
+  int32_t num_q_heads;   /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;  /* G: GQA groups = KV heads = index-query heads */
+  int32_t head_dim;      /* d: 128 */
+  int32_t index_dim;     /* d_idx: 64 or 128 */
+  int32_t block_size;    /* B: 32, 64 or 128 */
+  int32_t topk;          /* k >= 1, counts the forced local block; k > number of
+                            visible blocks selects all of them */
+  float softmax_scale;   /* <= 0 selects 1/sqrt(head_dim) */
+  uint32_t flags;        /* MSA_DENSE, MSA_GIVEN_INDICES */
+  int32_t query_chunk;   /* prefill: query tokens per internal pass, a multiple of
+                            block_size; 0 = the library's default (bounds the
+                            workspace).  Ignored by decode. */
+  int32_t reserved;      /* must be 0 */
+} msa_dims;
+
+/*
+ * Index Branch only (prefill shapes).
+ *   idx_q     [batch, T, G, index_dim] bf16
+ *   idx_k     [batch, T, index_dim]    bf16
+ *   block_idx [batch, T, G, topk]      int32, OUTPUT
+ * Flags must be 0.  Integer-valued idx inputs whose dot products stay below
+ * 2^24 in magnitude give exact scores, hence a unique, exact selection.
+ */
+int msa_index_topk(const msa_dims* dims, const void* idx_q, const void* idx_k,
+                   int32_t* block_idx, void* workspace, size_t workspace_bytes,
+                   void* hip_stream);
+
+/*
+ * Prefill: Index Branch + Main Branch over a whole causal sequence.
+ *   q         [batch, T, Hq, d] bf16
+ *   k, v      [batch, T, G, d]  bf16
+ *   idx_q     [batch, T, G, index_dim] bf16   (unused with MSA_DENSE or
+ *   idx_k     [batch, T, index_dim]    bf16    MSA_GIVEN_INDICES; may be NULL)
+ *   out       [batch, T, Hq, d] bf16 OUTPUT (round to nearest even)
+ *   lse       [batch, T, Hq] fp32 OUTPUT, natural-log sum of exp of the scaled
+ *             logits over the attended keys; may be NULL
+ *   block_idx [batch, T, G, topk] int32: OUTPUT (may be NULL), INPUT with
+ *             MSA_GIVEN_INDICES, must be NULL with MSA_DENSE
+ */
+int msa_prefill(const msa_dims* dims, const void* q, const void* k, const void* v,
+                const void* idx_q, const void* idx_k, void* out, float* lse,
+                int32_t* block_idx, void* workspace, size_t workspace_bytes,
+                void* hip_stream);
+
+/*
+ * Decode: one new query token per sequence against its caches.
+ *   q           [batch, Hq, d] bf16
+ *   k_cache,
+ *   v_cache     [batch, Lmax, G, d] bf16 (Lmax = dims->seqlen)
+ *   idx_q       [batch, G, index_dim] bf16      (unused with MSA_DENSE or
+ *   idx_k_cache [batch, Lmax, index_dim] bf16    MSA_GIVEN_INDICES; may be NULL)
+ *   cache_lens  [batch] int32, DEVICE: tokens in each cache INCLUDING the new
+ *               one (the query sits at position cache_lens[s]-1); each value
+ *               must lie in [1, Lmax] -- out-of-range values are clamped to
+ *               that range on the device
+ *   out         [batch, Hq, d] bf16 OUTPUT;  lse [batch, Hq] fp32 OUTPUT or NULL
+ *   block_idx   [batch, G, topk] int32: OUTPUT (may be NULL), INPUT with
+ *               MSA_GIVEN_INDICES, must be NULL with MSA_DENSE
+ */
+int msa_decode(const msa_dims* dims, const void* q, const void* k_cache,
+               const void* v_cache, const void* idx_q, const void* idx_k_cache,
+               const int32_t* cache_lens, void* out, float* lse, int32_t* block_idx,
+               void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes needed by op for dims (0 when none is needed).  Returns
+   (size_t)-1 when dims are invalid for op. */
+size_t msa_workspace_bytes(int op, const msa_dims* dims);
+
+/* Static text for a status code (never NULL). */
+const char* msa_status_string(int status);
+
+/* Text of the HIP error behind the calling thread's last MSA_ERR_HIP ("" if none). */
+const char* msa_last_hip_error(void);
+
+/* ABI version of this header: 1. */
+int msa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */
