@@ -1,0 +1,345 @@
+"""Benchmark of the MSA forward path on one MI355X.
+
+One step = one MSA layer prefill over T = 131072 tokens (64 query heads in 8
+GQA groups, head_dim 128, index_dim 128, block 128, top-k 16, idx_k with a
+per-block random mean offset) followed by one decode step for 8 sequences at
+1,048,576 tokens of context (same head layout).  Inputs are seeded synthetic
+bf16 tensors resident in HBM before timing starts.
+
+Prints one JSON line: `value` is prefill tokens/s; the decode rate, the dense
+(all-blocks) comparison, a sampled parity check against the CPU oracle, the
+roofline of the dominant kernel (index scoring + block max, MFMA-bound) timed
+live with HIP events, and the oracle's own rate on the host cores are
+reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from block_sparse_long_02_amd import binding as bd  # noqa: E402
+from block_sparse_long_02_amd import inputs  # noqa: E402
+
+METRIC = "MSA layer prefill tok/s @128K & decode tok/s @1M ctx; % MFMA/HBM roofline"
+PEAK_MFMA_BF16 = 2.5e15   # MI355X dense bf16, FLOP/s
+PEAK_HBM = 8.0e12         # MI355X HBM3E, B/s
+
+PF = dict(T=131072, Hq=64, G=8, d=128, di=128, B=128, k=16, skew=0.5, seed=0)
+DC = dict(batch=8, L=1 << 20, Hq=64, G=8, d=128, di=128, B=128, k=16, seed=1)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def n_att(t, B, k):
+    return (t % B) + 1 + B * min(k - 1, t // B)
+
+
+def prefill_flops(T, Hq, G, d, di, B, k):
+    t = np.arange(T, dtype=np.float64)
+    index = 2.0 * G * di * (t + 1).sum()
+    L = np.floor(t / B)
+    att = (t % B) + 1 + B * np.minimum(k - 1, L)
+    main = 4.0 * Hq * d * att.sum()
+    return index, main
+
+
+def dense_prefill_flops(T, Hq, d):
+    return 4.0 * Hq * d * T * (T + 1) / 2
+
+
+def decode_bytes(batch, L, Hq, G, d, di, B, k):
+    t = L - 1
+    per_seq = L * di * 2 + G * n_att(t, B, k) * d * 2 * 2 + Hq * d * 2 * 2 + G * di * 2
+    return batch * per_seq
+
+
+def timed(fn, reps, stream):
+    """Mean ms of reps launches of fn, HIP events on the launch stream."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    return float(np.mean(per)), per
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a stratified sample of tokens
+# ---------------------------------------------------------------------------
+def cpu_baseline_and_parity(pin, out_gpu, bidx_gpu, n_tokens, time_budget_s):
+    from oracle import msa_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    T, Hq, G, d, B, k = PF["T"], PF["Hq"], PF["G"], PF["d"], PF["B"], PF["k"]
+    R = Hq // G
+    scale = 1.0 / math.sqrt(d)
+    # stratified over t, visited in a seeded random order so that any prefix
+    # (when the time budget ends the loop early) is still a uniform sample
+    ts = [int((i + 0.5) * T / n_tokens) for i in range(n_tokens)]
+    ts = [ts[j] for j in np.random.default_rng(0).permutation(n_tokens)]
+    # inputs to float64 on the host (not timed)
+    K = pin.k[0].cpu().to(torch.float64).numpy()
+    V = pin.v[0].cpu().to(torch.float64).numpy()
+    IK = pin.idx_k[0].cpu().to(torch.float64).numpy()
+    Q = pin.q[0, ts].cpu().to(torch.float64).numpy()
+    IQ = pin.idx_q[0, ts].cpu().to(torch.float64).numpy()
+    og = out_gpu[0, ts].cpu().to(torch.float64).numpy()
+    bg = bidx_gpu[0, ts].cpu().numpy()
+    done, spent = 0, 0.0
+    sel_equal = sel_neartie = sel_other = 0
+    err_abs, err_sum, ref_sum = 0.0, 0.0, 0.0
+    for i, t in enumerate(ts):
+        t0 = time.perf_counter()
+        o_t = np.empty((Hq, d))
+        sels, Ss = [], []
+        for g in range(G):
+            S = orc.block_max(orc.index_scores(IQ[i, g], IK, t), t, B)
+            sel = orc.select_blocks(S, t, B, k)
+            toks = orc.selected_tokens(sel, t, B)
+            o, _ = orc.attention_row(Q[i, g * R:(g + 1) * R], K[:, g], V[:, g], toks, scale)
+            o_t[g * R:(g + 1) * R] = o
+            sels.append(sel)
+            Ss.append(S)
+        spent += time.perf_counter() - t0
+        done += 1
+        for g in range(G):
+            if np.array_equal(bg[i, g], sels[g]):
+                sel_equal += 1
+                diff = np.abs(og[i, g * R:(g + 1) * R] - o_t[g * R:(g + 1) * R])
+                err_abs = max(err_abs, float(diff.max()))
+                err_sum += float(diff.sum())
+                ref_sum += float(np.abs(o_t[g * R:(g + 1) * R]).sum())
+            elif orc.near_tie(Ss[g], t, B, k):
+                sel_neartie += 1
+            else:
+                sel_other += 1
+        if spent > time_budget_s and done >= 8:
+            break
+    # stratified sample over t: the mean per-token time estimates the mean
+    # over the whole sequence (the oracle's cost is linear in t)
+    used = ts[:done]
+    cover = (f"stratified over t" if done == n_tokens
+             else f"{done} of {n_tokens} stratified positions, in seeded random order")
+    cpu = {
+        "value": round(done / spent, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
+        "sample": f"{done} query tokens ({cover}) of the T=131072 prefill, all 8 groups and 64 heads "
+                  f"each: index scores, block max, top-k, gathered fp64 attention; "
+                  f"{spent:.1f} s of CPU work; tok/s = tokens / time",
+    }
+    parity = {
+        "rows_checked": done * G, "selection_equal": sel_equal, "selection_near_tie": sel_neartie,
+        "selection_other": sel_other, "out_max_abs": err_abs,
+        "out_mean_rel": err_sum / max(ref_sum, 1e-300), "t_range": [min(used), max(used)],
+    }
+    return cpu, parity
+
+
+def decode_parity(dec, out_gpu, bidx_gpu, seqs):
+    """Oracle check of sampled decode sequences, built from the oracle's own
+    steps; only the gathered K/V rows are converted to float64."""
+    from oracle import msa_oracle as orc
+    B, k, G, Hq, d = DC["B"], DC["k"], DC["G"], DC["Hq"], DC["d"]
+    R = Hq // G
+    scale = 1.0 / math.sqrt(d)
+    worst_abs, sel_ok = 0.0, True
+    for s in seqs:
+        t = int(dec.cache_lens[s]) - 1
+        IK = dec.idx_k_cache[s, : t + 1].cpu().to(torch.float64).numpy()
+        IQ = dec.idx_q[s].cpu().to(torch.float64).numpy()
+        Q = dec.q[s].cpu().to(torch.float64).numpy()
+        og = out_gpu[s].cpu().to(torch.float64).numpy()
+        for g in range(G):
+            S = orc.block_max(orc.index_scores(IQ[g], IK, t), t, B)
+            sel = orc.select_blocks(S, t, B, k)
+            if not np.array_equal(sel, bidx_gpu[s, g].cpu().numpy()):
+                sel_ok = sel_ok and orc.near_tie(S, t, B, k)
+                continue
+            toks = orc.selected_tokens(sel, t, B)
+            tk = torch.from_numpy(toks).to(dec.k_cache.device)
+            Kg = dec.k_cache[s, tk, g].cpu().to(torch.float64).numpy()
+            Vg = dec.v_cache[s, tk, g].cpu().to(torch.float64).numpy()
+            o, _ = orc.attention_row(Q[g * R:(g + 1) * R], Kg, Vg, np.arange(len(toks)), scale)
+            worst_abs = max(worst_abs, float(np.abs(og[g * R:(g + 1) * R] - o).max()))
+    return {"sequences_checked": list(seqs), "selection_ok": bool(sel_ok), "out_max_abs": worst_abs}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-dense", action="store_true", help="skip the all-blocks comparison")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (CPU baseline + parity)")
+    ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--cpu-seconds", type=float, default=25.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    bd.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    log("generating prefill inputs (T=131072)")
+    pin = inputs.make_prefill(PF["T"], PF["Hq"], PF["G"], PF["d"], PF["di"], seed=PF["seed"], device=dev,
+                              block_size=PF["B"], skew_std=PF["skew"])
+    pdims = bd.make_dims(1, PF["T"], PF["Hq"], PF["G"], index_dim=PF["di"], block_size=PF["B"], topk=PF["k"])
+    pout = torch.empty_like(pin.q)
+    plse = torch.empty((1, PF["T"], PF["Hq"]), dtype=torch.float32, device=dev)
+    pbidx = torch.empty((1, PF["T"], PF["G"], PF["k"]), dtype=torch.int32, device=dev)
+    pws = torch.empty(bd.msa_workspace_bytes(bd.MSA_OP_PREFILL, pdims), dtype=torch.uint8, device=dev)
+
+    log("generating decode inputs (8 x 1M context)")
+    dec = inputs.make_decode(DC["batch"], DC["L"], DC["Hq"], DC["G"], DC["d"], DC["di"], seed=DC["seed"],
+                             device=dev)
+    ddims = bd.make_dims(DC["batch"], DC["L"], DC["Hq"], DC["G"], index_dim=DC["di"], block_size=DC["B"],
+                         topk=DC["k"])
+    dout = torch.empty((DC["batch"], DC["Hq"], DC["d"]), dtype=torch.bfloat16, device=dev)
+    dlse = torch.empty((DC["batch"], DC["Hq"]), dtype=torch.float32, device=dev)
+    dbidx = torch.empty((DC["batch"], DC["G"], DC["k"]), dtype=torch.int32, device=dev)
+    dws = torch.empty(bd.msa_workspace_bytes(bd.MSA_OP_DECODE, ddims), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def prefill():
+        bd.msa_prefill(pdims, pin.q, pin.k, pin.v, pin.idx_q, pin.idx_k, pout, lse=plse, block_idx=pbidx,
+                       workspace=pws)
+
+    def decode():
+        bd.msa_decode(ddims, dec.q, dec.k_cache, dec.v_cache, dec.idx_q, dec.idx_k_cache, dec.cache_lens,
+                      dout, lse=dlse, block_idx=dbidx, workspace=dws)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        prefill()
+        evs[i][1].record(stream)
+        decode()
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    p_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    d_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    log(f"prefill {p_ms:.3f} ms  decode {d_ms:.3f} ms  wall/step {1e3 * wall / args.steps:.3f} ms")
+
+    # dominant kernel: index scoring + block max over the whole prefill,
+    # the same launch msa_prefill makes (one query chunk covers T=131072)
+    rs = bd.scores_row_stride(pdims, PF["T"])
+    scores = torch.empty((1, PF["T"], PF["G"], rs), dtype=torch.float32, device=dev)
+    idx_ms, _ = timed(lambda: bd.msa_index_scores(pdims, pin.idx_q, pin.idx_k, scores, 0, PF["T"], rs),
+                      args.steps, stream)
+    del scores
+
+    f_index, f_main = prefill_flops(PF["T"], PF["Hq"], PF["G"], PF["d"], PF["di"], PF["B"], PF["k"])
+    dbytes = decode_bytes(DC["batch"], DC["L"], DC["Hq"], DC["G"], DC["d"], DC["di"], DC["B"], DC["k"])
+    idx_tflops = f_index / (idx_ms * 1e-3) / 1e12
+
+    dense = None
+    if not args.no_dense:
+        log("dense (all blocks) comparison")
+        dpd = bd.make_dims(1, PF["T"], PF["Hq"], PF["G"], index_dim=PF["di"], block_size=PF["B"],
+                           topk=PF["k"], flags=bd.MSA_DENSE)
+        dout2 = torch.empty_like(pout)
+        pd_fn = lambda: bd.msa_prefill(dpd, pin.q, pin.k, pin.v, None, None, dout2)  # noqa: E731
+        pd_fn()
+        pd_ms, _ = timed(pd_fn, 2, stream)
+        ddd = bd.make_dims(DC["batch"], DC["L"], DC["Hq"], DC["G"], index_dim=DC["di"], block_size=DC["B"],
+                           topk=DC["k"], flags=bd.MSA_DENSE)
+        dws2 = torch.empty(bd.msa_workspace_bytes(bd.MSA_OP_DECODE, ddd), dtype=torch.uint8, device=dev)
+        dd_fn = lambda: bd.msa_decode(ddd, dec.q, dec.k_cache, dec.v_cache, None, None, dec.cache_lens,  # noqa: E731
+                                      torch.empty_like(dout), workspace=dws2)
+        dd_fn()
+        dd_ms, _ = timed(dd_fn, 3, stream)
+        del dout2, dws2
+        dense = {
+            "prefill_ms": round(pd_ms, 3), "decode_ms": round(dd_ms, 4),
+            "prefill_speedup": round(pd_ms / p_ms, 3), "decode_speedup": round(dd_ms / d_ms, 3),
+            "prefill_tflops": round(dense_prefill_flops(PF["T"], PF["Hq"], PF["d"]) / (pd_ms * 1e-3) / 1e12, 2),
+            "analytic_prefill_cap": round(dense_prefill_flops(PF["T"], PF["Hq"], PF["d"]) / (f_index + f_main), 3),
+        }
+        log(f"dense prefill {pd_ms:.2f} ms, dense decode {dd_ms:.3f} ms")
+
+    cpu, parity, dparity = None, None, None
+    if not args.no_cpu:
+        log("oracle leg on host cores")
+        cpu, parity = cpu_baseline_and_parity(pin, pout, pbidx, args.cpu_tokens, args.cpu_seconds)
+        dparity = decode_parity(dec, dout, dbidx, seqs=[0, 5])
+
+    prefill_tok_s = PF["T"] / (p_ms * 1e-3)
+    decode_tok_s = DC["batch"] / (d_ms * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": round(prefill_tok_s, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * wall / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "MSA prefill T=131072 (B=128, k=16, per-block skewed idx_k) + MSA decode 8 seq x 1,048,576 ctx (B=128, k=16)",
+            "batch": 1, "seq_len": PF["T"], "q_heads": PF["Hq"], "kv_heads": PF["G"], "head_dim": PF["d"],
+            "index_dim": PF["di"], "block_size": PF["B"], "topk": PF["k"],
+            "decode_batch": DC["batch"], "decode_context": DC["L"],
+        },
+        "prefill": {
+            "ms": round(p_ms, 4), "tok_s": round(prefill_tok_s, 1),
+            "algorithmic_tflop": round((f_index + f_main) / 1e12, 3),
+            "tflops": round((f_index + f_main) / (p_ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round((f_index + f_main) / (p_ms * 1e-3) / PEAK_MFMA_BF16, 4),
+        },
+        "decode": {
+            "ms": round(d_ms, 4), "tok_s": round(decode_tok_s, 1),
+            "algorithmic_gbytes": round(dbytes / 1e9, 4),
+            "roofline": {"bound": "hbm", "scope": "whole decode step (all kernels)",
+                         "achieved": round(dbytes / (d_ms * 1e-3) / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
+                         "frac": round(dbytes / (d_ms * 1e-3) / PEAK_HBM, 4)},
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": "index_blockmax_prefill_kernel (index scoring + block max)",
+            "achieved": round(idx_tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
+            "frac": round(idx_tflops * 1e12 / PEAK_MFMA_BF16, 4), "traffic": None,
+            "launch_ms": round(idx_ms, 4), "algorithmic_tflop_per_launch": round(f_index / 1e12, 3),
+        },
+        "dense": dense,
+        "parity": {"prefill_sampled": parity, "decode_sampled": dparity},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -30,7 +30,7 @@ MSA_OP_INDEX_TOPK = 0
 MSA_OP_PREFILL = 1
 MSA_OP_DECODE = 2
 
-EXPORTED = ("msa_index_topk", "msa_prefill", "msa_decode", "msa_workspace_bytes",
+EXPORTED = ("msa_index_scores", "msa_index_topk", "msa_prefill", "msa_decode", "msa_workspace_bytes",
             "msa_status_string", "msa_last_hip_error", "msa_abi_version")
 
 
@@ -76,6 +76,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     pd = ctypes.POINTER(msa_dims)
+    lib.msa_index_scores.argtypes = [pd, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
+    lib.msa_index_scores.restype = i32
     lib.msa_index_topk.argtypes = [pd, vp, vp, vp, vp, sz, vp]
     lib.msa_index_topk.restype = i32
     lib.msa_prefill.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -154,6 +156,24 @@ def _workspace(op, dims, workspace, device):
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device.type != "cuda":
         raise ValueError("workspace must be a contiguous uint8 device tensor")
     return workspace.data_ptr(), workspace.numel()
+
+
+def scores_row_stride(dims: msa_dims, t1: int) -> int:
+    """Smallest valid row_stride of msa_index_scores for query tokens < t1."""
+    L = (t1 - 1) // dims.block_size
+    return max(4, (L + 3) // 4 * 4)
+
+
+def msa_index_scores(dims: msa_dims, idx_q, idx_k, scores, t0: int, t1: int, row_stride: int,
+                     stream=None):
+    lib = load_library()
+    b, T, G, di = dims.batch, dims.seqlen, dims.num_kv_heads, dims.index_dim
+    p_iq = _ptr(idx_q, "idx_q", torch.bfloat16, (b, T, G, di))
+    p_ik = _ptr(idx_k, "idx_k", torch.bfloat16, (b, T, di))
+    p_s = _ptr(scores, "scores", torch.float32, (b, t1 - t0, G, row_stride))
+    _check(lib, lib.msa_index_scores(ctypes.byref(dims), p_iq, p_ik, p_s, t0, t1, row_stride,
+                                     _stream(stream)))
+    return scores
 
 
 def msa_index_topk(dims: msa_dims, idx_q, idx_k, block_idx, workspace=None, stream=None):

@@ -17,7 +17,7 @@ constexpr size_t kAlignWs = 256;
 // Default upper bound of the prefill workspace (per call).  Query chunks are
 // sized so that the block-score table and the block-major partials of one
 // chunk fit in it; MI355X has 288 GB of HBM per GPU.
-constexpr size_t kDefaultPrefillBudget = 32ull << 30;
+constexpr size_t kDefaultPrefillBudget = 80ull << 30;
 constexpr long kMaxInt32 = 2147483647L;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -64,8 +64,8 @@ struct PrefillPlan {
   int s_stride_max = 0;
   long max_work = 0;
   bool with_scores = false, with_main = false;
-  size_t off_S = 0, off_bidx = 0, off_cnt = 0, off_offs = 0, off_epos = 0, off_entries = 0,
-         off_work = 0, off_nwork = 0, off_pO = 0, off_pS = 0;
+  size_t off_S = 0, off_bidx = 0, off_cnt = 0, off_offs = 0, off_bsum = 0, off_epos = 0,
+         off_entries = 0, off_work = 0, off_nwork = 0, off_pO = 0, off_pS = 0;
   size_t total = 0;
 };
 
@@ -73,7 +73,7 @@ size_t per_token_bytes(const msa_dims* d, const PrefillPlan& p) {
   const size_t G = (size_t)d->num_kv_heads;
   size_t b = 0;
   if (p.with_scores) b += G * (size_t)p.s_stride_max * 4 + G * (size_t)d->topk * 4;
-  if (p.with_main) b += G * (size_t)p.KS * (4 + 4 + (size_t)p.R * (128 * 4 + 4));
+  if (p.with_main) b += G * (size_t)p.KS * (4 + 4 + (size_t)p.R * (128 * 2 + 8));
   return b;
 }
 
@@ -130,17 +130,20 @@ int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
     p->off_bidx = L.add(nb_ * Tc * G_ * (size_t)d->topk * 4);
   }
   if (p->with_main) {
-    const size_t nlists = nb_ * G_ * (size_t)p->nb;
+    const size_t nwin = ((size_t)p->Tc + msa::kListWindow - 1) / msa::kListWindow;
+    const size_t nlists = nb_ * G_ * nwin * (size_t)p->nb;
+    const size_t nscan = (nlists + msa::kScanItems - 1) / msa::kScanItems;
     const size_t emax = nb_ * Tc * G_ * (size_t)p->KS;
     p->max_work = (long)((emax + p->mt - 1) / p->mt + nlists);
     p->off_cnt = L.add(nlists * 4);
     p->off_offs = L.add(nlists * 4);
+    p->off_bsum = L.add(nscan * 8);
     p->off_epos = L.add(emax * 4);
     p->off_entries = L.add(emax * 4);
     p->off_work = L.add((size_t)p->max_work * 8);
     p->off_nwork = L.add(4);
-    p->off_pO = L.add(emax * (size_t)p->R * 128 * 4);
-    p->off_pS = L.add(emax * (size_t)p->R * 4);
+    p->off_pO = L.add(emax * (size_t)p->R * 128 * 2);
+    p->off_pS = L.add(emax * (size_t)p->R * 8);
   }
   p->total = L.total;
   return MSA_OK;
@@ -271,6 +274,23 @@ int msa_index_topk(const msa_dims* dims, const void* idx_q, const void* idx_k, i
   return MSA_OK;
 }
 
+int msa_index_scores(const msa_dims* dims, const void* idx_q, const void* idx_k, float* scores,
+                     int32_t t0, int32_t t1, int32_t row_stride, void* hip_stream) {
+  int st = check_dims(dims, false);
+  if (st != MSA_OK) return st;
+  if (dims->flags != 0) return MSA_ERR_INVALID_ARG;
+  if (idx_q == nullptr || idx_k == nullptr || scores == nullptr) return MSA_ERR_INVALID_ARG;
+  if (t0 < 0 || t1 <= t0 || t1 > dims->seqlen) return MSA_ERR_INVALID_ARG;
+  const int Lc = (t1 - 1) / dims->block_size;
+  if (row_stride < 4 || row_stride % 4 != 0 || row_stride < Lc) return MSA_ERR_INVALID_ARG;
+  if (misaligned(idx_q, 16) || misaligned(idx_k, 16) || misaligned(scores, 16)) return MSA_ERR_ALIGNMENT;
+  hipError_t e = msa::launch_index_blockmax_prefill(
+      static_cast<const uint16_t*>(idx_q), static_cast<const uint16_t*>(idx_k), scores, dims->batch,
+      dims->seqlen, dims->num_kv_heads, dims->index_dim, dims->block_size, t0, t1 - t0, row_stride,
+      static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
 int msa_prefill(const msa_dims* dims, const void* q, const void* k, const void* v, const void* idx_q,
                 const void* idx_k, void* out, float* lse, int32_t* block_idx, void* workspace,
                 size_t workspace_bytes, void* hip_stream) {
@@ -316,8 +336,9 @@ int msa_prefill(const msa_dims* dims, const void* q, const void* k, const void* 
   a.entries = at<int32_t>(workspace, p.off_entries);
   a.work = at<int2>(workspace, p.off_work);
   a.n_work = at<int32_t>(workspace, p.off_nwork);
-  a.pO = at<float>(workspace, p.off_pO);
-  a.pS = at<float>(workspace, p.off_pS);
+  a.bsum = at<int32_t>(workspace, p.off_bsum);
+  a.pO = at<uint16_t>(workspace, p.off_pO);
+  a.pS = at<float2>(workspace, p.off_pS);
 
   for (int c = 0; c < p.nchunks; ++c) {
     const int t0 = c * p.Tc;
@@ -344,7 +365,9 @@ int msa_prefill(const msa_dims* dims, const void* q, const void* k, const void* 
     a.t0 = t0;
     a.tc = tc;
     const long emax = (long)dims->batch * tc * dims->num_kv_heads * p.KS;
-    a.max_work = (emax + p.mt - 1) / p.mt + (long)dims->batch * dims->num_kv_heads * p.nb;
+    a.nwin = (tc + msa::kListWindow - 1) / msa::kListWindow;
+    a.nlists = (long)dims->batch * dims->num_kv_heads * a.nwin * p.nb;
+    a.max_work = (emax + p.mt - 1) / p.mt + a.nlists;
     hipError_t e = msa::launch_prefill_main_sparse(a, s);
     if (e != hipSuccess) return hip_fail(e);
   }

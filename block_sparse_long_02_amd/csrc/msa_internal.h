@@ -31,6 +31,13 @@ hipError_t launch_topk_decode(const float* S, int s_stride, int32_t* bidx, const
                               int Lmax, int batch, int G, int B, int k, hipStream_t st);
 
 // ---- Main Branch, prefill ----
+// Query tokens per window of the block lists: the lists of non-local
+// (token, slot) pairs are kept per (sequence, group, window, block), so that
+// consecutive block-major workgroups touch the q rows of one window.
+constexpr int kListWindow = 2048;
+// Workgroup size of the multi-workgroup scans over the lists.
+constexpr int kScanItems = 4096;
+
 struct PrefillMainArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -43,18 +50,21 @@ struct PrefillMainArgs {
   int batch, T, Hq, G, B, topk;
   int t0, tc;             // query chunk
   int KS;                 // partial slots per (token, group) = min(topk, nb)
-  int nbl;                // block lists per (batch, group) = nb
+  int nbl;                // block lists per (batch, group, window) = nb
+  int nwin;               // windows in this chunk = ceil(tc / kListWindow)
+  long nlists;            // batch * G * nwin * nbl
   float scale_log2;       // softmax_scale * log2(e)
   // workspace
-  int32_t* cnt;           // [batch*G*nbl]
-  int32_t* offs;          // [batch*G*nbl]
+  int32_t* cnt;           // [nlists]
+  int32_t* offs;          // [nlists]
+  int32_t* bsum;          // [2 * ceil(nlists / kScanItems)] per-scan-block totals (entries, tiles)
   int32_t* epos;          // [batch*tc*G*KS]
   int32_t* entries;       // [batch*tc*G*KS]
   int2* work;             // [max_work]
   int32_t* n_work;        // [1]
   long max_work;
-  float* pO;              // [batch*tc*G*KS*R*128]
-  float* pS;              // [batch*tc*G*KS*R]
+  uint16_t* pO;           // [batch*tc*G*KS*R*128] fp16, per-row power-of-two scaled
+  float2* pS;             // [batch*tc*G*KS*R] (lse2, log2 of the row's scale)
 };
 hipError_t launch_prefill_main_sparse(const PrefillMainArgs& a, hipStream_t st);
 hipError_t launch_prefill_main_dense(const PrefillMainArgs& a, hipStream_t st);

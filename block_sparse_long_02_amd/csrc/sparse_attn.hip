@@ -110,13 +110,19 @@ __device__ __forceinline__ void load_q(bf16x8* qop, const bf16_t* qp, bool ok, i
 }
 
 // ---------------------------------------------------------------------------
-// Block lists: counting sort of the (token, slot) pairs by (s, g, block).
-// Entry of a row = tl * KS + rank, rank = position among the row's valid
-// non-local entries (so partial storage needs only KS = min(k, nb) slots).
+// Block lists: counting sort of the (token, slot) pairs by
+// (s, g, window, block).  Entry of a row = tl * KS + rank, rank = position
+// among the row's valid non-local entries (so partial storage needs only
+// KS = min(k, nb) slots per row).
 // ---------------------------------------------------------------------------
 __global__ void fill_i32_kernel(int32_t* p, size_t n, int32_t v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     p[i] = v;
+}
+
+__device__ __forceinline__ size_t list_id(const PrefillMainArgs& a, int s, int g, int tl, int b) {
+  const int w = tl / kListWindow;
+  return (((size_t)s * a.G + g) * a.nwin + w) * a.nbl + b;
 }
 
 __global__ void lists_count_kernel(PrefillMainArgs a) {
@@ -134,49 +140,112 @@ __global__ void lists_count_kernel(PrefillMainArgs a) {
   for (int j = 0; j < a.topk && rank < a.KS; ++j) {
     const int e = br[j];
     if (e >= 0 && e < L) {
-      const size_t lid = ((size_t)s * a.G + g) * a.nbl + e;
-      a.epos[(size_t)row * a.KS + rank] = atomicAdd(&a.cnt[lid], 1);
+      a.epos[(size_t)row * a.KS + rank] = atomicAdd(&a.cnt[list_id(a, s, g, tl, e)], 1);
       ++rank;
     }
   }
 }
 
-// Single workgroup: exclusive scans of list sizes and of list tiles; writes
-// the flat work list (list id, tile index) and its length.
-__global__ __launch_bounds__(1024) void lists_scan_kernel(const int32_t* __restrict__ cnt,
-                                                          int32_t* __restrict__ offs, int2* __restrict__ work,
-                                                          int32_t* __restrict__ n_work, long nlists,
-                                                          int mt) {
-  __shared__ long s_e[1024];
-  __shared__ long s_t[1024];
-  const int tid = threadIdx.x;
-  long carry_e = 0, carry_t = 0;
-  for (long base = 0; base < nlists; base += 1024) {
-    const long i = base + tid;
-    const int c = i < nlists ? cnt[i] : 0;
-    const long tiles = (c + mt - 1) / mt;
-    s_e[tid] = c;
-    s_t[tid] = tiles;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      long ve = 0, vt = 0;
-      if (tid >= off) { ve = s_e[tid - off]; vt = s_t[tid - off]; }
-      __syncthreads();
-      s_e[tid] += ve;
-      s_t[tid] += vt;
-      __syncthreads();
-    }
-    const long ex_e = s_e[tid] - c, ex_t = s_t[tid] - tiles;
-    if (i < nlists) {
-      offs[i] = (int32_t)(carry_e + ex_e);
-      const long w0 = carry_t + ex_t;
-      for (long j = 0; j < tiles; ++j) work[w0 + j] = make_int2((int)i, (int)j);
-    }
-    carry_e += s_e[1023];
-    carry_t += s_t[1023];
-    __syncthreads();
+// Exclusive scan of (x, y) pairs across a 1024-thread workgroup; returns the
+// thread's exclusive prefix and writes the workgroup totals.
+__device__ __forceinline__ int2 block_exclusive_scan(int2 v, int2* total) {
+  __shared__ int2 wsum[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int2 x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int yx = __shfl_up(x.x, o, kWave), yy = __shfl_up(x.y, o, kWave);
+    if (lane >= o) { x.x += yx; x.y += yy; }
   }
-  if (tid == 0) n_work[0] = (int32_t)carry_t;
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int2 w = lane < 16 ? wsum[lane] : make_int2(0, 0);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int yx = __shfl_up(w.x, o, kWave), yy = __shfl_up(w.y, o, kWave);
+      if (lane >= o) { w.x += yx; w.y += yy; }
+    }
+    if (lane < 16) wsum[lane] = w;
+  }
+  __syncthreads();
+  const int2 base = wave > 0 ? wsum[wave - 1] : make_int2(0, 0);
+  *total = wsum[15];
+  __syncthreads();
+  return make_int2(base.x + x.x - v.x, base.y + x.y - v.y);
+}
+
+// Phase 1: per scan block (kScanItems lists) totals of entries and tiles.
+__global__ __launch_bounds__(1024) void lists_scan_reduce_kernel(const int32_t* __restrict__ cnt,
+                                                                 int32_t* __restrict__ bsum, long nlists,
+                                                                 int mt) {
+  const long i0 = (long)blockIdx.x * kScanItems + threadIdx.x * 4;
+  int2 v = make_int2(0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const long i = i0 + j;
+    const int c = i < nlists ? cnt[i] : 0;
+    v.x += c;
+    v.y += (c + mt - 1) / mt;
+  }
+  int2 tot;
+  block_exclusive_scan(v, &tot);
+  if (threadIdx.x == 0) {
+    bsum[2 * blockIdx.x] = tot.x;
+    bsum[2 * blockIdx.x + 1] = tot.y;
+  }
+}
+
+// Phase 2 (one workgroup): exclusive scan of the block totals, in place;
+// n_work = number of tiles.
+__global__ __launch_bounds__(1024) void lists_scan_top_kernel(int32_t* __restrict__ bsum, int nblk,
+                                                              int32_t* __restrict__ n_work) {
+  int2 carry = make_int2(0, 0);
+  for (int base = 0; base < nblk; base += 1024) {
+    const int i = base + threadIdx.x;
+    const int2 v = i < nblk ? make_int2(bsum[2 * i], bsum[2 * i + 1]) : make_int2(0, 0);
+    int2 tot;
+    const int2 ex = block_exclusive_scan(v, &tot);
+    if (i < nblk) {
+      bsum[2 * i] = carry.x + ex.x;
+      bsum[2 * i + 1] = carry.y + ex.y;
+    }
+    carry.x += tot.x;
+    carry.y += tot.y;
+  }
+  if (threadIdx.x == 0) n_work[0] = carry.y;
+}
+
+// Phase 3: list offsets and the flat work list (list id, tile index).
+__global__ __launch_bounds__(1024) void lists_scan_final_kernel(const int32_t* __restrict__ cnt,
+                                                                const int32_t* __restrict__ bsum,
+                                                                int32_t* __restrict__ offs,
+                                                                int2* __restrict__ work, long nlists, int mt) {
+  const long i0 = (long)blockIdx.x * kScanItems + threadIdx.x * 4;
+  int c[4];
+  int2 v = make_int2(0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const long i = i0 + j;
+    c[j] = i < nlists ? cnt[i] : 0;
+    v.x += c[j];
+    v.y += (c[j] + mt - 1) / mt;
+  }
+  int2 tot;
+  const int2 ex = block_exclusive_scan(v, &tot);
+  int e_off = bsum[2 * blockIdx.x] + ex.x;
+  int t_off = bsum[2 * blockIdx.x + 1] + ex.y;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const long i = i0 + j;
+    if (i < nlists) {
+      offs[i] = e_off;
+      const int tiles = (c[j] + mt - 1) / mt;
+      for (int tj = 0; tj < tiles; ++tj) work[t_off + tj] = make_int2((int)i, tj);
+      e_off += c[j];
+      t_off += tiles;
+    }
+  }
 }
 
 __global__ void lists_scatter_kernel(PrefillMainArgs a) {
@@ -194,11 +263,51 @@ __global__ void lists_scatter_kernel(PrefillMainArgs a) {
   for (int j = 0; j < a.topk && rank < a.KS; ++j) {
     const int e = br[j];
     if (e >= 0 && e < L) {
-      const size_t lid = ((size_t)s * a.G + g) * a.nbl + e;
+      const size_t lid = list_id(a, s, g, tl, e);
       a.entries[(size_t)a.offs[lid] + a.epos[(size_t)row * a.KS + rank]] = tl * a.KS + rank;
       ++rank;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// fp16 partial rows.  A row holds 128 values in a lane-native order: lane half
+// h of the MFMA output layout stores its 16 values of d-tile dt at positions
+// dt*32 + h*16 + i, where value i has d = 32*dt + 8*(i/4) + 4*h + (i%4).  The
+// row is scaled by 2^-e so that its largest magnitude lies in [2^14, 2^15)
+// (exact power-of-two scaling; no fp16 overflow for any finite input).
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ int row_scale_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int x;
+  frexpf(amax, &x);  // amax = m * 2^x, m in [0.5, 1)
+  int e = x - 15;
+  return e < -100 ? -100 : (e > 100 ? 100 : e);
+}
+
+__device__ __forceinline__ void store_partial_row(uint16_t* row, const f32x16* o, float mul, int half) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8) {
+      f16x8 v;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (_Float16)(o[dt][8 * h8 + j] * mul);
+      *reinterpret_cast<f16x8*>(row + dt * 32 + half * 16 + h8 * 8) = v;
+    }
+}
+
+__device__ __forceinline__ void accumulate_partial_row(float (*acc)[16], const uint16_t* row, float w, int half) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8) {
+      const f16x8 v = *reinterpret_cast<const f16x8*>(row + dt * 32 + half * 16 + h8 * 8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[dt][8 * h8 + j] += w * (float)v[j];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -218,7 +327,8 @@ __global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
   const int2 wk = a.work[w];
   const long lid = wk.x;
   const int b = (int)(lid % a.nbl);
-  const long sg = lid / a.nbl;
+  const long sgw = lid / a.nbl;
+  const long sg = sgw / a.nwin;
   const int g = (int)(sg % a.G);
   const int s = (int)(sg / a.G);
   const int R = a.Hq / a.G;
@@ -231,11 +341,7 @@ __global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
 
-  const size_t kvstride = (size_t)a.G * D;
-  const size_t kvoff = ((size_t)s * a.T + (size_t)b * a.B) * kvstride + (size_t)g * D;
-  stage_k(Ks, a.k + kvoff, kvstride, BS, BS, tid);
-  stage_vt(Vt, VROW, a.v + kvoff, kvstride, BS, BS, tid);
-
+  // this lane's query row: issue its loads before the K/V staging
   const int row = wave * 32 + col;
   const int e = row / R, r = row % R;
   const bool valid = e < ne;
@@ -249,6 +355,11 @@ __global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
   const int h = g * R + r;
   bf16x8 qop[D / 16];
   load_q(qop, a.q + (((size_t)s * a.T + t) * a.Hq + h) * D, valid, half);
+
+  const size_t kvstride = (size_t)a.G * D;
+  const size_t kvoff = ((size_t)s * a.T + (size_t)b * a.B) * kvstride + (size_t)g * D;
+  stage_k(Ks, a.k + kvoff, kvstride, BS, BS, tid);
+  stage_vt(Vt, VROW, a.v + kvoff, kvstride, BS, BS, tid);
   __syncthreads();
 
   f32x16 sacc[KT];
@@ -291,19 +402,19 @@ __global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
     }
   }
 
+  // normalised row = oacc / l, stored as fp16 scaled by 2^-e
+  const float inv = 1.0f / l;
+  float amax = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(oacc[dt][i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, kWave)) * inv;
+  const int ex = row_scale_exp(amax);
   if (valid) {
-    const float inv = 1.0f / l;
     const size_t prow = ((((size_t)s * a.tc + tl) * a.G + g) * a.KS + rank) * R + r;
-    float* dst = a.pO + prow * D;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const float4 vv = make_float4(oacc[dt][4 * i4] * inv, oacc[dt][4 * i4 + 1] * inv,
-                                      oacc[dt][4 * i4 + 2] * inv, oacc[dt][4 * i4 + 3] * inv);
-        *reinterpret_cast<float4*>(dst + dt * 32 + i4 * 8 + 4 * half) = vv;
-      }
-    if (half == 0) a.pS[prow] = mc + __log2f(l);
+    store_partial_row(a.pO + prow * D, oacc, inv * ldexpf(1.0f, -ex), half);
+    if (half == 0) a.pS[prow] = make_float2(mc + __log2f(l), (float)ex);
   }
 }
 
@@ -442,7 +553,7 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
     for (int j = 0; j < a.topk && rank < a.KS; ++j) {
       const int eb = br[j];
       if (eb >= 0 && eb < L) {
-        M2 = fmaxf(M2, a.pS[(prow0 + rank) * R_ + r]);
+        M2 = fmaxf(M2, a.pS[(prow0 + rank) * R_ + r].x);
         ++rank;
       }
     }
@@ -454,25 +565,15 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[dt][i] *= f;
-    // pass 2: weighted partials, in slot order
+    // pass 2: weighted partials, in slot order (weight folds in the row scale 2^e)
     rank = 0;
     for (int j = 0; j < a.topk && rank < a.KS; ++j) {
       const int eb = br[j];
       if (eb >= 0 && eb < L) {
         const size_t prow = (prow0 + rank) * R_ + r;
-        const float wj = __builtin_amdgcn_exp2f(a.pS[prow] - M2u);
-        sumw += wj;
-        const float* src = a.pO + prow * D;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const float4 pv = *reinterpret_cast<const float4*>(src + dt * 32 + i4 * 8 + 4 * half);
-            o[dt][4 * i4] += wj * pv.x;
-            o[dt][4 * i4 + 1] += wj * pv.y;
-            o[dt][4 * i4 + 2] += wj * pv.z;
-            o[dt][4 * i4 + 3] += wj * pv.w;
-          }
+        const float2 st = a.pS[prow];
+        sumw += __builtin_amdgcn_exp2f(st.x - M2u);
+        accumulate_partial_row(o, a.pO + prow * D, __builtin_amdgcn_exp2f(st.x - M2u + st.y), half);
         ++rank;
       }
     }
@@ -516,8 +617,7 @@ hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t value, hipStream_t st) 
 }
 
 hipError_t launch_prefill_main_sparse(const PrefillMainArgs& a, hipStream_t st) {
-  const long nlists = (long)a.batch * a.G * a.nbl;
-  hipError_t err = launch_fill_i32(a.cnt, (size_t)nlists, 0, st);
+  hipError_t err = launch_fill_i32(a.cnt, (size_t)a.nlists, 0, st);
   if (err != hipSuccess) return err;
   const long n_rows = (long)a.batch * a.tc * a.G;
   const unsigned rgrid = (unsigned)((n_rows + 255) / 256);
@@ -525,7 +625,12 @@ hipError_t launch_prefill_main_sparse(const PrefillMainArgs& a, hipStream_t st) 
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int R = a.Hq / a.G;
   const int mt = kAttnRows / R;
-  lists_scan_kernel<<<1, 1024, 0, st>>>(a.cnt, a.offs, a.work, a.n_work, nlists, mt);
+  const int nblk = (int)((a.nlists + kScanItems - 1) / kScanItems);
+  lists_scan_reduce_kernel<<<nblk, 1024, 0, st>>>(a.cnt, a.bsum, a.nlists, mt);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  lists_scan_top_kernel<<<1, 1024, 0, st>>>(a.bsum, nblk, a.n_work);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  lists_scan_final_kernel<<<nblk, 1024, 0, st>>>(a.cnt, a.bsum, a.offs, a.work, a.nlists, mt);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   lists_scatter_kernel<<<rgrid, 256, 0, st>>>(a);
   if ((err = hipGetLastError()) != hipSuccess) return err;

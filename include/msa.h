@@ -103,6 +103,18 @@ int msa_index_topk(const msa_dims* dims, const void* idx_q, const void* idx_k,
                    void* hip_stream);
 
 /*
+ * Index scores + Block-Max pooling only (the first half of the Index Branch),
+ * for query tokens [t0, t1) of prefill-shaped inputs:
+ *   scores[s][t - t0][g][b] = max over keys j of block b of idx_q[s,t,g] . idx_k[s,j]
+ * for every candidate block b < L(t) = t / block_size, in fp32 (products of
+ * bf16 values accumulated in fp32).  scores is [batch, t1 - t0, G, row_stride]
+ * fp32 with row_stride a multiple of 4 and >= L(t1 - 1); entries b >= L(t) of
+ * a row are unspecified.  No workspace.  Flags must be 0.
+ */
+int msa_index_scores(const msa_dims* dims, const void* idx_q, const void* idx_k, float* scores,
+                     int32_t t0, int32_t t1, int32_t row_stride, void* hip_stream);
+
+/*
  * Prefill: Index Branch + Main Branch over a whole causal sequence.
  *   q         [batch, T, Hq, d] bf16
  *   k, v      [batch, T, G, d]  bf16

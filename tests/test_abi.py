@@ -81,11 +81,11 @@ def test_workspace_bytes(lib):
     assert lib.msa_workspace_bytes(bd.MSA_OP_PREFILL, None) == BAD
     # a forced small chunk shrinks the workspace
     assert _ws(lib, bd.MSA_OP_PREFILL, _dims(query_chunk=256)) < n_pre
-    # 128K prefill, 64 q heads / 8 groups, default chunking stays within 32 GiB + overhead
+    # 128K and 1M prefill, 64 q heads / 8 groups: default chunking keeps the workspace near 80 GiB
     big = _dims(seqlen=131072, num_q_heads=64, num_kv_heads=8, index_dim=128, topk=16)
-    assert _ws(lib, bd.MSA_OP_PREFILL, big) < (33 << 30)
+    assert _ws(lib, bd.MSA_OP_PREFILL, big) < (81 << 30)
     big1m = _dims(seqlen=1 << 20, num_q_heads=64, num_kv_heads=8, index_dim=128, topk=16)
-    assert _ws(lib, bd.MSA_OP_PREFILL, big1m) < (33 << 30)
+    assert _ws(lib, bd.MSA_OP_PREFILL, big1m) < (81 << 30)
 
 
 @pytest.mark.parametrize("field,value,status", [
