@@ -10,12 +10,12 @@
 //    every idx_k byte read feeds all groups.  Grid: sequences x block ranges;
 //    each wave owns a few consecutive blocks.
 // 2. the shared top-k kernel selects the blocks (local block forced).
-// 3. decode_attn_kernel: one workgroup per (sequence, group, work item); a
-//    work item is one selected block (sparse) or a run of consecutive blocks
-//    (dense), attended with online softmax; it writes a normalised partial
-//    output and its base-2 log-sum-exp per head.
-// 4. decode_combine_kernel merges the work items of each (sequence, group) in
-//    fixed order (no atomics) and rounds to bf16.
+// 3. decode_attn_kernel: 8 waves per (sequence, group) share its selected
+//    blocks (or, in dense mode, runs of consecutive blocks), attend them on
+//    MFMA with online softmax and merge in LDS in fixed order (no atomics).
+// 4. only when one workgroup cannot hold all work items of a (sequence,
+//    group) (dense mode, large top-k), decode_combine_kernel merges the
+//    workgroups' normalised partials in fixed order.
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -24,9 +24,8 @@ namespace msa {
 namespace {
 
 constexpr int D = 128;
-constexpr int kDecMaxR = 16;     // query heads per group handled by the decode kernels
+constexpr int kDecMaxR = 16;     // query heads per group handled by the decode kernels (<= 32 MFMA columns)
 constexpr int kDecBlocksPerWave = 2;
-constexpr int kDecKeyTile = 64;
 
 template <int DI, int BS>
 __global__ __launch_bounds__(256) void decode_index_kernel(const bf16_t* __restrict__ idx_q,
@@ -77,132 +76,244 @@ __global__ __launch_bounds__(256) void decode_index_kernel(const bf16_t* __restr
   }
 }
 
-// One (s, g, work item) per workgroup of 256 threads.
-__global__ __launch_bounds__(256) void decode_attn_kernel(DecodeMainArgs a) {
-  __shared__ float qs[kDecMaxR][D];
-  __shared__ __attribute__((aligned(16))) bf16_t Kt[kDecKeyTile][D + 8];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[kDecKeyTile][D];
-  __shared__ float P[kDecMaxR][kDecKeyTile];
-  __shared__ float m_run[kDecMaxR], l_run[kDecMaxR], alpha_s[kDecMaxR];
+// ---------------------------------------------------------------------------
+// Decode attention.  A workgroup of kDecAttnWaves waves owns (s, g, part x)
+// and work items part*W*ipw .. ; wave w takes items x*W*ipw + w + W*i,
+// i < ipw.  A work item is one selected block (sparse / given) or a run of
+// blocks_per_split consecutive blocks (dense).  Each wave attends its keys
+// in sub-tiles of up to 64 with online softmax: S^T = K.Q^T on MFMA with the
+// K rows loaded straight into the A operand, V transposed through the
+// wave's own LDS area for the P.V product.  The waves then merge in LDS in
+// fixed order; with one part per (s, g) the merge writes the output, else a
+// normalised partial that decode_combine_kernel merges.
+// ---------------------------------------------------------------------------
+constexpr int kDecAttnWaves = 8;
 
-  const int j = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+template <int BS>
+struct DecTile {
+  static constexpr int NK = BS < 64 ? BS : 64;   // keys per sub-tile
+  static constexpr int VROW = NK + 4;
+  static constexpr int VT_BYTES = D * VROW * 2;  // per wave
+  static constexpr int CMB_BYTES = (64 * 64 + 2 * 64) * 4;
+  static constexpr int AREA = VT_BYTES > CMB_BYTES ? VT_BYTES : CMB_BYTES;
+};
+
+__device__ __forceinline__ void dec_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int BS>
+__global__ __launch_bounds__(kDecAttnWaves * 64) void decode_attn_kernel(DecodeMainArgs a, int ipw, int nparts) {
+  using Tl = DecTile<BS>;
+  constexpr int NK = Tl::NK, VROW = Tl::VROW, KTL = NK / 32;
+  __shared__ __attribute__((aligned(16))) unsigned char dec_smem[kDecAttnWaves * Tl::AREA];
+
+  const int x = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int R = a.Hq / a.G;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
+  unsigned char* area = dec_smem + (size_t)wave * Tl::AREA;
+  bf16_t* Vt = reinterpret_cast<bf16_t*>(area);
   const int len = min(max(a.lens[s], 1), a.Lmax);
   const int t = len - 1;
   const int L = t / a.B;
+  const float c = a.scale_log2;
 
-  int blk_lo, blk_hi;  // inclusive block range of this work item
-  if (a.dense) {
-    blk_lo = j * a.blocks_per_split;
-    blk_hi = min(blk_lo + a.blocks_per_split - 1, L);
-  } else {
-    const int e = a.bidx[((size_t)s * a.G + g) * a.topk + j];
-    blk_lo = e;
-    blk_hi = (e >= 0 && e <= L) ? e : e - 1;  // empty when not a visible block
-  }
-  const size_t prow0 = (((size_t)s * a.G + g) * a.nsplit + j) * R;
-  if (blk_lo > blk_hi || blk_lo < 0) {
-    for (int i = tid; i < R; i += 256) a.pS[prow0 + i] = -INFINITY;
-    for (int i = tid; i < R * D; i += 256) a.pO[prow0 * D + i] = 0.f;
-    return;
-  }
-  const int k_lo = blk_lo * a.B;
-  const int k_hi = min((blk_hi + 1) * a.B, len) - 1;
-
-  for (int i = tid; i < R * D; i += 256) {
-    const int r = i / D, d = i % D;
-    qs[r][d] = (float)__builtin_bit_cast(__bf16, a.q[((size_t)s * a.Hq + g * R + r) * D + d]);
-  }
-  if (tid < kDecMaxR) {
-    m_run[tid] = -INFINITY;
-    l_run[tid] = 0.f;
-  }
-  float o[kDecMaxR / 2];
+  // B operand: Q^T, column = head (col < R)
+  const bool hv = col < R;
+  bf16x8 qop[D / 16];
+  {
+    const bf16_t* qp = a.q + ((size_t)s * a.Hq + g * R + (hv ? col : 0)) * D;
 #pragma unroll
-  for (int i = 0; i < kDecMaxR / 2; ++i) o[i] = 0.f;
-  const int od = tid & (D - 1), oh = tid >> 7;  // PV ownership: d, heads oh + 2i
-
+    for (int ks = 0; ks < D / 16; ++ks) qop[ks] = hv ? load_bf16x8(qp + 16 * ks + 8 * half) : zero_bf16x8();
+  }
   const size_t kvstride = (size_t)a.G * D;
   const bf16_t* kseq = a.k + (size_t)s * a.Lmax * kvstride + (size_t)g * D;
   const bf16_t* vseq = a.v + (size_t)s * a.Lmax * kvstride + (size_t)g * D;
-  const float c = a.scale_log2;
 
-  for (int kb = k_lo; kb <= k_hi; kb += kDecKeyTile) {
-    const int nvalid = min(kDecKeyTile, k_hi + 1 - kb);
-    __syncthreads();
-    for (int ci = tid; ci < kDecKeyTile * (D / 8); ci += 256) {
-      const int key = ci >> 4, part = ci & 15;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (key < nvalid) {
-        kv = *reinterpret_cast<const uint4*>(kseq + (size_t)(kb + key) * kvstride + part * 8);
-        vv = *reinterpret_cast<const uint4*>(vseq + (size_t)(kb + key) * kvstride + part * 8);
-      }
-      *reinterpret_cast<uint4*>(&Kt[key][part * 8]) = kv;
-      *reinterpret_cast<uint4*>(&Vs[key][part * 8]) = vv;
-    }
-    __syncthreads();
-    // scores: key = lane, heads wave + 4i
-    for (int r = wave; r < R; r += 4) {
-      float acc = 0.f;
-      const bf16_t* kr = &Kt[lane][0];
-#pragma unroll 8
-      for (int d8 = 0; d8 < D / 8; ++d8) {
-        const uint4 kk = *reinterpret_cast<const uint4*>(kr + d8 * 8);
-        const uint32_t w[4] = {kk.x, kk.y, kk.z, kk.w};
+  float m = -INFINITY, l = 0.f;
+  f32x16 oacc[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc += qs[r][d8 * 8 + 2 * e] * __uint_as_float(w[e] << 16);
-          acc += qs[r][d8 * 8 + 2 * e + 1] * __uint_as_float(w[e] & 0xffff0000u);
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
+
+  for (int i = 0; i < ipw; ++i) {
+    const int item = x * kDecAttnWaves * ipw + wave + kDecAttnWaves * i;
+    if (item >= a.nsplit) break;
+    int blk_lo, blk_hi;
+    if (a.dense) {
+      blk_lo = item * a.blocks_per_split;
+      blk_hi = min(blk_lo + a.blocks_per_split - 1, L);
+    } else {
+      const int e = a.bidx[((size_t)s * a.G + g) * a.topk + item];
+      blk_lo = e;
+      blk_hi = (e >= 0 && e <= L) ? e : e - 1;
+    }
+    if (blk_lo < 0 || blk_lo > blk_hi) continue;
+    const int k_end = min((blk_hi + 1) * a.B, len);  // exclusive
+    for (int kb = blk_lo * a.B; kb < k_end; kb += NK) {
+      // K rows as MFMA A operands, V units for the transposed LDS tile
+      bf16x8 kop[KTL][D / 16];
+#pragma unroll
+      for (int kt = 0; kt < KTL; ++kt) {
+        const int key = kb + kt * 32 + col;
+        const bool kv = key < k_end;
+        const bf16_t* kr = kseq + (size_t)(kv ? key : kb) * kvstride + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) kop[kt][ks] = kv ? load_bf16x8(kr + 16 * ks) : zero_bf16x8();
+      }
+      constexpr int UNITS = (NK / 4) * (D / 4) / 64;  // 4x4 units per lane
+      u32x2 vr[UNITS][4];
+#pragma unroll
+      for (int u = 0; u < UNITS; ++u) {
+        const int unit = lane + 64 * u;
+        const int k4 = unit >> 5, dq = unit & 31;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = kb + k4 * 4 + j;
+          vr[u][j] = key < k_end ? *reinterpret_cast<const u32x2*>(vseq + (size_t)key * kvstride + dq * 4)
+                                 : u32x2{0u, 0u};
         }
       }
-      const float x = (lane < nvalid) ? acc * c : -INFINITY;
-      const float tmx = wave_max(x);
-      const float m_old = m_run[r];
-      const float m_new = fmaxf(m_old, tmx);
-      const float p = __builtin_amdgcn_exp2f(x - m_new);
-      const float ps = wave_sum(p);
-      P[r][lane] = p;
-      if (lane == 0) {
-        const float al = __builtin_amdgcn_exp2f(m_old - m_new);
-        alpha_s[r] = al;
-        l_run[r] = l_run[r] * al + ps;
-        m_run[r] = m_new;
-      }
-    }
-    __syncthreads();
-    // P.V: thread owns d = od for heads oh + 2i
+      dec_wave_sync();  // previous sub-tile's V reads are done
 #pragma unroll
-    for (int i = 0; i < kDecMaxR / 2; ++i) {
-      const int r = oh + 2 * i;
-      if (r < R) {
-        float acc = o[i] * alpha_s[r];
-        for (int key = 0; key < nvalid; ++key)
-          acc += P[r][key] * (float)__builtin_bit_cast(__bf16, Vs[key][od]);
-        o[i] = acc;
+      for (int u = 0; u < UNITS; ++u) {
+        const int unit = lane + 64 * u;
+        const int k4 = unit >> 5, dq = unit & 31;
+        const u32x2* xx = vr[u];
+        u32x2 o[4];
+        o[0] = u32x2{(xx[0][0] & 0xffffu) | (xx[1][0] << 16), (xx[2][0] & 0xffffu) | (xx[3][0] << 16)};
+        o[1] = u32x2{(xx[0][0] >> 16) | (xx[1][0] & 0xffff0000u), (xx[2][0] >> 16) | (xx[3][0] & 0xffff0000u)};
+        o[2] = u32x2{(xx[0][1] & 0xffffu) | (xx[1][1] << 16), (xx[2][1] & 0xffffu) | (xx[3][1] << 16)};
+        o[3] = u32x2{(xx[0][1] >> 16) | (xx[1][1] & 0xffff0000u), (xx[2][1] >> 16) | (xx[3][1] & 0xffff0000u)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(Vt + (dq * 4 + j) * VROW + k4 * 4) = o[j];
+      }
+      dec_wave_sync();
+
+      f32x16 sacc[KTL];
+#pragma unroll
+      for (int kt = 0; kt < KTL; ++kt) {
+        sacc[kt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) sacc[kt] = mfma32x32x16(kop[kt][ks], qop[ks], sacc[kt]);
+      }
+      float tmx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < KTL; ++kt)
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+          const int key = kb + kt * 32 + 8 * (ii / 4) + 4 * half + (ii % 4);
+          sacc[kt][ii] = key < k_end ? sacc[kt][ii] : -INFINITY;
+          tmx = fmaxf(tmx, sacc[kt][ii]);
+        }
+      tmx = fmaxf(tmx, __shfl_xor(tmx, 32, kWave));
+      const float m_new = fmaxf(m, tmx);  // finite: the sub-tile has >= 1 key
+      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
+      const float muc = m_new * c;
+      float ps = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < KTL; ++kt)
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+          const float p = __builtin_amdgcn_exp2f(sacc[kt][ii] * c - muc);
+          sacc[kt][ii] = p;
+          ps += p;
+        }
+      ps += __shfl_xor(ps, 32, kWave);
+      l = l * alpha + ps;
+      m = m_new;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) oacc[dt][ii] *= alpha;
+#pragma unroll
+        for (int kt = 0; kt < KTL; ++kt) {
+          bf16x8 p0, p1;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p0[e] = (__bf16)sacc[kt][e];
+            p1[e] = (__bf16)sacc[kt][8 + e];
+          }
+          const bf16_t* vr0 = Vt + (dt * 32 + col) * VROW + kt * 32 + 4 * half;
+          oacc[dt] = mfma32x32x16(join_bf16x4(*reinterpret_cast<const u32x2*>(vr0),
+                                              *reinterpret_cast<const u32x2*>(vr0 + 8)), p0, oacc[dt]);
+          oacc[dt] = mfma32x32x16(join_bf16x4(*reinterpret_cast<const u32x2*>(vr0 + 16),
+                                              *reinterpret_cast<const u32x2*>(vr0 + 24)), p1, oacc[dt]);
+        }
       }
     }
   }
+
+  // merge the waves (fixed order) through LDS
   __syncthreads();
+  float* cm = reinterpret_cast<float*>(area);  // [64 values][64 lanes], then m[64], l[64]
 #pragma unroll
-  for (int i = 0; i < kDecMaxR / 2; ++i) {
-    const int r = oh + 2 * i;
-    if (r < R) a.pO[(prow0 + r) * D + od] = o[i] / l_run[r];
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) cm[(dt * 16 + ii) * 64 + lane] = oacc[dt][ii];
+  cm[64 * 64 + lane] = m;
+  cm[64 * 64 + 64 + lane] = l;
+  __syncthreads();
+  // wave w merges value slots [8w, 8w+8) of every lane
+  float M = -INFINITY;
+  for (int w = 0; w < kDecAttnWaves; ++w) {
+    const float* cw = reinterpret_cast<const float*>(dec_smem + (size_t)w * Tl::AREA);
+    M = fmaxf(M, cw[64 * 64 + lane]);
   }
-  if (tid < R) a.pS[prow0 + tid] = m_run[tid] + __log2f(l_run[tid]);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float sw = 0.f, acc[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) acc[v] = 0.f;
+  for (int w = 0; w < kDecAttnWaves; ++w) {
+    const float* cw = reinterpret_cast<const float*>(dec_smem + (size_t)w * Tl::AREA);
+    const float mw = cw[64 * 64 + lane];
+    const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mw - Mu) * c);
+    sw += f * cw[64 * 64 + 64 + lane];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc[v] += f * cw[(wave * 8 + v) * 64 + lane];
+  }
+  if (!hv) return;
+  const int h = g * R + col;
+  const float inv = sw > 0.f ? 1.0f / sw : 0.f;
+  const float lse2 = sw > 0.f ? Mu * c + __log2f(sw) : -INFINITY;
+  // value slot (dt, ii) = wave*8 + v  ->  d = 32 dt + 8 (ii/4) + 4 half + ii%4
+  if (nparts == 1) {
+    bf16_t* dst = a.out + ((size_t)s * a.Hq + h) * D;
+#pragma unroll
+    for (int v = 0; v < 8; v += 4) {
+      const int slot = wave * 8 + v, dt = slot / 16, ii = slot % 16;
+      bf16x4 o4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o4[j] = (__bf16)(acc[v + j] * inv);
+      *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * (ii / 4) + 4 * half) = o4;
+    }
+    if (a.lse != nullptr && wave == 0 && half == 0) a.lse[(size_t)s * a.Hq + h] = lse2 * kLn2;
+  } else {
+    const size_t prow = (((size_t)s * a.G + g) * nparts + x) * R + col;
+    float* dst = a.pO + prow * D;
+#pragma unroll
+    for (int v = 0; v < 8; v += 4) {
+      const int slot = wave * 8 + v, dt = slot / 16, ii = slot % 16;
+      *reinterpret_cast<f32x4*>(dst + 32 * dt + 8 * (ii / 4) + 4 * half) =
+          f32x4{acc[v] * inv, acc[v + 1] * inv, acc[v + 2] * inv, acc[v + 3] * inv};
+    }
+    if (wave == 0 && half == 0) a.pS[prow] = lse2;
+  }
 }
 
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeMainArgs a) {
+// Merges the nparts partials of every (s, g) in fixed order.
+__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeMainArgs a, int nparts) {
   const int g = blockIdx.x, s = blockIdx.y;
   const int R = a.Hq / a.G;
   const int d = threadIdx.x;
   for (int r = 0; r < R; ++r) {
-    const size_t base = ((size_t)s * a.G + g) * a.nsplit;
+    const size_t base = ((size_t)s * a.G + g) * nparts;
     float M2 = -INFINITY;
-    for (int j = 0; j < a.nsplit; ++j) M2 = fmaxf(M2, a.pS[(base + j) * R + r]);
+    for (int j = 0; j < nparts; ++j) M2 = fmaxf(M2, a.pS[(base + j) * R + r]);
     const float Mu = (M2 == -INFINITY) ? 0.f : M2;
     float sw = 0.f, acc = 0.f;
-    for (int j = 0; j < a.nsplit; ++j) {
+    for (int j = 0; j < nparts; ++j) {
       const size_t prow = (base + j) * R + r;
       const float w = __builtin_amdgcn_exp2f(a.pS[prow] - Mu);
       sw += w;
@@ -239,11 +350,32 @@ hipError_t launch_index_blockmax_decode(const uint16_t* idx_q, const uint16_t* i
   return hipGetLastError();
 }
 
+// Work items per wave and workgroups per (s, g) for nsplit items.
+void decode_partition(int nsplit, int* ipw, int* nparts) {
+  // up to 4 items per wave keeps one workgroup per (s, g) for the sparse
+  // case (16 selected blocks); long dense runs use one item per wave
+  if (nsplit <= kDecAttnWaves * 4) {
+    *ipw = (nsplit + kDecAttnWaves - 1) / kDecAttnWaves;
+    *nparts = 1;
+  } else {
+    *ipw = 1;
+    *nparts = (nsplit + kDecAttnWaves - 1) / kDecAttnWaves;
+  }
+}
+
 hipError_t launch_decode_main(const DecodeMainArgs& a, hipStream_t st) {
-  decode_attn_kernel<<<dim3(a.nsplit, a.G, a.batch), 256, 0, st>>>(a);
+  int ipw, nparts;
+  decode_partition(a.nsplit, &ipw, &nparts);
+  const dim3 grid(nparts, a.G, a.batch);
+#define MSA_DEC_ATTN(BS_)                                                                          \
+  decode_attn_kernel<BS_><<<grid, kDecAttnWaves * 64, 0, st>>>(a, ipw, nparts)
+  if (a.B == 128) MSA_DEC_ATTN(128);
+  else if (a.B == 64) MSA_DEC_ATTN(64);
+  else MSA_DEC_ATTN(32);
+#undef MSA_DEC_ATTN
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  decode_combine_kernel<<<dim3(a.G, a.batch), 128, 0, st>>>(a);
+  if (err != hipSuccess || nparts == 1) return err;
+  decode_combine_kernel<<<dim3(a.G, a.batch), 128, 0, st>>>(a, nparts);
   return hipGetLastError();
 }
 

@@ -98,22 +98,31 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
     const int cur = b & 1;
     if (b + 1 < nblk) MSA_IDX_GLOAD(b + 1);
 
+    // KTS key tiles x 2 row tiles = independent MFMA accumulator chains
+    constexpr int KTS = ktiles >= 2 ? 2 : 1;
     float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < ktiles; ++kt) {
-      f32x16 acc0 = {}, acc1 = {};
+    for (int kt = 0; kt < ktiles; kt += KTS) {
+      f32x16 acc[KTS][2];
+#pragma unroll
+      for (int u = 0; u < KTS; ++u) acc[u][0] = acc[u][1] = f32x16{};
       const bf16_t* arow = &kbuf[cur][(kt * 32 + col) * KPAD + 8 * half];
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 16 * ks);
-        acc0 = mfma32x32x16(a, qop[0][ks], acc0);
-        acc1 = mfma32x32x16(a, qop[1][ks], acc1);
+#pragma unroll
+        for (int u = 0; u < KTS; ++u) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + u * 32 * KPAD + 16 * ks);
+          acc[u][0] = mfma32x32x16(a, qop[0][ks], acc[u][0]);
+          acc[u][1] = mfma32x32x16(a, qop[1][ks], acc[u][1]);
+        }
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        mx0 = fmaxf(mx0, acc0[i]);
-        mx1 = fmaxf(mx1, acc1[i]);
-      }
+      for (int u = 0; u < KTS; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          mx0 = fmaxf(mx0, fmaxf(acc[u][0][i], acc[u][0][i + 1]));
+          mx1 = fmaxf(mx1, fmaxf(acc[u][1][i], acc[u][1][i + 1]));
+        }
     }
     mx0 = fmaxf(mx0, __shfl_xor(mx0, 32, kWave));
     mx1 = fmaxf(mx1, __shfl_xor(mx1, 32, kWave));

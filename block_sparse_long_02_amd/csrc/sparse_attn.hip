@@ -77,6 +77,54 @@ __device__ __forceinline__ void stage_vt(bf16_t* Vt, int vrow, const bf16_t* __r
   }
 }
 
+// Whole-block K/V staging through registers with compile-time trip counts:
+// every global load of the block is issued before the first LDS write.
+template <int BS>
+struct BlockRegs {
+  u32x4 k[BS / 16];     // 16-byte chunks of K rows: chunk c = tid + 256 i
+  u32x2 v[BS / 32][4];  // 4 keys x 4 d units of V: unit u = tid + 256 i
+};
+
+template <int BS>
+__device__ __forceinline__ void block_load(BlockRegs<BS>& r, const bf16_t* __restrict__ kbase,
+                                           const bf16_t* __restrict__ vbase, size_t stride, int tid) {
+#pragma unroll
+  for (int i = 0; i < BS / 16; ++i) {
+    const int c = tid + 256 * i;
+    r.k[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(c >> 4) * stride + (c & 15) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < BS / 32; ++i) {
+    const int u = tid + 256 * i;
+    const int k4 = u >> 5, dq = u & 31;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      r.v[i][j] = *reinterpret_cast<const u32x2*>(vbase + (size_t)(k4 * 4 + j) * stride + dq * 4);
+  }
+}
+
+template <int BS>
+__device__ __forceinline__ void block_store(const BlockRegs<BS>& r, bf16_t* Ks, bf16_t* Vt, int vrow, int tid) {
+#pragma unroll
+  for (int i = 0; i < BS / 16; ++i) {
+    const int c = tid + 256 * i;
+    *reinterpret_cast<u32x4*>(Ks + (c >> 4) * KROW + (c & 15) * 8) = r.k[i];
+  }
+#pragma unroll
+  for (int i = 0; i < BS / 32; ++i) {
+    const int u = tid + 256 * i;
+    const int k4 = u >> 5, dq = u & 31;
+    const u32x2* x = r.v[i];
+    u32x2 o[4];
+    o[0] = u32x2{(x[0][0] & 0xffffu) | (x[1][0] << 16), (x[2][0] & 0xffffu) | (x[3][0] << 16)};
+    o[1] = u32x2{(x[0][0] >> 16) | (x[1][0] & 0xffff0000u), (x[2][0] >> 16) | (x[3][0] & 0xffff0000u)};
+    o[2] = u32x2{(x[0][1] & 0xffffu) | (x[1][1] << 16), (x[2][1] & 0xffffu) | (x[3][1] << 16)};
+    o[3] = u32x2{(x[0][1] >> 16) | (x[1][1] & 0xffff0000u), (x[2][1] >> 16) | (x[3][1] & 0xffff0000u)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(Vt + (dq * 4 + j) * vrow + k4 * 4) = o[j];
+  }
+}
+
 // S^T tile (32 keys x 32 query rows) = K[32 x D] . Q^T, A operand from LDS.
 __device__ __forceinline__ f32x16 qk_tile(const bf16_t* Ks, int key0, const bf16x8* qop, int col,
                                           int half) {
@@ -341,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
 
-  // this lane's query row: issue its loads before the K/V staging
+  // issue every global load first: list entry, the K/V block, the q row
   const int row = wave * 32 + col;
   const int e = row / R, r = row % R;
   const bool valid = e < ne;
@@ -351,15 +399,15 @@ __global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
     tl = ent / a.KS;
     rank = ent % a.KS;
   }
+  const size_t kvstride = (size_t)a.G * D;
+  const size_t kvoff = ((size_t)s * a.T + (size_t)b * a.B) * kvstride + (size_t)g * D;
+  BlockRegs<BS> regs;
+  block_load<BS>(regs, a.k + kvoff, a.v + kvoff, kvstride, tid);
   const int t = a.t0 + tl;
   const int h = g * R + r;
   bf16x8 qop[D / 16];
   load_q(qop, a.q + (((size_t)s * a.T + t) * a.Hq + h) * D, valid, half);
-
-  const size_t kvstride = (size_t)a.G * D;
-  const size_t kvoff = ((size_t)s * a.T + (size_t)b * a.B) * kvstride + (size_t)g * D;
-  stage_k(Ks, a.k + kvoff, kvstride, BS, BS, tid);
-  stage_vt(Vt, VROW, a.v + kvoff, kvstride, BS, BS, tid);
+  block_store<BS>(regs, Ks, Vt, VROW, tid);
   __syncthreads();
 
   f32x16 sacc[KT];
@@ -548,15 +596,17 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
   if (!DENSE) {
     const size_t prow0 = (((size_t)s * a.tc + tl) * a.G + g) * a.KS;
     const int R_ = R;
-    // pass 1: the merged maximum
-    int rank = 0;
-    for (int j = 0; j < a.topk && rank < a.KS; ++j) {
+    // the row's partial slots are its valid non-local entries, ranks 0..nv-1
+    int nv = 0;
+    for (int j = 0; j < a.topk && nv < a.KS; ++j) {
       const int eb = br[j];
-      if (eb >= 0 && eb < L) {
-        M2 = fmaxf(M2, a.pS[(prow0 + rank) * R_ + r].x);
-        ++rank;
-      }
+      nv += (eb >= 0 && eb < L) ? 1 : 0;
     }
+    const float2* ps = a.pS + prow0 * R_ + r;     // rank q at ps[q * R_]
+    const uint16_t* po = a.pO + (prow0 * R_ + r) * D;
+    const size_t po_step = (size_t)R_ * D;
+    // pass 1: the merged maximum
+    for (int q = 0; q < nv; ++q) M2 = fmaxf(M2, ps[(size_t)q * R_].x);
     const float M2u = (M2 == -INFINITY) ? 0.f : M2;
     const float wl = (l > 0.f) ? __builtin_amdgcn_exp2f(lse2_loc - M2u) : 0.f;
     sumw = wl;
@@ -565,17 +615,13 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[dt][i] *= f;
-    // pass 2: weighted partials, in slot order (weight folds in the row scale 2^e)
-    rank = 0;
-    for (int j = 0; j < a.topk && rank < a.KS; ++j) {
-      const int eb = br[j];
-      if (eb >= 0 && eb < L) {
-        const size_t prow = (prow0 + rank) * R_ + r;
-        const float2 st = a.pS[prow];
-        sumw += __builtin_amdgcn_exp2f(st.x - M2u);
-        accumulate_partial_row(o, a.pO + prow * D, __builtin_amdgcn_exp2f(st.x - M2u + st.y), half);
-        ++rank;
-      }
+    // pass 2: weighted partials in rank (= slot) order; the weight folds in
+    // the row scale 2^e
+#pragma unroll 2
+    for (int q = 0; q < nv; ++q) {
+      const float2 st = ps[(size_t)q * R_];
+      sumw += __builtin_amdgcn_exp2f(st.x - M2u);
+      accumulate_partial_row(o, po + (size_t)q * po_step, __builtin_amdgcn_exp2f(st.x - M2u + st.y), half);
     }
     M2 = M2u;
   } else {

@@ -51,8 +51,8 @@ __device__ __forceinline__ uint32_t kth_largest_lanes(uint32_t key, int kth) {
   return tau;
 }
 
-// Keys and block ids of the candidate list, either the compacted LDS list or
-// the whole S row.
+// Keys and block ids of a candidate list in ascending block order: a
+// compacted LDS list, or a contiguous range [b0, b0 + n) of an S row.
 struct LdsList {
   const uint32_t* key;
   const int32_t* blk;
@@ -60,19 +60,22 @@ struct LdsList {
   __device__ int32_t b(int i) const { return blk[i]; }
 };
 struct RowList {
-  const float* row;
+  const float* row;  // row + b0
+  int b0;
   __device__ uint32_t k(int i) const { return order_key(row[i]); }
-  __device__ int32_t b(int i) const { return i; }
+  __device__ int32_t b(int i) const { return b0 + i; }
 };
 
-template <class List>
-__device__ void select_and_write(const List& lst, int n, int mp, int L, int k, int32_t* out,
-                                 int lane) {
+// Selects the `want` (1 <= want <= n) best entries of lst[0, n) under
+// (key descending, block ascending) and hands them to emit(pos, key, blk) in
+// list order, pos = 0 .. want-1.  Wave-uniform control flow.
+template <class List, class Emit>
+__device__ void select_best(const List& lst, int n, int want, int lane, Emit emit) {
   const uint64_t lt = lanemask_lt();
   uint32_t tau = 0;
   if (n <= kWave) {
     const uint32_t key = lane < n ? lst.k(lane) : 0u;
-    tau = kth_largest_lanes(key, mp);
+    tau = kth_largest_lanes(key, want);
   } else {
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t c = tau | (1u << bit);
@@ -82,7 +85,7 @@ __device__ void select_and_write(const List& lst, int n, int mp, int L, int k, i
         const uint32_t key = i < n ? lst.k(i) : 0u;
         cnt += popc(__ballot(key >= c));
       }
-      if (cnt >= mp) tau = c;
+      if (cnt >= want) tau = c;
     }
   }
   int cgt = 0;
@@ -91,7 +94,7 @@ __device__ void select_and_write(const List& lst, int n, int mp, int L, int k, i
     const uint32_t key = i < n ? lst.k(i) : 0u;
     cgt += popc(__ballot(key > tau));
   }
-  const int need = mp - cgt;  // >= 1 by construction of tau
+  const int need = want - cgt;  // >= 1 by construction of tau
   int base = 0, eq_seen = 0;
   for (int i0 = 0; i0 < n; i0 += kWave) {
     const int i = i0 + lane;
@@ -102,51 +105,61 @@ __device__ void select_and_write(const List& lst, int n, int mp, int L, int k, i
     const int eq_rank = eq_seen + popc(beq & lt);
     const bool sel = in && (key > tau || (eq && eq_rank < need));
     const uint64_t bs = __ballot(sel);
-    if (sel) out[base + popc(bs & lt)] = lst.b(i);
+    if (sel) emit(base + popc(bs & lt), key, lst.b(i));
     base += popc(bs);
     eq_seen += popc(beq);
   }
-  if (lane == 0) out[mp] = L;
-  for (int j = mp + 1 + lane; j < k; j += kWave) out[j] = -1;
+}
+
+// Compacts the candidates of srow[b0, b0 + n) whose key may be among the
+// `want` best (key >= the want-th largest lane maximum, when want <= 64) into
+// skey/sblk in block order; returns the number of survivors (entries beyond
+// kCap are counted but not stored).
+__device__ int compact_candidates(const float* __restrict__ srow, int b0, int n, int want, uint32_t* skey,
+                                  int32_t* sblk, int lane) {
+  uint32_t lmax = 0;
+  for (int j = lane; j < n; j += kWave) lmax = max(lmax, order_key(srow[b0 + j]));
+  const uint32_t lb = (want <= kWave) ? kth_largest_lanes(lmax, want) : 0u;
+  const uint64_t lt = lanemask_lt();
+  int cnt = 0;
+  for (int j0 = 0; j0 < n; j0 += kWave) {
+    const int j = j0 + lane;
+    const uint32_t key = j < n ? order_key(srow[b0 + j]) : 0u;
+    const bool sv = j < n && key >= lb;
+    const uint64_t bal = __ballot(sv);
+    const int pos = cnt + popc(bal & lt);
+    if (sv && pos < kCap) {
+      skey[pos] = key;
+      sblk[pos] = b0 + j;
+    }
+    cnt += popc(bal);
+  }
+  wave_lds_sync();
+  return cnt;
+}
+
+__device__ void write_trivial(int L, int mp, int k, int32_t* out, int lane) {
+  if (mp == L) {  // every visible block is kept (covers L == 0)
+    for (int j = lane; j < k; j += kWave) out[j] = (j <= L) ? j : -1;
+  } else {        // k == 1: the local block alone
+    for (int j = lane; j < k; j += kWave) out[j] = (j == 0) ? L : -1;
+  }
 }
 
 __device__ void select_row(const float* __restrict__ srow, int L, int k, int32_t* __restrict__ out,
                            uint32_t* skey, int32_t* sblk, int lane) {
   const int m = (k < L + 1) ? k : L + 1;
   const int mp = m - 1;
-  if (mp == L) {  // every visible block is kept (covers L == 0)
-    for (int j = lane; j < k; j += kWave) out[j] = (j <= L) ? j : -1;
+  if (mp == L || mp == 0) {
+    write_trivial(L, mp, k, out, lane);
     return;
   }
-  if (mp == 0) {  // k == 1: the local block alone
-    for (int j = lane; j < k; j += kWave) out[j] = (j == 0) ? L : -1;
-    return;
-  }
-  // 1. lower bound from the lane maxima
-  uint32_t lmax = 0;
-  for (int j = lane; j < L; j += kWave) lmax = max(lmax, order_key(srow[j]));
-  const uint32_t lb = (mp <= kWave) ? kth_largest_lanes(lmax, mp) : 0u;
-  // 2. compact survivors in ascending block order
-  const uint64_t lt = lanemask_lt();
-  int n = 0;
-  for (int j0 = 0; j0 < L; j0 += kWave) {
-    const int j = j0 + lane;
-    const uint32_t key = j < L ? order_key(srow[j]) : 0u;
-    const bool sv = j < L && key >= lb;
-    const uint64_t bal = __ballot(sv);
-    const int pos = n + popc(bal & lt);
-    if (sv && pos < kCap) {
-      skey[pos] = key;
-      sblk[pos] = j;
-    }
-    n += popc(bal);
-  }
-  wave_lds_sync();
-  if (n <= kCap) {
-    select_and_write(LdsList{skey, sblk}, n, mp, L, k, out, lane);
-  } else {
-    select_and_write(RowList{srow}, L, mp, L, k, out, lane);
-  }
+  const int n = compact_candidates(srow, 0, L, mp, skey, sblk, lane);
+  auto emit = [&](int pos, uint32_t, int32_t blk) { out[pos] = blk; };
+  if (n <= kCap) select_best(LdsList{skey, sblk}, n, mp, lane, emit);
+  else select_best(RowList{srow, 0}, L, mp, lane, emit);
+  if (lane == 0) out[mp] = L;
+  for (int j = mp + 1 + lane; j < k; j += kWave) out[j] = -1;
 }
 
 __global__ __launch_bounds__(256) void topk_prefill_kernel(const float* __restrict__ S, int s_stride,
@@ -168,20 +181,74 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(const float* __restri
   select_row(srow, t / B, k, out, skey[wave], sblk[wave], lane);
 }
 
-__global__ __launch_bounds__(256) void topk_decode_kernel(const float* __restrict__ S, int s_stride,
-                                                          int32_t* __restrict__ bidx,
-                                                          const int32_t* __restrict__ lens, int Lmax,
-                                                          int G, int B, int k, long n_rows) {
-  __shared__ uint32_t skey[kTopkWaves][kCap];
-  __shared__ int32_t sblk[kTopkWaves][kCap];
+// Decode rows are few (batch x G) and long (up to Lmax / B candidates): one
+// 16-wave workgroup per row.  Each wave keeps the best min(m-1, n_w) blocks
+// of its contiguous partition; the union of those lists, in block order,
+// contains the row's best m-1 (a total order), and wave 0 selects them.
+constexpr int kDecWaves = 16;
+constexpr int kDecMaxKeep = kWave;  // two-level path for m-1 <= 64
+
+__global__ __launch_bounds__(1024) void topk_decode_kernel(const float* __restrict__ S, int s_stride,
+                                                           int32_t* __restrict__ bidx,
+                                                           const int32_t* __restrict__ lens, int Lmax,
+                                                           int G, int B, int k) {
+  __shared__ uint32_t skey[kDecWaves][kCap];
+  __shared__ int32_t sblk[kDecWaves][kCap];
+  __shared__ uint32_t mkey[kDecWaves * kDecMaxKeep];
+  __shared__ int32_t mblk[kDecWaves * kDecMaxKeep];
+  __shared__ int mcnt[kDecWaves];
+
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * kTopkWaves + wave;
-  if (row >= n_rows) return;
+  const long row = blockIdx.x;
   const long s = row / G;
   const int len = min(max(lens[s], 1), Lmax);
+  const int L = (len - 1) / B;
   const float* srow = S + (size_t)row * s_stride;
   int32_t* out = bidx + (size_t)row * k;
-  select_row(srow, (len - 1) / B, k, out, skey[wave], sblk[wave], lane);
+  const int m = (k < L + 1) ? k : L + 1;
+  const int mp = m - 1;
+  if (mp == L || mp == 0) {  // uniform across the workgroup
+    if (wave == 0) write_trivial(L, mp, k, out, lane);
+    return;
+  }
+  if (mp > kDecMaxKeep || L <= kWave * kDecWaves) {  // one wave does the whole row
+    if (wave == 0) select_row(srow, L, k, out, skey[0], sblk[0], lane);
+    return;
+  }
+  // level 1: per-wave partitions of the candidates 0..L-1
+  const int per = (L + kDecWaves - 1) / kDecWaves;
+  const int b0 = wave * per;
+  const int nw = max(0, min(per, L - b0));
+  int kept = 0;
+  if (nw > 0) {
+    const int want = min(mp, nw);
+    const int n = compact_candidates(srow, b0, nw, want, skey[wave], sblk[wave], lane);
+    uint32_t* ok = mkey + wave * kDecMaxKeep;
+    int32_t* ob = mblk + wave * kDecMaxKeep;
+    auto emit = [&](int pos, uint32_t key, int32_t blk) { ok[pos] = key; ob[pos] = blk; };
+    if (n <= kCap) select_best(LdsList{skey[wave], sblk[wave]}, n, want, lane, emit);
+    else select_best(RowList{srow + b0, b0}, nw, want, lane, emit);
+    kept = want;
+  }
+  if (lane == 0) mcnt[wave] = kept;
+  __syncthreads();
+  // level 2: wave 0 compacts the per-wave lists (block order) and selects
+  if (wave == 0) {
+    int n = 0;
+    for (int w = 0; w < kDecWaves; ++w) {
+      const int c = mcnt[w];
+      for (int i = lane; i < c; i += kWave) {
+        skey[0][n + i] = mkey[w * kDecMaxKeep + i];
+        sblk[0][n + i] = mblk[w * kDecMaxKeep + i];
+      }
+      n += c;
+    }
+    wave_lds_sync();
+    auto emit = [&](int pos, uint32_t, int32_t blk) { out[pos] = blk; };
+    select_best(LdsList{skey[0], sblk[0]}, n, mp, lane, emit);
+    if (lane == 0) out[mp] = L;
+    for (int j = mp + 1 + lane; j < k; j += kWave) out[j] = -1;
+  }
 }
 
 }  // namespace
@@ -199,9 +266,7 @@ hipError_t launch_topk_prefill(const float* S, int s_stride, int32_t* bidx, long
 hipError_t launch_topk_decode(const float* S, int s_stride, int32_t* bidx, const int32_t* lens,
                               int Lmax, int batch, int G, int B, int k, hipStream_t st) {
   const long n_rows = (long)batch * G;
-  const long grid = (n_rows + kTopkWaves - 1) / kTopkWaves;
-  topk_decode_kernel<<<dim3((unsigned)grid), 256, 0, st>>>(S, s_stride, bidx, lens, Lmax, G, B, k,
-                                                           n_rows);
+  topk_decode_kernel<<<dim3((unsigned)n_rows), 1024, 0, st>>>(S, s_stride, bidx, lens, Lmax, G, B, k);
   return hipGetLastError();
 }
 

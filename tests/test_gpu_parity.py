@@ -309,3 +309,36 @@ def test_decode_bitwise_deterministic():
     b = gpu_decode(dec, 64, 5)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("mode", ["integer", "gaussian"])
+def test_decode_many_candidates(mode):
+    # more than 16 x 64 candidate blocks: the workgroup-per-row two-level top-k
+    L, Hq, G, di, B, k = 70000, 16, 4, 64, 32, 20
+    lens = [70000, 40001]
+    say(f"[decode many candidates {mode}] L={L} B={B} k={k}")
+    dec = inputs.make_decode(len(lens), L, Hq, G, 128, di, seed=61, cache_lens=lens, idx_mode=mode)
+    out, lse, bidx = gpu_decode(dec, B, k)
+    ores = orc.decode(dec.q, dec.k_cache, dec.v_cache, dec.idx_q, dec.idx_k_cache, lens, B, k)
+    for s in range(len(lens)):
+        for g in range(G):
+            got, ref = bidx[s, g].numpy(), ores["block_idx"][s, g]
+            if not np.array_equal(got, ref):
+                assert mode == "gaussian" and orc.near_tie(ores["S"][s][g], lens[s] - 1, B, k), (s, g, got, ref)
+    cond = orc.decode(dec.q, dec.k_cache, dec.v_cache, dec.idx_q, dec.idx_k_cache, lens, B, k, block_idx=bidx)
+    check_attention(out.to(torch.float64).numpy(), cond["out"], "decode out")
+
+
+def test_decode_all_ties_partition_fallback():
+    # every score equal and more than 512 candidates per partition
+    L, Hq, G, di, B, k = 300000, 8, 2, 64, 32, 9
+    lens = [300000, 299990]
+    say(f"[decode all ties] L={L}")
+    dec = inputs.make_decode(len(lens), L, Hq, G, 128, di, seed=3, cache_lens=lens)
+    dec.idx_q.zero_()
+    _, _, bidx = gpu_decode(dec, B, k)
+    for s, n in enumerate(lens):
+        Lb = (n - 1) // B
+        exp = list(range(k - 1)) + [Lb]
+        for g in range(G):
+            assert bidx[s, g].tolist() == exp, (s, g)
