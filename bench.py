@@ -37,6 +37,10 @@ PEAK_HBM = 8.0e12         # MI355X HBM3E, B/s
 PF = dict(T=131072, Hq=64, G=8, d=128, di=128, B=128, k=16, skew=0.5, seed=0)
 DC = dict(batch=8, L=1 << 20, Hq=64, G=8, d=128, di=128, B=128, k=16, seed=1)
 
+DOMINANT = "index_blockmax_prefill_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_blockmax_prefill_t131072_traffic.json")
+COPY_BYTES = 1 << 30   # calibration copy for the --pmc passes
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -63,6 +67,56 @@ def decode_bytes(batch, L, Hq, G, d, di, B, k):
     t = L - 1
     per_seq = L * di * 2 + G * n_att(t, B, k) * d * 2 * 2 + Hq * d * 2 * 2 + G * di * 2
     return batch * per_seq
+
+
+def measured_traffic():
+    """Per-launch HBM bytes of the dominant kernel from the committed --pmc
+    summary, or None when absent or taken on different kernel sources."""
+    from block_sparse_long_02_amd import profiling
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != profiling.source_hash(DOMINANT):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def measured_peaks(dev):
+    """Context only: a vendor bf16 GEMM and a device copy on this GPU."""
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        a @ b
+    ms, _ = timed(lambda: a @ b, 10, torch.cuda.current_stream())
+    x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    cms, _ = timed(lambda: y.copy_(x), 10, torch.cuda.current_stream())
+    del a, b, x, y
+    return {"bf16_gemm_8192_tflops": round(2 * 8192 ** 3 / (ms * 1e-3) / 1e12, 1),
+            "device_copy_gbs": round(2 * (1 << 30) / (cms * 1e-3) / 1e9, 1)}
+
+
+def profile_kernel_only(args, dev):
+    """Inputs of the 128K prefill's index branch, one calibration copy of
+    COPY_BYTES, then --steps launches of the dominant kernel (the same launch
+    msa_prefill makes): the workload of the --pmc counter passes."""
+    stream = torch.cuda.current_stream()
+    pin = inputs.make_prefill(PF["T"], 1, PF["G"], 8, PF["di"], seed=PF["seed"], device=dev,
+                              block_size=PF["B"], skew_std=PF["skew"])
+    pdims = bd.make_dims(1, PF["T"], PF["G"], PF["G"], index_dim=PF["di"], block_size=PF["B"], topk=PF["k"])
+    rs = bd.scores_row_stride(pdims, PF["T"])
+    scores = torch.empty((1, PF["T"], PF["G"], rs), dtype=torch.float32, device=dev)
+    x = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    ms, _ = timed(lambda: bd.msa_index_scores(pdims, pin.idx_q, pin.idx_k, scores, 0, PF["T"], rs),
+                  args.steps, stream)
+    print(json.dumps({"profile_kernel": DOMINANT, "launches": args.steps, "launch_ms": round(ms, 4),
+                      "copy_bytes": COPY_BYTES}), flush=True)
 
 
 def timed(fn, reps, stream):
@@ -187,11 +241,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-dense", action="store_true", help="skip the all-blocks comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (CPU baseline + parity)")
-    ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
+    ap.add_argument("--profile-kernel", action="store_true",
+                    help="run only the dominant kernel (plus a calibration copy) for rocprofv3 --pmc passes")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
@@ -200,6 +256,9 @@ def main():
     bd.load_library()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    if args.profile_kernel:
+        profile_kernel_only(args, dev)
+        return
 
     log("generating prefill inputs (T=131072)")
     pin = inputs.make_prefill(PF["T"], PF["Hq"], PF["G"], PF["d"], PF["di"], seed=PF["seed"], device=dev,
@@ -288,6 +347,7 @@ def main():
         }
         log(f"dense prefill {pd_ms:.2f} ms, dense decode {dd_ms:.3f} ms")
 
+    peaks = measured_peaks(dev)
     cpu, parity, dparity = None, None, None
     if not args.no_cpu:
         log("oracle leg on host cores")
@@ -331,10 +391,11 @@ def main():
         "roofline": {
             "bound": "mfma", "kernel": "index_blockmax_prefill_kernel (index scoring + block max)",
             "achieved": round(idx_tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
-            "frac": round(idx_tflops * 1e12 / PEAK_MFMA_BF16, 4), "traffic": None,
+            "frac": round(idx_tflops * 1e12 / PEAK_MFMA_BF16, 4), "traffic": measured_traffic(),
             "launch_ms": round(idx_ms, 4), "algorithmic_tflop_per_launch": round(f_index / 1e12, 3),
         },
         "dense": dense,
+        "measured_peaks": peaks,
         "parity": {"prefill_sampled": parity, "decode_sampled": dparity},
         "cpu_baseline": cpu,
     }

@@ -12,10 +12,11 @@
 // The T x T score matrix is never stored: each 32x32 MFMA tile of scores is
 // max-reduced in registers and only one float per (row, block) leaves the CU.
 //
-// Prefill kernel layout: a workgroup owns 256 consecutive (t, g) rows (4 waves
-// x 2 column tiles of 32 rows, idx_q kept in registers as the MFMA B operand)
-// and streams idx_k one block at a time through double-buffered LDS as the A
-// operand, so each idx_k byte fetched feeds 256 rows (256 flop/B against L2).
+// Prefill kernel layout: a workgroup owns 128*NT consecutive (t, g) rows (4
+// waves x NT column tiles of 32 rows, idx_q kept in registers as the MFMA B
+// operand; NT = 3 for index_dim 128, 4 for 64) and streams idx_k one block at
+// a time through double-buffered LDS as the A operand, so each idx_k byte
+// fetched feeds 128*NT rows and each A operand read from LDS feeds NT MFMAs.
 // Workgroups are issued longest-first (latest tokens have the most blocks).
 #include "msa_device.h"
 #include "msa_internal.h"
@@ -24,24 +25,29 @@ namespace msa {
 
 namespace {
 
-constexpr int kIdxRows = 256;   // rows per workgroup
+// NT 32-row column tiles per wave, 4 waves: 128 * NT (t, g) rows per
+// workgroup; NT is as large as the register file allows without spills.
+template <int DI>
+constexpr int idx_nt() { return DI == 128 ? 3 : 4; }
 
-template <int DI, int B>
+template <int DI, int B, int NT>
 __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
     const bf16_t* __restrict__ idx_q, const bf16_t* __restrict__ idx_k, float* __restrict__ S,
     int T, int G, int t0, int tc, int s_stride, int n_tiles) {
+  constexpr int ROWS = 128 * NT;
   constexpr int KPAD = DI + 8;            // LDS row stride (bf16): +16 B against bank conflicts
   constexpr int KSTEPS = DI / 16;         // MFMA k-steps per 32x32 tile
   constexpr int CPR = DI / 8;             // 16-byte chunks per idx_k row
   constexpr int NCH = B * CPR;            // 16-byte chunks per block
   constexpr int MAXCH = (NCH + 255) / 256;  // staging chunks per thread
+  constexpr int KTILES = B / 32;
   __shared__ __attribute__((aligned(16))) bf16_t kbuf[2][B * KPAD];
 
   const int s = blockIdx.y;
-  const int tile = n_tiles - 1 - (int)blockIdx.x;
+  const int tile = n_tiles - 1 - (int)blockIdx.x;   // longest rows first
   const int rows_chunk = tc * G;
-  const int r0 = tile * kIdxRows;
-  const int r_last = min(r0 + kIdxRows, rows_chunk) - 1;
+  const int r0 = tile * ROWS;
+  const int r_last = min(r0 + ROWS, rows_chunk) - 1;
   const int nblk = (t0 + r_last / G) / B;  // candidate blocks needed by the last row
   if (nblk <= 0) return;                   // uniform across the workgroup
 
@@ -49,16 +55,16 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
 
-  // B operands: idx_q rows of this wave's two 32-row column tiles.
-  bf16x8 qop[2][KSTEPS];
-  int row_idx[2];
-  bool row_ok[2];
+  // B operands: idx_q rows of this wave's NT 32-row column tiles.
+  bf16x8 qop[NT][KSTEPS];
+  int row_idx[NT];
+  bool row_ok[NT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = r0 + wave * 64 + nt * 32 + col;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = r0 + wave * 32 * NT + nt * 32 + col;
     row_idx[nt] = r;
     row_ok[nt] = r < rows_chunk;
-    const bf16_t* qp = idx_q + ((size_t)s * T * G + (size_t)t0 * G + (size_t)r) * DI;
+    const bf16_t* qp = idx_q + ((size_t)s * T * G + (size_t)t0 * G + (size_t)(row_ok[nt] ? r : 0)) * DI;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
       qop[nt][ks] = row_ok[nt] ? load_bf16x8(qp + 16 * ks + 8 * half) : zero_bf16x8();
@@ -73,7 +79,7 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
     const u32x4* src_ = reinterpret_cast<const u32x4*>(kseq + (size_t)(BLK) * B * DI);   \
     _Pragma("unroll") for (int i = 0; i < MAXCH; ++i) {                                  \
       const int c_ = tid + i * 256;                                                      \
-      if (NCH % 256 == 0 || c_ < NCH) stg[i] = src_[c_];                                                   \
+      if (NCH % 256 == 0 || c_ < NCH) stg[i] = src_[c_];                                 \
     }                                                                                    \
   }
 #define MSA_IDX_LSTORE(BUF)                                                              \
@@ -89,57 +95,51 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
   MSA_IDX_LSTORE(0);
   __syncthreads();
 
-  f32x4 sb[2];
-  sb[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-  sb[1] = sb[0];
-  constexpr int ktiles = B / 32;
+  // block maxima of 4 consecutive blocks are buffered and written as float4
+  f32x4 sb[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) sb[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int b = 0; b < nblk; ++b) {
     const int cur = b & 1;
     if (b + 1 < nblk) MSA_IDX_GLOAD(b + 1);
 
-    // KTS key tiles x 2 row tiles = independent MFMA accumulator chains
-    constexpr int KTS = ktiles >= 2 ? 2 : 1;
-    float mx0 = -INFINITY, mx1 = -INFINITY;
+    float mx[NT];
 #pragma unroll
-    for (int kt = 0; kt < ktiles; kt += KTS) {
-      f32x16 acc[KTS][2];
+    for (int nt = 0; nt < NT; ++nt) mx[nt] = -INFINITY;
+    // one key tile at a time keeps NT accumulators live (no spills)
+#pragma unroll 1
+    for (int kt = 0; kt < KTILES; ++kt) {
+      f32x16 acc[NT];
 #pragma unroll
-      for (int u = 0; u < KTS; ++u) acc[u][0] = acc[u][1] = f32x16{};
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
       const bf16_t* arow = &kbuf[cur][(kt * 32 + col) * KPAD + 8 * half];
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 16 * ks);
 #pragma unroll
-        for (int u = 0; u < KTS; ++u) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + u * 32 * KPAD + 16 * ks);
-          acc[u][0] = mfma32x32x16(a, qop[0][ks], acc[u][0]);
-          acc[u][1] = mfma32x32x16(a, qop[1][ks], acc[u][1]);
-        }
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma32x32x16(a, qop[nt][ks], acc[nt]);
       }
 #pragma unroll
-      for (int u = 0; u < KTS; ++u)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          mx0 = fmaxf(mx0, fmaxf(acc[u][0][i], acc[u][0][i + 1]));
-          mx1 = fmaxf(mx1, fmaxf(acc[u][1][i], acc[u][1][i + 1]));
-        }
+        for (int i = 0; i < 16; i += 2) mx[nt] = fmaxf(mx[nt], fmaxf(acc[nt][i], acc[nt][i + 1]));
     }
-    mx0 = fmaxf(mx0, __shfl_xor(mx0, 32, kWave));
-    mx1 = fmaxf(mx1, __shfl_xor(mx1, 32, kWave));
-
     const int slot = b & 3;
-    if (slot == 0) { sb[0][0] = mx0; sb[1][0] = mx1; }
-    else if (slot == 1) { sb[0][1] = mx0; sb[1][1] = mx1; }
-    else if (slot == 2) { sb[0][2] = mx0; sb[1][2] = mx1; }
-    else { sb[0][3] = mx0; sb[1][3] = mx1; }
-    if (slot == 3 || b == nblk - 1) {
-      if (half == 0) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          if (row_ok[nt]) {
-            float* dst = S + ((size_t)s * rows_chunk + (size_t)row_idx[nt]) * s_stride + (b & ~3);
-            *reinterpret_cast<f32x4*>(dst) = sb[nt];
-          }
+    for (int nt = 0; nt < NT; ++nt) {
+      const float v = fmaxf(mx[nt], __shfl_xor(mx[nt], 32, kWave));
+      if (slot == 0) sb[nt][0] = v;
+      else if (slot == 1) sb[nt][1] = v;
+      else if (slot == 2) sb[nt][2] = v;
+      else sb[nt][3] = v;
+    }
+    if ((slot == 3 || b == nblk - 1) && half == 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (row_ok[nt]) {
+          float* dst = S + ((size_t)s * rows_chunk + (size_t)row_idx[nt]) * s_stride + (b & ~3);
+          *reinterpret_cast<f32x4*>(dst) = sb[nt];
         }
       }
     }
@@ -157,10 +157,11 @@ hipError_t launch_index_blockmax_prefill(const uint16_t* idx_q, const uint16_t* 
                                          int batch, int T, int G, int di, int B, int t0, int tc,
                                          int s_stride, hipStream_t st) {
   const long rows = (long)tc * G;
-  const int n_tiles = (int)((rows + kIdxRows - 1) / kIdxRows);
+  const int rows_per_wg = 128 * (di == 128 ? idx_nt<128>() : idx_nt<64>());
+  const int n_tiles = (int)((rows + rows_per_wg - 1) / rows_per_wg);
   dim3 grid(n_tiles, batch);
 #define MSA_IDX_LAUNCH(DI_, B_)                                                                   \
-  index_blockmax_prefill_kernel<DI_, B_><<<grid, 256, 0, st>>>(idx_q, idx_k, S, T, G, t0, tc,     \
+  index_blockmax_prefill_kernel<DI_, B_, idx_nt<DI_>()><<<grid, 256, 0, st>>>(idx_q, idx_k, S, T, G, t0, tc,     \
                                                                s_stride, n_tiles)
   if (di == 128) {
     if (B == 128) MSA_IDX_LAUNCH(128, 128);

@@ -34,9 +34,18 @@ hipError_t launch_topk_decode(const float* S, int s_stride, int32_t* bidx, const
 // Query tokens per window of the block lists: the lists of non-local
 // (token, slot) pairs are kept per (sequence, group, window, block), so that
 // consecutive block-major workgroups touch the q rows of one window.
-constexpr int kListWindow = 2048;
+#ifndef MSA_LIST_WINDOW
+#define MSA_LIST_WINDOW 2048
+#endif
+constexpr int kListWindow = MSA_LIST_WINDOW;
 // Workgroup size of the multi-workgroup scans over the lists.
 constexpr int kScanItems = 4096;
+// Tiles of one block list served by one block-major workgroup (the K/V
+// block is staged once for all of them).
+#ifndef MSA_TILES_PER_ITEM
+#define MSA_TILES_PER_ITEM 2
+#endif
+constexpr int kTilesPerItem = MSA_TILES_PER_ITEM;
 
 struct PrefillMainArgs {
   const uint16_t* q;

@@ -223,7 +223,14 @@ __device__ __forceinline__ int2 block_exclusive_scan(int2 v, int2* total) {
   return make_int2(base.x + x.x - v.x, base.y + x.y - v.y);
 }
 
-// Phase 1: per scan block (kScanItems lists) totals of entries and tiles.
+// Work items of a list of c entries: groups of up to kTilesPerItem tiles of
+// mt tokens.
+__device__ __forceinline__ int list_items(int c, int mt) {
+  const int tiles = (c + mt - 1) / mt;
+  return (tiles + kTilesPerItem - 1) / kTilesPerItem;
+}
+
+// Phase 1: per scan block (kScanItems lists) totals of entries and work items.
 __global__ __launch_bounds__(1024) void lists_scan_reduce_kernel(const int32_t* __restrict__ cnt,
                                                                  int32_t* __restrict__ bsum, long nlists,
                                                                  int mt) {
@@ -234,7 +241,7 @@ __global__ __launch_bounds__(1024) void lists_scan_reduce_kernel(const int32_t* 
     const long i = i0 + j;
     const int c = i < nlists ? cnt[i] : 0;
     v.x += c;
-    v.y += (c + mt - 1) / mt;
+    v.y += list_items(c, mt);
   }
   int2 tot;
   block_exclusive_scan(v, &tot);
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(1024) void lists_scan_reduce_kernel(const int32_t* 
 }
 
 // Phase 2 (one workgroup): exclusive scan of the block totals, in place;
-// n_work = number of tiles.
+// n_work = number of work items.
 __global__ __launch_bounds__(1024) void lists_scan_top_kernel(int32_t* __restrict__ bsum, int nblk,
                                                               int32_t* __restrict__ n_work) {
   int2 carry = make_int2(0, 0);
@@ -264,7 +271,7 @@ __global__ __launch_bounds__(1024) void lists_scan_top_kernel(int32_t* __restric
   if (threadIdx.x == 0) n_work[0] = carry.y;
 }
 
-// Phase 3: list offsets and the flat work list (list id, tile index).
+// Phase 3: list offsets and the flat work list (list id, tile group).
 __global__ __launch_bounds__(1024) void lists_scan_final_kernel(const int32_t* __restrict__ cnt,
                                                                 const int32_t* __restrict__ bsum,
                                                                 int32_t* __restrict__ offs,
@@ -277,7 +284,7 @@ __global__ __launch_bounds__(1024) void lists_scan_final_kernel(const int32_t* _
     const long i = i0 + j;
     c[j] = i < nlists ? cnt[i] : 0;
     v.x += c[j];
-    v.y += (c[j] + mt - 1) / mt;
+    v.y += list_items(c[j], mt);
   }
   int2 tot;
   const int2 ex = block_exclusive_scan(v, &tot);
@@ -288,10 +295,10 @@ __global__ __launch_bounds__(1024) void lists_scan_final_kernel(const int32_t* _
     const long i = i0 + j;
     if (i < nlists) {
       offs[i] = e_off;
-      const int tiles = (c[j] + mt - 1) / mt;
-      for (int tj = 0; tj < tiles; ++tj) work[t_off + tj] = make_int2((int)i, tj);
+      const int items = list_items(c[j], mt);
+      for (int tj = 0; tj < items; ++tj) work[t_off + tj] = make_int2((int)i, tj);
       e_off += c[j];
-      t_off += tiles;
+      t_off += items;
     }
   }
 }
@@ -359,9 +366,12 @@ __device__ __forceinline__ void accumulate_partial_row(float (*acc)[16], const u
 }
 
 // ---------------------------------------------------------------------------
-// Block-major kernel: one (s, g, block, tile of up to 128/R tokens) per
-// workgroup.  Writes, per (token, head) row, the normalised partial output
-// (fp32, natural d order) and lse2 = max*c + log2(sum) (base-2 domain).
+// Block-major kernel: one (s, g, window, block) list and up to
+// kTilesPerItem of its tiles of 128/R tokens per workgroup; the K/V block is
+// staged in LDS once and the next tile's q rows are fetched while the current
+// tile computes.  Writes, per (token, head) row, the normalised partial
+// output (fp16 row-scaled) and (lse2, scale exponent), lse2 = max*c +
+// log2(sum) in the base-2 domain.
 // ---------------------------------------------------------------------------
 template <int BS>
 __global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
@@ -382,87 +392,120 @@ __global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
   const int R = a.Hq / a.G;
   const int mt = kAttnRows / R;
   const int count = a.cnt[lid];
-  const int e0 = wk.y * mt;
-  const int ne = min(mt, count - e0);
   const int off = a.offs[lid];
+  const int tile0 = wk.y * kTilesPerItem;
+  const int ntile = min(kTilesPerItem, (count + mt - 1) / mt - tile0);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
-
-  // issue every global load first: list entry, the K/V block, the q row
   const int row = wave * 32 + col;
   const int e = row / R, r = row % R;
-  const bool valid = e < ne;
-  int tl = 0, rank = 0;
-  if (valid) {
-    const int ent = a.entries[(size_t)off + e0 + e];
-    tl = ent / a.KS;
-    rank = ent % a.KS;
-  }
+  const int h = g * R + r;
+  const float c = a.scale_log2;
+
+  // the lane's (token, rank) in tile `tile` of the list, and its q row
+  auto locate = [&](int tile, int& tl, int& rank) -> bool {
+    const int e0 = tile * mt;
+    const bool valid = e < mt && e0 + e < count;
+    tl = 0;
+    rank = 0;
+    if (valid) {
+      const int ent = a.entries[(size_t)off + e0 + e];
+      tl = ent / a.KS;
+      rank = ent % a.KS;
+    }
+    return valid;
+  };
+
+  // issue every global load first: list entry, the K/V block, the q row
+  int tl, rank;
+  bool valid = locate(tile0, tl, rank);
   const size_t kvstride = (size_t)a.G * D;
   const size_t kvoff = ((size_t)s * a.T + (size_t)b * a.B) * kvstride + (size_t)g * D;
   BlockRegs<BS> regs;
   block_load<BS>(regs, a.k + kvoff, a.v + kvoff, kvstride, tid);
-  const int t = a.t0 + tl;
-  const int h = g * R + r;
   bf16x8 qop[D / 16];
-  load_q(qop, a.q + (((size_t)s * a.T + t) * a.Hq + h) * D, valid, half);
+  load_q(qop, a.q + (((size_t)s * a.T + a.t0 + tl) * a.Hq + h) * D, valid, half);
   block_store<BS>(regs, Ks, Vt, VROW, tid);
   __syncthreads();
 
-  f32x16 sacc[KT];
-#pragma unroll
-  for (int kt = 0; kt < KT; ++kt) sacc[kt] = qk_tile(Ks, kt * 32, qop, col, half);
-
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-  const float c = a.scale_log2;
-  const float mc = mx * c;
-  float l = 0.f;
-#pragma unroll
-  for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(sacc[kt][i] * c - mc);
-      sacc[kt][i] = p;
-      l += p;
+  for (int it = 0; it < ntile; ++it) {
+    // prefetch the next tile's q rows while this one computes
+    int tl_n = 0, rank_n = 0;
+    bool valid_n = false;
+    bf16x8 qop_n[D / 16];
+    if (it + 1 < ntile) {
+      valid_n = locate(tile0 + it + 1, tl_n, rank_n);
+      load_q(qop_n, a.q + (((size_t)s * a.T + a.t0 + tl_n) * a.Hq + h) * D, valid_n, half);
     }
-  l += __shfl_xor(l, 32, kWave);
 
-  bf16x8 pop[KT][2];
+    // The K/V tile is loop-invariant; an opaque base keeps its LDS operand
+    // reads inside the loop instead of hoisting them into registers.
+    const bf16_t* ks_ = Ks;
+    const bf16_t* vt_ = Vt;
+    asm volatile("" : "+v"(ks_), "+v"(vt_));
+
+    f32x16 sacc[KT];
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    pop[kt][0] = to_bf16x8(sacc[kt], 0);
-    pop[kt][1] = to_bf16x8(sacc[kt], 8);
-  }
-  f32x16 oacc[4];
+    for (int kt = 0; kt < KT; ++kt) sacc[kt] = qk_tile(ks_, kt * 32, qop, col, half);
+
+    float mx = -INFINITY;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    oacc[dt] = f32x16{};
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float mc = mx * c;
+    float l = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sacc[kt][i] * c - mc);
+        sacc[kt][i] = p;
+        l += p;
+      }
+    l += __shfl_xor(l, 32, kWave);
+
+    bf16x8 pop[KT][2];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
-      oacc[dt] = pv_step(Vt, VROW, dt, kt * 32, pop[kt][0], oacc[dt], col, half);
-      oacc[dt] = pv_step(Vt, VROW, dt, kt * 32 + 16, pop[kt][1], oacc[dt], col, half);
+      pop[kt][0] = to_bf16x8(sacc[kt], 0);
+      pop[kt][1] = to_bf16x8(sacc[kt], 8);
     }
-  }
+    f32x16 oacc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      oacc[dt] = f32x16{};
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        oacc[dt] = pv_step(vt_, VROW, dt, kt * 32, pop[kt][0], oacc[dt], col, half);
+        oacc[dt] = pv_step(vt_, VROW, dt, kt * 32 + 16, pop[kt][1], oacc[dt], col, half);
+      }
+    }
 
-  // normalised row = oacc / l, stored as fp16 scaled by 2^-e
-  const float inv = 1.0f / l;
-  float amax = 0.f;
+    // normalised row = oacc / l, stored as fp16 scaled by 2^-e
+    const float inv = 1.0f / l;
+    float amax = 0.f;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(oacc[dt][i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 32, kWave)) * inv;
-  const int ex = row_scale_exp(amax);
-  if (valid) {
-    const size_t prow = ((((size_t)s * a.tc + tl) * a.G + g) * a.KS + rank) * R + r;
-    store_partial_row(a.pO + prow * D, oacc, inv * ldexpf(1.0f, -ex), half);
-    if (half == 0) a.pS[prow] = make_float2(mc + __log2f(l), (float)ex);
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(oacc[dt][i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave)) * inv;
+    const int ex = row_scale_exp(amax);
+    if (valid) {
+      const size_t prow = ((((size_t)s * a.tc + tl) * a.G + g) * a.KS + rank) * R + r;
+      store_partial_row(a.pO + prow * D, oacc, inv * ldexpf(1.0f, -ex), half);
+      if (half == 0) a.pS[prow] = make_float2(mc + __log2f(l), (float)ex);
+    }
+
+    if (it + 1 < ntile) {
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) qop[ks] = qop_n[ks];
+      valid = valid_n;
+      tl = tl_n;
+      rank = rank_n;
+    }
   }
 }
 
@@ -617,7 +660,10 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
       for (int i = 0; i < 16; ++i) o[dt][i] *= f;
     // pass 2: weighted partials in rank (= slot) order; the weight folds in
     // the row scale 2^e
-#pragma unroll 2
+#ifndef MSA_COMBINE_UNROLL
+#define MSA_COMBINE_UNROLL 2
+#endif
+#pragma unroll MSA_COMBINE_UNROLL
     for (int q = 0; q < nv; ++q) {
       const float2 st = ps[(size_t)q * R_];
       sumw += __builtin_amdgcn_exp2f(st.x - M2u);

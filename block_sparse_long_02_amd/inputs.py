@@ -92,9 +92,11 @@ def make_prefill(T: int, Hq: int, G: int, d: int, di: int, *, batch: int = 1,
                popularity).  Needs block_size.
     needles    number of distinct aligned blocks whose idx_k rows are shifted
                along a direction u.  'separable': u is a seeded unit vector,
-               idx_q = N(0,1) + 4u (so u is idx_q's mean direction) and needle
-               keys = N(0,1) + 2 sqrt(di) u.  'literal': idx_q iid N(0,1),
-               u = normalised mean of the drawn idx_q rows, needle keys += 2u.
+               idx_q = N(0,1) + 8u (so u is idx_q's mean direction, and every
+               row's projection q.u = 8 + N(0,1) stays well above 0 even over
+               millions of rows) and needle keys = N(0,1) + 2 sqrt(di) u.
+               'literal': idx_q iid N(0,1), u = normalised mean of the drawn
+               idx_q rows, needle keys += 2u.
     """
     gen = _gen(seed, device)
     q = gaussian_bf16((batch, T, Hq, d), gen, device)
@@ -118,7 +120,7 @@ def make_prefill(T: int, Hq: int, G: int, d: int, di: int, *, batch: int = 1,
         for r0 in range(0, fq.shape[0], step):
             r1 = min(fq.shape[0], r0 + step)
             x = torch.randn((r1 - r0, di), generator=gen, device=device, dtype=torch.float32)
-            fq[r0:r1].copy_(x + 4.0 * u)
+            fq[r0:r1].copy_(x + 8.0 * u)
         meta["needle_dir"] = u.cpu()
     else:
         idx_q = gaussian_bf16((batch, T, G, di), gen, device)

@@ -1,0 +1,116 @@
+"""Summaries of rocprofv3 output for the profiles/ folder.
+
+  python -m block_sparse_long_02_amd.profiling stats <kernel_stats.csv> --title T --command C
+      -> markdown table of per-kernel call counts and durations
+  python -m block_sparse_long_02_amd.profiling traffic --fetch <dir> --write <dir>
+         --kernel index_blockmax_prefill_kernel --copy-bytes N --out <json> --command C
+      -> per-launch HBM traffic of a kernel from two --pmc passes (FETCH_SIZE,
+         WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
+         reads for the blit copy kernel of N bytes in the same run
+
+The traffic file records a hash of the kernel's sources; bench.py reports the
+traffic only while the sources still match.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+# sources whose change invalidates measured counters of a kernel
+KERNEL_SOURCES = {
+    "index_blockmax_prefill_kernel": ["csrc/index_blockmax.hip", "csrc/msa_device.h", "csrc/msa_internal.h"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def kernel_stats_md(path: str, title: str, command: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    out = [f"# {title}", "", "Command (from the repository root, on one MI355X):", "", "```", command, "```", "",
+           "| kernel | calls | avg ms | total ms | % of kernel time |", "|---|---:|---:|---:|---:|"]
+    for r in rows:
+        out.append(f"| {r['Name'][:80]} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
+                   f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def _counter_rows(d: str):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def _per_dispatch(rows, kernel: str, counter: str):
+    vals = {}
+    for r in rows:
+        if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    return list(vals.values())
+
+
+def pmc_traffic(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int) -> dict:
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    f_k, w_k = _per_dispatch(fr, kernel, "FETCH_SIZE"), _per_dispatch(wr, kernel, "WRITE_SIZE")
+    f_c, w_c = _per_dispatch(fr, COPY_KERNEL, "FETCH_SIZE"), _per_dispatch(wr, COPY_KERNEL, "WRITE_SIZE")
+    if not (f_k and w_k and f_c and w_c):
+        raise ValueError("missing dispatches for the kernel or the calibration copy")
+    # the largest copy dispatch is the calibration copy of copy_bytes
+    fac_f = copy_bytes / (max(f_c) * 1024.0)
+    fac_w = copy_bytes / (max(w_c) * 1024.0)
+    fetch = sum(f_k) / len(f_k) * 1024.0 * fac_f
+    write = sum(w_k) / len(w_k) * 1024.0 * fac_w
+    return {"kernel": kernel, "launches": len(f_k), "fetch_bytes_per_launch": fetch,
+            "write_bytes_per_launch": write, "traffic_bytes_per_launch": fetch + write,
+            "fetch_kib_raw": sum(f_k) / len(f_k), "write_kib_raw": sum(w_k) / len(w_k),
+            "copy_factor_fetch": fac_f, "copy_factor_write": fac_w, "copy_bytes": copy_bytes,
+            "source_sha256": source_hash(kernel)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s1 = sub.add_parser("stats")
+    s1.add_argument("csv")
+    s1.add_argument("--title", required=True)
+    s1.add_argument("--command", required=True)
+    s1.add_argument("--out")
+    s2 = sub.add_parser("traffic")
+    s2.add_argument("--fetch", required=True)
+    s2.add_argument("--write", required=True)
+    s2.add_argument("--kernel", required=True)
+    s2.add_argument("--copy-bytes", type=int, required=True)
+    s2.add_argument("--command", required=True)
+    s2.add_argument("--out", required=True)
+    a = ap.parse_args()
+    if a.cmd == "stats":
+        md = kernel_stats_md(a.csv, a.title, a.command)
+        if a.out:
+            open(a.out, "w").write(md)
+        print(md)
+    else:
+        res = pmc_traffic(a.fetch, a.write, a.kernel, a.copy_bytes)
+        res["command"] = a.command
+        json.dump(res, open(a.out, "w"), indent=1)
+        print(json.dumps(res, indent=1))
+
+
+if __name__ == "__main__":
+    main()

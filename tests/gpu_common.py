@@ -108,3 +108,42 @@ def oracle_rows_out(ores, rows):
     out = np.stack([ores["out"][r] for r in rows])
     lse = np.stack([ores["lse"][r] for r in rows])
     return out, lse
+
+
+def oracle_rows_gathered(q, k, v, idx_q, idx_k, B, topk, rows, gpu_bidx, s=0):
+    """Oracle selection and attention for sampled prefill rows of a large
+    workload, using the oracle's own steps but converting to float64 only the
+    index keys up to t and the K/V rows the selection gathers.  Attention is
+    computed on the GPU's selection (conditioned), selection compared apart.
+    Tensors may live on the GPU.  Returns (sel_ok_rows, near_tie_rows,
+    bad_rows, out_ref {t: [Hq, d]} for rows whose selection matched)."""
+    import math
+    G = k.shape[2]
+    Hq, d = q.shape[2], q.shape[3]
+    R = Hq // G
+    scale = 1.0 / math.sqrt(d)
+    res = {"equal": 0, "near_tie": 0, "bad": [], "out": {}}
+    t_max = max(t for t in rows)
+    IK = idx_k[s, : t_max + 1].cpu().to(torch.float64).numpy()
+    for t in rows:
+        IQ = idx_q[s, t].cpu().to(torch.float64).numpy()
+        Q = q[s, t].cpu().to(torch.float64).numpy()
+        o_t = np.zeros((Hq, d))
+        for g in range(G):
+            S = orc.block_max(orc.index_scores(IQ[g], IK, t), t, B)
+            sel = orc.select_blocks(S, t, B, topk)
+            got = np.asarray(gpu_bidx[s, t, g])
+            if np.array_equal(got, sel):
+                res["equal"] += 1
+            elif orc.near_tie(S, t, B, topk):
+                res["near_tie"] += 1
+            else:
+                res["bad"].append((t, g, got.tolist(), sel.tolist()))
+            toks = orc.selected_tokens(got, t, B)
+            tk = torch.from_numpy(toks).to(k.device)
+            Kg = k[s, tk, g].cpu().to(torch.float64).numpy()
+            Vg = v[s, tk, g].cpu().to(torch.float64).numpy()
+            o, _ = orc.attention_row(Q[g * R:(g + 1) * R], Kg, Vg, np.arange(len(toks)), scale)
+            o_t[g * R:(g + 1) * R] = o
+        res["out"][t] = o_t
+    return res
