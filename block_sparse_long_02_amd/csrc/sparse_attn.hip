@@ -52,12 +52,22 @@ __device__ __forceinline__ void stage_k(bf16_t* Ks, const bf16_t* __restrict__ k
   }
 }
 
+// A 4-key x 4-d unit u of the V^T staging: the low 5 bits pick 8 d-quads x 4
+// key-quads, so the 32 lanes of a half-wave write 32 distinct bank pairs of
+// V^T rows whose stride is 2 (mod 64) dwords (conflict-free ds_write_b64),
+// while each 8-lane group still reads 64 contiguous bytes of a V row.
+__device__ __forceinline__ void vt_unit(int u, int& k4, int& dq) {
+  dq = ((u >> 5) & 3) * 8 + (u & 7);
+  k4 = (u >> 7) * 4 + ((u >> 3) & 3);
+}
+
 __device__ __forceinline__ void stage_vt(bf16_t* Vt, int vrow, const bf16_t* __restrict__ vbase,
                                          size_t vstride, int nkeys, int nvalid, int tid) {
   // unit = 4 keys x 4 d; 32 units per 4-key group
   const int nunits = (nkeys / 4) * (D / 4);
   for (int u = tid; u < nunits; u += 256) {
-    const int k4 = u >> 5, dq = u & 31;
+    int k4, dq;
+    vt_unit(u, k4, dq);
     u32x2 r[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -96,7 +106,8 @@ __device__ __forceinline__ void block_load(BlockRegs<BS>& r, const bf16_t* __res
 #pragma unroll
   for (int i = 0; i < BS / 32; ++i) {
     const int u = tid + 256 * i;
-    const int k4 = u >> 5, dq = u & 31;
+    int k4, dq;
+    vt_unit(u, k4, dq);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       r.v[i][j] = *reinterpret_cast<const u32x2*>(vbase + (size_t)(k4 * 4 + j) * stride + dq * 4);
@@ -113,7 +124,8 @@ __device__ __forceinline__ void block_store(const BlockRegs<BS>& r, bf16_t* Ks, 
 #pragma unroll
   for (int i = 0; i < BS / 32; ++i) {
     const int u = tid + 256 * i;
-    const int k4 = u >> 5, dq = u & 31;
+    int k4, dq;
+    vt_unit(u, k4, dq);
     const u32x2* x = r.v[i];
     u32x2 o[4];
     o[0] = u32x2{(x[0][0] & 0xffffu) | (x[1][0] << 16), (x[2][0] & 0xffffu) | (x[3][0] << 16)};
@@ -439,11 +451,13 @@ __global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
       load_q(qop_n, a.q + (((size_t)s * a.T + a.t0 + tl_n) * a.Hq + h) * D, valid_n, half);
     }
 
-    // The K/V tile is loop-invariant; an opaque base keeps its LDS operand
-    // reads inside the loop instead of hoisting them into registers.
-    const bf16_t* ks_ = Ks;
-    const bf16_t* vt_ = Vt;
-    asm volatile("" : "+v"(ks_), "+v"(vt_));
+    // The K/V tile is loop-invariant; an opaque zero offset keeps its LDS
+    // operand reads inside the loop instead of hoisting them into registers
+    // (the offset, not the pointer, is opaque, so the reads stay LDS reads).
+    int lds_off = 0;
+    asm volatile("" : "+s"(lds_off));
+    const bf16_t* ks_ = Ks + lds_off;
+    const bf16_t* vt_ = Vt + lds_off;
 
     f32x16 sacc[KT];
 #pragma unroll

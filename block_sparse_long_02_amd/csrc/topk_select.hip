@@ -70,7 +70,7 @@ struct RowList {
 // (key descending, block ascending) and hands them to emit(pos, key, blk) in
 // list order, pos = 0 .. want-1.  Wave-uniform control flow.
 template <class List, class Emit>
-__device__ void select_best(const List& lst, int n, int want, int lane, Emit emit) {
+__device__ __forceinline__ void select_best(const List& lst, int n, int want, int lane, Emit emit) {
   const uint64_t lt = lanemask_lt();
   uint32_t tau = 0;
   if (n <= kWave) {
@@ -115,7 +115,7 @@ __device__ void select_best(const List& lst, int n, int want, int lane, Emit emi
 // `want` best (key >= the want-th largest lane maximum, when want <= 64) into
 // skey/sblk in block order; returns the number of survivors (entries beyond
 // kCap are counted but not stored).
-__device__ int compact_candidates(const float* __restrict__ srow, int b0, int n, int want, uint32_t* skey,
+__device__ __forceinline__ int compact_candidates(const float* __restrict__ srow, int b0, int n, int want, uint32_t* skey,
                                   int32_t* sblk, int lane) {
   uint32_t lmax = 0;
   for (int j = lane; j < n; j += kWave) lmax = max(lmax, order_key(srow[b0 + j]));
@@ -138,7 +138,7 @@ __device__ int compact_candidates(const float* __restrict__ srow, int b0, int n,
   return cnt;
 }
 
-__device__ void write_trivial(int L, int mp, int k, int32_t* out, int lane) {
+__device__ __forceinline__ void write_trivial(int L, int mp, int k, int32_t* out, int lane) {
   if (mp == L) {  // every visible block is kept (covers L == 0)
     for (int j = lane; j < k; j += kWave) out[j] = (j <= L) ? j : -1;
   } else {        // k == 1: the local block alone
@@ -146,7 +146,7 @@ __device__ void write_trivial(int L, int mp, int k, int32_t* out, int lane) {
   }
 }
 
-__device__ void select_row(const float* __restrict__ srow, int L, int k, int32_t* __restrict__ out,
+__device__ __forceinline__ void select_row(const float* __restrict__ srow, int L, int k, int32_t* __restrict__ out,
                            uint32_t* skey, int32_t* sblk, int lane) {
   const int m = (k < L + 1) ? k : L + 1;
   const int mp = m - 1;

@@ -23,9 +23,10 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
-# sources whose change invalidates measured counters of a kernel
+# sources (and build flags) whose change invalidates measured counters of a kernel
 KERNEL_SOURCES = {
-    "index_blockmax_prefill_kernel": ["csrc/index_blockmax.hip", "csrc/msa_device.h", "csrc/msa_internal.h"],
+    "index_blockmax_prefill_kernel": ["csrc/index_blockmax.hip", "csrc/msa_device.h", "csrc/msa_internal.h",
+                                      "build.py"],
 }
 
 
