@@ -59,12 +59,12 @@ float log2_scale(const msa_dims* d) {
 // Prefill / index_topk plan
 // ---------------------------------------------------------------------------
 struct PrefillPlan {
-  int nb = 0, KS = 0, R = 0, mt = 0;
+  int nb = 0, KS = 0, R = 0, mt = 0, rank_bits = 0;
   int Tc = 0, nchunks = 0;
   int s_stride_max = 0;
   long max_work = 0;
   bool with_scores = false, with_main = false;
-  size_t off_S = 0, off_bidx = 0, off_cnt = 0, off_offs = 0, off_bsum = 0, off_epos = 0,
+  size_t off_S = 0, off_bidx = 0, off_cnt = 0, off_offs = 0, off_bsum = 0, off_rinfo = 0, off_epos = 0,
          off_entries = 0, off_work = 0, off_nwork = 0, off_pO = 0, off_pS = 0;
   size_t total = 0;
 };
@@ -73,7 +73,7 @@ size_t per_token_bytes(const msa_dims* d, const PrefillPlan& p) {
   const size_t G = (size_t)d->num_kv_heads;
   size_t b = 0;
   if (p.with_scores) b += G * (size_t)p.s_stride_max * 4 + G * (size_t)d->topk * 4;
-  if (p.with_main) b += G * (size_t)p.KS * (4 + 4 + (size_t)p.R * (128 * 2 + 8));
+  if (p.with_main) b += G * 4 + G * (size_t)p.KS * (4 + 4 + (size_t)p.R * (128 * 2 + 8));
   return b;
 }
 
@@ -84,6 +84,7 @@ int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
   const int T = d->seqlen, B = d->block_size, G = d->num_kv_heads;
   p->nb = (T + B - 1) / B;
   p->KS = d->topk < p->nb ? d->topk : p->nb;
+  while ((1 << p->rank_bits) < p->KS) ++p->rank_bits;
   p->R = d->num_q_heads / G;
   p->mt = msa::kAttnRows / p->R;
   p->with_scores = index_only || (d->flags == 0);
@@ -110,6 +111,9 @@ int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
   if (p->with_main) {
     const long lim = (kMaxInt32 / 2) / (per_tok_entries ? per_tok_entries : 1);
     if (tc_max > lim) tc_max = lim / B * B;
+    // packed list entries (local token << rank_bits | slot) stay in int32
+    const long lim2 = (long)kMaxInt32 >> p->rank_bits;
+    if (tc_max > lim2) tc_max = lim2 / B * B;
     if (tc_max < B) return MSA_ERR_UNSUPPORTED;
   }
   if (tc_max >= T) {
@@ -138,6 +142,7 @@ int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
     p->off_cnt = L.add(nlists * 4);
     p->off_offs = L.add(nlists * 4);
     p->off_bsum = L.add(nscan * 8);
+    p->off_rinfo = L.add(nb_ * Tc * G_ * 4);
     p->off_epos = L.add(emax * 4);
     p->off_entries = L.add(emax * 4);
     p->off_work = L.add((size_t)p->max_work * 8);
@@ -321,6 +326,7 @@ int msa_prefill(const msa_dims* dims, const void* q, const void* k, const void* 
   a.B = dims->block_size;
   a.topk = dims->topk;
   a.KS = p.KS;
+  a.rank_bits = p.rank_bits;
   a.nbl = p.nb;
   a.scale_log2 = log2_scale(dims);
 
@@ -332,6 +338,7 @@ int msa_prefill(const msa_dims* dims, const void* q, const void* k, const void* 
   }
   a.cnt = at<int32_t>(workspace, p.off_cnt);
   a.offs = at<int32_t>(workspace, p.off_offs);
+  a.rinfo = at<int32_t>(workspace, p.off_rinfo);
   a.epos = at<int32_t>(workspace, p.off_epos);
   a.entries = at<int32_t>(workspace, p.off_entries);
   a.work = at<int2>(workspace, p.off_work);

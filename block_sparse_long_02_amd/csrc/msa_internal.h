@@ -35,7 +35,7 @@ hipError_t launch_topk_decode(const float* S, int s_stride, int32_t* bidx, const
 // (token, slot) pairs are kept per (sequence, group, window, block), so that
 // consecutive block-major workgroups touch the q rows of one window.
 #ifndef MSA_LIST_WINDOW
-#define MSA_LIST_WINDOW 2048
+#define MSA_LIST_WINDOW 8192
 #endif
 constexpr int kListWindow = MSA_LIST_WINDOW;
 // Workgroup size of the multi-workgroup scans over the lists.
@@ -43,7 +43,7 @@ constexpr int kScanItems = 4096;
 // Tiles of one block list served by one block-major workgroup (the K/V
 // block is staged once for all of them).
 #ifndef MSA_TILES_PER_ITEM
-#define MSA_TILES_PER_ITEM 2
+#define MSA_TILES_PER_ITEM 8
 #endif
 constexpr int kTilesPerItem = MSA_TILES_PER_ITEM;
 
@@ -59,6 +59,7 @@ struct PrefillMainArgs {
   int batch, T, Hq, G, B, topk;
   int t0, tc;             // query chunk
   int KS;                 // partial slots per (token, group) = min(topk, nb)
+  int rank_bits;          // list entry = local token << rank_bits | slot; 2^rank_bits >= KS
   int nbl;                // block lists per (batch, group, window) = nb
   int nwin;               // windows in this chunk = ceil(tc / kListWindow)
   long nlists;            // batch * G * nwin * nbl
@@ -67,13 +68,15 @@ struct PrefillMainArgs {
   int32_t* cnt;           // [nlists]
   int32_t* offs;          // [nlists]
   int32_t* bsum;          // [2 * ceil(nlists / kScanItems)] per-scan-block totals (entries, tiles)
-  int32_t* epos;          // [batch*tc*G*KS]
+  int32_t* rinfo;         // [batch*tc*G] per (token, group) row: partial slots | has_local << 30
+  int32_t* epos;          // [batch*tc*G*KS] slot of an entry within its list; after the
+                          // scatter pass, the entry's absolute position in list order
   int32_t* entries;       // [batch*tc*G*KS]
   int2* work;             // [max_work]
   int32_t* n_work;        // [1]
   long max_work;
-  uint16_t* pO;           // [batch*tc*G*KS*R*128] fp16, per-row power-of-two scaled
-  float2* pS;             // [batch*tc*G*KS*R] (lse2, log2 of the row's scale)
+  uint16_t* pO;           // [entries*R][128] fp16 unnormalised partial outputs in list order, scaled by 2^-e
+  float2* pS;             // [entries*R] (max*c + e, sum * 2^-e), base-2 domain
 };
 hipError_t launch_prefill_main_sparse(const PrefillMainArgs& a, hipStream_t st);
 hipError_t launch_prefill_main_dense(const PrefillMainArgs& a, hipStream_t st);

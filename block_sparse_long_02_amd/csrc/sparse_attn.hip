@@ -24,6 +24,8 @@
 // Numerics: bf16 x bf16 products, fp32 accumulation, softmax in fp32 in the
 // base-2 domain (logit * scale * log2 e), probabilities rounded to bf16 for
 // the P.V product, output rounded to bf16 (nearest even).
+#include <type_traits>
+
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -32,6 +34,10 @@ namespace msa {
 namespace {
 
 constexpr int D = 128;          // head_dim
+// Fourth word of a raw (unswizzled, stride 0) buffer resource on gfx9-family
+// chips: 32-bit data format, no index stride; byte offsets >= the record count
+// are out of range (loads return 0, stores are dropped).
+constexpr int kBufferWord3 = 0x00020000;
 constexpr int KROW = D + 8;     // LDS row stride of K tiles (bf16)
 
 // ---------------------------------------------------------------------------
@@ -171,7 +177,7 @@ __device__ __forceinline__ void load_q(bf16x8* qop, const bf16_t* qp, bool ok, i
 
 // ---------------------------------------------------------------------------
 // Block lists: counting sort of the (token, slot) pairs by
-// (s, g, window, block).  Entry of a row = tl * KS + rank, rank = position
+// (s, g, window, block).  Entry of a row = tl << rank_bits | rank, rank = position
 // among the row's valid non-local entries (so partial storage needs only
 // KS = min(k, nb) slots per row).
 // ---------------------------------------------------------------------------
@@ -185,6 +191,19 @@ __device__ __forceinline__ size_t list_id(const PrefillMainArgs& a, int s, int g
   return (((size_t)s * a.G + g) * a.nwin + w) * a.nbl + b;
 }
 
+// Selection entries are read kSelChunk at a time so that their loads are all
+// in flight together.
+constexpr int kSelChunk = 8;
+
+__device__ __forceinline__ void load_sel_chunk(int (&ev)[kSelChunk], const int32_t* __restrict__ br, int j0,
+                                               int topk) {
+#pragma unroll
+  for (int u = 0; u < kSelChunk; ++u) ev[u] = (j0 + u < topk) ? br[j0 + u] : -1;
+}
+
+// Counts the entries of every block list and records per row the number of
+// partial slots (valid non-local entries, at most KS) and whether the row
+// attends its local block (a given selection may omit it).
 __global__ void lists_count_kernel(PrefillMainArgs a) {
   const long n_rows = (long)a.batch * a.tc * a.G;
   const long row = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -197,13 +216,21 @@ __global__ void lists_count_kernel(PrefillMainArgs a) {
   const int L = t / a.B;
   const int32_t* br = a.bidx + ((size_t)((long)s * a.bidx_rows + (t - a.bidx_t_off)) * a.G + g) * a.topk;
   int rank = 0;
-  for (int j = 0; j < a.topk && rank < a.KS; ++j) {
-    const int e = br[j];
-    if (e >= 0 && e < L) {
-      a.epos[(size_t)row * a.KS + rank] = atomicAdd(&a.cnt[list_id(a, s, g, tl, e)], 1);
-      ++rank;
+  bool has_local = false;
+  for (int j0 = 0; j0 < a.topk; j0 += kSelChunk) {
+    int ev[kSelChunk];
+    load_sel_chunk(ev, br, j0, a.topk);
+#pragma unroll
+    for (int u = 0; u < kSelChunk; ++u) {
+      const int e = ev[u];
+      has_local |= (e == L);
+      if (e >= 0 && e < L && rank < a.KS) {
+        a.epos[(size_t)row * a.KS + rank] = atomicAdd(&a.cnt[list_id(a, s, g, tl, e)], 1);
+        ++rank;
+      }
     }
   }
+  a.rinfo[row] = rank | (has_local ? (1 << 30) : 0);
 }
 
 // Exclusive scan of (x, y) pairs across a 1024-thread workgroup; returns the
@@ -326,43 +353,67 @@ __global__ void lists_scatter_kernel(PrefillMainArgs a) {
   const int t = a.t0 + tl;
   const int L = t / a.B;
   const int32_t* br = a.bidx + ((size_t)((long)s * a.bidx_rows + (t - a.bidx_t_off)) * a.G + g) * a.topk;
+  const int nv = a.rinfo[row] & 0x3fffffff;
   int rank = 0;
-  for (int j = 0; j < a.topk && rank < a.KS; ++j) {
-    const int e = br[j];
-    if (e >= 0 && e < L) {
-      const size_t lid = list_id(a, s, g, tl, e);
-      a.entries[(size_t)a.offs[lid] + a.epos[(size_t)row * a.KS + rank]] = tl * a.KS + rank;
-      ++rank;
+  for (int j0 = 0; j0 < a.topk && rank < nv; j0 += kSelChunk) {
+    int ev[kSelChunk];
+    load_sel_chunk(ev, br, j0, a.topk);
+#pragma unroll
+    for (int u = 0; u < kSelChunk; ++u) {
+      const int e = ev[u];
+      if (e >= 0 && e < L && rank < a.KS) {
+        const size_t lid = list_id(a, s, g, tl, e);
+        const size_t slot = (size_t)row * a.KS + rank;
+        const int pos = a.offs[lid] + a.epos[slot];
+        a.entries[pos] = (tl << a.rank_bits) | rank;
+        a.epos[slot] = pos;  // from here on: the entry's position in the list order
+        ++rank;
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// fp16 partial rows.  A row holds 128 values in a lane-native order: lane half
-// h of the MFMA output layout stores its 16 values of d-tile dt at positions
-// dt*32 + h*16 + i, where value i has d = 32*dt + 8*(i/4) + 4*h + (i%4).  The
-// row is scaled by 2^-e so that its largest magnitude lies in [2^14, 2^15)
-// (exact power-of-two scaling; no fp16 overflow for any finite input).
+// fp16 partial rows, stored in list order: the R rows of the list entry at
+// position p are rows p*R .. p*R+R-1, so that a block-major tile writes one
+// contiguous range.  A row holds 128 values in a lane-native order: value i
+// (= 8*h8 + j) of d-tile dt of lane half h sits at dt*32 + h8*16 + h*8 + j
+// and has d = 32*dt + 8*(i/4) + 4*h + (i%4), so one store instruction covers
+// 32 contiguous bytes of every row.
+// The row is the unnormalised sum O = sum_j p_j v_j over one block's keys
+// (p_j <= 1 after subtracting the row maximum), scaled by 2^-e with e chosen
+// per K/V block from max|V|: |O| <= BS * max|V| * 2^-e < 2^15, so the fp16
+// store cannot overflow for any finite input.  e = 0 (no multiply) whenever
+// max|V| lies in [2^-6, 2^8), where values too small for fp16 normals are
+// below 2^-8 max|V| and their absolute error is negligible.
 // ---------------------------------------------------------------------------
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ int row_scale_exp(float amax) {
-  if (!(amax > 0.f)) return 0;
+__device__ __forceinline__ int block_scale_exp(float vmax) {
+  if (!(vmax > 0.f) || (vmax >= 0x1p-6f && vmax < 0x1p8f)) return 0;
   int x;
-  frexpf(amax, &x);  // amax = m * 2^x, m in [0.5, 1)
-  int e = x - 15;
-  return e < -100 ? -100 : (e > 100 ? 100 : e);
+  frexpf(vmax, &x);  // vmax = m * 2^x, m in [0.5, 1)
+  const int e = x - 8;
+  return e < -100 ? -100 : (e > 126 ? 126 : e);
 }
 
-__device__ __forceinline__ void store_partial_row(uint16_t* row, const f32x16* o, float mul, int half) {
+__device__ __forceinline__ int partial_pos(int dt, int h8, int half) { return dt * 32 + h8 * 16 + half * 8; }
+
+// Stores a lane's half of a row through a buffer resource; byte offsets at or
+// beyond the resource's size (lanes without a list entry) are dropped by the
+// hardware range check.
+template <bool SCALED>
+__device__ __forceinline__ void store_partial_row(__amdgpu_buffer_rsrc_t rs, int row_byte, const f32x16* o,
+                                                  float mul, int half) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int h8 = 0; h8 < 2; ++h8) {
       f16x8 v;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = (_Float16)(o[dt][8 * h8 + j] * mul);
-      *reinterpret_cast<f16x8*>(row + dt * 32 + half * 16 + h8 * 8) = v;
+      for (int j = 0; j < 8; ++j) v[j] = (_Float16)(SCALED ? o[dt][8 * h8 + j] * mul : o[dt][8 * h8 + j]);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs,
+                                             row_byte + 2 * partial_pos(dt, h8, half), 0, 0);
     }
 }
 
@@ -371,19 +422,43 @@ __device__ __forceinline__ void accumulate_partial_row(float (*acc)[16], const u
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int h8 = 0; h8 < 2; ++h8) {
-      const f16x8 v = *reinterpret_cast<const f16x8*>(row + dt * 32 + half * 16 + h8 * 8);
+      const f16x8 v = *reinterpret_cast<const f16x8*>(row + partial_pos(dt, h8, half));
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[dt][8 * h8 + j] += w * (float)v[j];
     }
+}
+
+// Largest |v| of the block's V values a thread staged (bf16 bit patterns;
+// the magnitude order of non-NaN bf16 equals the unsigned order of their
+// low 15 bits).
+template <int BS>
+__device__ __forceinline__ float block_vmax_part(const BlockRegs<BS>& r) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < BS / 32; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const uint32_t x = r.v[i][j][w] & 0x7fff7fffu;
+        m = max(m, max(x & 0xffffu, x >> 16));
+      }
+  return __uint_as_float(m << 16);
 }
 
 // ---------------------------------------------------------------------------
 // Block-major kernel: one (s, g, window, block) list and up to
 // kTilesPerItem of its tiles of 128/R tokens per workgroup; the K/V block is
 // staged in LDS once and the next tile's q rows are fetched while the current
-// tile computes.  Writes, per (token, head) row, the normalised partial
-// output (fp16 row-scaled) and (lse2, scale exponent), lse2 = max*c +
-// log2(sum) in the base-2 domain.
+// tile computes.  Writes, per (list entry, head) row, the unnormalised
+// partial output O (fp16, scaled by 2^-e) and (max*c + e, sum * 2^-e) in the
+// base-2 domain, so that the partial's softmax weight is 2^(max*c) * sum.
+//
+// The tile loop has no branch around memory operations: the prefetches are
+// clamped to rows that exist and lanes without an entry store through a
+// buffer resource that drops their writes.  With identical memory-operation
+// counts on every path, the wait for the prefetched q rows need not also wait
+// for the previous tile's partial stores.
 // ---------------------------------------------------------------------------
 template <int BS>
 __global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
@@ -391,6 +466,7 @@ __global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
   constexpr int KT = BS / 32;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[BS * KROW];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[D * VROW];
+  __shared__ float vmax_w[4];
 
   const int w = blockIdx.x;
   if (w >= a.n_work[0]) return;
@@ -403,7 +479,7 @@ __global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
   const int s = (int)(sg / a.G);
   const int R = a.Hq / a.G;
   const int mt = kAttnRows / R;
-  const int count = a.cnt[lid];
+  const int count = a.cnt[lid];  // >= 1: work items exist for non-empty lists only
   const int off = a.offs[lid];
   const int tile0 = wk.y * kTilesPerItem;
   const int ntile = min(kTilesPerItem, (count + mt - 1) / mt - tile0);
@@ -415,112 +491,105 @@ __global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
   const int h = g * R + r;
   const float c = a.scale_log2;
 
-  // the lane's (token, rank) in tile `tile` of the list, and its q row
-  auto locate = [&](int tile, int& tl, int& rank) -> bool {
-    const int e0 = tile * mt;
-    const bool valid = e < mt && e0 + e < count;
-    tl = 0;
-    rank = 0;
-    if (valid) {
-      const int ent = a.entries[(size_t)off + e0 + e];
-      tl = ent / a.KS;
-      rank = ent % a.KS;
-    }
-    return valid;
-  };
+  // The lane's list entry (token << rank_bits | rank) in tile `tile`, clamped
+  // into the list: a lane without an entry computes on another entry's q row
+  // and its stores are dropped (every MFMA column and lane statistic belongs
+  // to one row only).
+  auto entry_at = [&](int tile) -> int { return a.entries[(size_t)off + min(tile * mt + e, count - 1)]; };
+  const size_t q_base = ((size_t)s * a.T + a.t0) * a.Hq + h;
+  auto q_row = [&](int ent) -> const bf16_t* { return a.q + (q_base + (size_t)(ent >> a.rank_bits) * a.Hq) * D; };
 
-  // issue every global load first: list entry, the K/V block, the q row
-  int tl, rank;
-  bool valid = locate(tile0, tl, rank);
+  // first tile's entries and q rows, then the K/V block; staging the block
+  // waits for all of them
+  const int ent0 = entry_at(tile0);
+  int ent_n = entry_at(tile0 + min(1, ntile - 1));
+  bf16x8 qop[D / 16];
+  load_q(qop, q_row(ent0), true, half);
   const size_t kvstride = (size_t)a.G * D;
   const size_t kvoff = ((size_t)s * a.T + (size_t)b * a.B) * kvstride + (size_t)g * D;
   BlockRegs<BS> regs;
   block_load<BS>(regs, a.k + kvoff, a.v + kvoff, kvstride, tid);
-  bf16x8 qop[D / 16];
-  load_q(qop, a.q + (((size_t)s * a.T + a.t0 + tl) * a.Hq + h) * D, valid, half);
   block_store<BS>(regs, Ks, Vt, VROW, tid);
+  {
+    const float vm = wave_max(block_vmax_part<BS>(regs));
+    if (lane == 0) vmax_w[wave] = vm;
+  }
   __syncthreads();
+  // per-block power-of-two scale of the stored partials
+  const int ex = block_scale_exp(fmaxf(fmaxf(vmax_w[0], vmax_w[1]), fmaxf(vmax_w[2], vmax_w[3])));
+  const float emul = ldexpf(1.0f, -ex);
+  const int row_byte = (e * R + r) * (D * 2);                 // >= the range for e >= mt
+  const int stat_byte = half == 0 ? (e * R + r) * 8 : 0x40000000;
 
-  for (int it = 0; it < ntile; ++it) {
-    // prefetch the next tile's q rows while this one computes
-    int tl_n = 0, rank_n = 0;
-    bool valid_n = false;
-    bf16x8 qop_n[D / 16];
-    if (it + 1 < ntile) {
-      valid_n = locate(tile0 + it + 1, tl_n, rank_n);
-      load_q(qop_n, a.q + (((size_t)s * a.T + a.t0 + tl_n) * a.Hq + h) * D, valid_n, half);
-    }
+  auto run = [&](auto scaled) {
+    constexpr bool SCALED = decltype(scaled)::value;
+    for (int it = 0; it < ntile; ++it) {
+      // The K/V tile is loop-invariant; an opaque zero offset keeps its LDS
+      // operand reads inside the loop instead of hoisting them into registers
+      // (the offset, not the pointer, is opaque, so the reads stay LDS reads).
+      int lds_off = 0;
+      asm volatile("" : "+s"(lds_off));
+      const bf16_t* ks_ = Ks + lds_off;
+      const bf16_t* vt_ = Vt + lds_off;
 
-    // The K/V tile is loop-invariant; an opaque zero offset keeps its LDS
-    // operand reads inside the loop instead of hoisting them into registers
-    // (the offset, not the pointer, is opaque, so the reads stay LDS reads).
-    int lds_off = 0;
-    asm volatile("" : "+s"(lds_off));
-    const bf16_t* ks_ = Ks + lds_off;
-    const bf16_t* vt_ = Vt + lds_off;
+      f32x16 sacc[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) sacc[kt] = qk_tile(ks_, kt * 32, qop, col, half);
 
-    f32x16 sacc[KT];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) sacc[kt] = qk_tile(ks_, kt * 32, qop, col, half);
+      // q of this tile is dead: fetch the next tile's rows into the same
+      // registers (the last tile re-reads its own), and the entries after it
+      load_q(qop, q_row(ent_n), true, half);
+      ent_n = entry_at(tile0 + min(it + 2, ntile - 1));
 
-    float mx = -INFINITY;
+      float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float mc = mx * c;
-    float l = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sacc[kt][i] * c - mc);
-        sacc[kt][i] = p;
-        l += p;
-      }
-    l += __shfl_xor(l, 32, kWave);
-
-    bf16x8 pop[KT][2];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      pop[kt][0] = to_bf16x8(sacc[kt], 0);
-      pop[kt][1] = to_bf16x8(sacc[kt], 8);
-    }
-    f32x16 oacc[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      oacc[dt] = f32x16{};
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float mc = mx * c;
+      bf16x8 pop[KT][2];
+      float l0 = 0.f, l1 = 0.f;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-        oacc[dt] = pv_step(vt_, VROW, dt, kt * 32, pop[kt][0], oacc[dt], col, half);
-        oacc[dt] = pv_step(vt_, VROW, dt, kt * 32 + 16, pop[kt][1], oacc[dt], col, half);
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          sacc[kt][i] = __builtin_amdgcn_exp2f(sacc[kt][i] * c - mc);
+          sacc[kt][i + 1] = __builtin_amdgcn_exp2f(sacc[kt][i + 1] * c - mc);
+          l0 += sacc[kt][i];
+          l1 += sacc[kt][i + 1];
+        }
+        pop[kt][0] = to_bf16x8(sacc[kt], 0);
+        pop[kt][1] = to_bf16x8(sacc[kt], 8);
       }
-    }
+      float l = l0 + l1;
+      l += __shfl_xor(l, 32, kWave);
 
-    // normalised row = oacc / l, stored as fp16 scaled by 2^-e
-    const float inv = 1.0f / l;
-    float amax = 0.f;
+      f32x16 oacc[4];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt) {
+        oacc[dt] = f32x16{};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(oacc[dt][i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave)) * inv;
-    const int ex = row_scale_exp(amax);
-    if (valid) {
-      const size_t prow = ((((size_t)s * a.tc + tl) * a.G + g) * a.KS + rank) * R + r;
-      store_partial_row(a.pO + prow * D, oacc, inv * ldexpf(1.0f, -ex), half);
-      if (half == 0) a.pS[prow] = make_float2(mc + __log2f(l), (float)ex);
-    }
+        for (int kt = 0; kt < KT; ++kt) {
+          oacc[dt] = pv_step(vt_, VROW, dt, kt * 32, pop[kt][0], oacc[dt], col, half);
+          oacc[dt] = pv_step(vt_, VROW, dt, kt * 32 + 16, pop[kt][1], oacc[dt], col, half);
+        }
+      }
 
-    if (it + 1 < ntile) {
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) qop[ks] = qop_n[ks];
-      valid = valid_n;
-      tl = tl_n;
-      rank = rank_n;
+      // rows of this tile: list positions off + (tile0+it)*mt ... + nrow - 1
+      const int p0 = off + (tile0 + it) * mt;
+      const int nrow = min(mt, count - (tile0 + it) * mt);
+      const __amdgpu_buffer_rsrc_t ro =
+          __builtin_amdgcn_make_buffer_rsrc(a.pO + (size_t)p0 * R * D, (short)0, nrow * R * D * 2, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(a.pS + (size_t)p0 * R, (short)0, nrow * R * 8, kBufferWord3);
+      store_partial_row<SCALED>(ro, row_byte, oacc, emul, half);
+      const float2 st = make_float2(mc + (float)ex, l * emul);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, st), rs, stat_byte, 0, 0);
     }
-  }
+  };
+  if (ex == 0) run(std::false_type{});
+  else run(std::true_type{});
 }
 
 // ---------------------------------------------------------------------------
@@ -548,20 +617,18 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
   const int e = row / R, r = row % R;
   const int tl = tl0 + e;
   const bool valid = e < mt && tl < a.tc;
-  const int t = a.t0 + min(tl, a.tc - 1);
+  const int tlc = min(tl, a.tc - 1);
+  const int t = a.t0 + tlc;
   const int h = g * R + r;
   const int L = t / a.B;
 
-  // the row's own key window
+  // the row's own key window; a given selection may omit the local block
   int lo = DENSE ? 0 : L * a.B;
+  int info = 0;
   bool has_local = true;
-  const int32_t* br = nullptr;
   if (!DENSE) {
-    br = a.bidx + ((size_t)((long)s * a.bidx_rows + (t - a.bidx_t_off)) * a.G + g) * a.topk;
-    // given selections may omit the local block
-    has_local = false;
-    for (int j = 0; j < a.topk; ++j)
-      if (br[j] == L) { has_local = true; break; }
+    info = a.rinfo[((size_t)s * a.tc + tlc) * a.G + g];
+    has_local = (info >> 30) & 1;
   }
   const int hi = (valid && has_local) ? t : lo - 1;  // empty window when not attended
 
@@ -608,24 +675,21 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f((m - m_use) * c);
     const float muc = m_use * c;
+    bf16x8 pop[KT][2];
     float ps = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+    for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sacc[kt][i] * c - muc);
-        sacc[kt][i] = p;
-        ps += p;
+        sacc[kt][i] = __builtin_amdgcn_exp2f(sacc[kt][i] * c - muc);
+        ps += sacc[kt][i];
       }
-    ps += __shfl_xor(ps, 32, kWave);
-    l = l * alpha + ps;
-    m = m_new;
-    bf16x8 pop[KT][2];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
       pop[kt][0] = to_bf16x8(sacc[kt], 0);
       pop[kt][1] = to_bf16x8(sacc[kt], 8);
     }
+    ps += __shfl_xor(ps, 32, kWave);
+    l = l * alpha + ps;
+    m = m_new;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -639,58 +703,49 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
   }
   if (!valid) return;
 
-  // lse2 of the local window (base-2 domain); -inf when nothing was attended
+  // The row's terms in the base-2 domain: the local window has weight
+  // 2^(m*c) * l and unnormalised output oacc; partial q has weight
+  // 2^(s1_q) * s2_q and stored output O_q, both relative to 2^(s1_q).
   const float lse2_loc = (l > 0.f) ? m * c + __log2f(l) : -INFINITY;
   float M2 = lse2_loc;
-  float scale_loc = (l > 0.f) ? 1.0f / l : 0.f;  // oacc is unnormalised
   float o[4][16];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[dt][i] = oacc[dt][i];
-
-  float sumw = 0.f;
+  float sumw;
   if (!DENSE) {
-    const size_t prow0 = (((size_t)s * a.tc + tl) * a.G + g) * a.KS;
-    const int R_ = R;
-    // the row's partial slots are its valid non-local entries, ranks 0..nv-1
-    int nv = 0;
-    for (int j = 0; j < a.topk && nv < a.KS; ++j) {
-      const int eb = br[j];
-      nv += (eb >= 0 && eb < L) ? 1 : 0;
+    const int nv = info & 0x3fffffff;  // partial slots 0..nv-1
+    // list positions of the row's partials; rows pos*R + r of pO / pS
+    const int32_t* pos = a.epos + (((size_t)s * a.tc + tl) * a.G + g) * a.KS;
+    // pass 1: the largest log-weight
+    for (int q = 0; q < nv; ++q) {
+      const float2 st = a.pS[(size_t)pos[q] * R + r];
+      M2 = fmaxf(M2, st.x + __log2f(st.y));
     }
-    const float2* ps = a.pS + prow0 * R_ + r;     // rank q at ps[q * R_]
-    const uint16_t* po = a.pO + (prow0 * R_ + r) * D;
-    const size_t po_step = (size_t)R_ * D;
-    // pass 1: the merged maximum
-    for (int q = 0; q < nv; ++q) M2 = fmaxf(M2, ps[(size_t)q * R_].x);
     const float M2u = (M2 == -INFINITY) ? 0.f : M2;
-    const float wl = (l > 0.f) ? __builtin_amdgcn_exp2f(lse2_loc - M2u) : 0.f;
-    sumw = wl;
-    const float f = wl * scale_loc;
+    const float wl = (l > 0.f) ? __builtin_amdgcn_exp2f(m * c - M2u) : 0.f;
+    sumw = wl * l;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= f;
-    // pass 2: weighted partials in rank (= slot) order; the weight folds in
-    // the row scale 2^e
+      for (int i = 0; i < 16; ++i) o[dt][i] = oacc[dt][i] * wl;
+    // pass 2: weighted partials in slot order
 #ifndef MSA_COMBINE_UNROLL
 #define MSA_COMBINE_UNROLL 2
 #endif
 #pragma unroll MSA_COMBINE_UNROLL
     for (int q = 0; q < nv; ++q) {
-      const float2 st = ps[(size_t)q * R_];
-      sumw += __builtin_amdgcn_exp2f(st.x - M2u);
-      accumulate_partial_row(o, po + (size_t)q * po_step, __builtin_amdgcn_exp2f(st.x - M2u + st.y), half);
+      const size_t prow = (size_t)pos[q] * R + r;
+      const float2 st = a.pS[prow];
+      const float w = __builtin_amdgcn_exp2f(st.x - M2u);
+      sumw += w * st.y;
+      accumulate_partial_row(o, a.pO + prow * D, w, half);
     }
     M2 = M2u;
   } else {
+    const float inv_l = (l > 0.f) ? 1.0f / l : 0.f;
     sumw = (l > 0.f) ? 1.f : 0.f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= scale_loc;
-    M2 = lse2_loc;
+      for (int i = 0; i < 16; ++i) o[dt][i] = oacc[dt][i] * inv_l;
   }
 
   const float invw = (sumw > 0.f) ? 1.0f / sumw : 0.f;

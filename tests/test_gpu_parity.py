@@ -206,6 +206,50 @@ def test_all_blocks_selected_matches_dense_mode():
     assert mx < 2e-2
 
 
+@pytest.mark.parametrize("u", [-30, -9, 12, 40])
+def test_prefill_value_scale_uniform(u):
+    """V scaled by 2^u (exact in bf16): the output scales by 2^u.  Exercises
+    the power-of-two rescaling of the stored partials outside the range where
+    they are stored unscaled."""
+    T, Hq, G, di, B, k = 1536, 16, 4, 64, 64, 6
+    say(f"[prefill V*2^{u}]")
+    inp = inputs.make_prefill(T, Hq, G, 128, di, seed=21, idx_mode="integer")
+    inp.v = (inp.v.float() * 2.0 ** u).to(torch.bfloat16)
+    out, lse, bidx = gpu_prefill(inp, B, k)
+    rows = [(0, t) for t in range(0, T, 7)] + [(0, T - 1)]
+    ores = orc.prefill(inp.q, inp.k, inp.v, inp.idx_q, inp.idx_k, B, k, rows=rows)
+    compare_selection(bidx, ores, B, k, exact=True)
+    o_ref = np.stack([ores["out"][r] for r in rows]) * 2.0 ** -u
+    o_got = np.stack([out[s, t].to(torch.float64).numpy() for s, t in rows]) * 2.0 ** -u
+    check_attention(o_got, o_ref, f"out/2^{u}")
+
+
+def test_prefill_value_scale_per_block():
+    """Every (block, group) of V carries its own power-of-two scale, so that
+    partials of one row are stored with different exponents; outputs are
+    compared per row relative to the row's largest reference magnitude."""
+    T, Hq, G, di, B, k = 1536, 16, 4, 64, 64, 6
+    say("[prefill V per-block 2^u]")
+    inp = inputs.make_prefill(T, Hq, G, 128, di, seed=22, idx_mode="integer")
+    rng = np.random.default_rng(5)
+    nb = T // B
+    ex = rng.choice([-40, -12, -7, -3, 0, 4, 9, 20, 60], size=(nb, G))
+    scale = torch.from_numpy(np.repeat(2.0 ** ex, B, axis=0)).float()  # [T, G]
+    inp.v = (inp.v.float() * scale[None, :, :, None]).to(torch.bfloat16)
+    out, lse, bidx = gpu_prefill(inp, B, k)
+    rows = [(0, t) for t in range(0, T, 5)] + [(0, T - 1)]
+    ores = orc.prefill(inp.q, inp.k, inp.v, inp.idx_q, inp.idx_k, B, k, rows=rows)
+    compare_selection(bidx, ores, B, k, exact=True)
+    o_ref = np.stack([ores["out"][r] for r in rows])
+    o_got = np.stack([out[s, t].to(torch.float64).numpy() for s, t in rows])
+    norm = np.abs(o_ref).max(axis=-1, keepdims=True)  # per (row, head)
+    norm[norm == 0] = 1.0
+    check_attention(o_got / norm, o_ref / norm, "out/rowmax")
+    l_ref = np.stack([ores["lse"][r] for r in rows])
+    l_got = np.stack([lse[s, t].to(torch.float64).numpy() for s, t in rows])
+    assert np.abs(l_got - l_ref).max() < 1e-3, np.abs(l_got - l_ref).max()
+
+
 def test_prefill_bitwise_deterministic():
     T, Hq, G, di, B, k = 2048, 16, 4, 64, 64, 6
     say("[prefill determinism]")
