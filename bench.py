@@ -8,9 +8,10 @@ bf16 tensors resident in HBM before timing starts.
 
 Prints one JSON line: `value` is prefill tokens/s; the decode rate, the dense
 (all-blocks) comparison, a sampled parity check against the CPU oracle, the
-roofline of the dominant kernel (index scoring + block max, MFMA-bound) timed
-live with HIP events, and the oracle's own rate on the host cores are
-reported beside it.
+roofline of the dominant prefill kernel (the stage with the largest time,
+timed live with the library's per-stage HIP events over the timed steps), the
+rooflines of the other main kernels, and the oracle's own rate on the host
+cores are reported beside it.
 """
 from __future__ import annotations
 
@@ -37,9 +38,11 @@ PEAK_HBM = 8.0e12         # MI355X HBM3E, B/s
 PF = dict(T=131072, Hq=64, G=8, d=128, di=128, B=128, k=16, skew=0.5, seed=0)
 DC = dict(batch=8, L=1 << 20, Hq=64, G=8, d=128, di=128, B=128, k=16, seed=1)
 
-DOMINANT = "index_blockmax_prefill_kernel"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_blockmax_prefill_t131072_traffic.json")
 COPY_BYTES = 1 << 30   # calibration copy for the --pmc passes
+
+
+def traffic_file(kernel):
+    return os.path.join(ROOT, "profiles", f"{kernel}_prefill_t131072_traffic.json")
 
 
 def log(msg):
@@ -69,18 +72,45 @@ def decode_bytes(batch, L, Hq, G, d, di, B, k):
     return batch * per_seq
 
 
-def measured_traffic():
-    """Per-launch HBM bytes of the dominant kernel from the committed --pmc
-    summary, or None when absent or taken on different kernel sources."""
+def measured_traffic(kernel):
+    """Per-launch HBM bytes of a kernel from the committed --pmc summary, or
+    None when absent or taken on different kernel sources."""
     from block_sparse_long_02_amd import profiling
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(kernel)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != profiling.source_hash(DOMINANT):
+    if rec.get("source_sha256") != profiling.source_hash(kernel):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def kv_outer_bytes(bidx, T, Hq, G, d, B, k):
+    """Algorithmic bytes of one block-major launch over the whole prefill:
+    per (token, group, selected non-local block) entry the group's R q rows
+    are read and R partial rows (fp16 values + 8-byte statistics) written,
+    plus the 4-byte list entry; every distinct selected (group, block) K/V
+    block is read once."""
+    R = Hq // G
+    t = torch.arange(T, device=bidx.device).view(1, T, 1, 1)
+    sel = bidx.long()
+    valid = (sel >= 0) & (sel < t // B)
+    entries = int(valid.sum().item())
+    gb = (torch.arange(G, device=bidx.device).view(1, 1, G, 1) * ((T + B - 1) // B) + sel)[valid]
+    blocks = int(torch.unique(gb).numel())
+    per_entry = R * d * 2 + R * (d * 2 + 8) + 4
+    return entries * per_entry + blocks * 2 * B * d * 2, entries, blocks
+
+
+def query_major_bytes(entries, T, Hq, G, d, B):
+    """Algorithmic bytes of the query-major launch: per (token, head) the q row
+    is read and the output row and lse written; per partial the fp16 row,
+    its statistics and its list position are read; the local blocks' K/V
+    (each block once per group)."""
+    R = Hq // G
+    nb = (T + B - 1) // B
+    return T * Hq * (d * 2 + d * 2 + 4) + entries * (R * (d * 2 + 8) + 4) + G * nb * 2 * B * d * 2
 
 
 def measured_peaks(dev):
@@ -99,24 +129,26 @@ def measured_peaks(dev):
             "device_copy_gbs": round(2 * (1 << 30) / (cms * 1e-3) / 1e9, 1)}
 
 
-def profile_kernel_only(args, dev):
-    """Inputs of the 128K prefill's index branch, one calibration copy of
-    COPY_BYTES, then --steps launches of the dominant kernel (the same launch
-    msa_prefill makes): the workload of the --pmc counter passes."""
+def profile_kernels_only(args, dev):
+    """The 128K prefill's inputs, one calibration copy of COPY_BYTES, then
+    --steps prefills (every kernel launched as in the timed steps): the
+    workload of the --pmc counter passes and of the kernel-trace summary."""
     stream = torch.cuda.current_stream()
-    pin = inputs.make_prefill(PF["T"], 1, PF["G"], 8, PF["di"], seed=PF["seed"], device=dev,
+    pin = inputs.make_prefill(PF["T"], PF["Hq"], PF["G"], PF["d"], PF["di"], seed=PF["seed"], device=dev,
                               block_size=PF["B"], skew_std=PF["skew"])
-    pdims = bd.make_dims(1, PF["T"], PF["G"], PF["G"], index_dim=PF["di"], block_size=PF["B"], topk=PF["k"])
-    rs = bd.scores_row_stride(pdims, PF["T"])
-    scores = torch.empty((1, PF["T"], PF["G"], rs), dtype=torch.float32, device=dev)
+    pdims = bd.make_dims(1, PF["T"], PF["Hq"], PF["G"], index_dim=PF["di"], block_size=PF["B"], topk=PF["k"])
+    pout = torch.empty_like(pin.q)
+    pws = torch.empty(bd.msa_workspace_bytes(bd.MSA_OP_PREFILL, pdims), dtype=torch.uint8, device=dev)
     x = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
     torch.cuda.synchronize()
     y.copy_(x)
-    ms, _ = timed(lambda: bd.msa_index_scores(pdims, pin.idx_q, pin.idx_k, scores, 0, PF["T"], rs),
+    bd.msa_profile_begin()
+    ms, _ = timed(lambda: bd.msa_prefill(pdims, pin.q, pin.k, pin.v, pin.idx_q, pin.idx_k, pout, workspace=pws),
                   args.steps, stream)
-    print(json.dumps({"profile_kernel": DOMINANT, "launches": args.steps, "launch_ms": round(ms, 4),
-                      "copy_bytes": COPY_BYTES}), flush=True)
+    stages = bd.msa_profile_end()
+    print(json.dumps({"profile_prefills": args.steps, "prefill_ms": round(ms, 4), "copy_bytes": COPY_BYTES,
+                      "stage_ms": {n: round(t / c, 4) for n, (c, t) in stages.items()}}), flush=True)
 
 
 def timed(fn, reps, stream):
@@ -243,8 +275,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (CPU baseline + parity)")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
-    ap.add_argument("--profile-kernel", action="store_true",
-                    help="run only the dominant kernel (plus a calibration copy) for rocprofv3 --pmc passes")
+    ap.add_argument("--profile-kernels", action="store_true",
+                    help="run only prefills (plus a calibration copy) for rocprofv3 --pmc passes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path "
@@ -256,8 +288,8 @@ def main():
     bd.load_library()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    if args.profile_kernel:
-        profile_kernel_only(args, dev)
+    if args.profile_kernels:
+        profile_kernels_only(args, dev)
         return
 
     log("generating prefill inputs (T=131072)")
@@ -297,6 +329,7 @@ def main():
     log(f"timing {args.steps} steps")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    bd.msa_profile_begin()  # per-stage HIP events on the launch stream
     w0 = time.perf_counter()
     for i in range(args.steps):
         evs[i][0].record(stream)
@@ -306,21 +339,45 @@ def main():
         evs[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
+    stage = {n: t / c for n, (c, t) in bd.msa_profile_end().items()}
+    log("stage ms: " + ", ".join(f"{n} {v:.3f}" for n, v in stage.items()))
     p_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     d_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     log(f"prefill {p_ms:.3f} ms  decode {d_ms:.3f} ms  wall/step {1e3 * wall / args.steps:.3f} ms")
 
-    # dominant kernel: index scoring + block max over the whole prefill,
-    # the same launch msa_prefill makes (one query chunk covers T=131072)
-    rs = bd.scores_row_stride(pdims, PF["T"])
-    scores = torch.empty((1, PF["T"], PF["G"], rs), dtype=torch.float32, device=dev)
-    idx_ms, _ = timed(lambda: bd.msa_index_scores(pdims, pin.idx_q, pin.idx_k, scores, 0, PF["T"], rs),
-                      args.steps, stream)
-    del scores
-
+    # per-kernel rooflines of the prefill (one query chunk covers T=131072,
+    # so each stage is one launch per prefill)
     f_index, f_main = prefill_flops(PF["T"], PF["Hq"], PF["G"], PF["d"], PF["di"], PF["B"], PF["k"])
     dbytes = decode_bytes(DC["batch"], DC["L"], DC["Hq"], DC["G"], DC["d"], DC["di"], DC["B"], DC["k"])
-    idx_tflops = f_index / (idx_ms * 1e-3) / 1e12
+    kvb, n_entries, n_blocks = kv_outer_bytes(pbidx, PF["T"], PF["Hq"], PF["G"], PF["d"], PF["B"], PF["k"])
+    qmb = query_major_bytes(n_entries, PF["T"], PF["Hq"], PF["G"], PF["d"], PF["B"])
+    rooflines = {}
+    name_idx, name_kv, name_qm = (bd.msa_stage_name(bd.MSA_STAGE_INDEX_PREFILL), bd.msa_stage_name(bd.MSA_STAGE_KV_OUTER),
+                                  bd.msa_stage_name(bd.MSA_STAGE_QUERY_MAJOR))
+    if name_idx in stage:
+        a = f_index / (stage[name_idx] * 1e-3)
+        rooflines[name_idx] = {"bound": "mfma", "achieved": round(a / 1e12, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                               "frac": round(a / PEAK_MFMA_BF16, 4),
+                               "traffic": measured_traffic("index_blockmax_prefill_kernel"),
+                               "launch_ms": round(stage[name_idx], 4),
+                               "algorithmic_tflop_per_launch": round(f_index / 1e12, 3)}
+    if name_kv in stage:
+        a = kvb / (stage[name_kv] * 1e-3)
+        rooflines[name_kv] = {"bound": "hbm", "achieved": round(a / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
+                              "frac": round(a / PEAK_HBM, 4), "traffic": measured_traffic("kv_outer_kernel"),
+                              "launch_ms": round(stage[name_kv], 4),
+                              "algorithmic_gbytes_per_launch": round(kvb / 1e9, 3),
+                              "entries": n_entries, "distinct_blocks": n_blocks,
+                              "mfma_tflops": round(4.0 * PF["d"] * PF["B"] * n_entries * (PF["Hq"] // PF["G"])
+                                                   / (stage[name_kv] * 1e-3) / 1e12, 1)}
+    if name_qm in stage:
+        a = qmb / (stage[name_qm] * 1e-3)
+        rooflines[name_qm] = {"bound": "hbm", "achieved": round(a / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
+                              "frac": round(a / PEAK_HBM, 4), "traffic": measured_traffic("query_major_kernel"),
+                              "launch_ms": round(stage[name_qm], 4),
+                              "algorithmic_gbytes_per_launch": round(qmb / 1e9, 3)}
+    prefill_stages = [n for n in stage if n in rooflines]
+    dominant = max(prefill_stages, key=lambda n: stage[n]) if prefill_stages else None
 
     dense = None
     if not args.no_dense:
@@ -388,12 +445,9 @@ def main():
                          "achieved": round(dbytes / (d_ms * 1e-3) / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
                          "frac": round(dbytes / (d_ms * 1e-3) / PEAK_HBM, 4)},
         },
-        "roofline": {
-            "bound": "mfma", "kernel": "index_blockmax_prefill_kernel (index scoring + block max)",
-            "achieved": round(idx_tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
-            "frac": round(idx_tflops * 1e12 / PEAK_MFMA_BF16, 4), "traffic": measured_traffic(),
-            "launch_ms": round(idx_ms, 4), "algorithmic_tflop_per_launch": round(f_index / 1e12, 3),
-        },
+        "roofline": dict(kernel=dominant, **rooflines[dominant]) if dominant else None,
+        "kernel_rooflines": rooflines,
+        "stage_ms": {n: round(v, 4) for n, v in stage.items()},
         "dense": dense,
         "measured_peaks": peaks,
         "parity": {"prefill_sampled": parity, "decode_sampled": dparity},

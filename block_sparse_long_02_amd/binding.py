@@ -30,8 +30,25 @@ MSA_OP_INDEX_TOPK = 0
 MSA_OP_PREFILL = 1
 MSA_OP_DECODE = 2
 
+MSA_STAGE_INDEX_PREFILL = 0
+MSA_STAGE_TOPK_PREFILL = 1
+MSA_STAGE_BLOCK_LISTS = 2
+MSA_STAGE_KV_OUTER = 3
+MSA_STAGE_QUERY_MAJOR = 4
+MSA_STAGE_QUERY_MAJOR_DENSE = 5
+MSA_STAGE_INDEX_DECODE = 6
+MSA_STAGE_TOPK_DECODE = 7
+MSA_STAGE_DECODE_ATTN = 8
+MSA_STAGE_DECODE_COMBINE = 9
+MSA_STAGE_COUNT = 10
+
 EXPORTED = ("msa_index_scores", "msa_index_topk", "msa_prefill", "msa_decode", "msa_workspace_bytes",
-            "msa_status_string", "msa_last_hip_error", "msa_abi_version")
+            "msa_status_string", "msa_last_hip_error", "msa_abi_version", "msa_profile_begin",
+            "msa_profile_end", "msa_stage_name")
+
+
+class msa_stage_time(ctypes.Structure):
+    _fields_ = [("stage", ctypes.c_int32), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
 
 
 class msa_dims(ctypes.Structure):
@@ -92,6 +109,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_last_hip_error.restype = ctypes.c_char_p
     lib.msa_abi_version.argtypes = []
     lib.msa_abi_version.restype = i32
+    lib.msa_profile_begin.argtypes = []
+    lib.msa_profile_begin.restype = i32
+    lib.msa_profile_end.argtypes = [ctypes.POINTER(msa_stage_time), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.msa_profile_end.restype = i32
+    lib.msa_stage_name.argtypes = [ctypes.c_int32]
+    lib.msa_stage_name.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -226,3 +249,22 @@ def msa_decode(dims: msa_dims, q, k_cache, v_cache, idx_q, idx_k_cache, cache_le
     _check(lib, lib.msa_decode(ctypes.byref(dims), p_q, p_k, p_v, p_iq, p_ik, p_len, p_o, p_l, p_bi,
                                ws, nws, _stream(stream)))
     return out
+
+
+def msa_profile_begin() -> None:
+    """Start recording per-stage HIP events of the library's calls."""
+    lib = load_library()
+    _check(lib, lib.msa_profile_begin())
+
+
+def msa_profile_end() -> dict:
+    """Stop recording; {stage name: (launches, total ms)} for stages that ran."""
+    lib = load_library()
+    arr = (msa_stage_time * MSA_STAGE_COUNT)()
+    n = ctypes.c_int32(0)
+    _check(lib, lib.msa_profile_end(arr, MSA_STAGE_COUNT, ctypes.byref(n)))
+    return {msa_stage_name(r.stage): (r.launches, r.total_ms) for r in arr[: n.value] if r.launches > 0}
+
+
+def msa_stage_name(stage: int) -> str:
+    return load_library().msa_stage_name(stage).decode()

@@ -219,10 +219,12 @@ hipError_t run_index_chunk(const msa_dims* d, const PrefillPlan& p, const void* 
   const int Lc = (t0 + tc - 1) / B;
   const int s_stride = (int)round_up((size_t)(Lc > 1 ? Lc : 1), 4);
   float* S = at<float>(ws, p.off_S);
+  msa::prof_mark(st, MSA_STAGE_INDEX_PREFILL);
   hipError_t e = msa::launch_index_blockmax_prefill(
       static_cast<const uint16_t*>(idx_q), static_cast<const uint16_t*>(idx_k), S, d->batch,
       d->seqlen, d->num_kv_heads, d->index_dim, B, t0, tc, s_stride, st);
   if (e != hipSuccess) return e;
+  msa::prof_mark(st, MSA_STAGE_TOPK_PREFILL);
   return msa::launch_topk_prefill(S, s_stride, bidx, bidx_rows, t_off, d->batch, d->num_kv_heads, B,
                                   d->topk, t0, tc, st);
 }
@@ -276,6 +278,7 @@ int msa_index_topk(const msa_dims* dims, const void* idx_q, const void* idx_k, i
     hipError_t e = run_index_chunk(dims, p, idx_q, idx_k, workspace, t0, tc, block_idx, dims->seqlen, 0, s);
     if (e != hipSuccess) return hip_fail(e);
   }
+  msa::prof_mark(s, -1);
   return MSA_OK;
 }
 
@@ -289,10 +292,12 @@ int msa_index_scores(const msa_dims* dims, const void* idx_q, const void* idx_k,
   const int Lc = (t1 - 1) / dims->block_size;
   if (row_stride < 4 || row_stride % 4 != 0 || row_stride < Lc) return MSA_ERR_INVALID_ARG;
   if (misaligned(idx_q, 16) || misaligned(idx_k, 16) || misaligned(scores, 16)) return MSA_ERR_ALIGNMENT;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  msa::prof_mark(s, MSA_STAGE_INDEX_PREFILL);
   hipError_t e = msa::launch_index_blockmax_prefill(
       static_cast<const uint16_t*>(idx_q), static_cast<const uint16_t*>(idx_k), scores, dims->batch,
-      dims->seqlen, dims->num_kv_heads, dims->index_dim, dims->block_size, t0, t1 - t0, row_stride,
-      static_cast<hipStream_t>(hip_stream));
+      dims->seqlen, dims->num_kv_heads, dims->index_dim, dims->block_size, t0, t1 - t0, row_stride, s);
+  msa::prof_mark(s, -1);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
@@ -333,7 +338,9 @@ int msa_prefill(const msa_dims* dims, const void* q, const void* k, const void* 
   if (dense) {
     a.t0 = 0;
     a.tc = dims->seqlen;
+    msa::prof_mark(s, MSA_STAGE_QUERY_MAJOR_DENSE);
     hipError_t e = msa::launch_prefill_main_dense(a, s);
+    msa::prof_mark(s, -1);
     return e == hipSuccess ? MSA_OK : hip_fail(e);
   }
   a.cnt = at<int32_t>(workspace, p.off_cnt);
@@ -378,6 +385,7 @@ int msa_prefill(const msa_dims* dims, const void* q, const void* k, const void* 
     hipError_t e = msa::launch_prefill_main_sparse(a, s);
     if (e != hipSuccess) return hip_fail(e);
   }
+  msa::prof_mark(s, -1);
   return MSA_OK;
 }
 
@@ -405,10 +413,12 @@ int msa_decode(const msa_dims* dims, const void* q, const void* k_cache, const v
   if (!dense && !given) {
     if (bidx == nullptr) bidx = at<int32_t>(workspace, p.off_bidx);
     float* S = at<float>(workspace, p.off_S);
+    msa::prof_mark(s, MSA_STAGE_INDEX_DECODE);
     hipError_t e = msa::launch_index_blockmax_decode(
         static_cast<const uint16_t*>(idx_q), static_cast<const uint16_t*>(idx_k_cache), cache_lens, S,
         dims->batch, dims->seqlen, dims->num_kv_heads, dims->index_dim, dims->block_size, p.s_stride, s);
     if (e != hipSuccess) return hip_fail(e);
+    msa::prof_mark(s, MSA_STAGE_TOPK_DECODE);
     e = msa::launch_topk_decode(S, p.s_stride, bidx, cache_lens, dims->seqlen, dims->batch,
                                 dims->num_kv_heads, dims->block_size, dims->topk, s);
     if (e != hipSuccess) return hip_fail(e);
@@ -434,6 +444,7 @@ int msa_decode(const msa_dims* dims, const void* q, const void* k_cache, const v
   a.pO = at<float>(workspace, p.off_pO);
   a.pS = at<float>(workspace, p.off_pS);
   hipError_t e = msa::launch_decode_main(a, s);
+  msa::prof_mark(s, -1);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 

@@ -367,6 +367,7 @@ hipError_t launch_decode_main(const DecodeMainArgs& a, hipStream_t st) {
   int ipw, nparts;
   decode_partition(a.nsplit, &ipw, &nparts);
   const dim3 grid(nparts, a.G, a.batch);
+  prof_mark(st, MSA_STAGE_DECODE_ATTN);
 #define MSA_DEC_ATTN(BS_)                                                                          \
   decode_attn_kernel<BS_><<<grid, kDecAttnWaves * 64, 0, st>>>(a, ipw, nparts)
   if (a.B == 128) MSA_DEC_ATTN(128);
@@ -375,6 +376,7 @@ hipError_t launch_decode_main(const DecodeMainArgs& a, hipStream_t st) {
 #undef MSA_DEC_ATTN
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nparts == 1) return err;
+  prof_mark(st, MSA_STAGE_DECODE_COMBINE);
   decode_combine_kernel<<<dim3(a.G, a.batch), 128, 0, st>>>(a, nparts);
   return hipGetLastError();
 }

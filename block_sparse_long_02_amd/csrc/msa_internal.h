@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "msa.h"
+
 namespace msa {
 
 // Tokens (query rows) handled by one workgroup of the attention kernels:
@@ -13,6 +15,10 @@ namespace msa {
 constexpr int kAttnRows = 128;
 
 hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t value, hipStream_t st);
+
+// Stage boundary for msa_profile_*: records an event on st while profiling
+// is on (stage = MSA_STAGE_*, or -1 at the end of a call); no-op otherwise.
+void prof_mark(hipStream_t st, int stage);
 
 // ---- Index Branch, prefill: scores + Block-Max for query tokens [t0, t0+tc) ----
 // S is [batch][tc*G][s_stride] fp32; row (t-t0)*G+g holds blocks 0..L(t)-1.

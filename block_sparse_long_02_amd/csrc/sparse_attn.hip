@@ -778,6 +778,7 @@ hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t value, hipStream_t st) 
 }
 
 hipError_t launch_prefill_main_sparse(const PrefillMainArgs& a, hipStream_t st) {
+  prof_mark(st, MSA_STAGE_BLOCK_LISTS);
   hipError_t err = launch_fill_i32(a.cnt, (size_t)a.nlists, 0, st);
   if (err != hipSuccess) return err;
   const long n_rows = (long)a.batch * a.tc * a.G;
@@ -796,6 +797,7 @@ hipError_t launch_prefill_main_sparse(const PrefillMainArgs& a, hipStream_t st) 
   lists_scatter_kernel<<<rgrid, 256, 0, st>>>(a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (a.max_work > 0) {
+    prof_mark(st, MSA_STAGE_KV_OUTER);
     const dim3 grid((unsigned)a.max_work);
     if (a.B == 128) kv_outer_kernel<128><<<grid, 256, 0, st>>>(a);
     else if (a.B == 64) kv_outer_kernel<64><<<grid, 256, 0, st>>>(a);
@@ -803,6 +805,7 @@ hipError_t launch_prefill_main_sparse(const PrefillMainArgs& a, hipStream_t st) 
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const dim3 qgrid((unsigned)((a.tc + mt - 1) / mt), a.G, a.batch);
+  prof_mark(st, MSA_STAGE_QUERY_MAJOR);
   query_major_kernel<false><<<qgrid, 256, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -3,7 +3,7 @@
   python -m block_sparse_long_02_amd.profiling stats <kernel_stats.csv> --title T --command C
       -> markdown table of per-kernel call counts and durations
   python -m block_sparse_long_02_amd.profiling traffic --fetch <dir> --write <dir>
-         --kernel index_blockmax_prefill_kernel --copy-bytes N --out <json> --command C
+         --kernel kv_outer_kernel --copy-bytes N --out <json> --command C
       -> per-launch HBM traffic of a kernel from two --pmc passes (FETCH_SIZE,
          WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
          reads for the blit copy kernel of N bytes in the same run
@@ -27,6 +27,10 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 KERNEL_SOURCES = {
     "index_blockmax_prefill_kernel": ["csrc/index_blockmax.hip", "csrc/msa_device.h", "csrc/msa_internal.h",
                                       "build.py"],
+    "kv_outer_kernel": ["csrc/sparse_attn.hip", "csrc/msa_device.h", "csrc/msa_internal.h", "csrc/api.hip",
+                        "build.py"],
+    "query_major_kernel": ["csrc/sparse_attn.hip", "csrc/msa_device.h", "csrc/msa_internal.h", "csrc/api.hip",
+                           "build.py"],
 }
 
 

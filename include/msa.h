@@ -164,6 +164,45 @@ const char* msa_last_hip_error(void);
 /* ABI version of this header: 1. */
 int msa_abi_version(void);
 
+/*
+ * Stage timing (a measurement aid; not part of the attention computation).
+ * Between msa_profile_begin() and msa_profile_end(), every stage of every
+ * msa_prefill / msa_decode / msa_index_topk call records a HIP event on the
+ * call's stream at its start, and each call records one at its end; a
+ * stage's time is the elapsed time from its event to the next event on the
+ * same stream.  While profiling is off nothing is recorded.
+ *
+ * msa_profile_end() stops recording, waits for the recorded events and writes
+ * MSA_STAGE_COUNT entries to out (indexed by stage; launches = number of
+ * timed launches of the stage, total_ms = their summed time).  It returns
+ * MSA_ERR_INVALID_ARG when out or n_stages is NULL or max_stages <
+ * MSA_STAGE_COUNT, MSA_ERR_HIP when an event could not be created, recorded
+ * or read.  Profiling is process-wide; calls on several host threads are
+ * recorded together.
+ */
+#define MSA_STAGE_INDEX_PREFILL 0      /* index scores + Block-Max, prefill      */
+#define MSA_STAGE_TOPK_PREFILL 1       /* Top-k with the forced local block       */
+#define MSA_STAGE_BLOCK_LISTS 2        /* per-block lists of (token, slot) pairs  */
+#define MSA_STAGE_KV_OUTER 3           /* block-major attention, partial outputs  */
+#define MSA_STAGE_QUERY_MAJOR 4        /* local block + merge of the partials     */
+#define MSA_STAGE_QUERY_MAJOR_DENSE 5  /* all-blocks (MSA_DENSE) prefill          */
+#define MSA_STAGE_INDEX_DECODE 6       /* index scores + Block-Max, decode        */
+#define MSA_STAGE_TOPK_DECODE 7
+#define MSA_STAGE_DECODE_ATTN 8        /* per-(sequence, group) attention         */
+#define MSA_STAGE_DECODE_COMBINE 9     /* combine of the split partials (dense)   */
+#define MSA_STAGE_COUNT 10
+
+typedef struct msa_stage_time {
+  int32_t stage;
+  int32_t launches;
+  double total_ms;
+} msa_stage_time;
+
+int msa_profile_begin(void);
+int msa_profile_end(msa_stage_time* out, int32_t max_stages, int32_t* n_stages);
+/* Static name of a stage (never NULL). */
+const char* msa_stage_name(int32_t stage);
+
 #ifdef __cplusplus
 }
 #endif

@@ -163,3 +163,20 @@ def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 256, 16, 128, dtype=torch.bfloat16)
     with pytest.raises((ValueError, RuntimeError)):
         bd.msa_prefill(d, q, q, q, q, q, q)
+
+
+def test_profile_calls_without_gpu_work(lib):
+    """Profiling with no recorded calls: every stage reports zero launches;
+    bad arguments are rejected and leave profiling off."""
+    assert lib.msa_profile_begin() == bd.MSA_OK
+    arr = (bd.msa_stage_time * bd.MSA_STAGE_COUNT)()
+    n = ctypes.c_int32(-1)
+    assert lib.msa_profile_end(arr, bd.MSA_STAGE_COUNT, ctypes.byref(n)) == bd.MSA_OK
+    assert n.value == bd.MSA_STAGE_COUNT
+    assert [r.stage for r in arr] == list(range(bd.MSA_STAGE_COUNT))
+    assert all(r.launches == 0 and r.total_ms == 0.0 for r in arr)
+    assert lib.msa_profile_end(arr, bd.MSA_STAGE_COUNT - 1, ctypes.byref(n)) == bd.MSA_ERR_INVALID_ARG
+    assert lib.msa_profile_end(None, bd.MSA_STAGE_COUNT, ctypes.byref(n)) == bd.MSA_ERR_INVALID_ARG
+    names = [lib.msa_stage_name(i).decode() for i in range(bd.MSA_STAGE_COUNT)]
+    assert len(set(names)) == bd.MSA_STAGE_COUNT and "kv_outer_kernel" in names
+    assert lib.msa_stage_name(99).decode() == "unknown stage"

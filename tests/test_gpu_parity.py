@@ -386,3 +386,40 @@ def test_decode_all_ties_partition_fallback():
         exp = list(range(k - 1)) + [Lb]
         for g in range(G):
             assert bidx[s, g].tolist() == exp, (s, g)
+
+
+def test_stage_profiling_accounts_for_the_calls():
+    """Per-stage event times of real prefill and decode calls: every stage
+    that ran is counted once per call and the stages add up to the calls'
+    own event-timed duration."""
+    T, Hq, G, di, B, k = 2048, 16, 4, 64, 64, 6
+    say("[stage profiling]")
+    inp = inputs.make_prefill(T, Hq, G, 128, di, seed=31, device="cuda")
+    dims = bd.make_dims(1, T, Hq, G, index_dim=di, block_size=B, topk=k)
+    out = torch.empty_like(inp.q)
+    ws = torch.empty(bd.msa_workspace_bytes(bd.MSA_OP_PREFILL, dims), dtype=torch.uint8, device="cuda")
+    run = lambda: bd.msa_prefill(dims, inp.q, inp.k, inp.v, inp.idx_q, inp.idx_k, out, workspace=ws)  # noqa: E731
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    bd.msa_profile_begin()
+    e0.record()
+    for _ in range(3):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    st = bd.msa_profile_end()
+    names = [bd.msa_stage_name(s) for s in (bd.MSA_STAGE_INDEX_PREFILL, bd.MSA_STAGE_TOPK_PREFILL,
+                                            bd.MSA_STAGE_BLOCK_LISTS, bd.MSA_STAGE_KV_OUTER,
+                                            bd.MSA_STAGE_QUERY_MAJOR)]
+    assert set(st) == set(names), st
+    assert all(c == 3 and t > 0 for c, t in st.values()), st
+    total = e0.elapsed_time(e1)
+    stages = sum(t for _, t in st.values())
+    say(f"  stages {stages:.3f} ms of {total:.3f} ms")
+    assert 0.5 * total < stages <= total * 1.01 + 0.05
+    # nothing is recorded once profiling is off
+    run()
+    bd.msa_profile_begin()
+    assert bd.msa_profile_end() == {}
+
