@@ -114,6 +114,11 @@ int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
     // packed list entries (local token << rank_bits | slot) stay in int32
     const long lim2 = (long)kMaxInt32 >> p->rank_bits;
     if (tc_max > lim2) tc_max = lim2 / B * B;
+    // list ids (batch, group, window, block) stay in int32
+    const long lists_per_win = (long)d->batch * G * p->nb;
+    const long max_win = (kMaxInt32 - 1) / lists_per_win;
+    if (max_win < 1) return MSA_ERR_UNSUPPORTED;
+    if ((tc_max + msa::kListWindow - 1) / msa::kListWindow > max_win) tc_max = max_win * msa::kListWindow;
     if (tc_max < B) return MSA_ERR_UNSUPPORTED;
   }
   if (tc_max >= T) {

@@ -204,33 +204,84 @@ __device__ __forceinline__ void load_sel_chunk(int (&ev)[kSelChunk], const int32
 // Counts the entries of every block list and records per row the number of
 // partial slots (valid non-local entries, at most KS) and whether the row
 // attends its local block (a given selection may omit it).
-__global__ void lists_count_kernel(PrefillMainArgs a) {
+//
+// Popular blocks gather thousands of entries per list, so one global atomic
+// per entry would serialise on a few addresses.  A workgroup of
+// kCountRows rows therefore aggregates in LDS first: each entry's list id is
+// hashed into an LDS table whose counter hands out the entry's local rank;
+// then one global atomicAdd per distinct list reserves the workgroup's range,
+// and each entry's slot is that base plus its local rank.  Entries whose id
+// finds no free LDS slot take a global atomic directly.  epos holds, between
+// the phases, (table slot << 16 | local rank), or the direct slot | bit 31.
+constexpr int kCountRows = 128;
+constexpr int kHashBits = 12;
+constexpr int kHashSlots = 1 << kHashBits;
+constexpr uint32_t kHashEmpty = 0xffffffffu;
+constexpr uint32_t kDirect = 0x80000000u;
+
+__global__ __launch_bounds__(kCountRows) void lists_count_kernel(PrefillMainArgs a) {
+  __shared__ uint32_t hkey[kHashSlots];
+  __shared__ int32_t hval[kHashSlots];  // local counts, then the reserved global bases
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kHashSlots; i += kCountRows) {
+    hkey[i] = kHashEmpty;
+    hval[i] = 0;
+  }
+  __syncthreads();
+
   const long n_rows = (long)a.batch * a.tc * a.G;
-  const long row = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= n_rows) return;
-  const long per_b = (long)a.tc * a.G;
-  const int s = (int)(row / per_b);
-  const int tl = (int)((row % per_b) / a.G);
-  const int g = (int)(row % a.G);
-  const int t = a.t0 + tl;
-  const int L = t / a.B;
-  const int32_t* br = a.bidx + ((size_t)((long)s * a.bidx_rows + (t - a.bidx_t_off)) * a.G + g) * a.topk;
+  const long row = (long)blockIdx.x * kCountRows + tid;
+  // local ranks fit 16 bits while a workgroup holds fewer than 2^16 entries
+  const bool use_lds = (long)kCountRows * a.KS < 65536;
   int rank = 0;
-  bool has_local = false;
-  for (int j0 = 0; j0 < a.topk; j0 += kSelChunk) {
-    int ev[kSelChunk];
-    load_sel_chunk(ev, br, j0, a.topk);
+  if (row < n_rows) {
+    const long per_b = (long)a.tc * a.G;
+    const int s = (int)(row / per_b);
+    const int tl = (int)((row % per_b) / a.G);
+    const int g = (int)(row % a.G);
+    const int t = a.t0 + tl;
+    const int L = t / a.B;
+    const int32_t* br = a.bidx + ((size_t)((long)s * a.bidx_rows + (t - a.bidx_t_off)) * a.G + g) * a.topk;
+    bool has_local = false;
+    for (int j0 = 0; j0 < a.topk; j0 += kSelChunk) {
+      int ev[kSelChunk];
+      load_sel_chunk(ev, br, j0, a.topk);
 #pragma unroll
-    for (int u = 0; u < kSelChunk; ++u) {
-      const int e = ev[u];
-      has_local |= (e == L);
-      if (e >= 0 && e < L && rank < a.KS) {
-        a.epos[(size_t)row * a.KS + rank] = atomicAdd(&a.cnt[list_id(a, s, g, tl, e)], 1);
-        ++rank;
+      for (int u = 0; u < kSelChunk; ++u) {
+        const int e = ev[u];
+        has_local |= (e == L);
+        if (e >= 0 && e < L && rank < a.KS) {
+          const size_t lid = list_id(a, s, g, tl, e);
+          uint32_t code = kDirect;
+          if (use_lds) {
+            const uint32_t key = (uint32_t)lid;
+            uint32_t slot = (key * 2654435761u) >> (32 - kHashBits);
+            for (int p = 0; p < kHashSlots; ++p) {
+              const uint32_t prev = atomicCAS(&hkey[slot], kHashEmpty, key);
+              if (prev == kHashEmpty || prev == key) {
+                code = (slot << 16) | (uint32_t)atomicAdd(&hval[slot], 1);
+                break;
+              }
+              slot = (slot + 1) & (kHashSlots - 1);
+            }
+          }
+          if (code == kDirect) code = kDirect | (uint32_t)atomicAdd(&a.cnt[lid], 1);
+          a.epos[(size_t)row * a.KS + rank] = (int32_t)code;
+          ++rank;
+        }
       }
     }
+    a.rinfo[row] = rank | (has_local ? (1 << 30) : 0);
   }
-  a.rinfo[row] = rank | (has_local ? (1 << 30) : 0);
+  __syncthreads();
+  for (int i = tid; i < kHashSlots; i += kCountRows)
+    if (hkey[i] != kHashEmpty) hval[i] = atomicAdd(&a.cnt[hkey[i]], hval[i]);
+  __syncthreads();
+  for (int q = 0; q < rank; ++q) {
+    int32_t* ep = a.epos + (size_t)row * a.KS + q;
+    const uint32_t code = (uint32_t)*ep;
+    *ep = (code & kDirect) ? (int32_t)(code & ~kDirect) : hval[code >> 16] + (int32_t)(code & 0xffffu);
+  }
 }
 
 // Exclusive scan of (x, y) pairs across a 1024-thread workgroup; returns the
@@ -783,7 +834,7 @@ hipError_t launch_prefill_main_sparse(const PrefillMainArgs& a, hipStream_t st) 
   if (err != hipSuccess) return err;
   const long n_rows = (long)a.batch * a.tc * a.G;
   const unsigned rgrid = (unsigned)((n_rows + 255) / 256);
-  lists_count_kernel<<<rgrid, 256, 0, st>>>(a);
+  lists_count_kernel<<<(unsigned)((n_rows + kCountRows - 1) / kCountRows), kCountRows, 0, st>>>(a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int R = a.Hq / a.G;
   const int mt = kAttnRows / R;

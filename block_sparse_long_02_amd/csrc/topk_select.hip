@@ -111,28 +111,59 @@ __device__ __forceinline__ void select_best(const List& lst, int n, int want, in
   }
 }
 
+// Candidates per lane held in registers by the one-read path of
+// compact_candidates (rows of up to 64 * kRegKeys candidates).
+constexpr int kRegKeys = 16;
+
 // Compacts the candidates of srow[b0, b0 + n) whose key may be among the
 // `want` best (key >= the want-th largest lane maximum, when want <= 64) into
 // skey/sblk in block order; returns the number of survivors (entries beyond
-// kCap are counted but not stored).
+// kCap are counted but not stored).  Rows of up to 64 * kRegKeys candidates
+// are read once, all loads in flight together, and compacted from registers.
 __device__ __forceinline__ int compact_candidates(const float* __restrict__ srow, int b0, int n, int want, uint32_t* skey,
                                   int32_t* sblk, int lane) {
-  uint32_t lmax = 0;
-  for (int j = lane; j < n; j += kWave) lmax = max(lmax, order_key(srow[b0 + j]));
-  const uint32_t lb = (want <= kWave) ? kth_largest_lanes(lmax, want) : 0u;
   const uint64_t lt = lanemask_lt();
   int cnt = 0;
-  for (int j0 = 0; j0 < n; j0 += kWave) {
-    const int j = j0 + lane;
-    const uint32_t key = j < n ? order_key(srow[b0 + j]) : 0u;
-    const bool sv = j < n && key >= lb;
-    const uint64_t bal = __ballot(sv);
-    const int pos = cnt + popc(bal & lt);
-    if (sv && pos < kCap) {
-      skey[pos] = key;
-      sblk[pos] = b0 + j;
+  if (n <= kWave * kRegKeys) {
+    uint32_t key[kRegKeys];
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i) {
+      const int j = i * kWave + lane;
+      key[i] = j < n ? order_key(srow[b0 + j]) : 0u;
     }
-    cnt += popc(bal);
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i) lmax = max(lmax, key[i]);
+    const uint32_t lb = (want <= kWave) ? kth_largest_lanes(lmax, want) : 0u;
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i) {
+      if (i * kWave >= n) break;  // wave-uniform
+      const int j = i * kWave + lane;
+      const bool sv = j < n && key[i] >= lb;
+      const uint64_t bal = __ballot(sv);
+      const int pos = cnt + popc(bal & lt);
+      if (sv && pos < kCap) {
+        skey[pos] = key[i];
+        sblk[pos] = b0 + j;
+      }
+      cnt += popc(bal);
+    }
+  } else {
+    uint32_t lmax = 0;
+    for (int j = lane; j < n; j += kWave) lmax = max(lmax, order_key(srow[b0 + j]));
+    const uint32_t lb = (want <= kWave) ? kth_largest_lanes(lmax, want) : 0u;
+    for (int j0 = 0; j0 < n; j0 += kWave) {
+      const int j = j0 + lane;
+      const uint32_t key = j < n ? order_key(srow[b0 + j]) : 0u;
+      const bool sv = j < n && key >= lb;
+      const uint64_t bal = __ballot(sv);
+      const int pos = cnt + popc(bal & lt);
+      if (sv && pos < kCap) {
+        skey[pos] = key;
+        sblk[pos] = b0 + j;
+      }
+      cnt += popc(bal);
+    }
   }
   wave_lds_sync();
   return cnt;
