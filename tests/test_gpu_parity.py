@@ -388,6 +388,31 @@ def test_decode_all_ties_partition_fallback():
             assert bidx[s, g].tolist() == exp, (s, g)
 
 
+@pytest.mark.parametrize("with_bidx", [False, True])
+def test_query_chunks_equal_one_chunk(with_bidx):
+    """Query chunks change which tokens share a block list, never a row's
+    partials or their merge order: results are bitwise equal to one chunk,
+    whether the selection rows live in the workspace or in the caller's
+    array."""
+    T, Hq, G, di, B, k = 3000, 16, 4, 64, 64, 6
+    say(f"[query chunks] with_bidx={with_bidx}")
+    inp = inputs.make_prefill(T, Hq, G, 128, di, batch=2, seed=41)
+    ref = gpu_prefill(inp, B, k, query_chunk=0)
+    for chunk in (512, 1024):
+        if with_bidx:
+            got = gpu_prefill(inp, B, k, query_chunk=chunk)
+        else:
+            q = inp.q.cuda()
+            dims = bd.make_dims(2, T, Hq, G, index_dim=di, block_size=B, topk=k, query_chunk=chunk)
+            out = torch.empty_like(q)
+            lse = torch.empty((2, T, Hq), dtype=torch.float32, device="cuda")
+            bd.msa_prefill(dims, q, inp.k.cuda(), inp.v.cuda(), inp.idx_q.cuda(), inp.idx_k.cuda(), out, lse=lse)
+            torch.cuda.synchronize()
+            got = (out.cpu(), lse.cpu(), ref[2])
+        for x, y in zip(ref, got):
+            assert torch.equal(x, y), chunk
+
+
 def test_stage_profiling_accounts_for_the_calls():
     """Per-stage event times of real prefill and decode calls: every stage
     that ran is counted once per call and the stages add up to the calls'
