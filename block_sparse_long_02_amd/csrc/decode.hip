@@ -88,6 +88,9 @@ __global__ __launch_bounds__(256) void decode_index_kernel(const bf16_t* __restr
 // normalised partial that decode_combine_kernel merges.
 // ---------------------------------------------------------------------------
 constexpr int kDecAttnWaves = 8;
+// (s, g) rows below which a decode step splits each row over several
+// workgroups: one per CU of the 256 on MI355X.
+constexpr long kDecFillRows = 256;
 
 template <int BS>
 struct DecTile {
@@ -350,11 +353,14 @@ hipError_t launch_index_blockmax_decode(const uint16_t* idx_q, const uint16_t* i
   return hipGetLastError();
 }
 
-// Work items per wave and workgroups per (s, g) for nsplit items.
-void decode_partition(int nsplit, int* ipw, int* nparts) {
-  // up to 4 items per wave keeps one workgroup per (s, g) for the sparse
-  // case (16 selected blocks); long dense runs use one item per wave
-  if (nsplit <= kDecAttnWaves * 4) {
+// Work items per wave and workgroups per (s, g) for nsplit items over
+// `rows` = batch * G (s, g) rows.
+void decode_partition(int nsplit, long rows, int* ipw, int* nparts) {
+  // Up to 4 items per wave keep one workgroup per (s, g) when there are
+  // enough rows to fill the chip; with fewer than one row per CU, or long
+  // dense runs, each wave takes one item and the combine kernel merges the
+  // workgroups of a row.
+  if (nsplit <= kDecAttnWaves * 4 && rows >= kDecFillRows) {
     *ipw = (nsplit + kDecAttnWaves - 1) / kDecAttnWaves;
     *nparts = 1;
   } else {
@@ -365,7 +371,7 @@ void decode_partition(int nsplit, int* ipw, int* nparts) {
 
 hipError_t launch_decode_main(const DecodeMainArgs& a, hipStream_t st) {
   int ipw, nparts;
-  decode_partition(a.nsplit, &ipw, &nparts);
+  decode_partition(a.nsplit, (long)a.batch * a.G, &ipw, &nparts);
   const dim3 grid(nparts, a.G, a.batch);
   prof_mark(st, MSA_STAGE_DECODE_ATTN);
 #define MSA_DEC_ATTN(BS_)                                                                          \

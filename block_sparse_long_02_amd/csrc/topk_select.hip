@@ -66,27 +66,71 @@ struct RowList {
   __device__ int32_t b(int i) const { return b0 + i; }
 };
 
+// Candidates per lane held in registers by the one-read paths of
+// select_best and compact_candidates (lists of up to 64 * kRegKeys).
+constexpr int kRegKeys = 16;
+
 // Selects the `want` (1 <= want <= n) best entries of lst[0, n) under
 // (key descending, block ascending) and hands them to emit(pos, key, blk) in
-// list order, pos = 0 .. want-1.  Wave-uniform control flow.
+// list order, pos = 0 .. want-1.  Wave-uniform control flow.  Lists of up to
+// 64 * kRegKeys entries are read once into registers; the 32-step threshold
+// search then needs only ballots.
 template <class List, class Emit>
 __device__ __forceinline__ void select_best(const List& lst, int n, int want, int lane, Emit emit) {
   const uint64_t lt = lanemask_lt();
-  uint32_t tau = 0;
-  if (n <= kWave) {
-    const uint32_t key = lane < n ? lst.k(lane) : 0u;
-    tau = kth_largest_lanes(key, want);
-  } else {
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = tau | (1u << bit);
-      int cnt = 0;
-      for (int i0 = 0; i0 < n; i0 += kWave) {
-        const int i = i0 + lane;
-        const uint32_t key = i < n ? lst.k(i) : 0u;
-        cnt += popc(__ballot(key >= c));
-      }
-      if (cnt >= want) tau = c;
+  if (n <= kWave * kRegKeys) {
+    uint32_t key[kRegKeys];
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i) {
+      const int j = i * kWave + lane;
+      key[i] = j < n ? lst.k(j) : 0u;
     }
+    const int nch = (n + kWave - 1) / kWave;
+    uint32_t tau = 0;
+    if (n <= kWave) {
+      tau = kth_largest_lanes(key[0], want);
+    } else {
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = tau | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < kRegKeys; ++i)
+          if (i < nch) cnt += popc(__ballot(key[i] >= c));
+        if (cnt >= want) tau = c;
+      }
+    }
+    int cgt = 0;
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i)
+      if (i < nch) cgt += popc(__ballot(key[i] > tau));
+    const int need = want - cgt;  // >= 1 by construction of tau
+    int base = 0, eq_seen = 0;
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i) {
+      if (i >= nch) break;  // wave-uniform
+      const int j = i * kWave + lane;
+      const bool in = j < n;
+      const bool eq = in && key[i] == tau;
+      const uint64_t beq = __ballot(eq);
+      const int eq_rank = eq_seen + popc(beq & lt);
+      const bool sel = in && (key[i] > tau || (eq && eq_rank < need));
+      const uint64_t bs = __ballot(sel);
+      if (sel) emit(base + popc(bs & lt), key[i], lst.b(j));
+      base += popc(bs);
+      eq_seen += popc(beq);
+    }
+    return;
+  }
+  uint32_t tau = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = tau | (1u << bit);
+    int cnt = 0;
+    for (int i0 = 0; i0 < n; i0 += kWave) {
+      const int i = i0 + lane;
+      const uint32_t key = i < n ? lst.k(i) : 0u;
+      cnt += popc(__ballot(key >= c));
+    }
+    if (cnt >= want) tau = c;
   }
   int cgt = 0;
   for (int i0 = 0; i0 < n; i0 += kWave) {
@@ -110,10 +154,6 @@ __device__ __forceinline__ void select_best(const List& lst, int n, int want, in
     eq_seen += popc(beq);
   }
 }
-
-// Candidates per lane held in registers by the one-read path of
-// compact_candidates (rows of up to 64 * kRegKeys candidates).
-constexpr int kRegKeys = 16;
 
 // Compacts the candidates of srow[b0, b0 + n) whose key may be among the
 // `want` best (key >= the want-th largest lane maximum, when want <= 64) into
