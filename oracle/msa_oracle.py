@@ -21,6 +21,8 @@ are exact in float64):
                  min(k, L(t)+1) - 1 blocks are the highest S among blocks
                  0..L(t)-1, equal scores broken by the lower block index;
                  output ascending, padded with -1             [HA 方法, 核心贡献; TG Метод]
+                 variant sink=True: block 0 (sequence start) is kept too
+                 when there is room for it                    [HA 实验]
   attention_row  exact softmax attention of each query head h of group
                  g = floor(h / R) over the keys of the selected blocks that
                  are <= t, scale 1/sqrt(d)                    [HA 方法; HN]
@@ -78,18 +80,31 @@ def block_max(scores: np.ndarray, t: int, B: int) -> np.ndarray:
     return out
 
 
-def select_blocks(S: np.ndarray, t: int, B: int, k: int) -> np.ndarray:
-    """Top-k block selection with the forced local block.
-
-    m = min(k, L+1) blocks are kept: the local block L and the m-1 highest of
-    the candidate blocks 0..L-1, ordered by score (descending) then block id
-    (ascending).  Returned ascending and padded with -1 to length k
-    [HA 方法: top-k per query group, local block always included; TG Метод]."""
+def forced_blocks(t: int, B: int, k: int, sink: bool = False) -> list:
+    """Blocks kept whatever their scores: the local block L(t) always [HA 方法];
+    with sink=True also block 0, the start of the sequence, when the row has
+    room for a second block (m = min(k, L+1) >= 2) -- the forced
+    sequence-start variant the pages ablate [HA 实验: hard-coded selection of
+    the sequence start and of the local window]."""
     L = local_block(t, B)
     m = min(k, L + 1)
-    cand = np.arange(L)
-    order = np.lexsort((cand, -S[:L]))  # primary: -score, secondary: block id
-    chosen = np.concatenate([cand[order[: m - 1]], [L]]).astype(np.int64)
+    return [L, 0] if (sink and L >= 1 and m >= 2) else [L]
+
+
+def select_blocks(S: np.ndarray, t: int, B: int, k: int, sink: bool = False) -> np.ndarray:
+    """Top-k block selection with the forced block(s).
+
+    m = min(k, L+1) blocks are kept: the forced blocks (the local block L, and
+    with sink=True block 0) and the highest of the remaining candidate blocks
+    below L, ordered by score (descending) then block id (ascending).
+    Returned ascending and padded with -1 to length k [HA 方法: top-k per
+    query group, local block always included; TG Метод; HA 实验 for sink]."""
+    L = local_block(t, B)
+    m = min(k, L + 1)
+    forced = forced_blocks(t, B, k, sink)
+    cand = np.array([b for b in range(L) if b not in forced], dtype=np.int64)
+    order = np.lexsort((cand, -S[cand]))  # primary: -score, secondary: block id
+    chosen = np.concatenate([cand[order[: m - len(forced)]], forced]).astype(np.int64)
     chosen.sort()
     out = np.full(k, -1, dtype=np.int64)
     out[:m] = chosen
@@ -127,13 +142,14 @@ def default_scale(d: int) -> float:
 
 
 def prefill(q, k, v, idx_q, idx_k, B: int, topk: int, scale: float | None = None,
-            rows=None, dense: bool = False, block_idx=None):
+            rows=None, dense: bool = False, block_idx=None, sink: bool = False):
     """MSA prefill over a batch.
 
     q [b,T,Hq,d], k/v [b,T,G,d], idx_q [b,T,G,di], idx_k [b,T,di] (any float
     type; converted to float64).  rows: iterable of (batch, t) to compute, or
     None for all.  dense: select every visible block (index branch skipped).
     block_idx: optional given selection [b,T,G,topk] (main branch only).
+    sink: also force block 0 into every selection (see forced_blocks).
 
     Returns dict with 'out' {(s,t): [Hq,d]}, 'lse' {(s,t): [Hq]},
     'block_idx' {(s,t): [G,topk]} (None in dense mode) for the rows computed,
@@ -164,7 +180,7 @@ def prefill(q, k, v, idx_q, idx_k, B: int, topk: int, scale: float | None = None
                 sc = index_scores(idx_q[s, t, g], idx_k[s], t)
                 Sg = block_max(sc, t, B)
                 S_t.append(Sg)
-                sel = select_blocks(Sg, t, B, topk)
+                sel = select_blocks(Sg, t, B, topk, sink)
             if not dense:
                 sel_t[g] = sel
             toks = selected_tokens(sel, t, B)
@@ -181,7 +197,7 @@ def prefill(q, k, v, idx_q, idx_k, B: int, topk: int, scale: float | None = None
 
 
 def decode(q, k_cache, v_cache, idx_q, idx_k_cache, cache_lens, B: int, topk: int,
-           scale: float | None = None, dense: bool = False, block_idx=None):
+           scale: float | None = None, dense: bool = False, block_idx=None, sink: bool = False):
     """One decode step per sequence: the new token sits at position len-1 of
     its cache and runs the same index branch and main branch against cache
     positions 0..len-1 [HA 方法; the pages' decode speed-up at 1M context].
@@ -214,7 +230,7 @@ def decode(q, k_cache, v_cache, idx_q, idx_k_cache, cache_lens, B: int, topk: in
                 sc = index_scores(idx_q[s, g], idx_k_cache[s], t)
                 Sg = block_max(sc, t, B)
                 S_s.append(Sg)
-                sel = select_blocks(Sg, t, B, topk)
+                sel = select_blocks(Sg, t, B, topk, sink)
                 sel_all[s, g] = sel
             toks = selected_tokens(sel, t, B)
             heads = slice(g * R, (g + 1) * R)
@@ -225,16 +241,19 @@ def decode(q, k_cache, v_cache, idx_q, idx_k_cache, cache_lens, B: int, topk: in
     return {"out": out, "lse": lse, "block_idx": None if dense else sel_all, "S": S_all}
 
 
-def near_tie(S_g: np.ndarray, t: int, B: int, k: int, rel: float = 1e-3) -> bool:
+def near_tie(S_g: np.ndarray, t: int, B: int, k: int, rel: float = 1e-3, sink: bool = False) -> bool:
     """True when the selection of this (token, group) row is decided by a
-    near-tie: the last selected non-local candidate and the first unselected
-    one (in the oracle's score order) differ by less than rel relative."""
+    near-tie: the last selected candidate and the first unselected one (in
+    the oracle's score order, forced blocks excluded) differ by less than rel
+    relative."""
     L = local_block(t, B)
     m = min(k, L + 1)
-    if m - 1 == 0 or m - 1 >= L:
+    forced = forced_blocks(t, B, k, sink)
+    cand = np.array([b for b in range(L) if b not in forced], dtype=np.int64)
+    want = m - len(forced)
+    if want == 0 or want >= len(cand):
         return False          # nothing chosen among candidates, or all of them
-    cand = np.arange(L)
-    order = np.lexsort((cand, -S_g[:L]))
-    sc = S_g[:L][order]
-    a, b = sc[m - 2], sc[m - 1]
+    order = np.lexsort((cand, -S_g[cand]))
+    sc = S_g[cand][order]
+    a, b = sc[want - 1], sc[want]
     return abs(a - b) < rel * max(abs(a), abs(b), 1e-30)

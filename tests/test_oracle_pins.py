@@ -332,3 +332,101 @@ def test_near_tie_helper():
     assert not orc.near_tie(S, t, B, k)
     S2 = np.array([10.0, 8.0, 8.0 * (1 - 1e-4), 7.0, 1.0, 0.0])
     assert orc.near_tie(S2, t, B, k)
+
+
+# --------------------------------------------------------------------------
+# Forced sink block (variant): block 0 is kept beside the local block when the
+# row has room for two blocks; k counts both.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("k", [1, 2, 3, 5])
+def test_sink_exhaustive_enumeration(k):
+    # brute force from explicit integer loops: {0, L} plus the max-sum subset
+    # of size m-2 of blocks 1..L-1, ties to the lexicographically first tuple
+    T, B, G, di = 150, 10, 2, 6
+    inp = inputs.make_prefill(T, 2 * G, G, 8, di, seed=31 + k, idx_mode="integer")
+    res = _run_all(inp, B, k, sink=True)
+    iq = inp.idx_q.to(torch.int64).numpy()
+    ik = inp.idx_k.to(torch.int64).numpy()
+    for t in range(0, T, 3):
+        for g in range(G):
+            S = _brute_block_max(iq[0, t, g], ik[0], t, B)
+            L = t // B
+            m = min(k, L + 1)
+            if m >= 2 and L >= 1:
+                best, best_sum = None, None
+                for comb in itertools.combinations(range(1, L), m - 2):
+                    sm = sum(S[b] for b in comb)
+                    if best_sum is None or sm > best_sum:
+                        best, best_sum = comb, sm
+                expect = sorted([0] + list(best) + [L])
+            else:
+                expect = [L]
+            expect = expect + [-1] * (k - m)
+            assert res["block_idx"][(0, t)][g].tolist() == expect, (t, g, S)
+
+
+def test_sink_closed_form_and_invariants():
+    T, B, k = 200, 16, 5
+    inp = _closed_form_inputs(T, lambda j: j)  # ascending scores: latest blocks win
+    res = _run_all(inp, B, k, sink=True)
+    for t in range(T):
+        L = t // B
+        m = min(k, L + 1)
+        if m >= 2:
+            exp = [0] + list(range(L - (m - 2), L)) + [L] if m > 2 else [0, L]
+            exp = sorted(set(exp))
+        else:
+            exp = [L]
+        assert len(exp) == m
+        exp = exp + [-1] * (k - m)
+        for g in range(2):
+            assert res["block_idx"][(0, t)][g].tolist() == exp, t
+    # block 0 already among the best: the sink changes nothing
+    inp = _closed_form_inputs(T, lambda j: -j)
+    a = _run_all(inp, B, k)["block_idx"]
+    b = _run_all(inp, B, k, sink=True)["block_idx"]
+    for key in a:
+        assert np.array_equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("mode", ["gaussian", "integer"])
+def test_sink_invariants_and_nesting(mode):
+    T, B, G = 300, 16, 3
+    inp = inputs.make_prefill(T, G, G, 8, 8, seed=23, idx_mode=mode)
+    nb = (T + B - 1) // B
+    sels = {}
+    rows = [(0, t) for t in range(0, T, 7)]
+    for k in range(1, nb + 2):
+        res = _run_all(inp, B, k, rows=rows, sink=True)
+        plain = _run_all(inp, B, k, rows=rows)
+        sels[k] = res["block_idx"]
+        for (s, t), sel in res["block_idx"].items():
+            L = t // B
+            m = min(k, L + 1)
+            for g in range(G):
+                row = sel[g]
+                live = row[:m]
+                assert L in live and (row[m:] == -1).all() and (np.diff(live) > 0).all()
+                if m >= 2:
+                    assert live[0] == 0
+                p = plain["block_idx"][(s, t)][g]
+                if m < 2 or 0 in p[:m] or m == L + 1:
+                    assert np.array_equal(row, p), (k, t, g)
+                else:   # the sink displaces exactly the weakest non-local pick
+                    assert len(set(p[:m]) - set(live)) == 1 and len(set(live) - set(p[:m])) == 1
+    for k in range(1, nb + 1):
+        for key in sels[k]:
+            for g in range(G):
+                a = set(sels[k][key][g].tolist()) - {-1}
+                b = set(sels[k + 1][key][g].tolist()) - {-1}
+                assert a <= b, (k, key, g)
+
+
+def test_sink_near_tie_helper():
+    B, k = 4, 3
+    t = 5 * B  # L = 5; sink 0 and L forced; one pick among blocks 1..4
+    S = np.array([0.0, 10.0, 9.0, 8.0, 1.0, 0.0])
+    assert not orc.near_tie(S, t, B, k, sink=True)
+    S2 = np.array([0.0, 10.0, 10.0 * (1 - 1e-4), 8.0, 1.0, 0.0])
+    assert orc.near_tie(S2, t, B, k, sink=True)
+    assert not orc.near_tie(S2, t, B, 2, sink=True)  # m = 2: both places forced
