@@ -38,9 +38,11 @@ int check_dims(const msa_dims* d, bool decode) {
   if (d->num_q_heads % d->num_kv_heads != 0) return MSA_ERR_INVALID_ARG;
   if (d->reserved != 0 || d->query_chunk < 0) return MSA_ERR_INVALID_ARG;
   if (!isfinite(d->softmax_scale)) return MSA_ERR_INVALID_ARG;
-  const uint32_t known = MSA_DENSE | MSA_GIVEN_INDICES;
+  const uint32_t known = MSA_DENSE | MSA_GIVEN_INDICES | MSA_FORCE_SINK;
   if ((d->flags & ~known) != 0) return MSA_ERR_INVALID_ARG;
   if ((d->flags & MSA_DENSE) && (d->flags & MSA_GIVEN_INDICES)) return MSA_ERR_INVALID_ARG;
+  // the sink is a rule of the index branch's selection
+  if ((d->flags & MSA_FORCE_SINK) && (d->flags & (MSA_DENSE | MSA_GIVEN_INDICES))) return MSA_ERR_INVALID_ARG;
   if (d->head_dim != 128) return MSA_ERR_UNSUPPORTED;
   if (d->index_dim != 64 && d->index_dim != 128) return MSA_ERR_UNSUPPORTED;
   if (d->block_size != 32 && d->block_size != 64 && d->block_size != 128) return MSA_ERR_UNSUPPORTED;
@@ -80,14 +82,14 @@ size_t per_token_bytes(const msa_dims* d, const PrefillPlan& p) {
 int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
   int st = check_dims(d, false);
   if (st != MSA_OK) return st;
-  if (index_only && d->flags != 0) return MSA_ERR_INVALID_ARG;
+  if (index_only && (d->flags & ~MSA_FORCE_SINK) != 0) return MSA_ERR_INVALID_ARG;
   const int T = d->seqlen, B = d->block_size, G = d->num_kv_heads;
   p->nb = (T + B - 1) / B;
   p->KS = d->topk < p->nb ? d->topk : p->nb;
   while ((1 << p->rank_bits) < p->KS) ++p->rank_bits;
   p->R = d->num_q_heads / G;
   p->mt = msa::kAttnRows / p->R;
-  p->with_scores = index_only || (d->flags == 0);
+  p->with_scores = index_only || !(d->flags & (MSA_DENSE | MSA_GIVEN_INDICES));
   p->with_main = !index_only && !(d->flags & MSA_DENSE);
   const int Lmax = (T - 1) / B;
   p->s_stride_max = (int)round_up((size_t)(Lmax > 1 ? Lmax : 1), 4);
@@ -175,7 +177,7 @@ int make_decode_plan(const msa_dims* d, DecodePlan* p) {
   p->nbmax = (d->seqlen + B - 1) / B;
   p->R = d->num_q_heads / G;
   p->s_stride = (int)round_up((size_t)p->nbmax, 4);
-  p->with_scores = (d->flags == 0);
+  p->with_scores = !(d->flags & (MSA_DENSE | MSA_GIVEN_INDICES));
   if (d->flags & MSA_DENSE) {
     p->bps = 2048 / B;  // 2048 keys per work item
     p->nsplit = (p->nbmax + p->bps - 1) / p->bps;
@@ -231,7 +233,7 @@ hipError_t run_index_chunk(const msa_dims* d, const PrefillPlan& p, const void* 
   if (e != hipSuccess) return e;
   msa::prof_mark(st, MSA_STAGE_TOPK_PREFILL);
   return msa::launch_topk_prefill(S, s_stride, bidx, bidx_rows, t_off, d->batch, d->num_kv_heads, B,
-                                  d->topk, t0, tc, st);
+                                  d->topk, (d->flags & MSA_FORCE_SINK) != 0, t0, tc, st);
 }
 
 }  // namespace
@@ -291,7 +293,7 @@ int msa_index_scores(const msa_dims* dims, const void* idx_q, const void* idx_k,
                      int32_t t0, int32_t t1, int32_t row_stride, void* hip_stream) {
   int st = check_dims(dims, false);
   if (st != MSA_OK) return st;
-  if (dims->flags != 0) return MSA_ERR_INVALID_ARG;
+  if ((dims->flags & ~MSA_FORCE_SINK) != 0) return MSA_ERR_INVALID_ARG;  // scores do not depend on it
   if (idx_q == nullptr || idx_k == nullptr || scores == nullptr) return MSA_ERR_INVALID_ARG;
   if (t0 < 0 || t1 <= t0 || t1 > dims->seqlen) return MSA_ERR_INVALID_ARG;
   const int Lc = (t1 - 1) / dims->block_size;
@@ -425,7 +427,8 @@ int msa_decode(const msa_dims* dims, const void* q, const void* k_cache, const v
     if (e != hipSuccess) return hip_fail(e);
     msa::prof_mark(s, MSA_STAGE_TOPK_DECODE);
     e = msa::launch_topk_decode(S, p.s_stride, bidx, cache_lens, dims->seqlen, dims->batch,
-                                dims->num_kv_heads, dims->block_size, dims->topk, s);
+                                dims->num_kv_heads, dims->block_size, dims->topk,
+                                (dims->flags & MSA_FORCE_SINK) != 0, s);
     if (e != hipSuccess) return hip_fail(e);
   }
   msa::DecodeMainArgs a{};

@@ -29,12 +29,13 @@ hipError_t launch_index_blockmax_prefill(const uint16_t* idx_q, const uint16_t* 
 // ---- Top-k with the forced local block ----
 // prefill rows: (s, t in [t0, t0+tc), g); output row address
 //   bidx + ((s*bidx_rows + (t - bidx_t_off))*G + g)*k
+// sink: block 0 is forced too when a row keeps at least two blocks.
 hipError_t launch_topk_prefill(const float* S, int s_stride, int32_t* bidx, long bidx_rows,
-                               int bidx_t_off, int batch, int G, int B, int k, int t0, int tc,
+                               int bidx_t_off, int batch, int G, int B, int k, bool sink, int t0, int tc,
                                hipStream_t st);
 // decode rows: (s, g); query position cache_lens[s]-1; output bidx + (s*G+g)*k
 hipError_t launch_topk_decode(const float* S, int s_stride, int32_t* bidx, const int32_t* lens,
-                              int Lmax, int batch, int G, int B, int k, hipStream_t st);
+                              int Lmax, int batch, int G, int B, int k, bool sink, hipStream_t st);
 
 // ---- Main Branch, prefill ----
 // Query tokens per window of the block lists: the lists of non-local

@@ -7,7 +7,11 @@
 // the unstated details: the local block L counts inside k, so m = min(k, L+1)
 // blocks are kept -- L itself plus the m-1 best of the candidate blocks
 // 0..L-1 under the order (score descending, block index ascending); the row
-// is written in ascending block order and padded with -1.
+// is written in ascending block order and padded with -1.  With the sink
+// variant (the pages' experiments compare hard-coded selection of the
+// sequence start and the local window), block 0 is forced as well whenever
+// the row keeps two or more blocks, and the remaining picks come from blocks
+// 1..L-1.
 //
 // The selection is exp-free and exact (it compares the same fp32 maxima the
 // index kernel produced, mapped to order-preserving uint32 keys):
@@ -217,25 +221,49 @@ __device__ __forceinline__ void write_trivial(int L, int mp, int k, int32_t* out
   }
 }
 
-__device__ __forceinline__ void select_row(const float* __restrict__ srow, int L, int k, int32_t* __restrict__ out,
-                           uint32_t* skey, int32_t* sblk, int lane) {
-  const int m = (k < L + 1) ? k : L + 1;
-  const int mp = m - 1;
-  if (mp == L || mp == 0) {
+// Forced blocks of a row: the local block L always; with `sink`, block 0 too
+// whenever the row keeps at least two blocks.  The free picks are the `want`
+// best of the candidates c0..L-1 (c0 = 1 when block 0 is forced).
+struct RowPlan {
+  int m;      // blocks kept: min(k, L+1)
+  bool fs;    // block 0 forced
+  int c0;     // first free candidate
+  int want;   // free picks among c0..L-1
+};
+__device__ __forceinline__ RowPlan row_plan(int L, int k, bool sink) {
+  RowPlan r;
+  r.m = (k < L + 1) ? k : L + 1;
+  r.fs = sink && L >= 1 && r.m >= 2;
+  r.c0 = r.fs ? 1 : 0;
+  r.want = r.m - 1 - (r.fs ? 1 : 0);
+  return r;
+}
+
+__device__ __forceinline__ void select_row(const float* __restrict__ srow, int L, int k, bool sink,
+                                           int32_t* __restrict__ out, uint32_t* skey, int32_t* sblk, int lane) {
+  const RowPlan rp = row_plan(L, k, sink);
+  const int mp = rp.m - 1;
+  if (mp == L || mp == 0) {  // every visible block, or the local block alone
     write_trivial(L, mp, k, out, lane);
     return;
   }
-  const int n = compact_candidates(srow, 0, L, mp, skey, sblk, lane);
-  auto emit = [&](int pos, uint32_t, int32_t blk) { out[pos] = blk; };
-  if (n <= kCap) select_best(LdsList{skey, sblk}, n, mp, lane, emit);
-  else select_best(RowList{srow, 0}, L, mp, lane, emit);
-  if (lane == 0) out[mp] = L;
+  if (rp.want > 0) {
+    const int off = rp.fs ? 1 : 0;
+    const int n = compact_candidates(srow, rp.c0, L - rp.c0, rp.want, skey, sblk, lane);
+    auto emit = [&](int pos, uint32_t, int32_t blk) { out[off + pos] = blk; };
+    if (n <= kCap) select_best(LdsList{skey, sblk}, n, rp.want, lane, emit);
+    else select_best(RowList{srow + rp.c0, rp.c0}, L - rp.c0, rp.want, lane, emit);
+  }
+  if (lane == 0) {
+    if (rp.fs) out[0] = 0;
+    out[mp] = L;
+  }
   for (int j = mp + 1 + lane; j < k; j += kWave) out[j] = -1;
 }
 
 __global__ __launch_bounds__(256) void topk_prefill_kernel(const float* __restrict__ S, int s_stride,
                                                            int32_t* __restrict__ bidx, long bidx_rows,
-                                                           int bidx_t_off, int G, int B, int k,
+                                                           int bidx_t_off, int G, int B, int k, bool sink,
                                                            int t0, int tc, long n_rows) {
   __shared__ uint32_t skey[kTopkWaves][kCap];
   __shared__ int32_t sblk[kTopkWaves][kCap];
@@ -249,7 +277,7 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(const float* __restri
   const int g = (int)(r % G);
   const float* srow = S + (size_t)row * s_stride;
   int32_t* out = bidx + ((size_t)(s * bidx_rows + (t - bidx_t_off)) * G + g) * (size_t)k;
-  select_row(srow, t / B, k, out, skey[wave], sblk[wave], lane);
+  select_row(srow, t / B, k, sink, out, skey[wave], sblk[wave], lane);
 }
 
 // Decode rows are few (batch x G) and long (up to Lmax / B candidates): one
@@ -262,7 +290,7 @@ constexpr int kDecMaxKeep = kWave;  // two-level path for m-1 <= 64
 __global__ __launch_bounds__(1024) void topk_decode_kernel(const float* __restrict__ S, int s_stride,
                                                            int32_t* __restrict__ bidx,
                                                            const int32_t* __restrict__ lens, int Lmax,
-                                                           int G, int B, int k) {
+                                                           int G, int B, int k, bool sink) {
   __shared__ uint32_t skey[kDecWaves][kCap];
   __shared__ int32_t sblk[kDecWaves][kCap];
   __shared__ uint32_t mkey[kDecWaves * kDecMaxKeep];
@@ -276,23 +304,21 @@ __global__ __launch_bounds__(1024) void topk_decode_kernel(const float* __restri
   const int L = (len - 1) / B;
   const float* srow = S + (size_t)row * s_stride;
   int32_t* out = bidx + (size_t)row * k;
-  const int m = (k < L + 1) ? k : L + 1;
-  const int mp = m - 1;
-  if (mp == L || mp == 0) {  // uniform across the workgroup
-    if (wave == 0) write_trivial(L, mp, k, out, lane);
+  const RowPlan rp = row_plan(L, k, sink);
+  const int mp = rp.m - 1;
+  const int ncand = L - rp.c0;
+  if (mp == L || mp == 0 || rp.want == 0 || rp.want > kDecMaxKeep || ncand <= kWave * kDecWaves) {
+    // uniform across the workgroup: one wave does the whole row
+    if (wave == 0) select_row(srow, L, k, sink, out, skey[0], sblk[0], lane);
     return;
   }
-  if (mp > kDecMaxKeep || L <= kWave * kDecWaves) {  // one wave does the whole row
-    if (wave == 0) select_row(srow, L, k, out, skey[0], sblk[0], lane);
-    return;
-  }
-  // level 1: per-wave partitions of the candidates 0..L-1
-  const int per = (L + kDecWaves - 1) / kDecWaves;
-  const int b0 = wave * per;
+  // level 1: per-wave partitions of the candidates c0..L-1
+  const int per = (ncand + kDecWaves - 1) / kDecWaves;
+  const int b0 = rp.c0 + wave * per;
   const int nw = max(0, min(per, L - b0));
   int kept = 0;
   if (nw > 0) {
-    const int want = min(mp, nw);
+    const int want = min(rp.want, nw);
     const int n = compact_candidates(srow, b0, nw, want, skey[wave], sblk[wave], lane);
     uint32_t* ok = mkey + wave * kDecMaxKeep;
     int32_t* ob = mblk + wave * kDecMaxKeep;
@@ -315,9 +341,13 @@ __global__ __launch_bounds__(1024) void topk_decode_kernel(const float* __restri
       n += c;
     }
     wave_lds_sync();
-    auto emit = [&](int pos, uint32_t, int32_t blk) { out[pos] = blk; };
-    select_best(LdsList{skey[0], sblk[0]}, n, mp, lane, emit);
-    if (lane == 0) out[mp] = L;
+    const int off = rp.fs ? 1 : 0;
+    auto emit = [&](int pos, uint32_t, int32_t blk) { out[off + pos] = blk; };
+    select_best(LdsList{skey[0], sblk[0]}, n, rp.want, lane, emit);
+    if (lane == 0) {
+      if (rp.fs) out[0] = 0;
+      out[mp] = L;
+    }
     for (int j = mp + 1 + lane; j < k; j += kWave) out[j] = -1;
   }
 }
@@ -325,19 +355,19 @@ __global__ __launch_bounds__(1024) void topk_decode_kernel(const float* __restri
 }  // namespace
 
 hipError_t launch_topk_prefill(const float* S, int s_stride, int32_t* bidx, long bidx_rows,
-                               int bidx_t_off, int batch, int G, int B, int k, int t0, int tc,
+                               int bidx_t_off, int batch, int G, int B, int k, bool sink, int t0, int tc,
                                hipStream_t st) {
   const long n_rows = (long)batch * tc * G;
   const long grid = (n_rows + kTopkWaves - 1) / kTopkWaves;
   topk_prefill_kernel<<<dim3((unsigned)grid), 256, 0, st>>>(S, s_stride, bidx, bidx_rows, bidx_t_off,
-                                                            G, B, k, t0, tc, n_rows);
+                                                            G, B, k, sink, t0, tc, n_rows);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_decode(const float* S, int s_stride, int32_t* bidx, const int32_t* lens,
-                              int Lmax, int batch, int G, int B, int k, hipStream_t st) {
+                              int Lmax, int batch, int G, int B, int k, bool sink, hipStream_t st) {
   const long n_rows = (long)batch * G;
-  topk_decode_kernel<<<dim3((unsigned)n_rows), 1024, 0, st>>>(S, s_stride, bidx, lens, Lmax, G, B, k);
+  topk_decode_kernel<<<dim3((unsigned)n_rows), 1024, 0, st>>>(S, s_stride, bidx, lens, Lmax, G, B, k, sink);
   return hipGetLastError();
 }
 

@@ -66,6 +66,14 @@ extern "C" {
    index branch is skipped.  Entries outside [0, L(t)] (e.g. -1) are ignored;
    valid entries of a row must be distinct. */
 #define MSA_GIVEN_INDICES 0x2u
+/* Forced sink block: block 0, the start of the sequence, is selected beside
+   the local block whenever a row keeps at least two blocks (m = min(k, L+1)
+   >= 2); k counts both, and the other m-2 places go to the best of blocks
+   1..L-1.  The variant the pages ablate [hyper.ai paper page 2606.13392,
+   实验 (Experiments): hard-coded selection of the sequence start and of the
+   local window].  A rule of the index branch: invalid with MSA_DENSE or
+   MSA_GIVEN_INDICES. */
+#define MSA_FORCE_SINK 0x4u
 
 /* ---- operations for msa_workspace_bytes ---- */
 #define MSA_OP_INDEX_TOPK 0
@@ -83,7 +91,7 @@ typedef struct msa_dims {
   int32_t topk;          /* k >= 1, counts the forced local block; k > number of
                             visible blocks selects all of them */
   float softmax_scale;   /* <= 0 selects 1/sqrt(head_dim) */
-  uint32_t flags;        /* MSA_DENSE, MSA_GIVEN_INDICES */
+  uint32_t flags;        /* MSA_DENSE, MSA_GIVEN_INDICES, MSA_FORCE_SINK */
   int32_t query_chunk;   /* prefill: query tokens per internal pass, a multiple of
                             block_size; 0 = the library's default (bounds the
                             workspace).  Ignored by decode. */
@@ -95,8 +103,9 @@ typedef struct msa_dims {
  *   idx_q     [batch, T, G, index_dim] bf16
  *   idx_k     [batch, T, index_dim]    bf16
  *   block_idx [batch, T, G, topk]      int32, OUTPUT
- * Flags must be 0.  Integer-valued idx inputs whose dot products stay below
- * 2^24 in magnitude give exact scores, hence a unique, exact selection.
+ * Flags must be 0 or MSA_FORCE_SINK.  Integer-valued idx inputs whose dot
+ * products stay below 2^24 in magnitude give exact scores, hence a unique,
+ * exact selection.
  */
 int msa_index_topk(const msa_dims* dims, const void* idx_q, const void* idx_k,
                    int32_t* block_idx, void* workspace, size_t workspace_bytes,
@@ -109,7 +118,7 @@ int msa_index_topk(const msa_dims* dims, const void* idx_q, const void* idx_k,
  * for every candidate block b < L(t) = t / block_size, in fp32 (products of
  * bf16 values accumulated in fp32).  scores is [batch, t1 - t0, G, row_stride]
  * fp32 with row_stride a multiple of 4 and >= L(t1 - 1); entries b >= L(t) of
- * a row are unspecified.  No workspace.  Flags must be 0.
+ * a row are unspecified.  No workspace.  Flags must be 0 or MSA_FORCE_SINK (scores do not depend on it).
  */
 int msa_index_scores(const msa_dims* dims, const void* idx_q, const void* idx_k, float* scores,
                      int32_t t0, int32_t t1, int32_t row_stride, void* hip_stream);

@@ -96,6 +96,8 @@ def test_workspace_bytes(lib):
     ("reserved", 1, bd.MSA_ERR_INVALID_ARG),
     ("flags", 0x3, bd.MSA_ERR_INVALID_ARG),            # dense and given together
     ("flags", 0x8, bd.MSA_ERR_INVALID_ARG),            # unknown flag
+    ("flags", 0x5, bd.MSA_ERR_INVALID_ARG),            # sink with dense
+    ("flags", 0x6, bd.MSA_ERR_INVALID_ARG),            # sink with given indices
     ("query_chunk", 100, bd.MSA_ERR_INVALID_ARG),      # not a multiple of block_size
     ("softmax_scale", float("nan"), bd.MSA_ERR_INVALID_ARG),
     ("head_dim", 64, bd.MSA_ERR_UNSUPPORTED),
@@ -180,3 +182,11 @@ def test_profile_calls_without_gpu_work(lib):
     names = [lib.msa_stage_name(i).decode() for i in range(bd.MSA_STAGE_COUNT)]
     assert len(set(names)) == bd.MSA_STAGE_COUNT and "kv_outer_kernel" in names
     assert lib.msa_stage_name(99).decode() == "unknown stage"
+
+
+def test_sink_flag_accepted_with_the_index_branch(lib):
+    d = bd.make_dims(1, 4096, 16, 4, index_dim=64, block_size=64, topk=8, flags=bd.MSA_FORCE_SINK)
+    plain = bd.make_dims(1, 4096, 16, 4, index_dim=64, block_size=64, topk=8)
+    for op in (bd.MSA_OP_INDEX_TOPK, bd.MSA_OP_PREFILL, bd.MSA_OP_DECODE):
+        assert lib.msa_workspace_bytes(op, ctypes.byref(d)) == lib.msa_workspace_bytes(op, ctypes.byref(plain))
+

@@ -263,7 +263,7 @@ def test_prefill_bitwise_deterministic():
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
-def gpu_decode(dec, B, k, flags=0, block_idx=None):
+def gpu_decode(dec, B, k, flags=0, block_idx=None):  # flags may carry MSA_FORCE_SINK
     b, L, G, d = dec.k_cache.shape
     Hq = dec.q.shape[1]
     di = dec.idx_q.shape[-1]
@@ -447,4 +447,70 @@ def test_stage_profiling_accounts_for_the_calls():
     run()
     bd.msa_profile_begin()
     assert bd.msa_profile_end() == {}
+
+
+# ---------------------------------------------------------------------------
+# forced sink block (variant)
+# ---------------------------------------------------------------------------
+SINK_INDEX_CASES = [
+    # T, G, di, B, k, query_chunk
+    (2048, 4, 64, 128, 4, 0),
+    (1000, 3, 128, 32, 2, 256),     # m = 2: sink and local block only
+    (777, 8, 64, 64, 1, 0),         # k = 1: the local block alone
+    (512, 2, 64, 64, 20, 0),        # k beyond the block count
+    (4160, 1, 128, 32, 70, 1024),   # more than 64 picks
+]
+
+
+@pytest.mark.parametrize("T,G,di,B,k,chunk", SINK_INDEX_CASES)
+def test_sink_index_topk_integer_exact(T, G, di, B, k, chunk):
+    say(f"[sink index_topk] T={T} G={G} di={di} B={B} k={k} chunk={chunk}")
+    inp = inputs.make_prefill(T, G, G, 8, di, seed=700 + T, idx_mode="integer")
+    dims = bd.make_dims(1, T, G, G, index_dim=di, block_size=B, topk=k, query_chunk=chunk,
+                        flags=bd.MSA_FORCE_SINK)
+    bidx = torch.full((1, T, G, k), -7, dtype=torch.int32, device="cuda")
+    bd.msa_index_topk(dims, inp.idx_q.cuda(), inp.idx_k.cuda(), bidx)
+    torch.cuda.synchronize()
+    bidx = bidx.cpu()
+    iq = inp.idx_q.to(torch.float64).numpy()
+    ik = inp.idx_k.to(torch.float64).numpy()
+    for t in list(range(0, T, 13)) + [T - 1]:
+        for g in range(G):
+            S = orc.block_max(orc.index_scores(iq[0, t, g], ik[0], t), t, B)
+            exp = orc.select_blocks(S, t, B, k, sink=True)
+            assert bidx[0, t, g].tolist() == exp.tolist(), (t, g)
+
+
+def test_sink_prefill_end_to_end():
+    T, Hq, G, di, B, k = 1536, 16, 4, 64, 64, 5
+    say("[sink prefill]")
+    inp = inputs.make_prefill(T, Hq, G, 128, di, seed=711, idx_mode="integer")
+    out, lse, bidx = gpu_prefill(inp, B, k, flags=bd.MSA_FORCE_SINK)
+    rows = [(0, t) for t in range(0, T, 11)] + [(0, T - 1)]
+    ores = orc.prefill(inp.q, inp.k, inp.v, inp.idx_q, inp.idx_k, B, k, rows=rows, sink=True)
+    compare_selection(bidx, ores, B, k, exact=True)
+    o_ref = np.stack([ores["out"][r] for r in rows])
+    o_got = np.stack([out[s, t].to(torch.float64).numpy() for s, t in rows])
+    check_attention(o_got, o_ref, "sink out")
+    l_ref = np.stack([ores["lse"][r] for r in rows])
+    l_got = np.stack([lse[s, t].to(torch.float64).numpy() for s, t in rows])
+    assert np.abs(l_got - l_ref).max() < 1e-3
+
+
+@pytest.mark.parametrize("mode", ["integer", "gaussian"])
+@pytest.mark.parametrize("L,B,k,lens", [(9000, 64, 6, [9000, 1, 64, 65, 4321]), (70000, 32, 20, [70000, 40001])])
+def test_sink_decode(mode, L, B, k, lens):
+    Hq, G, di = 16, 4, 64
+    say(f"[sink decode {mode}] L={L} B={B} k={k}")
+    dec = inputs.make_decode(len(lens), L, Hq, G, 128, di, seed=720 + L, cache_lens=lens, idx_mode=mode)
+    out, lse, bidx = gpu_decode(dec, B, k, flags=bd.MSA_FORCE_SINK)
+    ores = orc.decode(dec.q, dec.k_cache, dec.v_cache, dec.idx_q, dec.idx_k_cache, lens, B, k, sink=True)
+    for s in range(len(lens)):
+        t = lens[s] - 1
+        for g in range(G):
+            got, ref = bidx[s, g].numpy(), ores["block_idx"][s, g]
+            if not np.array_equal(got, ref):
+                assert mode == "gaussian" and orc.near_tie(ores["S"][s][g], t, B, k, sink=True), (s, g, got, ref)
+    cond = orc.decode(dec.q, dec.k_cache, dec.v_cache, dec.idx_q, dec.idx_k_cache, lens, B, k, block_idx=bidx)
+    check_attention(out.to(torch.float64).numpy(), cond["out"], "sink decode out")
 
