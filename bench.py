@@ -42,7 +42,8 @@ COPY_BYTES = 1 << 30   # calibration copy for the --pmc passes
 
 
 def traffic_file(kernel):
-    return os.path.join(ROOT, "profiles", f"{kernel}_prefill_t131072_traffic.json")
+    workload = "decode_8x1m" if kernel.startswith("decode_") else "prefill_t131072"
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
 
 
 def log(msg):
@@ -131,8 +132,9 @@ def measured_peaks(dev):
 
 def profile_kernels_only(args, dev):
     """The 128K prefill's inputs, one calibration copy of COPY_BYTES, then
-    --steps prefills (every kernel launched as in the timed steps): the
-    workload of the --pmc counter passes and of the kernel-trace summary."""
+    --steps prefills and --steps decode steps (8 x 1M context), every kernel
+    launched as in the timed steps: the workload of the --pmc counter passes
+    and of the kernel-trace summary."""
     stream = torch.cuda.current_stream()
     pin = inputs.make_prefill(PF["T"], PF["Hq"], PF["G"], PF["d"], PF["di"], seed=PF["seed"], device=dev,
                               block_size=PF["B"], skew_std=PF["skew"])
@@ -146,8 +148,19 @@ def profile_kernels_only(args, dev):
     bd.msa_profile_begin()
     ms, _ = timed(lambda: bd.msa_prefill(pdims, pin.q, pin.k, pin.v, pin.idx_q, pin.idx_k, pout, workspace=pws),
                   args.steps, stream)
+    del pws
+    dec = inputs.make_decode(DC["batch"], DC["L"], DC["Hq"], DC["G"], DC["d"], DC["di"], seed=DC["seed"],
+                             device=dev)
+    ddims = bd.make_dims(DC["batch"], DC["L"], DC["Hq"], DC["G"], index_dim=DC["di"], block_size=DC["B"],
+                         topk=DC["k"])
+    dout = torch.empty((DC["batch"], DC["Hq"], DC["d"]), dtype=torch.bfloat16, device=dev)
+    dws = torch.empty(bd.msa_workspace_bytes(bd.MSA_OP_DECODE, ddims), dtype=torch.uint8, device=dev)
+    dfn = lambda: bd.msa_decode(ddims, dec.q, dec.k_cache, dec.v_cache, dec.idx_q, dec.idx_k_cache,  # noqa: E731
+                                dec.cache_lens, dout, workspace=dws)
+    dms, _ = timed(dfn, args.steps, stream)
     stages = bd.msa_profile_end()
-    print(json.dumps({"profile_prefills": args.steps, "prefill_ms": round(ms, 4), "copy_bytes": COPY_BYTES,
+    print(json.dumps({"profile_steps": args.steps, "prefill_ms": round(ms, 4), "decode_ms": round(dms, 4),
+                      "copy_bytes": COPY_BYTES,
                       "stage_ms": {n: round(t / c, 4) for n, (c, t) in stages.items()}}), flush=True)
 
 
@@ -273,10 +286,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true", help="skip the all-blocks comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (CPU baseline + parity)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the block-size sweep, 32K prefill and forced-sink timings")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--profile-kernels", action="store_true",
-                    help="run only prefills (plus a calibration copy) for rocprofv3 --pmc passes")
+                    help="run only prefills and decode steps (plus a calibration copy) for rocprofv3 passes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path "
@@ -414,6 +429,51 @@ def main():
         }
         log(f"dense prefill {pd_ms:.2f} ms, dense decode {dd_ms:.3f} ms")
 
+    # The other prefill workloads of the pages' shapes, one timing each (not
+    # the headline): the 128K block-size sweep (same 2048 attended tokens),
+    # the 32K prefill, and the forced-sink variant of the headline workloads.
+    variants = None
+    if not args.no_variants:
+        log("variant workloads")
+        variants = {}
+        for B_, k_ in ((64, 32), (32, 64)):
+            vd = bd.make_dims(1, PF["T"], PF["Hq"], PF["G"], index_dim=PF["di"], block_size=B_, topk=k_)
+            vin = inputs.make_prefill(PF["T"], PF["Hq"], PF["G"], PF["d"], PF["di"], seed=PF["seed"], device=dev,
+                                      block_size=B_, skew_std=PF["skew"])
+            vws = torch.empty(bd.msa_workspace_bytes(bd.MSA_OP_PREFILL, vd), dtype=torch.uint8, device=dev)
+            fn = lambda: bd.msa_prefill(vd, vin.q, vin.k, vin.v, vin.idx_q, vin.idx_k, pout, workspace=vws)  # noqa: E731
+            fn()
+            ms, _ = timed(fn, 3, stream)
+            variants[f"prefill_t131072_b{B_}_k{k_}"] = {"ms": round(ms, 3),
+                                                        "tok_s": round(PF["T"] / (ms * 1e-3), 1)}
+            del vin, vws
+        T2 = 32768
+        vd = bd.make_dims(1, T2, PF["Hq"], PF["G"], index_dim=PF["di"], block_size=PF["B"], topk=PF["k"])
+        vin = inputs.make_prefill(T2, PF["Hq"], PF["G"], PF["d"], PF["di"], seed=2, device=dev, block_size=PF["B"])
+        vout = torch.empty_like(vin.q)
+        vws = torch.empty(bd.msa_workspace_bytes(bd.MSA_OP_PREFILL, vd), dtype=torch.uint8, device=dev)
+        fn = lambda: bd.msa_prefill(vd, vin.q, vin.k, vin.v, vin.idx_q, vin.idx_k, vout, workspace=vws)  # noqa: E731
+        fn()
+        ms, _ = timed(fn, 5, stream)
+        fi2, fm2 = prefill_flops(T2, PF["Hq"], PF["G"], PF["d"], PF["di"], PF["B"], PF["k"])
+        variants["prefill_t32768_b128_k16"] = {"ms": round(ms, 3), "tok_s": round(T2 / (ms * 1e-3), 1),
+                                               "tflops": round((fi2 + fm2) / (ms * 1e-3) / 1e12, 2)}
+        del vin, vout, vws
+        sd = bd.make_dims(1, PF["T"], PF["Hq"], PF["G"], index_dim=PF["di"], block_size=PF["B"], topk=PF["k"],
+                          flags=bd.MSA_FORCE_SINK)
+        fn = lambda: bd.msa_prefill(sd, pin.q, pin.k, pin.v, pin.idx_q, pin.idx_k, pout, workspace=pws)  # noqa: E731
+        fn()
+        ms, _ = timed(fn, 3, stream)
+        variants["prefill_t131072_sink"] = {"ms": round(ms, 3), "tok_s": round(PF["T"] / (ms * 1e-3), 1)}
+        sdd = bd.make_dims(DC["batch"], DC["L"], DC["Hq"], DC["G"], index_dim=DC["di"], block_size=DC["B"],
+                           topk=DC["k"], flags=bd.MSA_FORCE_SINK)
+        fn = lambda: bd.msa_decode(sdd, dec.q, dec.k_cache, dec.v_cache, dec.idx_q, dec.idx_k_cache,  # noqa: E731
+                                   dec.cache_lens, dout, workspace=dws)
+        fn()
+        ms, _ = timed(fn, 10, stream)
+        variants["decode_8x1m_sink"] = {"ms": round(ms, 4), "tok_s": round(DC["batch"] / (ms * 1e-3), 1)}
+        log(f"variants: {variants}")
+
     peaks = measured_peaks(dev)
     cpu, parity, dparity = None, None, None
     if not args.no_cpu:
@@ -456,12 +516,14 @@ def main():
             "roofline": {"bound": "hbm", "scope": "whole decode step (all kernels)",
                          "achieved": round(dbytes / (d_ms * 1e-3) / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
                          "frac": round(dbytes / (d_ms * 1e-3) / PEAK_HBM, 4),
-                         "frac_of_measured_copy": round(dbytes / (d_ms * 1e-3) / 1e9 / peaks["device_copy_gbs"], 4)},
+                         "frac_of_measured_copy": round(dbytes / (d_ms * 1e-3) / 1e9 / peaks["device_copy_gbs"], 4),
+                         "traffic": {k_: measured_traffic(k_) for k_ in ("decode_index_kernel", "decode_attn_kernel")}},
         },
         "roofline": dict(kernel=dominant, **rooflines[dominant]) if dominant else None,
         "kernel_rooflines": rooflines,
         "stage_ms": {n: round(v, 4) for n, v in stage.items()},
         "dense": dense,
+        "variants": variants,
         "measured_peaks": peaks,
         "parity": {"prefill_sampled": parity, "decode_sampled": dparity},
         "cpu_baseline": cpu,

@@ -31,6 +31,10 @@ KERNEL_SOURCES = {
                         "build.py"],
     "query_major_kernel": ["csrc/sparse_attn.hip", "csrc/msa_device.h", "csrc/msa_internal.h", "csrc/api.hip",
                            "build.py"],
+    "decode_index_kernel": ["csrc/decode.hip", "csrc/msa_device.h", "csrc/msa_internal.h", "csrc/api.hip",
+                            "build.py"],
+    "decode_attn_kernel": ["csrc/decode.hip", "csrc/msa_device.h", "csrc/msa_internal.h", "csrc/api.hip",
+                           "build.py"],
 }
 
 
