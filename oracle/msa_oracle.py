@@ -27,6 +27,10 @@ are exact in float64):
                  g = floor(h / R) over the keys of the selected blocks that
                  are <= t, scale 1/sqrt(d)                    [HA 方法; HN]
   decode_row     the same for the one new token at position len-1 of a cache
+  indexer_kl     KL(p_M || p_I) per (token, group) row over the selected tokens,
+                 p_I the softmax of the index scores, p_M the main branch's
+                 head-averaged attention (held constant), and its gradient
+                 into idx_q and idx_k                         [TG Метод; HA 方法]
 
 Readings where the pages are silent (the plainest reading the rest supports):
   - no scale or activation on the index score; a positive scale would not
@@ -257,3 +261,67 @@ def near_tie(S_g: np.ndarray, t: int, B: int, k: int, rel: float = 1e-3, sink: b
     sc = S_g[cand][order]
     a, b = sc[want - 1], sc[want]
     return abs(a - b) < rel * max(abs(a), abs(b), 1e-30)
+
+
+def indexer_kl(q, k, idx_q, idx_k, block_idx, B: int, scale: float | None = None, rows=None):
+    """Indexer KL loss and its gradient into the index branch inputs.
+
+    The index branch is trained by aligning its distribution with the main
+    branch's on the selected tokens: a KL divergence between the index
+    branch's distribution and the main branch's head-averaged one, with a
+    stop-gradient through the main branch's probabilities and the index
+    inputs detached, so that only the index projections learn [TG Метод: KL
+    between the index branch's outputs and the averaged main-branch outputs,
+    stopgrad through the main-branch probabilities and on the index inputs;
+    HA 方法: KL loss aligning the Index Branch with the Main Branch on the
+    selected tokens, gradient detach on the Index Branch inputs].
+
+    Per (s, t, g) row, J = the tokens <= t of the row's selected blocks:
+      p_I(j) = softmax_j(idx_q[t,g] . idx_k[j])            (raw index score)
+      p_M(j) = mean over the R heads h of group g of softmax_j(scale q[t,h] . k[j,g])
+      KL     = sum_j p_M(j) (log p_M(j) - log p_I(j))
+    and, for L = sum of KL over the rows computed, with p_M held constant,
+      dL/d idx_q[t,g] = sum_j (p_I(j) - p_M(j)) idx_k[j]
+      dL/d idx_k[j]  += (p_I(j) - p_M(j)) idx_q[t,g]       (over every row using j)
+
+    q [b,T,Hq,d], k [b,T,G,d], idx_q [b,T,G,di], idx_k [b,T,di], block_idx
+    [b,T,G,topk] (entries outside [0, L(t)] ignored).  rows: iterable of
+    (batch, t), default all.  Returns {'kl': {(s,t): [G]}, 'd_idx_q':
+    {(s,t): [G,di]}, 'd_idx_k': [b,T,di] accumulated over the rows computed}.
+    """
+    q, k = _f64(q), _f64(k)
+    idx_q, idx_k = _f64(idx_q), _f64(idx_k)
+    sel_all = np.asarray(_f64(block_idx), dtype=np.int64)
+    nbatch, T, Hq, d = q.shape
+    G = k.shape[2]
+    R = Hq // G
+    if scale is None:
+        scale = default_scale(d)
+    if rows is None:
+        rows = [(s, t) for s in range(nbatch) for t in range(T)]
+    res = {"kl": {}, "d_idx_q": {}, "d_idx_k": np.zeros(idx_k.shape)}
+    for s, t in rows:
+        L = local_block(t, B)
+        kl_t = np.zeros(G)
+        dq_t = np.zeros((G, idx_q.shape[-1]))
+        for g in range(G):
+            sel = [b for b in sel_all[s, t, g] if 0 <= b <= L]
+            toks = selected_tokens(np.array(sorted(set(sel)), dtype=np.int64), t, B)
+            if len(toks) == 0:
+                continue
+            sI = idx_k[s, toks] @ idx_q[s, t, g]
+            log_pI = sI - (sI.max() + np.log(np.exp(sI - sI.max()).sum()))
+            pM = np.zeros(len(toks))
+            for h in range(g * R, (g + 1) * R):
+                x = scale * (k[s, toks, g] @ q[s, t, h])
+                a = np.exp(x - x.max())
+                pM += a / a.sum()
+            pM /= R
+            nz = pM > 0
+            kl_t[g] = float((pM[nz] * (np.log(pM[nz]) - log_pI[nz])).sum())
+            ds = np.exp(log_pI) - pM
+            dq_t[g] = ds @ idx_k[s, toks]
+            res["d_idx_k"][s, toks] += ds[:, None] * idx_q[s, t, g][None, :]
+        res["kl"][(s, t)] = kl_t
+        res["d_idx_q"][(s, t)] = dq_t
+    return res

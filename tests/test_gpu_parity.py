@@ -305,6 +305,20 @@ def test_decode_vs_oracle(mode, L, Hq, G, di, B, k, lens):
     assert np.abs(lse.double().numpy() - cond["lse"]).max() < 1e-3
 
 
+def test_decode_many_rows_one_workgroup_per_row():
+    """batch * G >= 256 (s, g) rows: each row's attention stays in one
+    workgroup (no combine step); fewer rows split it over two."""
+    lens = [int(x) for x in np.random.default_rng(3).integers(1, 3000, 64)]
+    L, Hq, G, di, B, k = 3000, 32, 4, 64, 64, 8
+    say(f"[decode {len(lens)} x {G} rows]")
+    dec = inputs.make_decode(len(lens), L, Hq, G, 128, di, seed=77, cache_lens=lens, idx_mode="integer")
+    out, lse, bidx = gpu_decode(dec, B, k)
+    ores = orc.decode(dec.q, dec.k_cache, dec.v_cache, dec.idx_q, dec.idx_k_cache, lens, B, k)
+    assert np.array_equal(bidx.numpy(), ores["block_idx"])
+    check_attention(out.to(torch.float64).numpy(), ores["out"], "decode out")
+    assert np.abs(lse.double().numpy() - ores["lse"]).max() < 1e-3
+
+
 def test_decode_dense_and_given():
     L, Hq, G, di, B, k = 5000, 16, 4, 64, 64, 6
     lens = [5000, 777, 64]

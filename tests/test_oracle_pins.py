@@ -430,3 +430,93 @@ def test_sink_near_tie_helper():
     S2 = np.array([0.0, 10.0, 10.0 * (1 - 1e-4), 8.0, 1.0, 0.0])
     assert orc.near_tie(S2, t, B, k, sink=True)
     assert not orc.near_tie(S2, t, B, 2, sink=True)  # m = 2: both places forced
+
+
+# --------------------------------------------------------------------------
+# Indexer KL loss (KL(p_M || p_I) over the selected tokens) and its gradient.
+# --------------------------------------------------------------------------
+def _kl_inputs(T, Hq, G, d, di, B, k, seed):
+    inp = inputs.make_prefill(T, Hq, G, d, di, seed=seed)
+    sel = orc.prefill(inp.q, inp.k, inp.v, inp.idx_q, inp.idx_k, B, k)["block_idx"]
+    bidx = np.stack([sel[(0, t)] for t in range(T)])[None]
+    return inp, bidx
+
+
+def test_kl_nonnegative_and_single_token_rows():
+    T, Hq, G, d, di, B, k = 64, 4, 2, 8, 8, 8, 3
+    inp, bidx = _kl_inputs(T, Hq, G, d, di, B, k, seed=51)
+    res = orc.indexer_kl(inp.q, inp.k, inp.idx_q, inp.idx_k, bidx, B)
+    kl = np.stack([res["kl"][(0, t)] for t in range(T)])
+    assert (kl >= -1e-12).all() and kl.max() > 0.01
+    # t = 0 attends one token: both distributions are a point mass
+    assert np.abs(res["kl"][(0, 0)]).max() < 1e-12
+    assert np.abs(res["d_idx_q"][(0, 0)]).max() < 1e-12
+
+
+@pytest.mark.parametrize("R", [1, 2])
+def test_kl_zero_when_the_index_branch_equals_the_main_branch(R):
+    # one group; every head's q equals idx_q and k equals idx_k, scale 1:
+    # p_I = p_M exactly, so the loss and both gradients vanish
+    T, d, B, k = 48, 8, 8, 4
+    base = inputs.make_prefill(T, R, 1, d, d, seed=52)
+    q = base.idx_q.repeat(1, 1, R, 1)            # [1, T, R, d]
+    kk = base.idx_k[:, :, None, :]                # [1, T, 1, d]
+    sel = orc.prefill(q, kk, kk, base.idx_q, base.idx_k, B, k)["block_idx"]
+    bidx = np.stack([sel[(0, t)] for t in range(T)])[None]
+    res = orc.indexer_kl(q, kk, base.idx_q, base.idx_k, bidx, B, scale=1.0)
+    assert max(np.abs(v).max() for v in res["kl"].values()) < 1e-12
+    assert max(np.abs(v).max() for v in res["d_idx_q"].values()) < 1e-12
+    assert np.abs(res["d_idx_k"]).max() < 1e-12
+
+
+def test_kl_mirrored_heads_closed_form():
+    # two heads with q_1 = -q_0 over two tokens give p_M = (1/2, 1/2) whatever
+    # the logits; then KL = -log 2 - (log p_I(0) + log p_I(1)) / 2 and
+    # d idx_q = sum_j (p_I(j) - 1/2) idx_k[j]
+    T, d, di, B = 2, 4, 3, 4
+    q = torch.zeros(1, T, 2, d)
+    q[0, 1, 0] = torch.tensor([1.0, -2.0, 0.5, 3.0])
+    q[0, 1, 1] = -q[0, 1, 0]
+    kk = torch.tensor([[[[0.5, 1.0, -1.0, 2.0]], [[-1.5, 0.25, 2.0, 1.0]]]])  # [1, 2, 1, 4]
+    iq = torch.zeros(1, T, 1, di)
+    iq[0, 1, 0] = torch.tensor([1.0, 2.0, -1.0])
+    ik = torch.tensor([[[0.5, -1.0, 2.0], [1.0, 1.0, 0.0]]])                  # [1, 2, 3]
+    bidx = np.array([[[[0]], [[0]]]])                                           # block 0 = local block
+    res = orc.indexer_kl(q, kk, iq, ik, bidx, B, scale=0.7)
+    s0, s1 = 0.5 * 1 - 1.0 * 2 + 2.0 * -1, 1.0 * 1 + 1.0 * 2 + 0.0    # -3.5, 3.0
+    p0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    p1 = 1.0 - p0
+    kl = -math.log(2) - 0.5 * (math.log(p0) + math.log(p1))
+    assert abs(res["kl"][(0, 1)][0] - kl) < 1e-12
+    dq = (p0 - 0.5) * np.array([0.5, -1.0, 2.0]) + (p1 - 0.5) * np.array([1.0, 1.0, 0.0])
+    np.testing.assert_allclose(res["d_idx_q"][(0, 1)][0], dq, atol=1e-12)
+
+
+def test_kl_gradient_finite_differences():
+    # central differences of the summed loss in float64, the selection held fixed
+    T, Hq, G, d, di, B, k = 40, 4, 2, 8, 4, 8, 3
+    inp, bidx = _kl_inputs(T, Hq, G, d, di, B, k, seed=53)
+    iq = _np(inp.idx_q).copy()
+    ik = _np(inp.idx_k).copy()
+    q, kk = _np(inp.q), _np(inp.k)
+
+    def loss(iq_, ik_):
+        r = orc.indexer_kl(q, kk, iq_, ik_, bidx, B)
+        return sum(v.sum() for v in r["kl"].values())
+
+    res = orc.indexer_kl(q, kk, iq, ik, bidx, B)
+    rng = np.random.default_rng(4)
+    eps = 1e-6
+    for _ in range(6):
+        t, g, c = int(rng.integers(1, T)), int(rng.integers(0, G)), int(rng.integers(0, di))
+        a, b = iq.copy(), iq.copy()
+        a[0, t, g, c] += eps
+        b[0, t, g, c] -= eps
+        fd = (loss(a, ik) - loss(b, ik)) / (2 * eps)
+        assert abs(fd - res["d_idx_q"][(0, t)][g, c]) < 1e-6 * max(1.0, abs(fd)), (t, g, c)
+        j = int(rng.integers(0, T))
+        a, b = ik.copy(), ik.copy()
+        a[0, j, c] += eps
+        b[0, j, c] -= eps
+        fd = (loss(iq, a) - loss(iq, b)) / (2 * eps)
+        assert abs(fd - res["d_idx_k"][0, j, c]) < 1e-6 * max(1.0, abs(fd)), (j, c)
