@@ -30,6 +30,7 @@ MSA_FORCE_SINK = 0x4
 MSA_OP_INDEX_TOPK = 0
 MSA_OP_PREFILL = 1
 MSA_OP_DECODE = 2
+MSA_OP_INDEXER_KL = 3
 
 MSA_STAGE_INDEX_PREFILL = 0
 MSA_STAGE_TOPK_PREFILL = 1
@@ -41,11 +42,12 @@ MSA_STAGE_INDEX_DECODE = 6
 MSA_STAGE_TOPK_DECODE = 7
 MSA_STAGE_DECODE_ATTN = 8
 MSA_STAGE_DECODE_COMBINE = 9
-MSA_STAGE_COUNT = 10
+MSA_STAGE_INDEXER_KL = 10
+MSA_STAGE_COUNT = 11
 
 EXPORTED = ("msa_index_scores", "msa_index_topk", "msa_prefill", "msa_decode", "msa_workspace_bytes",
             "msa_status_string", "msa_last_hip_error", "msa_abi_version", "msa_profile_begin",
-            "msa_profile_end", "msa_stage_name")
+            "msa_profile_end", "msa_stage_name", "msa_indexer_kl")
 
 
 class msa_stage_time(ctypes.Structure):
@@ -110,6 +112,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_last_hip_error.restype = ctypes.c_char_p
     lib.msa_abi_version.argtypes = []
     lib.msa_abi_version.restype = i32
+    lib.msa_indexer_kl.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_indexer_kl.restype = i32
     lib.msa_profile_begin.argtypes = []
     lib.msa_profile_begin.restype = i32
     lib.msa_profile_end.argtypes = [ctypes.POINTER(msa_stage_time), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
@@ -229,6 +233,28 @@ def msa_prefill(dims: msa_dims, q, k, v, idx_q, idx_k, out, lse=None, block_idx=
     _check(lib, lib.msa_prefill(ctypes.byref(dims), p_q, p_k, p_v, p_iq, p_ik, p_o, p_l, p_bi,
                                 ws, nws, _stream(stream)))
     return out
+
+
+def msa_indexer_kl(dims: msa_dims, q, k, idx_q, idx_k, block_idx, lse, kl, d_idx_q, d_idx_k,
+                   workspace=None, stream=None):
+    """Indexer KL loss per (token, group) row and its gradient into idx_q and
+    idx_k (see include/msa.h); outputs are written into kl, d_idx_q, d_idx_k."""
+    lib = load_library()
+    b, T, Hq, G, d, di, kk = (dims.batch, dims.seqlen, dims.num_q_heads, dims.num_kv_heads,
+                             dims.head_dim, dims.index_dim, dims.topk)
+    p_q = _ptr(q, "q", torch.bfloat16, (b, T, Hq, d))
+    p_k = _ptr(k, "k", torch.bfloat16, (b, T, G, d))
+    p_iq = _ptr(idx_q, "idx_q", torch.bfloat16, (b, T, G, di))
+    p_ik = _ptr(idx_k, "idx_k", torch.bfloat16, (b, T, di))
+    p_bi = _ptr(block_idx, "block_idx", torch.int32, (b, T, G, kk))
+    p_l = _ptr(lse, "lse", torch.float32, (b, T, Hq))
+    p_kl = _ptr(kl, "kl", torch.float32, (b, T, G))
+    p_dq = _ptr(d_idx_q, "d_idx_q", torch.float32, (b, T, G, di))
+    p_dk = _ptr(d_idx_k, "d_idx_k", torch.float32, (b, T, di))
+    ws, nws = _workspace(MSA_OP_INDEXER_KL, dims, workspace, q.device)
+    _check(lib, lib.msa_indexer_kl(ctypes.byref(dims), p_q, p_k, p_iq, p_ik, p_bi, p_l, p_kl, p_dq, p_dk,
+                                   ws, nws, _stream(stream)))
+    return kl, d_idx_q, d_idx_k
 
 
 def msa_decode(dims: msa_dims, q, k_cache, v_cache, idx_q, idx_k_cache, cache_lens, out,

@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmsa.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.hip", "index_blockmax.hip", "topk_select.hip", "sparse_attn.hip", "decode.hip", "profile.hip"]
+SOURCES = ["api.hip", "index_blockmax.hip", "topk_select.hip", "sparse_attn.hip", "decode.hip", "profile.hip",
+           "indexer_kl.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

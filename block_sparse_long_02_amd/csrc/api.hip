@@ -162,6 +162,92 @@ int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
 }
 
 // ---------------------------------------------------------------------------
+// Indexer KL plan: block lists over every selected block (local included),
+// per-entry terms and per-list d idx_k partials of one query chunk.
+// ---------------------------------------------------------------------------
+constexpr size_t kDefaultKlBudget = 64ull << 30;
+
+struct KlPlan {
+  int nb = 0, KS = 0, R = 0, mt = 0, rank_bits = 0;
+  int Tc = 0, nchunks = 0;
+  size_t off_cnt = 0, off_offs = 0, off_bsum = 0, off_rinfo = 0, off_epos = 0, off_entries = 0, off_work = 0,
+         off_nwork = 0, off_work_a = 0, off_nwork_a = 0, off_stat = 0, off_lse_i = 0, off_ds = 0, off_kl_e = 0,
+         off_dq_e = 0, off_dk = 0, total = 0;
+  long max_work = 0, max_work_a = 0;
+};
+
+// workspace bytes of a chunk of tc tokens
+size_t kl_chunk_bytes(const msa_dims* d, const KlPlan& p, long tc, KlPlan* out) {
+  Layout L;
+  const size_t nb_ = (size_t)d->batch, G_ = (size_t)d->num_kv_heads, B_ = (size_t)d->block_size;
+  const size_t di = (size_t)d->index_dim;
+  const size_t nwin = ((size_t)tc + msa::kListWindow - 1) / msa::kListWindow;
+  const size_t nlists = nb_ * G_ * nwin * (size_t)p.nb;
+  const size_t nscan = (nlists + msa::kScanItems - 1) / msa::kScanItems;
+  const size_t rows = nb_ * (size_t)tc * G_;
+  const size_t emax = rows * (size_t)p.KS;
+  KlPlan q = p;
+  q.max_work = (long)((emax + p.mt - 1) / p.mt + nlists);
+  q.max_work_a = (long)((emax + 127) / 128 + nlists);
+  q.off_cnt = L.add(nlists * 4);
+  q.off_offs = L.add(nlists * 4);
+  q.off_bsum = L.add(nscan * 8);
+  q.off_rinfo = L.add(rows * 4);
+  q.off_epos = L.add(emax * 4);
+  q.off_entries = L.add(emax * 4);
+  q.off_work = L.add((size_t)q.max_work * 8);
+  q.off_nwork = L.add(4);
+  q.off_work_a = L.add((size_t)q.max_work_a * 8);
+  q.off_nwork_a = L.add(4);
+  q.off_stat = L.add(emax * 8);
+  q.off_lse_i = L.add(rows * 4);
+  q.off_ds = L.add(emax * B_ * 2);
+  q.off_kl_e = L.add(emax * 4);
+  q.off_dq_e = L.add(emax * di * 4);
+  q.off_dk = L.add(nlists * B_ * di * 4);
+  q.total = L.total;
+  if (out != nullptr) *out = q;
+  return q.total;
+}
+
+int make_kl_plan(const msa_dims* d, KlPlan* p) {
+  int st = check_dims(d, false);
+  if (st != MSA_OK) return st;
+  if (d->flags != 0) return MSA_ERR_INVALID_ARG;
+  const int T = d->seqlen, B = d->block_size, G = d->num_kv_heads;
+  p->R = d->num_q_heads / G;
+  if (p->R > 32 || (p->R & (p->R - 1)) != 0) return MSA_ERR_UNSUPPORTED;  // p_M sums aligned lane groups
+  p->nb = (T + B - 1) / B;
+  p->KS = d->topk < p->nb ? d->topk : p->nb;
+  p->mt = msa::kAttnRows / p->R;
+  while ((1 << p->rank_bits) < p->KS) ++p->rank_bits;
+  // largest chunk (a multiple of the list window, else of B) within the budget and the int32 limits
+  const long per_tok_entries = (long)d->batch * G * p->KS;
+  long lim = (kMaxInt32 / 2) / (per_tok_entries ? per_tok_entries : 1);
+  const long lim2 = (long)kMaxInt32 >> p->rank_bits;
+  if (lim2 < lim) lim = lim2;
+  const long lists_per_win = (long)d->batch * G * p->nb;
+  const long max_win = (kMaxInt32 - 1) / lists_per_win;
+  if (max_win < 1) return MSA_ERR_UNSUPPORTED;
+  if (max_win * msa::kListWindow < lim) lim = max_win * msa::kListWindow;
+  long tc;
+  if (d->query_chunk > 0) {
+    tc = d->query_chunk < T ? d->query_chunk : T;
+  } else {
+    tc = ((long)T + msa::kListWindow - 1) / msa::kListWindow * msa::kListWindow;
+    while (tc > msa::kListWindow && kl_chunk_bytes(d, *p, tc, nullptr) > kDefaultKlBudget) tc -= msa::kListWindow;
+    while (tc > B && kl_chunk_bytes(d, *p, tc, nullptr) > kDefaultKlBudget) tc -= B;
+    if (tc > T) tc = T;
+  }
+  if (tc > lim) tc = lim / B * B;
+  if (tc < 1) return MSA_ERR_UNSUPPORTED;
+  p->Tc = (int)tc;
+  p->nchunks = (int)((T + tc - 1) / tc);
+  kl_chunk_bytes(d, *p, tc, p);
+  return MSA_OK;
+}
+
+// ---------------------------------------------------------------------------
 // Decode plan
 // ---------------------------------------------------------------------------
 struct DecodePlan {
@@ -265,6 +351,11 @@ size_t msa_workspace_bytes(int op, const msa_dims* dims) {
   if (op == MSA_OP_DECODE) {
     DecodePlan p;
     if (make_decode_plan(dims, &p) != MSA_OK) return (size_t)-1;
+    return p.total;
+  }
+  if (op == MSA_OP_INDEXER_KL) {
+    KlPlan p;
+    if (make_kl_plan(dims, &p) != MSA_OK) return (size_t)-1;
     return p.total;
   }
   return (size_t)-1;
@@ -390,6 +481,81 @@ int msa_prefill(const msa_dims* dims, const void* q, const void* k, const void* 
     a.nlists = (long)dims->batch * dims->num_kv_heads * a.nwin * p.nb;
     a.max_work = (emax + p.mt - 1) / p.mt + a.nlists;
     hipError_t e = msa::launch_prefill_main_sparse(a, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  msa::prof_mark(s, -1);
+  return MSA_OK;
+}
+
+int msa_indexer_kl(const msa_dims* dims, const void* q, const void* k, const void* idx_q, const void* idx_k,
+                   const int32_t* block_idx, const float* lse, float* kl, float* d_idx_q, float* d_idx_k,
+                   void* workspace, size_t workspace_bytes, void* hip_stream) {
+  KlPlan p;
+  int st = make_kl_plan(dims, &p);
+  if (st != MSA_OK) return st;
+  if (q == nullptr || k == nullptr || idx_q == nullptr || idx_k == nullptr || block_idx == nullptr ||
+      lse == nullptr || kl == nullptr || d_idx_q == nullptr || d_idx_k == nullptr)
+    return MSA_ERR_INVALID_ARG;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(idx_q, 16) || misaligned(idx_k, 16) ||
+      misaligned(block_idx, 4) || misaligned(lse, 4) || misaligned(kl, 4) || misaligned(d_idx_q, 4) ||
+      misaligned(d_idx_k, 4))
+    return MSA_ERR_ALIGNMENT;
+  if ((st = check_workspace(p.total, workspace, workspace_bytes)) != MSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  msa::IndexerKlArgs a{};
+  msa::PrefillMainArgs& l = a.l;
+  l.q = static_cast<const uint16_t*>(q);
+  l.k = static_cast<const uint16_t*>(k);
+  l.batch = dims->batch;
+  l.T = dims->seqlen;
+  l.Hq = dims->num_q_heads;
+  l.G = dims->num_kv_heads;
+  l.B = dims->block_size;
+  l.topk = dims->topk;
+  l.KS = p.KS;
+  l.rank_bits = p.rank_bits;
+  l.include_local = 1;
+  l.nbl = p.nb;
+  l.scale_log2 = log2_scale(dims);
+  l.bidx = block_idx;
+  l.bidx_rows = dims->seqlen;
+  l.bidx_t_off = 0;
+  l.cnt = at<int32_t>(workspace, p.off_cnt);
+  l.offs = at<int32_t>(workspace, p.off_offs);
+  l.bsum = at<int32_t>(workspace, p.off_bsum);
+  l.rinfo = at<int32_t>(workspace, p.off_rinfo);
+  l.epos = at<int32_t>(workspace, p.off_epos);
+  l.entries = at<int32_t>(workspace, p.off_entries);
+  l.work = at<int2>(workspace, p.off_work);
+  l.n_work = at<int32_t>(workspace, p.off_nwork);
+  a.idx_q = static_cast<const uint16_t*>(idx_q);
+  a.idx_k = static_cast<const uint16_t*>(idx_k);
+  a.lse = lse;
+  a.di = dims->index_dim;
+  a.kl = kl;
+  a.d_idx_q = d_idx_q;
+  a.d_idx_k = d_idx_k;
+  a.work_a = at<int2>(workspace, p.off_work_a);
+  a.n_work_a = at<int32_t>(workspace, p.off_nwork_a);
+  a.stat = at<float2>(workspace, p.off_stat);
+  a.lse_i = at<float>(workspace, p.off_lse_i);
+  a.ds = at<uint16_t>(workspace, p.off_ds);
+  a.kl_e = at<float>(workspace, p.off_kl_e);
+  a.dq_e = at<float>(workspace, p.off_dq_e);
+  a.dk_part = at<float>(workspace, p.off_dk);
+  msa::prof_mark(s, MSA_STAGE_INDEXER_KL);
+  for (int c = 0; c < p.nchunks; ++c) {
+    const int t0 = c * p.Tc;
+    const int tc = (dims->seqlen - t0) < p.Tc ? dims->seqlen - t0 : p.Tc;
+    const long emax = (long)dims->batch * tc * dims->num_kv_heads * p.KS;
+    l.t0 = t0;
+    l.tc = tc;
+    l.nwin = (tc + msa::kListWindow - 1) / msa::kListWindow;
+    l.nlists = (long)dims->batch * dims->num_kv_heads * l.nwin * p.nb;
+    l.max_work = (emax + p.mt - 1) / p.mt + l.nlists;
+    a.max_work_a = (emax + 127) / 128 + l.nlists;
+    a.accumulate_dk = c > 0;
+    hipError_t e = msa::launch_indexer_kl(a, s);
     if (e != hipSuccess) return hip_fail(e);
   }
   msa::prof_mark(s, -1);

@@ -1,0 +1,475 @@
+// Indexer KL loss of MSA on gfx950: the loss that trains the Index Branch and
+// its gradient into the index-branch inputs.
+//
+// Definition [Telegram review quant_prune_distill post 751, "Метод": a KL
+// divergence between the index branch's outputs and the main branch's
+// head-averaged outputs, stop-gradient through the main branch's
+// probabilities and on the index inputs; hyper.ai paper page 2606.13392,
+// 方法 (Method): the KL loss aligns the Index Branch's distribution with the
+// Main Branch's on the selected tokens, with the index inputs detached].
+// Per (token t, group g) row over the tokens J of its selected blocks (j <= t):
+//   p_I(j) = softmax_j(idx_q[t,g] . idx_k[j])
+//   p_M(j) = mean over the R heads h of g of exp(scale q[t,h].k[j,g] - lse[t,h])
+//   KL     = sum_j p_M(j) (ln p_M(j) - ln p_I(j))
+//   dS(j)  = p_I(j) - p_M(j)          (gradient of the summed KL w.r.t. the score)
+//   d idx_q[t,g] = sum_j dS(j) idx_k[j],   d idx_k[j] += dS(j) idx_q[t,g]
+// lse is the main branch's log-sum-exp over the same selection (the prefill's
+// lse output), so exp(x - lse) is exactly the main branch's attention weight.
+//
+// Work split (block-major, the same (s, g, window, block) lists as the
+// prefill's main branch, here including each row's local block):
+//  1. kl_index_stats_kernel: per list entry, the max and sum of 2^(s log2 e)
+//     over the block's keys <= t (MFMA, tiles of 128 entries);
+//  2. kl_row_lse_kernel: per row, the index log-sum-exp (fixed slot order);
+//  3. kl_entry_kernel: per entry, the R heads' logits and the index logits on
+//     MFMA in one layout, p_M (mean over the R head lanes), p_I, the entry's
+//     KL term and dS (bf16, row-major per entry);
+//  4. kl_list_kernel: per list, d idx_q of each entry (dS . idx_k) and the
+//     list's d idx_k partial (dS^T . idx_q) on MFMA;
+//  5. kl_row_out_kernel / kl_dk_reduce_kernel: fixed-order sums per row and
+//     per key block.  No atomic touches a value: results are reproducible.
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+namespace {
+
+constexpr int D = 128;  // head_dim
+
+__device__ __forceinline__ size_t kl_list_of(const PrefillMainArgs& l, long lid, int* b, int* g, int* s) {
+  *b = (int)(lid % l.nbl);
+  const long sgw = lid / l.nbl;
+  const long sg = sgw / l.nwin;
+  *g = (int)(sg % l.G);
+  *s = (int)(sg / l.G);
+  return (size_t)lid;
+}
+
+// Rows [0, nrows) of a B x C bf16 block (row stride `stride` elements) into
+// LDS with row stride ldsr; rows >= nvalid are zero-filled.
+template <int C>
+__device__ __forceinline__ void stage_rows(bf16_t* dst, int ldsr, const bf16_t* __restrict__ src, size_t stride,
+                                           int nrows, int nvalid, int tid, int nthr) {
+  constexpr int CPR = C / 8;
+  for (int c = tid; c < nrows * CPR; c += nthr) {
+    const int r = c / CPR, part = c % CPR;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < nvalid) v = *reinterpret_cast<const u32x4*>(src + (size_t)r * stride + part * 8);
+    *reinterpret_cast<u32x4*>(dst + r * ldsr + part * 8) = v;
+  }
+}
+
+// S^T tile (32 keys x 32 rows) = A[32 keys x C] . Qop^T, A rows from LDS.
+template <int C>
+__device__ __forceinline__ f32x16 logit_tile(const bf16_t* As, int ldsr, int key0, const bf16x8* qop, int col,
+                                             int half) {
+  f32x16 acc = {};
+  const bf16_t* arow = As + (key0 + col) * ldsr + 8 * half;
+#pragma unroll
+  for (int ks = 0; ks < C / 16; ++ks)
+    acc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(arow + 16 * ks), qop[ks], acc);
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// 1. Index statistics per entry: (m, l) with m = max of s log2 e over the
+//    block's keys <= t and l = sum of 2^(s log2 e - m).  Tiles of 128 entries
+//    (4 waves x 32), one entry per MFMA column.
+// ---------------------------------------------------------------------------
+template <int DI, int BS>
+__global__ __launch_bounds__(256, 2) void kl_index_stats_kernel(IndexerKlArgs a) {
+  constexpr int KP = DI + 8;
+  constexpr int KT = BS / 32;
+  constexpr int MT = 128;
+  __shared__ __attribute__((aligned(16))) bf16_t Is[BS * KP];
+  const PrefillMainArgs& l = a.l;
+  const int w = blockIdx.x;
+  if (w >= a.n_work_a[0]) return;
+  const int2 wk = a.work_a[w];
+  int b, g, s;
+  const size_t lid = kl_list_of(l, wk.x, &b, &g, &s);
+  const int count = l.cnt[lid];
+  const int off = l.offs[lid];
+  const int tile0 = wk.y * kTilesPerItem;
+  const int ntile = min(kTilesPerItem, (count + MT - 1) / MT - tile0);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int kb = b * l.B;
+  stage_rows<DI>(Is, KP, a.idx_k + ((size_t)s * l.T + kb) * DI, DI, BS, min(BS, l.T - kb), tid, 256);
+  __syncthreads();
+  for (int it = 0; it < ntile; ++it) {
+    const int pos = (tile0 + it) * MT + wave * 32 + col;
+    const bool valid = pos < count;
+    const int ent = l.entries[off + min(pos, count - 1)];
+    const int t = l.t0 + (ent >> l.rank_bits);
+    bf16x8 qop[DI / 16];
+    const bf16_t* qp = a.idx_q + (((size_t)s * l.T + t) * l.G + g) * DI;
+#pragma unroll
+    for (int ks = 0; ks < DI / 16; ++ks) qop[ks] = load_bf16x8(qp + 16 * ks + 8 * half);
+    // online max and sum over the key tiles; key kb <= t, so the first tile
+    // of the row's lane pair always has a finite entry
+    float m = -INFINITY, sum = 0.f;
+#pragma unroll 1
+    for (int kt = 0; kt < KT; ++kt) {
+      const f32x16 acc = logit_tile<DI>(Is, KP, kt * 32, qop, col, half);
+      float sv[16];
+      float tm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = kb + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        sv[i] = (j <= t) ? acc[i] * kLog2e : -INFINITY;
+        tm = fmaxf(tm, sv[i]);
+      }
+      tm = fmaxf(tm, __shfl_xor(tm, 32, kWave));
+      const float mn = fmaxf(m, tm);
+      float ts = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ts += __builtin_amdgcn_exp2f(sv[i] - mn);
+      ts += __shfl_xor(ts, 32, kWave);
+      sum = (m == -INFINITY ? 0.f : sum * __builtin_amdgcn_exp2f(m - mn)) + ts;
+      m = mn;
+    }
+    if (valid && half == 0) a.stat[off + pos] = make_float2(m, sum);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. Per row (s, t, g): log2-sum-exp of the index scores over its entries.
+// ---------------------------------------------------------------------------
+__global__ void kl_row_lse_kernel(IndexerKlArgs a) {
+  const PrefillMainArgs& l = a.l;
+  const long n_rows = (long)l.batch * l.tc * l.G;
+  const long row = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= n_rows) return;
+  const int nv = l.rinfo[row] & 0x3fffffff;
+  const int32_t* pos = l.epos + (size_t)row * l.KS;
+  float M = -INFINITY;
+  for (int q = 0; q < nv; ++q) M = fmaxf(M, a.stat[pos[q]].x);
+  float sum = 0.f;
+  for (int q = 0; q < nv; ++q) {
+    const float2 st = a.stat[pos[q]];
+    sum += st.y * __builtin_amdgcn_exp2f(st.x - M);
+  }
+  a.lse_i[row] = nv > 0 ? M + __log2f(sum) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// 3. Per entry: the main branch's and the index branch's distributions over
+//    the block's keys, the entry's KL term and dS = p_I - p_M (bf16).  Tiles
+//    of 128/R tokens x R heads, as the block-major attention kernel; the
+//    index operand of a row is its token's idx_q, so both logit tiles share
+//    one layout and p_M is a sum over the R head lanes of a token.
+// ---------------------------------------------------------------------------
+template <int DI, int BS>
+__global__ __launch_bounds__(256, 2) void kl_entry_kernel(IndexerKlArgs a) {
+  constexpr int KROW = D + 8, KP = DI + 8;
+  constexpr int KT = BS / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[BS * KROW];
+  __shared__ __attribute__((aligned(16))) bf16_t Is[BS * KP];
+  const PrefillMainArgs& l = a.l;
+  const int w = blockIdx.x;
+  if (w >= l.n_work[0]) return;
+  const int2 wk = l.work[w];
+  int b, g, s;
+  const size_t lid = kl_list_of(l, wk.x, &b, &g, &s);
+  const int R = l.Hq / l.G;
+  const int mt = kAttnRows / R;
+  const int count = l.cnt[lid];
+  const int off = l.offs[lid];
+  const int tile0 = wk.y * kTilesPerItem;
+  const int ntile = min(kTilesPerItem, (count + mt - 1) / mt - tile0);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int row = wave * 32 + col;
+  const int e = row / R, r = row % R;
+  const int h = g * R + r;
+  const int kb = b * l.B;
+  const size_t kvstride = (size_t)l.G * D;
+  const int nkey = min(BS, l.T - kb);
+  stage_rows<D>(Ks, KROW, l.k + ((size_t)s * l.T + kb) * kvstride + (size_t)g * D, kvstride, BS, nkey, tid, 256);
+  stage_rows<DI>(Is, KP, a.idx_k + ((size_t)s * l.T + kb) * DI, DI, BS, nkey, tid, 256);
+  __syncthreads();
+  const float c = l.scale_log2;
+  const float invR = 1.0f / (float)R;
+
+  for (int it = 0; it < ntile; ++it) {
+    const int pos = (tile0 + it) * mt + e;
+    const bool valid = e < mt && pos < count;
+    const int ent = l.entries[off + min(pos, count - 1)];
+    const int tl = ent >> l.rank_bits;
+    const int t = l.t0 + tl;
+    bf16x8 qop[D / 16], iop[DI / 16];
+    const bf16_t* qp = l.q + (((size_t)s * l.T + t) * l.Hq + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qop[ks] = load_bf16x8(qp + 16 * ks + 8 * half);
+    const bf16_t* ip = a.idx_q + (((size_t)s * l.T + t) * l.G + g) * DI;
+#pragma unroll
+    for (int ks = 0; ks < DI / 16; ++ks) iop[ks] = load_bf16x8(ip + 16 * ks + 8 * half);
+    const float lse2_h = a.lse[((size_t)s * l.T + t) * l.Hq + h] * kLog2e;
+    const float lse2_i = a.lse_i[((size_t)s * l.tc + tl) * l.G + g];
+    float kl = 0.f;
+    bf16_t* dsrow = a.ds + (size_t)(off + min(pos, count - 1)) * BS;
+    const bool writer = valid && r == 0;
+#pragma unroll 1
+    for (int kt = 0; kt < KT; ++kt) {
+      const f32x16 x = logit_tile<D>(Ks, KROW, kt * 32, qop, col, half);
+      const f32x16 si = logit_tile<DI>(Is, KP, kt * 32, iop, col, half);
+      float pm[16], ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = kb + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        pm[i] = (j <= t) ? __builtin_amdgcn_exp2f(x[i] * c - lse2_h) : 0.f;
+      }
+      // mean over the R head lanes of the token (aligned groups of R lanes)
+      for (int o = 1; o < R; o <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pm[i] += __shfl_xor(pm[i], o, kWave);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = kb + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        const bool ok = j <= t;
+        const float p_m = pm[i] * invR;
+        const float l2pi = si[i] * kLog2e - lse2_i;
+        const float p_i = ok ? __builtin_amdgcn_exp2f(l2pi) : 0.f;
+        if (ok && p_m > 0.f) kl += p_m * (__log2f(p_m) - l2pi);
+        ds[i] = p_i - p_m;
+      }
+      if (writer) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          bf16x4 v;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = (__bf16)ds[4 * i4 + u];
+          *reinterpret_cast<bf16x4*>(dsrow + kt * 32 + 8 * i4 + 4 * half) = v;
+        }
+      }
+    }
+    kl += __shfl_xor(kl, 32, kWave);
+    if (writer && half == 0) a.kl_e[off + pos] = kl * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. Per list: d idx_q of every entry (dS . idx_k of the block) and the
+//    list's d idx_k partial (dS^T . idx_q over its entries), both on MFMA,
+//    over chunks of 32 entries.
+// ---------------------------------------------------------------------------
+template <int DI, int BS>
+__global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
+  constexpr int EC = 32;                  // entries per chunk
+  constexpr int IKR = BS + 8;             // idx_k^T row stride (keys)
+  constexpr int DRR = BS + 8;             // dS row stride (keys)
+  constexpr int ER = EC + 8;              // transposed rows (entries)
+  constexpr int NT = (BS / 32) * (DI / 32);  // d idx_k output tiles of the list
+  constexpr int TPW = (NT + 3) / 4;          // tiles per wave
+  __shared__ __attribute__((aligned(16))) bf16_t IkT[DI * IKR];
+  __shared__ __attribute__((aligned(16))) bf16_t Dr[EC * DRR];
+  __shared__ __attribute__((aligned(16))) bf16_t DT[BS * ER];
+  __shared__ __attribute__((aligned(16))) bf16_t QT[DI * ER];
+  // the list's entries sorted by (token, slot): its d idx_k partial is then
+  // accumulated in an order that does not depend on how the list was filled
+  __shared__ uint64_t order[kListWindow];
+  const PrefillMainArgs& l = a.l;
+  const long lid = blockIdx.x;
+  const int count = l.cnt[lid];
+  if (count == 0) return;
+  int b, g, s;
+  kl_list_of(l, lid, &b, &g, &s);
+  const int off = l.offs[lid];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int kb = b * l.B;
+  const int nkey = min(BS, l.T - kb);
+
+  // One entry per token of the list's window when a row's valid selections are
+  // distinct, so count <= kListWindow; otherwise the list order is kept.
+  const bool sorted = count <= kListWindow;
+  if (sorted) {
+    int n2 = 1;
+    while (n2 < count) n2 <<= 1;
+    for (int i = tid; i < n2; i += 256)
+      order[i] = i < count ? ((uint64_t)(uint32_t)l.entries[off + i] << 32) | (uint32_t)i : ~0ull;
+    __syncthreads();
+    for (int kk = 2; kk <= n2; kk <<= 1)
+      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+        for (int i = tid; i < n2; i += 256) {
+          const int p = i ^ jj;
+          if (p > i) {
+            const uint64_t x = order[i], y = order[p];
+            const bool up = (i & kk) == 0;
+            if ((x > y) == up) {
+              order[i] = y;
+              order[p] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+  }
+  auto at_rank = [&](int i) -> int { return sorted ? (int)(uint32_t)order[i] : i; };
+
+  // idx_k block, transposed: IkT[c][key]
+  for (int u = tid; u < BS * DI; u += 256) {
+    const int key = u / DI, cc = u % DI;
+    IkT[cc * IKR + key] = key < nkey ? a.idx_k[((size_t)s * l.T + kb + key) * DI + cc] : bf16_t(0);
+  }
+
+  f32x16 dk[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) dk[i] = f32x16{};
+
+  for (int c0 = 0; c0 < count; c0 += EC) {
+    const int n = min(EC, count - c0);
+    __syncthreads();  // the previous chunk's LDS reads are done (and IkT is written)
+    for (int u = tid; u < EC * BS; u += 256) {
+      const int en = u / BS, key = u % BS;
+      const bf16_t v = en < n ? a.ds[(size_t)(off + at_rank(c0 + en)) * BS + key] : bf16_t(0);
+      Dr[en * DRR + key] = v;
+      DT[key * ER + en] = v;
+    }
+    for (int u = tid; u < EC * DI; u += 256) {
+      const int en = u / DI, cc = u % DI;
+      bf16_t v = bf16_t(0);
+      if (en < n) {
+        const int ent = l.entries[off + at_rank(c0 + en)];
+        const int t = l.t0 + (ent >> l.rank_bits);
+        v = a.idx_q[(((size_t)s * l.T + t) * l.G + g) * DI + cc];
+      }
+      QT[cc * ER + en] = v;
+    }
+    __syncthreads();
+    // d idx_q of the chunk's entries: [entry][c] = sum_key dS[entry][key] idx_k[key][c]
+    if (wave < DI / 32) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < BS / 16; ++ks) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(Dr + col * DRR + 16 * ks + 8 * half);
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(IkT + (32 * wave + col) * IKR + 16 * ks + 8 * half);
+        acc = mfma32x32x16(av, bv, acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int en = 8 * (i / 4) + 4 * half + (i % 4);
+        if (en < n) a.dq_e[(size_t)(off + at_rank(c0 + en)) * DI + 32 * wave + col] = acc[i];
+      }
+    }
+    // d idx_k partial: [key][c] += sum_entry dS[entry][key] idx_q[entry][c]
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tix = wave + 4 * i;
+      if (tix < NT) {
+        const int kt = tix / (DI / 32), dt = tix % (DI / 32);
+#pragma unroll
+        for (int ks = 0; ks < EC / 16; ++ks) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(DT + (32 * kt + col) * ER + 16 * ks + 8 * half);
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(QT + (32 * dt + col) * ER + 16 * ks + 8 * half);
+          dk[i] = mfma32x32x16(av, bv, dk[i]);
+        }
+      }
+    }
+  }
+  float* part = a.dk_part + (size_t)lid * BS * DI;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int tix = wave + 4 * i;
+    if (tix < NT) {
+      const int kt = tix / (DI / 32), dt = tix % (DI / 32);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = 32 * kt + 8 * (v / 4) + 4 * half + (v % 4);
+        part[(size_t)key * DI + 32 * dt + col] = dk[i][v];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 5a. Per row and index dimension: KL and d idx_q, summed in slot order.
+// ---------------------------------------------------------------------------
+__global__ void kl_row_out_kernel(IndexerKlArgs a) {
+  const PrefillMainArgs& l = a.l;
+  const long n = (long)l.batch * l.tc * l.G * a.di;
+  const long x = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (x >= n) return;
+  const long row = x / a.di;
+  const int cc = (int)(x % a.di);
+  const long per_b = (long)l.tc * l.G;
+  const int s = (int)(row / per_b);
+  const int tl = (int)((row % per_b) / l.G);
+  const int g = (int)(row % l.G);
+  const size_t orow = ((size_t)s * l.T + l.t0 + tl) * l.G + g;
+  const int nv = l.rinfo[row] & 0x3fffffff;
+  const int32_t* pos = l.epos + (size_t)row * l.KS;
+  float dq = 0.f, kl = 0.f;
+  for (int q = 0; q < nv; ++q) {
+    dq += a.dq_e[(size_t)pos[q] * a.di + cc];
+    if (cc == 0) kl += a.kl_e[pos[q]];
+  }
+  a.d_idx_q[orow * a.di + cc] = dq;
+  if (cc == 0) a.kl[orow] = kl;
+}
+
+// ---------------------------------------------------------------------------
+// 5b. Per key block: d idx_k = sum over the block's lists (group, window) of
+//     their partials, in that order; added onto earlier query chunks.
+// ---------------------------------------------------------------------------
+template <int DI, int BS>
+__global__ __launch_bounds__(256) void kl_dk_reduce_kernel(IndexerKlArgs a) {
+  const PrefillMainArgs& l = a.l;
+  const int b = blockIdx.x, s = blockIdx.y;
+  const int kb = b * l.B;
+  const int nkey = min(BS, l.T - kb);
+  for (int u = threadIdx.x; u < nkey * DI; u += 256) {
+    const int key = u / DI, cc = u % DI;
+    float acc = 0.f;
+    for (int g = 0; g < l.G; ++g)
+      for (int w = 0; w < l.nwin; ++w) {
+        const size_t lid = (((size_t)s * l.G + g) * l.nwin + w) * l.nbl + b;
+        if (l.cnt[lid] > 0) acc += a.dk_part[lid * BS * DI + (size_t)key * DI + cc];
+      }
+    float* dst = a.d_idx_k + ((size_t)s * l.T + kb + key) * DI + cc;
+    *dst = a.accumulate_dk ? *dst + acc : acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_indexer_kl(const IndexerKlArgs& a, hipStream_t st) {
+  const PrefillMainArgs& l = a.l;
+  const int R = l.Hq / l.G;
+  const int mt = kAttnRows / R;
+  hipError_t err = launch_block_lists(l, mt, st);
+  if (err != hipSuccess) return err;
+  if ((err = launch_list_work(l, 128, a.work_a, a.n_work_a, st)) != hipSuccess) return err;
+  const long n_rows = (long)l.batch * l.tc * l.G;
+#define MSA_KL_DISPATCH(KERNEL, GRID, ...)                                                        \
+  do {                                                                                            \
+    if (a.di == 128) {                                                                            \
+      if (l.B == 128) KERNEL<128, 128><<<GRID, 256, 0, st>>>(__VA_ARGS__);                        \
+      else if (l.B == 64) KERNEL<128, 64><<<GRID, 256, 0, st>>>(__VA_ARGS__);                     \
+      else KERNEL<128, 32><<<GRID, 256, 0, st>>>(__VA_ARGS__);                                    \
+    } else {                                                                                      \
+      if (l.B == 128) KERNEL<64, 128><<<GRID, 256, 0, st>>>(__VA_ARGS__);                         \
+      else if (l.B == 64) KERNEL<64, 64><<<GRID, 256, 0, st>>>(__VA_ARGS__);                      \
+      else KERNEL<64, 32><<<GRID, 256, 0, st>>>(__VA_ARGS__);                                     \
+    }                                                                                             \
+  } while (0)
+  if (a.max_work_a > 0) MSA_KL_DISPATCH(kl_index_stats_kernel, dim3((unsigned)a.max_work_a), a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  kl_row_lse_kernel<<<(unsigned)((n_rows + 255) / 256), 256, 0, st>>>(a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (l.max_work > 0) MSA_KL_DISPATCH(kl_entry_kernel, dim3((unsigned)l.max_work), a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  MSA_KL_DISPATCH(kl_list_kernel, dim3((unsigned)l.nlists), a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const long nout = n_rows * a.di;
+  kl_row_out_kernel<<<(unsigned)((nout + 255) / 256), 256, 0, st>>>(a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int nb = (l.T + l.B - 1) / l.B;
+  MSA_KL_DISPATCH(kl_dk_reduce_kernel, dim3((unsigned)nb, (unsigned)l.batch), a);
+#undef MSA_KL_DISPATCH
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -67,6 +67,7 @@ struct PrefillMainArgs {
   int t0, tc;             // query chunk
   int KS;                 // partial slots per (token, group) = min(topk, nb)
   int rank_bits;          // list entry = local token << rank_bits | slot; 2^rank_bits >= KS
+  int include_local;      // lists also hold each row's local block (entries b <= L(t))
   int nbl;                // block lists per (batch, group, window) = nb
   int nwin;               // windows in this chunk = ceil(tc / kListWindow)
   long nlists;            // batch * G * nwin * nbl
@@ -86,7 +87,36 @@ struct PrefillMainArgs {
   float2* pS;             // [entries*R] (max*c + e, sum * 2^-e), base-2 domain
 };
 hipError_t launch_prefill_main_sparse(const PrefillMainArgs& a, hipStream_t st);
+// Block lists of a chunk (cnt, offs, epos -> list positions, entries, rinfo)
+// and the work list of tiles of mt entries (a.work, a.n_work).
+hipError_t launch_block_lists(const PrefillMainArgs& a, int mt, hipStream_t st);
+// Another work list over the same lists, tiles of mt entries (a.bsum reused).
+hipError_t launch_list_work(const PrefillMainArgs& a, int mt, int2* work, int32_t* n_work, hipStream_t st);
 hipError_t launch_prefill_main_dense(const PrefillMainArgs& a, hipStream_t st);
+
+// ---- Indexer KL loss (training signal of the index branch) ----
+struct IndexerKlArgs {
+  PrefillMainArgs l;      // lists of the chunk (include_local = 1); q, k, scale used
+  const uint16_t* idx_q;  // [batch][T][G][di]
+  const uint16_t* idx_k;  // [batch][T][di]
+  const float* lse;       // [batch][T][Hq] main branch log-sum-exp (natural log)
+  int di;
+  float* kl;              // [batch][T][G]
+  float* d_idx_q;         // [batch][T][G][di]
+  float* d_idx_k;         // [batch][T][di]
+  bool accumulate_dk;     // add onto d_idx_k (query chunks after the first)
+  // workspace
+  int2* work_a;           // work list over tiles of 128 entries
+  int32_t* n_work_a;
+  long max_work_a;
+  float2* stat;           // [E] per entry (max, sum) of the index scores, base 2
+  float* lse_i;           // [batch*tc*G] per row index log2-sum-exp
+  uint16_t* ds;           // [E][B] bf16 p_I - p_M per entry and key
+  float* kl_e;            // [E] per entry KL term
+  float* dq_e;            // [E][di] per entry d idx_q term
+  float* dk_part;         // [nlists][B][di] per list d idx_k partial
+};
+hipError_t launch_indexer_kl(const IndexerKlArgs& a, hipStream_t st);
 
 // ---- Decode ----
 hipError_t launch_index_blockmax_decode(const uint16_t* idx_q, const uint16_t* idx_k,

@@ -104,6 +104,7 @@ const char* msa_stage_name(int32_t stage) {
     case MSA_STAGE_TOPK_DECODE: return "topk_decode_kernel";
     case MSA_STAGE_DECODE_ATTN: return "decode_attn_kernel";
     case MSA_STAGE_DECODE_COMBINE: return "decode_combine_kernel";
+    case MSA_STAGE_INDEXER_KL: return "indexer KL (lists, stats, entry, list, reduction kernels)";
     default: return "unknown stage";
   }
 }

@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kCountRows) void lists_count_kernel(PrefillMainArgs
       for (int u = 0; u < kSelChunk; ++u) {
         const int e = ev[u];
         has_local |= (e == L);
-        if (e >= 0 && e < L && rank < a.KS) {
+        if (e >= 0 && (e < L || (a.include_local && e == L)) && rank < a.KS) {
           const size_t lid = list_id(a, s, g, tl, e);
           uint32_t code = kDirect;
           if (use_lds) {
@@ -412,7 +412,7 @@ __global__ void lists_scatter_kernel(PrefillMainArgs a) {
 #pragma unroll
     for (int u = 0; u < kSelChunk; ++u) {
       const int e = ev[u];
-      if (e >= 0 && e < L && rank < a.KS) {
+      if (e >= 0 && (e < L || (a.include_local && e == L)) && rank < a.KS) {
         const size_t lid = list_id(a, s, g, tl, e);
         const size_t slot = (size_t)row * a.KS + rank;
         const int pos = a.offs[lid] + a.epos[slot];
@@ -828,25 +828,34 @@ hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t value, hipStream_t st) 
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_main_sparse(const PrefillMainArgs& a, hipStream_t st) {
-  prof_mark(st, MSA_STAGE_BLOCK_LISTS);
+hipError_t launch_list_work(const PrefillMainArgs& a, int mt, int2* work, int32_t* n_work, hipStream_t st) {
+  const int nblk = (int)((a.nlists + kScanItems - 1) / kScanItems);
+  lists_scan_reduce_kernel<<<nblk, 1024, 0, st>>>(a.cnt, a.bsum, a.nlists, mt);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  lists_scan_top_kernel<<<1, 1024, 0, st>>>(a.bsum, nblk, n_work);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  lists_scan_final_kernel<<<nblk, 1024, 0, st>>>(a.cnt, a.bsum, a.offs, work, a.nlists, mt);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_lists(const PrefillMainArgs& a, int mt, hipStream_t st) {
   hipError_t err = launch_fill_i32(a.cnt, (size_t)a.nlists, 0, st);
   if (err != hipSuccess) return err;
   const long n_rows = (long)a.batch * a.tc * a.G;
-  const unsigned rgrid = (unsigned)((n_rows + 255) / 256);
   lists_count_kernel<<<(unsigned)((n_rows + kCountRows - 1) / kCountRows), kCountRows, 0, st>>>(a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = launch_list_work(a, mt, a.work, a.n_work, st)) != hipSuccess) return err;
+  lists_scatter_kernel<<<(unsigned)((n_rows + 255) / 256), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_main_sparse(const PrefillMainArgs& a, hipStream_t st) {
+  prof_mark(st, MSA_STAGE_BLOCK_LISTS);
   const int R = a.Hq / a.G;
   const int mt = kAttnRows / R;
-  const int nblk = (int)((a.nlists + kScanItems - 1) / kScanItems);
-  lists_scan_reduce_kernel<<<nblk, 1024, 0, st>>>(a.cnt, a.bsum, a.nlists, mt);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  lists_scan_top_kernel<<<1, 1024, 0, st>>>(a.bsum, nblk, a.n_work);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  lists_scan_final_kernel<<<nblk, 1024, 0, st>>>(a.cnt, a.bsum, a.offs, a.work, a.nlists, mt);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  lists_scatter_kernel<<<rgrid, 256, 0, st>>>(a);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipError_t err = launch_block_lists(a, mt, st);
+  if (err != hipSuccess) return err;
   if (a.max_work > 0) {
     prof_mark(st, MSA_STAGE_KV_OUTER);
     const dim3 grid((unsigned)a.max_work);

@@ -111,17 +111,18 @@ __device__ __forceinline__ void select_best(const List& lst, int n, int want, in
     int base = 0, eq_seen = 0;
 #pragma unroll
     for (int i = 0; i < kRegKeys; ++i) {
-      if (i >= nch) break;  // wave-uniform
-      const int j = i * kWave + lane;
-      const bool in = j < n;
-      const bool eq = in && key[i] == tau;
-      const uint64_t beq = __ballot(eq);
-      const int eq_rank = eq_seen + popc(beq & lt);
-      const bool sel = in && (key[i] > tau || (eq && eq_rank < need));
-      const uint64_t bs = __ballot(sel);
-      if (sel) emit(base + popc(bs & lt), key[i], lst.b(j));
-      base += popc(bs);
-      eq_seen += popc(beq);
+      if (i < nch) {  // wave-uniform
+        const int j = i * kWave + lane;
+        const bool in = j < n;
+        const bool eq = in && key[i] == tau;
+        const uint64_t beq = __ballot(eq);
+        const int eq_rank = eq_seen + popc(beq & lt);
+        const bool sel = in && (key[i] > tau || (eq && eq_rank < need));
+        const uint64_t bs = __ballot(sel);
+        if (sel) emit(base + popc(bs & lt), key[i], lst.b(j));
+        base += popc(bs);
+        eq_seen += popc(beq);
+      }
     }
     return;
   }
@@ -181,16 +182,17 @@ __device__ __forceinline__ int compact_candidates(const float* __restrict__ srow
     const uint32_t lb = (want <= kWave) ? kth_largest_lanes(lmax, want) : 0u;
 #pragma unroll
     for (int i = 0; i < kRegKeys; ++i) {
-      if (i * kWave >= n) break;  // wave-uniform
-      const int j = i * kWave + lane;
-      const bool sv = j < n && key[i] >= lb;
-      const uint64_t bal = __ballot(sv);
-      const int pos = cnt + popc(bal & lt);
-      if (sv && pos < kCap) {
-        skey[pos] = key[i];
-        sblk[pos] = b0 + j;
+      if (i * kWave < n) {  // wave-uniform
+        const int j = i * kWave + lane;
+        const bool sv = j < n && key[i] >= lb;
+        const uint64_t bal = __ballot(sv);
+        const int pos = cnt + popc(bal & lt);
+        if (sv && pos < kCap) {
+          skey[pos] = key[i];
+          sblk[pos] = b0 + j;
+        }
+        cnt += popc(bal);
       }
-      cnt += popc(bal);
     }
   } else {
     uint32_t lmax = 0;

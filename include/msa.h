@@ -79,6 +79,7 @@ extern "C" {
 #define MSA_OP_INDEX_TOPK 0
 #define MSA_OP_PREFILL 1
 #define MSA_OP_DECODE 2
+#define MSA_OP_INDEXER_KL 3
 
 typedef struct msa_dims {
   int32_t batch;         /* sequences, >= 1 */
@@ -160,6 +161,41 @@ int msa_decode(const msa_dims* dims, const void* q, const void* k_cache,
                const int32_t* cache_lens, void* out, float* lse, int32_t* block_idx,
                void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/*
+ * Indexer KL loss and its gradient into the index-branch inputs: the signal
+ * that trains the Index Branch [Telegram review quant_prune_distill post 751,
+ * "Метод": KL between the index branch and the head-averaged main branch,
+ * stop-gradient through the main branch's probabilities and on the index
+ * inputs; hyper.ai paper page 2606.13392, 方法 (Method): KL on the selected
+ * tokens, gradient detach on the Index Branch inputs].
+ * Per (token t, group g) row, over the tokens J = {j <= t in the row's
+ * selected blocks}:
+ *   p_I(j) = softmax over J of idx_q[t,g] . idx_k[j]
+ *   p_M(j) = mean over the group's heads h of exp(scale q[t,h].k[j,g] - lse[t,h])
+ *   kl[t,g] = sum_j p_M(j) (ln p_M(j) - ln p_I(j))
+ * and, for the loss sum_{t,g} kl[t,g] with p_M held constant,
+ *   d_idx_q[t,g] = sum_j (p_I(j) - p_M(j)) idx_k[j]
+ *   d_idx_k[j]   = sum over rows using j of (p_I(j) - p_M(j)) idx_q[t,g]
+ *   q         [batch, T, Hq, d] bf16;  k [batch, T, G, d] bf16
+ *   idx_q     [batch, T, G, index_dim] bf16;  idx_k [batch, T, index_dim] bf16
+ *   block_idx [batch, T, G, topk] int32: the selection (e.g. msa_prefill's);
+ *             entries outside [0, L(t)] are ignored, valid entries must be
+ *             distinct
+ *   lse       [batch, T, Hq] fp32: the main branch's log-sum-exp over the same
+ *             selection (msa_prefill's lse output)
+ *   kl        [batch, T, G] fp32 OUTPUT (0 for a row without valid entries)
+ *   d_idx_q   [batch, T, G, index_dim] fp32 OUTPUT
+ *   d_idx_k   [batch, T, index_dim] fp32 OUTPUT (keys never selected get 0)
+ * dims: prefill shapes, flags must be 0; Hq / G must be a power of two <= 32
+ * (else MSA_ERR_UNSUPPORTED).  fp32 pointers 4-byte aligned.  dS = p_I - p_M
+ * enters the gradient products rounded to bf16 (fp32 accumulation).
+ * Deterministic: fixed-order sums, no atomics on values.
+ */
+int msa_indexer_kl(const msa_dims* dims, const void* q, const void* k, const void* idx_q,
+                   const void* idx_k, const int32_t* block_idx, const float* lse, float* kl,
+                   float* d_idx_q, float* d_idx_k, void* workspace, size_t workspace_bytes,
+                   void* hip_stream);
+
 /* Workspace bytes needed by op for dims (0 when none is needed).  Returns
    (size_t)-1 when dims are invalid for op. */
 size_t msa_workspace_bytes(int op, const msa_dims* dims);
@@ -199,7 +235,8 @@ int msa_abi_version(void);
 #define MSA_STAGE_TOPK_DECODE 7
 #define MSA_STAGE_DECODE_ATTN 8        /* per-(sequence, group) attention         */
 #define MSA_STAGE_DECODE_COMBINE 9     /* combine of the split partials (dense)   */
-#define MSA_STAGE_COUNT 10
+#define MSA_STAGE_INDEXER_KL 10        /* msa_indexer_kl, all of its kernels      */
+#define MSA_STAGE_COUNT 11
 
 typedef struct msa_stage_time {
   int32_t stage;

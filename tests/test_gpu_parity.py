@@ -528,3 +528,70 @@ def test_sink_decode(mode, L, B, k, lens):
     cond = orc.decode(dec.q, dec.k_cache, dec.v_cache, dec.idx_q, dec.idx_k_cache, lens, B, k, block_idx=bidx)
     check_attention(out.to(torch.float64).numpy(), cond["out"], "sink decode out")
 
+
+# ---------------------------------------------------------------------------
+# indexer KL loss and its gradient into idx_q / idx_k
+# ---------------------------------------------------------------------------
+KL_CASES = [
+    # T, Hq, G, di, B, k, query_chunk, batch
+    (1000, 16, 4, 64, 64, 6, 0, 1),     # R = 4
+    (777, 8, 8, 128, 32, 9, 256, 2),    # R = 1, several query chunks, batch 2
+    (600, 32, 4, 64, 128, 3, 0, 1),     # R = 8, one partial block per row beyond the local one
+]
+
+
+def _rel_close(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    mx = np.abs(got - ref).max()
+    scale = np.abs(ref).max()
+    mr = np.abs(got - ref).sum() / max(np.abs(ref).sum(), 1e-300)
+    say(f"  {what}: max-abs {mx:.3e} (of {scale:.3e})  mean-rel {mr:.3e}")
+    assert mx <= 1e-2 * scale, what
+    assert mr <= 5e-3, what
+
+
+@pytest.mark.parametrize("T,Hq,G,di,B,k,chunk,nb", KL_CASES)
+def test_indexer_kl_vs_oracle(T, Hq, G, di, B, k, chunk, nb):
+    say(f"[indexer KL] T={T} Hq={Hq} G={G} di={di} B={B} k={k} chunk={chunk} batch={nb}")
+    inp = inputs.make_prefill(T, Hq, G, 128, di, batch=nb, seed=800 + T)
+    _, lse, bidx = gpu_prefill(inp, B, k)
+    dims = bd.make_dims(nb, T, Hq, G, index_dim=di, block_size=B, topk=k, query_chunk=chunk)
+    kl = torch.full((nb, T, G), float("nan"), device="cuda")
+    dq = torch.full((nb, T, G, di), float("nan"), device="cuda")
+    dk = torch.full((nb, T, di), float("nan"), device="cuda")
+    bd.msa_indexer_kl(dims, inp.q.cuda(), inp.k.cuda(), inp.idx_q.cuda(), inp.idx_k.cuda(), bidx.cuda(),
+                      lse.cuda(), kl, dq, dk)
+    torch.cuda.synchronize()
+    ores = orc.indexer_kl(inp.q, inp.k, inp.idx_q, inp.idx_k, bidx, B)
+    kl_ref = np.stack([[ores["kl"][(s, t)] for t in range(T)] for s in range(nb)])
+    dq_ref = np.stack([[ores["d_idx_q"][(s, t)] for t in range(T)] for s in range(nb)])
+    kl_got = kl.cpu().double().numpy()
+    assert np.isfinite(kl_got).all()
+    err = np.abs(kl_got - kl_ref)
+    say(f"  kl: max-abs {err.max():.3e}  max |kl| {np.abs(kl_ref).max():.3e}")
+    assert (err <= 1e-3 * np.abs(kl_ref) + 1e-4).all()
+    _rel_close(dq.cpu().numpy(), dq_ref, "d_idx_q")
+    _rel_close(dk.cpu().numpy(), ores["d_idx_k"], "d_idx_k")
+
+
+def test_indexer_kl_deterministic_and_zero_case():
+    T, Hq, G, di, B, k = 900, 8, 2, 128, 64, 5
+    say("[indexer KL determinism]")
+    inp = inputs.make_prefill(T, Hq, G, 128, di, seed=811)
+    _, lse, bidx = gpu_prefill(inp, B, k)
+    dims = bd.make_dims(1, T, Hq, G, index_dim=di, block_size=B, topk=k)
+    outs = []
+    for _ in range(2):
+        kl = torch.empty((1, T, G), device="cuda")
+        dq = torch.empty((1, T, G, di), device="cuda")
+        dk = torch.empty((1, T, di), device="cuda")
+        bd.msa_indexer_kl(dims, inp.q.cuda(), inp.k.cuda(), inp.idx_q.cuda(), inp.idx_k.cuda(), bidx.cuda(),
+                          lse.cuda(), kl, dq, dk)
+        torch.cuda.synchronize()
+        outs.append((kl.cpu(), dq.cpu(), dk.cpu()))
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+    # t = 0 attends a single token: both distributions are a point mass
+    assert outs[0][0][0, 0].abs().max() < 1e-6 and outs[0][1][0, 0].abs().max() < 1e-6
+
