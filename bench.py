@@ -63,6 +63,29 @@ def prefill_flops(T, Hq, G, d, di, B, k):
     return index, main
 
 
+def indexer_kl_flops(T, Hq, G, d, di, B, k):
+    """Per (row, attended token): the index score (2 di), the R heads' logits
+    (2 d R), and the two gradient products (2 di each)."""
+    t = np.arange(T, dtype=np.float64)
+    L = np.floor(t / B)
+    att = (t % B) + 1 + B * np.minimum(k - 1, L)
+    return G * (6.0 * di + 2.0 * d * (Hq // G)) * att.sum()
+
+
+def indexer_kl_ms(pin, bidx, lse, dev, stream, reps):
+    T, Hq, G, di = PF["T"], PF["Hq"], PF["G"], PF["di"]
+    kd = bd.make_dims(1, T, Hq, G, index_dim=di, block_size=PF["B"], topk=PF["k"])
+    kl = torch.empty((1, T, G), dtype=torch.float32, device=dev)
+    dq = torch.empty((1, T, G, di), dtype=torch.float32, device=dev)
+    dk = torch.empty((1, T, di), dtype=torch.float32, device=dev)
+    kws = torch.empty(bd.msa_workspace_bytes(bd.MSA_OP_INDEXER_KL, kd), dtype=torch.uint8, device=dev)
+    fn = lambda: bd.msa_indexer_kl(kd, pin.q, pin.k, pin.idx_q, pin.idx_k, bidx, lse, kl, dq, dk,  # noqa: E731
+                                   workspace=kws)
+    fn()
+    ms, _ = timed(fn, reps, stream)
+    return ms
+
+
 def dense_prefill_flops(T, Hq, d):
     return 4.0 * Hq * d * T * (T + 1) / 2
 
@@ -132,7 +155,8 @@ def measured_peaks(dev):
 
 def profile_kernels_only(args, dev):
     """The 128K prefill's inputs, one calibration copy of COPY_BYTES, then
-    --steps prefills and --steps decode steps (8 x 1M context), every kernel
+    --steps prefills, --steps indexer KL calls on the last prefill's selection
+    (+1 warmup) and --steps decode steps (8 x 1M context), every kernel
     launched as in the timed steps: the workload of the --pmc counter passes
     and of the kernel-trace summary."""
     stream = torch.cuda.current_stream()
@@ -145,10 +169,13 @@ def profile_kernels_only(args, dev):
     y = torch.empty_like(x)
     torch.cuda.synchronize()
     y.copy_(x)
+    plse = torch.empty((1, PF["T"], PF["Hq"]), dtype=torch.float32, device=dev)
+    pbidx = torch.empty((1, PF["T"], PF["G"], PF["k"]), dtype=torch.int32, device=dev)
     bd.msa_profile_begin()
-    ms, _ = timed(lambda: bd.msa_prefill(pdims, pin.q, pin.k, pin.v, pin.idx_q, pin.idx_k, pout, workspace=pws),
-                  args.steps, stream)
+    ms, _ = timed(lambda: bd.msa_prefill(pdims, pin.q, pin.k, pin.v, pin.idx_q, pin.idx_k, pout, lse=plse,
+                                         block_idx=pbidx, workspace=pws), args.steps, stream)
     del pws
+    kms = indexer_kl_ms(pin, pbidx, plse, dev, stream, args.steps)
     dec = inputs.make_decode(DC["batch"], DC["L"], DC["Hq"], DC["G"], DC["d"], DC["di"], seed=DC["seed"],
                              device=dev)
     ddims = bd.make_dims(DC["batch"], DC["L"], DC["Hq"], DC["G"], index_dim=DC["di"], block_size=DC["B"],
@@ -160,6 +187,7 @@ def profile_kernels_only(args, dev):
     dms, _ = timed(dfn, args.steps, stream)
     stages = bd.msa_profile_end()
     print(json.dumps({"profile_steps": args.steps, "prefill_ms": round(ms, 4), "decode_ms": round(dms, 4),
+                      "indexer_kl_ms": round(kms, 4),
                       "copy_bytes": COPY_BYTES,
                       "stage_ms": {n: round(t / c, 4) for n, (c, t) in stages.items()}}), flush=True)
 
@@ -472,6 +500,12 @@ def main():
         fn()
         ms, _ = timed(fn, 10, stream)
         variants["decode_8x1m_sink"] = {"ms": round(ms, 4), "tok_s": round(DC["batch"] / (ms * 1e-3), 1)}
+        # indexer KL loss + gradient on the headline prefill's own selection and lse
+        ms = indexer_kl_ms(pin, pbidx, plse, dev, stream, 3)
+        kl_flops = indexer_kl_flops(PF["T"], PF["Hq"], PF["G"], PF["d"], PF["di"], PF["B"], PF["k"])
+        variants["indexer_kl_t131072"] = {"ms": round(ms, 3), "tok_s": round(PF["T"] / (ms * 1e-3), 1),
+                                          "algorithmic_tflop": round(kl_flops / 1e12, 3),
+                                          "tflops": round(kl_flops / (ms * 1e-3) / 1e12, 2)}
         log(f"variants: {variants}")
 
     peaks = measured_peaks(dev)

@@ -60,6 +60,15 @@ __device__ __forceinline__ void stage_rows(bf16_t* dst, int ldsr, const bf16_t* 
   }
 }
 
+// 4x4 transpose of 16-bit values: r[i] holds 4 values of row i; o[j] gets
+// column j (rows 0..3).
+__device__ __forceinline__ void transpose4x4(const u32x2 (&r)[4], u32x2 (&o)[4]) {
+  o[0] = u32x2{(r[0][0] & 0xffffu) | (r[1][0] << 16), (r[2][0] & 0xffffu) | (r[3][0] << 16)};
+  o[1] = u32x2{(r[0][0] >> 16) | (r[1][0] & 0xffff0000u), (r[2][0] >> 16) | (r[3][0] & 0xffff0000u)};
+  o[2] = u32x2{(r[0][1] & 0xffffu) | (r[1][1] << 16), (r[2][1] & 0xffffu) | (r[3][1] << 16)};
+  o[3] = u32x2{(r[0][1] >> 16) | (r[1][1] & 0xffff0000u), (r[2][1] >> 16) | (r[3][1] & 0xffff0000u)};
+}
+
 // S^T tile (32 keys x 32 rows) = A[32 keys x C] . Qop^T, A rows from LDS.
 template <int C>
 __device__ __forceinline__ f32x16 logit_tile(const bf16_t* As, int ldsr, int key0, const bf16x8* qop, int col,
@@ -309,11 +318,21 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
   }
   auto at_rank = [&](int i) -> int { return sorted ? (int)(uint32_t)order[i] : i; };
 
-  // idx_k block, transposed: IkT[c][key]
-  for (int u = tid; u < BS * DI; u += 256) {
-    const int key = u / DI, cc = u % DI;
-    IkT[cc * IKR + key] = key < nkey ? a.idx_k[((size_t)s * l.T + kb + key) * DI + cc] : bf16_t(0);
+  // idx_k block, transposed: IkT[c][key], in 4 keys x 4 c units
+  for (int u = tid; u < (BS / 4) * (DI / 4); u += 256) {
+    const int k4 = u / (DI / 4), c4 = u % (DI / 4);
+    u32x2 r[4], o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = 4 * k4 + i;
+      r[i] = key < nkey ? *reinterpret_cast<const u32x2*>(a.idx_k + ((size_t)s * l.T + kb + key) * DI + 4 * c4)
+                        : u32x2{0u, 0u};
+    }
+    transpose4x4(r, o);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(IkT + (4 * c4 + j) * IKR + 4 * k4) = o[j];
   }
+  __shared__ int qrow[EC];  // idx_q row offsets of the chunk's entries
 
   f32x16 dk[TPW];
 #pragma unroll
@@ -322,21 +341,42 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
   for (int c0 = 0; c0 < count; c0 += EC) {
     const int n = min(EC, count - c0);
     __syncthreads();  // the previous chunk's LDS reads are done (and IkT is written)
-    for (int u = tid; u < EC * BS; u += 256) {
-      const int en = u / BS, key = u % BS;
-      const bf16_t v = en < n ? a.ds[(size_t)(off + at_rank(c0 + en)) * BS + key] : bf16_t(0);
-      Dr[en * DRR + key] = v;
-      DT[key * ER + en] = v;
-    }
-    for (int u = tid; u < EC * DI; u += 256) {
-      const int en = u / DI, cc = u % DI;
-      bf16_t v = bf16_t(0);
-      if (en < n) {
-        const int ent = l.entries[off + at_rank(c0 + en)];
-        const int t = l.t0 + (ent >> l.rank_bits);
-        v = a.idx_q[(((size_t)s * l.T + t) * l.G + g) * DI + cc];
+    if (tid < EC) {
+      int qr = -1;
+      if (tid < n) {
+        const int ent = l.entries[off + at_rank(c0 + tid)];
+        qr = (int)(((size_t)s * l.T + l.t0 + (ent >> l.rank_bits)) * l.G + g);
       }
-      QT[cc * ER + en] = v;
+      qrow[tid] = qr;
+    }
+    // dS rows of the chunk, row-major and transposed, in 4 entries x 4 keys units
+    for (int u = tid; u < (EC / 4) * (BS / 4); u += 256) {
+      const int e4 = u / (BS / 4), k4 = u % (BS / 4);
+      u32x2 r[4], o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int en = 4 * e4 + i;
+        r[i] = en < n ? *reinterpret_cast<const u32x2*>(a.ds + (size_t)(off + at_rank(c0 + en)) * BS + 4 * k4)
+                      : u32x2{0u, 0u};
+        *reinterpret_cast<u32x2*>(Dr + en * DRR + 4 * k4) = r[i];
+      }
+      transpose4x4(r, o);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(DT + (4 * k4 + j) * ER + 4 * e4) = o[j];
+    }
+    __syncthreads();  // qrow
+    // idx_q rows of the chunk, transposed: QT[c][entry]
+    for (int u = tid; u < (EC / 4) * (DI / 4); u += 256) {
+      const int e4 = u / (DI / 4), c4 = u % (DI / 4);
+      u32x2 r[4], o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qr = qrow[4 * e4 + i];
+        r[i] = qr >= 0 ? *reinterpret_cast<const u32x2*>(a.idx_q + (size_t)qr * DI + 4 * c4) : u32x2{0u, 0u};
+      }
+      transpose4x4(r, o);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(QT + (4 * c4 + j) * ER + 4 * e4) = o[j];
     }
     __syncthreads();
     // d idx_q of the chunk's entries: [entry][c] = sum_key dS[entry][key] idx_k[key][c]
@@ -416,20 +456,45 @@ __global__ void kl_row_out_kernel(IndexerKlArgs a) {
 // ---------------------------------------------------------------------------
 template <int DI, int BS>
 __global__ __launch_bounds__(256) void kl_dk_reduce_kernel(IndexerKlArgs a) {
+  constexpr int kMaxLists = 1024;  // lists of the block staged at a time
+  __shared__ long lids[kMaxLists];
+  __shared__ int nl;
   const PrefillMainArgs& l = a.l;
   const int b = blockIdx.x, s = blockIdx.y;
   const int kb = b * l.B;
   const int nkey = min(BS, l.T - kb);
-  for (int u = threadIdx.x; u < nkey * DI; u += 256) {
-    const int key = u / DI, cc = u % DI;
-    float acc = 0.f;
-    for (int g = 0; g < l.G; ++g)
-      for (int w = 0; w < l.nwin; ++w) {
-        const size_t lid = (((size_t)s * l.G + g) * l.nwin + w) * l.nbl + b;
-        if (l.cnt[lid] > 0) acc += a.dk_part[lid * BS * DI + (size_t)key * DI + cc];
+  const int nall = l.G * l.nwin;  // lists of this key block, in (group, window) order
+  float acc[(BS * DI + 255) / 256];
+#pragma unroll
+  for (int i = 0; i < (BS * DI + 255) / 256; ++i) acc[i] = 0.f;
+  for (int base = 0; base < nall; base += kMaxLists) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int n = 0;
+      for (int x = base; x < min(nall, base + kMaxLists); ++x) {
+        const size_t lid = (((size_t)s * l.G + x / l.nwin) * l.nwin + x % l.nwin) * l.nbl + b;
+        if (l.cnt[lid] > 0) lids[n++] = (long)lid;
       }
-    float* dst = a.d_idx_k + ((size_t)s * l.T + kb + key) * DI + cc;
-    *dst = a.accumulate_dk ? *dst + acc : acc;
+      nl = n;
+    }
+    __syncthreads();
+    const int n = nl;
+    for (int x = 0; x < n; ++x) {
+      const float* part = a.dk_part + (size_t)lids[x] * BS * DI;
+#pragma unroll
+      for (int i = 0; i < (BS * DI + 255) / 256; ++i) {
+        const int u = threadIdx.x + 256 * i;
+        if (u < nkey * DI) acc[i] += part[u];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < (BS * DI + 255) / 256; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    if (u < nkey * DI) {
+      float* dst = a.d_idx_k + ((size_t)s * l.T + kb) * DI + u;
+      *dst = a.accumulate_dk ? *dst + acc[i] : acc[i];
+    }
   }
 }
 
