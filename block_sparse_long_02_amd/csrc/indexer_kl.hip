@@ -21,9 +21,9 @@
 //  1. kl_index_stats_kernel: per list entry, the max and sum of 2^(s log2 e)
 //     over the block's keys <= t (MFMA, tiles of 128 entries);
 //  2. kl_row_lse_kernel: per row, the index log-sum-exp (fixed slot order);
-//  3. kl_entry_kernel: per entry, the R heads' logits and the index logits on
-//     MFMA in one layout, p_M (mean over the R head lanes), p_I, the entry's
-//     KL term and dS (bf16, row-major per entry);
+//  3. kl_entry_kernel: per entry, the R heads' logits (summed in the lane)
+//     and the index logits on MFMA, p_M, p_I, the entry's KL term and dS
+//     (bf16, row-major per entry);
 //  4. kl_list_kernel: per list, d idx_q of each entry (dS . idx_k) and the
 //     list's d idx_k partial (dS^T . idx_q) on MFMA;
 //  5. kl_row_out_kernel / kl_dk_reduce_kernel: fixed-order sums per row and
@@ -166,33 +166,31 @@ __global__ void kl_row_lse_kernel(IndexerKlArgs a) {
 // ---------------------------------------------------------------------------
 // 3. Per entry: the main branch's and the index branch's distributions over
 //    the block's keys, the entry's KL term and dS = p_I - p_M (bf16).  Tiles
-//    of 128/R tokens x R heads, as the block-major attention kernel; the
-//    index operand of a row is its token's idx_q, so both logit tiles share
-//    one layout and p_M is a sum over the R head lanes of a token.
+//    of 128 entries (4 waves x 32, one entry per MFMA column); the R heads of
+//    the group are visited in turn and their exp(x - lse) summed in the lane,
+//    so p_M needs no cross-lane work and the index logits are computed once.
 // ---------------------------------------------------------------------------
 template <int DI, int BS>
 __global__ __launch_bounds__(256, 2) void kl_entry_kernel(IndexerKlArgs a) {
   constexpr int KROW = D + 8, KP = DI + 8;
   constexpr int KT = BS / 32;
+  constexpr int KC = KT < 2 ? KT : 2;
+  constexpr int MT = 128;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[BS * KROW];
   __shared__ __attribute__((aligned(16))) bf16_t Is[BS * KP];
   const PrefillMainArgs& l = a.l;
   const int w = blockIdx.x;
-  if (w >= l.n_work[0]) return;
-  const int2 wk = l.work[w];
+  if (w >= a.n_work_a[0]) return;
+  const int2 wk = a.work_a[w];
   int b, g, s;
   const size_t lid = kl_list_of(l, wk.x, &b, &g, &s);
   const int R = l.Hq / l.G;
-  const int mt = kAttnRows / R;
   const int count = l.cnt[lid];
   const int off = l.offs[lid];
   const int tile0 = wk.y * kTilesPerItem;
-  const int ntile = min(kTilesPerItem, (count + mt - 1) / mt - tile0);
+  const int ntile = min(kTilesPerItem, (count + MT - 1) / MT - tile0);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
-  const int row = wave * 32 + col;
-  const int e = row / R, r = row % R;
-  const int h = g * R + r;
   const int kb = b * l.B;
   const size_t kvstride = (size_t)l.G * D;
   const int nkey = min(BS, l.T - kb);
@@ -203,59 +201,67 @@ __global__ __launch_bounds__(256, 2) void kl_entry_kernel(IndexerKlArgs a) {
   const float invR = 1.0f / (float)R;
 
   for (int it = 0; it < ntile; ++it) {
-    const int pos = (tile0 + it) * mt + e;
-    const bool valid = e < mt && pos < count;
+    const int pos = (tile0 + it) * MT + wave * 32 + col;
+    const bool valid = pos < count;
     const int ent = l.entries[off + min(pos, count - 1)];
     const int tl = ent >> l.rank_bits;
     const int t = l.t0 + tl;
-    bf16x8 qop[D / 16], iop[DI / 16];
-    const bf16_t* qp = l.q + (((size_t)s * l.T + t) * l.Hq + h) * D;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qop[ks] = load_bf16x8(qp + 16 * ks + 8 * half);
+    const size_t qrow = ((size_t)s * l.T + t) * l.Hq + (size_t)g * R;  // first head of the group
+    bf16x8 iop[DI / 16];
     const bf16_t* ip = a.idx_q + (((size_t)s * l.T + t) * l.G + g) * DI;
 #pragma unroll
     for (int ks = 0; ks < DI / 16; ++ks) iop[ks] = load_bf16x8(ip + 16 * ks + 8 * half);
-    const float lse2_h = a.lse[((size_t)s * l.T + t) * l.Hq + h] * kLog2e;
     const float lse2_i = a.lse_i[((size_t)s * l.tc + tl) * l.G + g];
-    float kl = 0.f;
     bf16_t* dsrow = a.ds + (size_t)(off + min(pos, count - 1)) * BS;
-    const bool writer = valid && r == 0;
+    float kl = 0.f;
+    // chunks of KC key tiles keep the accumulators few and statically indexed
 #pragma unroll 1
-    for (int kt = 0; kt < KT; ++kt) {
-      const f32x16 x = logit_tile<D>(Ks, KROW, kt * 32, qop, col, half);
-      const f32x16 si = logit_tile<DI>(Is, KP, kt * 32, iop, col, half);
-      float pm[16], ds[16];
+    for (int k0 = 0; k0 < KT; k0 += KC) {
+      float pm[KC][16];  // sum over the heads of exp(x - lse): R * p_M
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = kb + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        pm[i] = (j <= t) ? __builtin_amdgcn_exp2f(x[i] * c - lse2_h) : 0.f;
+      for (int kt = 0; kt < KC; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pm[kt][i] = 0.f;
+#pragma unroll 1
+      for (int r = 0; r < R; ++r) {
+        bf16x8 qop[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) qop[ks] = load_bf16x8(l.q + (qrow + r) * D + 16 * ks + 8 * half);
+        const float lse2 = a.lse[qrow + r] * kLog2e;
+#pragma unroll
+        for (int kt = 0; kt < KC; ++kt) {
+          const f32x16 x = logit_tile<D>(Ks, KROW, (k0 + kt) * 32, qop, col, half);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pm[kt][i] += __builtin_amdgcn_exp2f(x[i] * c - lse2);
+        }
       }
-      // mean over the R head lanes of the token (aligned groups of R lanes)
-      for (int o = 1; o < R; o <<= 1)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pm[i] += __shfl_xor(pm[i], o, kWave);
+      for (int kt = 0; kt < KC; ++kt) {
+        const f32x16 si = logit_tile<DI>(Is, KP, (k0 + kt) * 32, iop, col, half);
+        float ds[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = kb + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        const bool ok = j <= t;
-        const float p_m = pm[i] * invR;
-        const float l2pi = si[i] * kLog2e - lse2_i;
-        const float p_i = ok ? __builtin_amdgcn_exp2f(l2pi) : 0.f;
-        if (ok && p_m > 0.f) kl += p_m * (__log2f(p_m) - l2pi);
-        ds[i] = p_i - p_m;
-      }
-      if (writer) {
+        for (int i = 0; i < 16; ++i) {
+          const int j = kb + (k0 + kt) * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+          const bool ok = j <= t;
+          const float p_m = ok ? pm[kt][i] * invR : 0.f;
+          const float l2pi = si[i] * kLog2e - lse2_i;
+          const float p_i = ok ? __builtin_amdgcn_exp2f(l2pi) : 0.f;
+          if (ok && p_m > 0.f) kl += p_m * (__log2f(p_m) - l2pi);
+          ds[i] = p_i - p_m;
+        }
+        if (valid) {
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          bf16x4 v;
+          for (int i4 = 0; i4 < 4; ++i4) {
+            bf16x4 v;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] = (__bf16)ds[4 * i4 + u];
-          *reinterpret_cast<bf16x4*>(dsrow + kt * 32 + 8 * i4 + 4 * half) = v;
+            for (int u = 0; u < 4; ++u) v[u] = (__bf16)ds[4 * i4 + u];
+            *reinterpret_cast<bf16x4*>(dsrow + (k0 + kt) * 32 + 8 * i4 + 4 * half) = v;
+          }
         }
       }
     }
     kl += __shfl_xor(kl, 32, kWave);
-    if (writer && half == 0) a.kl_e[off + pos] = kl * kLn2;
+    if (valid && half == 0) a.kl_e[off + pos] = kl * kLn2;
   }
 }
 
@@ -524,7 +530,7 @@ hipError_t launch_indexer_kl(const IndexerKlArgs& a, hipStream_t st) {
   if ((err = hipGetLastError()) != hipSuccess) return err;
   kl_row_lse_kernel<<<(unsigned)((n_rows + 255) / 256), 256, 0, st>>>(a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (l.max_work > 0) MSA_KL_DISPATCH(kl_entry_kernel, dim3((unsigned)l.max_work), a);
+  if (a.max_work_a > 0) MSA_KL_DISPATCH(kl_entry_kernel, dim3((unsigned)a.max_work_a), a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   MSA_KL_DISPATCH(kl_list_kernel, dim3((unsigned)l.nlists), a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
