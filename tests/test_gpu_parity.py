@@ -537,6 +537,9 @@ KL_CASES = [
     (1000, 16, 4, 64, 64, 6, 0, 1),     # R = 4
     (777, 8, 8, 128, 32, 9, 256, 2),    # R = 1, several query chunks, batch 2
     (600, 32, 4, 64, 128, 3, 0, 1),     # R = 8, one partial block per row beyond the local one
+    (700, 64, 8, 128, 128, 4, 0, 1),    # the 128K workload's heads, index dim and block size
+    (520, 32, 2, 128, 64, 4, 0, 1),     # R = 16
+    (450, 32, 1, 64, 32, 7, 0, 1),      # R = 32, one group
 ]
 
 
