@@ -27,6 +27,9 @@ are exact in float64):
                  g = floor(h / R) over the keys of the selected blocks that
                  are <= t, scale 1/sqrt(d)                    [HA 方法; HN]
   decode_row     the same for the one new token at position len-1 of a cache
+  attention_backward
+                 the gradient of the main branch's output with the selection
+                 held fixed: dq, dk, dv from d out       [HA 方法; TG Метод]
   indexer_kl     KL(p_M || p_I) per (token, group) row over the selected tokens,
                  p_I the softmax of the index scores, p_M the main branch's
                  head-averaged attention (held constant), and its gradient
@@ -325,3 +328,57 @@ def indexer_kl(q, k, idx_q, idx_k, block_idx, B: int, scale: float | None = None
         res["kl"][(s, t)] = kl_t
         res["d_idx_q"][(s, t)] = dq_t
     return res
+
+
+def attention_backward(q, k, v, dout, block_idx, B: int, scale: float | None = None):
+    """Gradient of the main branch's output with respect to q, k and v, the
+    selection held fixed.
+
+    The selection is a top-k of block maxima, piecewise constant in the index
+    inputs, and the index branch is trained only through its own loss with
+    its inputs detached [TG Метод: stop-gradient on the index branch; HA 方法:
+    gradient detach on the Index Branch inputs].  So the main branch is
+    differentiated as the plain softmax attention it is on the fixed token set
+    J of each row [HA 方法: standard scaled dot-product attention over the
+    gathered Key/Value vectors].  Per (s, t, h), g = floor(h / R), J = the
+    tokens <= t of the row's selected blocks (entries outside [0, L(t)]
+    ignored, as in the given-selection prefill), x_j = scale q[t,h] . k[j,g],
+    P = softmax_J(x), o = sum_j P_j v[j,g]; for a loss with d loss / d o = dO:
+      dv[j,g] += P_j dO
+      dP_j     = dO . v[j,g]
+      dx_j     = P_j (dP_j - sum_i P_i dP_i)
+      dq[t,h]  = scale sum_j dx_j k[j,g]
+      dk[j,g] += scale dx_j q[t,h]
+    A row with nothing to attend contributes nothing.
+
+    q, dout [b,T,Hq,d]; k, v [b,T,G,d]; block_idx [b,T,G,topk].
+    Returns (dq [b,T,Hq,d], dk [b,T,G,d], dv [b,T,G,d]) in float64.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    sel_all = np.asarray(_f64(block_idx), dtype=np.int64)
+    nbatch, T, Hq, d = q.shape
+    G = k.shape[2]
+    R = Hq // G
+    if scale is None:
+        scale = default_scale(d)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for s in range(nbatch):
+        for t in range(T):
+            for g in range(G):
+                toks = selected_tokens(sel_all[s, t, g], t, B)
+                if len(toks) == 0:
+                    continue
+                heads = slice(g * R, (g + 1) * R)
+                Kg, Vg = k[s, toks, g], v[s, toks, g]          # [n, d]
+                x = scale * (q[s, t, heads] @ Kg.T)            # [R, n]
+                P = np.exp(x - x.max(axis=1, keepdims=True))
+                P /= P.sum(axis=1, keepdims=True)
+                dO = dout[s, t, heads]                         # [R, d]
+                dP = dO @ Vg.T                                 # [R, n]
+                dx = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                dq[s, t, heads] = scale * (dx @ Kg)
+                np.add.at(dk[s, :, g], toks, scale * (dx.T @ q[s, t, heads]))
+                np.add.at(dv[s, :, g], toks, P.T @ dO)
+    return dq, dk, dv

@@ -520,3 +520,132 @@ def test_kl_gradient_finite_differences():
         b[0, j, c] -= eps
         fd = (loss(iq, a) - loss(iq, b)) / (2 * eps)
         assert abs(fd - res["d_idx_k"][0, j, c]) < 1e-6 * max(1.0, abs(fd)), (j, c)
+
+
+# --------------------------------------------------------------------------
+# Backward of the main branch (selection held fixed).
+# --------------------------------------------------------------------------
+def _random_selection(T, G, B, k, rng, drop_local=False, junk=False):
+    """Valid distinct entries per row (local block first unless dropped), -1
+    padded; junk adds out-of-range entries that must be ignored."""
+    bidx = np.full((1, T, G, k), -1, dtype=np.int32)
+    for t in range(T):
+        L = t // B
+        for g in range(G):
+            cand = list(rng.permutation(L)[: k - 1]) if L > 0 else []
+            sel = ([] if (drop_local and t % 5 == 3) else [L]) + cand
+            if junk and len(sel) < k and t % 3 == 0:
+                sel.append(L + 1 + (t % 4))
+            bidx[0, t, g, : len(sel)] = sel
+    return bidx
+
+
+def _sel_mask(bidx, T, Hq, G, B):
+    """Boolean attention mask [1, Hq, T, T] of the selected tokens <= t."""
+    R = Hq // G
+    m = torch.zeros(1, Hq, T, T, dtype=torch.bool)
+    for t in range(T):
+        for g in range(G):
+            for b in bidx[0, t, g]:
+                if 0 <= b <= t // B:
+                    m[0, g * R:(g + 1) * R, t, b * B:min((b + 1) * B, t + 1)] = True
+    return m
+
+
+def _sdpa_grads(inp, dout, mask=None):
+    q = inp.q.to(torch.float64).transpose(1, 2).clone().requires_grad_(True)
+    k = inp.k.to(torch.float64).transpose(1, 2).clone().requires_grad_(True)
+    v = inp.v.to(torch.float64).transpose(1, 2).clone().requires_grad_(True)
+    if mask is None:
+        o = F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=True)
+    else:
+        o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, enable_gqa=True)
+    o.backward(dout.to(torch.float64).transpose(1, 2))
+    return [_np(x.grad.transpose(1, 2)) for x in (q, k, v)]
+
+
+@pytest.mark.parametrize("T,Hq,G,d,B", [(96, 4, 2, 16, 16), (70, 6, 3, 8, 32)])
+def test_backward_dense_equals_sdpa_autograd(T, Hq, G, d, B):
+    """All visible blocks selected: the gradient of dense causal GQA attention,
+    by torch autograd through SDPA in fp64."""
+    inp = inputs.make_prefill(T, Hq, G, d, 8, seed=61)
+    dout = torch.randn(1, T, Hq, d, generator=torch.Generator().manual_seed(62), dtype=torch.float64)
+    nb = (T + B - 1) // B
+    bidx = np.tile(np.arange(nb, dtype=np.int32), (1, T, G, 1))
+    dq, dk, dv = orc.attention_backward(inp.q, inp.k, inp.v, dout, bidx, B)
+    rq, rk, rv = _sdpa_grads(inp, dout)
+    for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("drop_local,junk", [(False, False), (True, True)])
+def test_backward_sparse_equals_masked_sdpa_autograd(drop_local, junk):
+    """Random selections (some rows without their local block, some with
+    out-of-range entries): the gradient of SDPA with the selection as a
+    boolean mask, by torch autograd in fp64."""
+    T, Hq, G, d, B, k = 80, 4, 2, 8, 8, 3
+    rng = np.random.default_rng(63)
+    inp = inputs.make_prefill(T, Hq, G, d, 8, seed=64)
+    dout = torch.randn(1, T, Hq, d, generator=torch.Generator().manual_seed(65), dtype=torch.float64)
+    bidx = _random_selection(T, G, B, k, rng, drop_local=drop_local, junk=junk)
+    mask = _sel_mask(bidx, T, Hq, G, B)
+    empty = ~mask.any(dim=-1)                      # rows with nothing to attend
+    assert not drop_local or empty.any()
+    safe = mask.clone()
+    safe[empty.unsqueeze(-1).expand_as(safe) & (torch.arange(T) == 0)] = True  # keep SDPA finite
+    d_safe = dout.clone()
+    d_safe[empty.transpose(1, 2)] = 0.0            # such rows get no gradient
+    dq, dk, dv = orc.attention_backward(inp.q, inp.k, inp.v, d_safe, bidx, B)
+    rq, rk, rv = _sdpa_grads(inp, d_safe, mask=safe)
+    rq[empty.transpose(1, 2).numpy()] = 0.0
+    for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
+    # and the oracle itself leaves empty rows at zero whatever dout holds
+    dq2, _, _ = orc.attention_backward(inp.q, inp.k, inp.v, dout, bidx, B)
+    assert np.abs(dq2[empty.transpose(1, 2).numpy()]).max(initial=0.0) == 0.0
+
+
+def test_backward_finite_differences():
+    """Central differences of sum(dout * out) over every input coordinate, the
+    output from the oracle's own forward on the same fixed selection."""
+    T, Hq, G, d, B, k = 9, 4, 2, 3, 4, 2
+    rng = np.random.default_rng(66)
+    inp = inputs.make_prefill(T, Hq, G, d, 8, seed=67)
+    q, kk, v = _np(inp.q), _np(inp.k), _np(inp.v)
+    dout = rng.standard_normal((1, T, Hq, d))
+    bidx = _random_selection(T, G, B, k, rng)
+
+    def loss(q_, k_, v_):
+        r = orc.prefill(q_, k_, v_, inp.idx_q, inp.idx_k, B, k, block_idx=bidx)
+        return sum(float((r["out"][(0, t)] * dout[0, t]).sum()) for t in range(T))
+
+    dq, dk, dv = orc.attention_backward(q, kk, v, dout, bidx, B)
+    h = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        base = [q, kk, v]
+        num = np.zeros_like(grad)
+        for idx in np.ndindex(grad.shape):
+            xp = [x.copy() for x in base]
+            xm = [x.copy() for x in base]
+            xp[which][idx] += h
+            xm[which][idx] -= h
+            num[idx] = (loss(*xp) - loss(*xm)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8)
+
+
+def test_backward_invariants():
+    """Softmax rows sum to one: per (sequence, group) the key gradients sum to
+    zero and the value gradients sum to the d out of the non-empty rows."""
+    T, Hq, G, d, B, k = 150, 6, 2, 16, 16, 4
+    rng = np.random.default_rng(68)
+    inp = inputs.make_prefill(T, Hq, G, d, 8, batch=2, seed=69)
+    dout = rng.standard_normal((2, T, Hq, d))
+    bidx = np.concatenate([_random_selection(T, G, B, k, rng, drop_local=True) for _ in range(2)])
+    dq, dk, dv = orc.attention_backward(inp.q, inp.k, inp.v, dout, bidx, B)
+    R = Hq // G
+    for s in range(2):
+        for g in range(G):
+            np.testing.assert_allclose(dk[s, :, g].sum(axis=0), 0.0, atol=1e-10)
+            rows = [t for t in range(T) if any(0 <= b <= t // B for b in bidx[s, t, g])]
+            ref = dout[s, rows][:, g * R:(g + 1) * R].sum(axis=(0, 1))
+            np.testing.assert_allclose(dv[s, :, g].sum(axis=0), ref, atol=1e-10)
