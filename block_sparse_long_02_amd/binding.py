@@ -31,6 +31,7 @@ MSA_OP_INDEX_TOPK = 0
 MSA_OP_PREFILL = 1
 MSA_OP_DECODE = 2
 MSA_OP_INDEXER_KL = 3
+MSA_OP_BACKWARD = 4
 
 MSA_STAGE_INDEX_PREFILL = 0
 MSA_STAGE_TOPK_PREFILL = 1
@@ -43,11 +44,14 @@ MSA_STAGE_TOPK_DECODE = 7
 MSA_STAGE_DECODE_ATTN = 8
 MSA_STAGE_DECODE_COMBINE = 9
 MSA_STAGE_INDEXER_KL = 10
-MSA_STAGE_COUNT = 11
+MSA_STAGE_BWD_PREP = 11
+MSA_STAGE_BWD_LISTS = 12
+MSA_STAGE_BWD_MERGE = 13
+MSA_STAGE_COUNT = 14
 
 EXPORTED = ("msa_index_scores", "msa_index_topk", "msa_prefill", "msa_decode", "msa_workspace_bytes",
             "msa_status_string", "msa_last_hip_error", "msa_abi_version", "msa_profile_begin",
-            "msa_profile_end", "msa_stage_name", "msa_indexer_kl")
+            "msa_profile_end", "msa_stage_name", "msa_indexer_kl", "msa_prefill_backward")
 
 
 class msa_stage_time(ctypes.Structure):
@@ -114,6 +118,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_abi_version.restype = i32
     lib.msa_indexer_kl.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_indexer_kl.restype = i32
+    lib.msa_prefill_backward.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_prefill_backward.restype = i32
     lib.msa_profile_begin.argtypes = []
     lib.msa_profile_begin.restype = i32
     lib.msa_profile_end.argtypes = [ctypes.POINTER(msa_stage_time), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
@@ -255,6 +261,29 @@ def msa_indexer_kl(dims: msa_dims, q, k, idx_q, idx_k, block_idx, lse, kl, d_idx
     _check(lib, lib.msa_indexer_kl(ctypes.byref(dims), p_q, p_k, p_iq, p_ik, p_bi, p_l, p_kl, p_dq, p_dk,
                                    ws, nws, _stream(stream)))
     return kl, d_idx_q, d_idx_k
+
+
+def msa_prefill_backward(dims: msa_dims, q, k, v, out, lse, dout, block_idx, dq, dk, dv,
+                         workspace=None, stream=None):
+    """Gradient of the main branch's output into q, k and v with the selection
+    held fixed (see include/msa.h); written into dq, dk, dv (fp32)."""
+    lib = load_library()
+    b, T, Hq, G, d, kk = (dims.batch, dims.seqlen, dims.num_q_heads, dims.num_kv_heads, dims.head_dim,
+                          dims.topk)
+    p_q = _ptr(q, "q", torch.bfloat16, (b, T, Hq, d))
+    p_k = _ptr(k, "k", torch.bfloat16, (b, T, G, d))
+    p_v = _ptr(v, "v", torch.bfloat16, (b, T, G, d))
+    p_o = _ptr(out, "out", torch.bfloat16, (b, T, Hq, d))
+    p_l = _ptr(lse, "lse", torch.float32, (b, T, Hq))
+    p_do = _ptr(dout, "dout", torch.bfloat16, (b, T, Hq, d))
+    p_bi = _ptr(block_idx, "block_idx", torch.int32, (b, T, G, kk))
+    p_dq = _ptr(dq, "dq", torch.float32, (b, T, Hq, d))
+    p_dk = _ptr(dk, "dk", torch.float32, (b, T, G, d))
+    p_dv = _ptr(dv, "dv", torch.float32, (b, T, G, d))
+    ws, nws = _workspace(MSA_OP_BACKWARD, dims, workspace, q.device)
+    _check(lib, lib.msa_prefill_backward(ctypes.byref(dims), p_q, p_k, p_v, p_o, p_l, p_do, p_bi, p_dq, p_dk,
+                                         p_dv, ws, nws, _stream(stream)))
+    return dq, dk, dv
 
 
 def msa_decode(dims: msa_dims, q, k_cache, v_cache, idx_q, idx_k_cache, cache_lens, out,

@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "libmsa.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["api.hip", "index_blockmax.hip", "topk_select.hip", "sparse_attn.hip", "decode.hip", "profile.hip",
-           "indexer_kl.hip"]
+           "indexer_kl.hip", "backward.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

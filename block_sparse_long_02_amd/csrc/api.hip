@@ -248,6 +248,106 @@ int make_kl_plan(const msa_dims* d, KlPlan* p) {
 }
 
 // ---------------------------------------------------------------------------
+// Backward plan: block lists over every selected block (local included), the
+// dq partial rows (bf16, one per entry and head) and one dk/dv partial block
+// per non-empty list, for one query chunk.
+// ---------------------------------------------------------------------------
+constexpr size_t kDefaultBwdBudget = 64ull << 30;
+
+struct BwdPlan {
+  int nb = 0, KS = 0, R = 0, rank_bits = 0;
+  int Tc = 0, nchunks = 0;
+  size_t off_delta = 0, off_cnt = 0, off_offs = 0, off_bsum = 0, off_rinfo = 0, off_epos = 0, off_entries = 0,
+         off_work = 0, off_nwork = 0, off_slot = 0, off_dqp = 0, off_part = 0, total = 0;
+  long max_lists = 0;  // non-empty lists of a chunk, at most
+};
+
+// Non-empty lists of any chunk of a tc-token split, at most: block b of window
+// w can hold entries only when b <= L of the window's last token.
+long bwd_max_lists(const msa_dims* d, const BwdPlan& p, long tc) {
+  const long W = msa::kListWindow, B = d->block_size, T = d->seqlen;
+  long best = 0;
+  for (long t0 = 0; t0 < T; t0 += tc) {
+    const long len = T - t0 < tc ? T - t0 : tc;
+    long n = 0;
+    for (long w = 0; w * W < len; ++w) {
+      const long last = t0 + ((w + 1) * W < len ? (w + 1) * W : len) - 1;
+      const long nbw = last / B + 1;
+      n += nbw < p.nb ? nbw : p.nb;
+    }
+    if (n > best) best = n;
+  }
+  best *= (long)d->batch * d->num_kv_heads;
+  const long emax = (long)d->batch * tc * d->num_kv_heads * p.KS;
+  return best < emax ? best : emax;
+}
+
+size_t bwd_chunk_bytes(const msa_dims* d, const BwdPlan& p, long tc, BwdPlan* out) {
+  Layout L;
+  const size_t nb_ = (size_t)d->batch, G_ = (size_t)d->num_kv_heads, B_ = (size_t)d->block_size;
+  const size_t nwin = ((size_t)tc + msa::kListWindow - 1) / msa::kListWindow;
+  const size_t nlists = nb_ * G_ * nwin * (size_t)p.nb;
+  const size_t nscan = (nlists + msa::kScanItems - 1) / msa::kScanItems;
+  const size_t rows = nb_ * (size_t)tc * G_;
+  const size_t emax = rows * (size_t)p.KS;
+  BwdPlan q = p;
+  q.max_lists = bwd_max_lists(d, p, tc);
+  q.off_delta = L.add(nb_ * (size_t)tc * (size_t)d->num_q_heads * 4);
+  q.off_cnt = L.add(nlists * 4);
+  q.off_offs = L.add(nlists * 4);
+  q.off_bsum = L.add(nscan * 8);
+  q.off_rinfo = L.add(rows * 4);
+  q.off_epos = L.add(emax * 4);
+  q.off_entries = L.add(emax * 4);
+  q.off_work = L.add((size_t)q.max_lists * 8);
+  q.off_nwork = L.add(4);
+  q.off_slot = L.add(nlists * 4);
+  q.off_dqp = L.add(emax * (size_t)p.R * 128 * 2);
+  q.off_part = L.add((size_t)q.max_lists * 2 * B_ * 128 * 4);
+  q.total = L.total;
+  if (out != nullptr) *out = q;
+  return q.total;
+}
+
+int make_bwd_plan(const msa_dims* d, BwdPlan* p) {
+  int st = check_dims(d, false);
+  if (st != MSA_OK) return st;
+  if (d->flags != 0) return MSA_ERR_INVALID_ARG;
+  const int T = d->seqlen, B = d->block_size, G = d->num_kv_heads;
+  p->R = d->num_q_heads / G;
+  p->nb = (T + B - 1) / B;
+  p->KS = d->topk < p->nb ? d->topk : p->nb;
+  while ((1 << p->rank_bits) < p->KS) ++p->rank_bits;
+  // largest chunk (a multiple of the list window, else of B) within the budget and the int32 limits
+  const long per_tok_entries = (long)d->batch * G * p->KS;
+  long lim = (kMaxInt32 / 2) / (per_tok_entries ? per_tok_entries : 1);
+  const long lim2 = (long)kMaxInt32 >> p->rank_bits;
+  if (lim2 < lim) lim = lim2;
+  const long lists_per_win = (long)d->batch * G * p->nb;
+  const long max_win = (kMaxInt32 - 1) / lists_per_win;
+  if (max_win < 1) return MSA_ERR_UNSUPPORTED;
+  if (max_win * msa::kListWindow < lim) lim = max_win * msa::kListWindow;
+  // dq partial rows are addressed as (list position * R + head) in int32 arithmetic per list
+  const long lim3 = (kMaxInt32 / 2) / ((long)per_tok_entries * p->R > 0 ? (long)per_tok_entries * p->R : 1);
+  if (lim3 < lim) lim = lim3;
+  long tc;
+  if (d->query_chunk > 0) {
+    tc = d->query_chunk < T ? d->query_chunk : T;
+  } else {
+    tc = ((long)T + msa::kListWindow - 1) / msa::kListWindow * msa::kListWindow;
+    while (tc > msa::kListWindow && bwd_chunk_bytes(d, *p, tc, nullptr) > kDefaultBwdBudget) tc -= msa::kListWindow;
+    while (tc > B && bwd_chunk_bytes(d, *p, tc, nullptr) > kDefaultBwdBudget) tc -= B;
+    if (tc > T) tc = T;
+  }
+  if (tc > lim) tc = lim / B * B;
+  if (tc < 1) return MSA_ERR_UNSUPPORTED;
+  p->Tc = (int)tc;
+  p->nchunks = (int)((T + tc - 1) / tc);
+  bwd_chunk_bytes(d, *p, tc, p);
+  return MSA_OK;
+}
+
+// ---------------------------------------------------------------------------
 // Decode plan
 // ---------------------------------------------------------------------------
 struct DecodePlan {
@@ -356,6 +456,11 @@ size_t msa_workspace_bytes(int op, const msa_dims* dims) {
   if (op == MSA_OP_INDEXER_KL) {
     KlPlan p;
     if (make_kl_plan(dims, &p) != MSA_OK) return (size_t)-1;
+    return p.total;
+  }
+  if (op == MSA_OP_BACKWARD) {
+    BwdPlan p;
+    if (make_bwd_plan(dims, &p) != MSA_OK) return (size_t)-1;
     return p.total;
   }
   return (size_t)-1;
@@ -556,6 +661,74 @@ int msa_indexer_kl(const msa_dims* dims, const void* q, const void* k, const voi
     a.max_work_a = (emax + 127) / 128 + l.nlists;
     a.accumulate_dk = c > 0;
     hipError_t e = msa::launch_indexer_kl(a, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  msa::prof_mark(s, -1);
+  return MSA_OK;
+}
+
+int msa_prefill_backward(const msa_dims* dims, const void* q, const void* k, const void* v, const void* out,
+                         const float* lse, const void* dout, const int32_t* block_idx, float* dq, float* dk,
+                         float* dv, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  BwdPlan p;
+  int st = make_bwd_plan(dims, &p);
+  if (st != MSA_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr || dout == nullptr ||
+      block_idx == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+    return MSA_ERR_INVALID_ARG;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) || misaligned(dout, 16) ||
+      misaligned(lse, 4) || misaligned(block_idx, 4) || misaligned(dq, 16) || misaligned(dk, 4) ||
+      misaligned(dv, 4))
+    return MSA_ERR_ALIGNMENT;
+  if ((st = check_workspace(p.total, workspace, workspace_bytes)) != MSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  msa::BwdArgs a{};
+  msa::PrefillMainArgs& l = a.l;
+  l.q = static_cast<const uint16_t*>(q);
+  l.k = static_cast<const uint16_t*>(k);
+  l.v = static_cast<const uint16_t*>(v);
+  l.lse = const_cast<float*>(lse);  // read only
+  l.batch = dims->batch;
+  l.T = dims->seqlen;
+  l.Hq = dims->num_q_heads;
+  l.G = dims->num_kv_heads;
+  l.B = dims->block_size;
+  l.topk = dims->topk;
+  l.KS = p.KS;
+  l.rank_bits = p.rank_bits;
+  l.include_local = 1;
+  l.nbl = p.nb;
+  l.scale_log2 = log2_scale(dims);
+  l.bidx = block_idx;
+  l.bidx_rows = dims->seqlen;
+  l.bidx_t_off = 0;
+  l.cnt = at<int32_t>(workspace, p.off_cnt);
+  l.offs = at<int32_t>(workspace, p.off_offs);
+  l.bsum = at<int32_t>(workspace, p.off_bsum);
+  l.rinfo = at<int32_t>(workspace, p.off_rinfo);
+  l.epos = at<int32_t>(workspace, p.off_epos);
+  l.entries = at<int32_t>(workspace, p.off_entries);
+  l.work = at<int2>(workspace, p.off_work);
+  l.n_work = at<int32_t>(workspace, p.off_nwork);
+  a.o = static_cast<const uint16_t*>(out);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = at<float>(workspace, p.off_delta);
+  a.slot_of = at<int32_t>(workspace, p.off_slot);
+  a.dqp = at<uint16_t>(workspace, p.off_dqp);
+  a.part = at<float>(workspace, p.off_part);
+  for (int c = 0; c < p.nchunks; ++c) {
+    const int t0 = c * p.Tc;
+    const int tc = (dims->seqlen - t0) < p.Tc ? dims->seqlen - t0 : p.Tc;
+    l.t0 = t0;
+    l.tc = tc;
+    l.nwin = (tc + msa::kListWindow - 1) / msa::kListWindow;
+    l.nlists = (long)dims->batch * dims->num_kv_heads * l.nwin * p.nb;
+    l.max_work = p.max_lists;
+    a.accumulate = c > 0;
+    hipError_t e = msa::launch_prefill_backward(a, s);
     if (e != hipSuccess) return hip_fail(e);
   }
   msa::prof_mark(s, -1);

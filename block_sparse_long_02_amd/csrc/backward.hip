@@ -1,0 +1,493 @@
+// Backward of the MSA Main Branch on gfx950: dq, dk, dv of the block-sparse
+// softmax attention with the selection held fixed.
+//
+// The selection is a top-k of block maxima, piecewise constant in the index
+// inputs, and the index branch learns only through its own KL loss with its
+// inputs detached [Telegram review quant_prune_distill post 751, "Метод":
+// stop-gradient on the index branch; hyper.ai paper page 2606.13392, 方法
+// (Method): gradient detach on the Index Branch inputs].  What remains is the
+// gradient of plain softmax attention over each row's gathered tokens J
+// [same page, 方法: standard scaled dot-product attention over the gathered
+// Key/Value vectors].  Per (token t, head h), g = h / R, P = softmax_J(x),
+// x_j = scale q[t,h].k[j,g], with dO = d loss / d out[t,h]:
+//   dv[j,g] += P_j dO,   dP_j = dO . v[j,g],   Delta = dO . out[t,h]
+//   dS_j = scale P_j (dP_j - Delta)
+//   dq[t,h] = sum_j dS_j k[j,g],   dk[j,g] += dS_j q[t,h]
+// P is rebuilt from the forward's lse: P_j = exp(x_j - lse[t,h]).
+//
+// Work split (block-major, the prefill's (s, g, window, block) lists, here
+// holding every selected block of a row, its local block included):
+//  1. bwd_delta_kernel: Delta per (token, head) row;
+//  2. the lists, then bwd_sort_kernel: each list's entries sorted by
+//     (token, slot), so that the dk/dv sums below run in an order that does
+//     not depend on how the lists were filled (their positions come from
+//     integer atomics);
+//  3. bwd_list_kernel: one workgroup per list.  K^T of the block sits in LDS,
+//     each wave owns one 32-key tile (its K and V rows in registers) and
+//     steps over the list's (entry, head) rows: S = Q K^T and dP = dO V^T on
+//     MFMA, P and dS in the accumulator layout (one key per lane), dv += P^T dO
+//     and dk += dS^T Q straight from there, and dq = dS K through LDS.  dq
+//     leaves as one bf16 partial row per (entry, head), in list order; dk and
+//     dv as one fp32 partial block per list;
+//  4. bwd_dq_kernel: per (token, head), the partials summed in slot order;
+//  5. bwd_dkv_kernel: per (sequence, group, key block), the lists' partials
+//     summed in (window) order.  No atomic touches a value.
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+namespace {
+
+constexpr int D = 128;  // head_dim
+
+__device__ __forceinline__ void bwd_list_of(const PrefillMainArgs& l, long lid, int* b, int* g, int* s) {
+  *b = (int)(lid % l.nbl);
+  const long sg = (lid / l.nbl) / l.nwin;
+  *g = (int)(sg % l.G);
+  *s = (int)(sg / l.G);
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// ---------------------------------------------------------------------------
+// 1. Delta[s, tl, h] = dO . out over the head dimension (fp32); 16 lanes per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
+  const PrefillMainArgs& l = a.l;
+  const long nrows = (long)l.batch * l.tc * l.Hq;
+  const long row = (long)blockIdx.x * 16 + threadIdx.x / 16;
+  const int part = threadIdx.x % 16;
+  float acc = 0.f;
+  if (row < nrows) {
+    const long per_b = (long)l.tc * l.Hq;
+    const size_t grow = ((size_t)(row / per_b) * l.T + l.t0) * l.Hq + (size_t)(row % per_b);
+    const bf16x8 o = load_bf16x8(a.o + grow * D + part * 8);
+    const bf16x8 d = load_bf16x8(a.dout + grow * D + part * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += (float)o[i] * (float)d[i];
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
+  if (row < nrows && part == 0) a.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// 2. Sort each list's entries (tl << rank_bits | slot, all distinct) in LDS
+//    and point every row slot at its entry's new list position.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_sort_kernel(BwdArgs a) {
+  __shared__ uint32_t key[kListWindow];
+  const PrefillMainArgs& l = a.l;
+  const int w = blockIdx.x;
+  if (w >= l.n_work[0]) return;
+  const long lid = l.work[w].x;
+  const int count = l.cnt[lid];
+  // one entry per token of the window when a row's valid entries are
+  // distinct; a longer list (duplicate input) keeps its order
+  if (count > kListWindow) return;
+  int b, g, s;
+  bwd_list_of(l, lid, &b, &g, &s);
+  const int off = l.offs[lid];
+  const int tid = threadIdx.x;
+  int n2 = 1;
+  while (n2 < count) n2 <<= 1;
+  for (int i = tid; i < n2; i += 256) key[i] = i < count ? (uint32_t)l.entries[off + i] : 0xffffffffu;
+  __syncthreads();
+  for (int kk = 2; kk <= n2; kk <<= 1)
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int i = tid; i < n2; i += 256) {
+        const int p = i ^ jj;
+        if (p > i) {
+          const uint32_t x = key[i], y = key[p];
+          const bool up = (i & kk) == 0;
+          if ((x > y) == up) {
+            key[i] = y;
+            key[p] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  const uint32_t mask = (1u << l.rank_bits) - 1u;
+  for (int i = tid; i < count; i += 256) {
+    const uint32_t e = key[i];
+    l.entries[off + i] = (int32_t)e;
+    const long row = ((long)s * l.tc + (long)(e >> l.rank_bits)) * l.G + g;
+    l.epos[(size_t)row * l.KS + (e & mask)] = off + i;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. Per list: dq partial rows, dk / dv partial block.
+// ---------------------------------------------------------------------------
+template <int BS>
+struct BwdLds {
+  static constexpr int KT = BS / 32;     // key tiles of the block = waves per row tile
+  static constexpr int NRT = 4 / KT;     // row tiles per step
+  static constexpr int SR = 32 * NRT;    // (entry, head) rows per step
+  static constexpr int KTR = BS + 8;     // K^T row stride (keys)
+  static constexpr int QR = D + 8;       // row-major q / dO row stride
+  static constexpr int QTR = SR + 4;     // transposed q / dO row stride (rows)
+  static constexpr int DSR = BS + 8;     // dS row stride (keys)
+  static constexpr int o_kt = 0;
+  static constexpr int o_qr = o_kt + D * KTR * 2;
+  static constexpr int o_or = o_qr + SR * QR * 2;
+  static constexpr int o_qt = o_or + SR * QR * 2;
+  static constexpr int o_ot = o_qt + D * QTR * 2;
+  static constexpr int o_ds = o_ot + D * QTR * 2;
+  static constexpr int o_lse = o_ds + SR * DSR * 2;
+  static constexpr int o_del = o_lse + SR * 4;
+  static constexpr int o_tok = o_del + SR * 4;
+  static constexpr int bytes = o_tok + SR * 4;
+  // after the row loop: dk/dv accumulators of the row groups, KT * 32 keys x 128 x 2
+  static constexpr int red_bytes = KT * 32 * D * 2 * 4;
+  static_assert(NRT == 1 || red_bytes <= bytes, "reduction buffer fits the LDS of the loop");
+  static_assert(bytes <= 160 * 1024, "LDS of one workgroup");
+};
+
+template <int BS>
+__global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
+  using Lds = BwdLds<BS>;
+  constexpr int KT = Lds::KT, NRT = Lds::NRT, SR = Lds::SR;
+  constexpr int KTR = Lds::KTR, QR = Lds::QR, QTR = Lds::QTR, DSR = Lds::DSR;
+  constexpr int CPT = SR * (D / 8) / 256;  // 16-byte chunks of q (and of dO) per thread per step
+  __shared__ __attribute__((aligned(16))) unsigned char smem[Lds::bytes];
+  bf16_t* KTs = reinterpret_cast<bf16_t*>(smem + Lds::o_kt);
+  bf16_t* Qr = reinterpret_cast<bf16_t*>(smem + Lds::o_qr);
+  bf16_t* Or = reinterpret_cast<bf16_t*>(smem + Lds::o_or);
+  bf16_t* Qt = reinterpret_cast<bf16_t*>(smem + Lds::o_qt);
+  bf16_t* Ot = reinterpret_cast<bf16_t*>(smem + Lds::o_ot);
+  bf16_t* DSr = reinterpret_cast<bf16_t*>(smem + Lds::o_ds);
+  float* rlse = reinterpret_cast<float*>(smem + Lds::o_lse);
+  float* rdel = reinterpret_cast<float*>(smem + Lds::o_del);
+  int* rtok = reinterpret_cast<int*>(smem + Lds::o_tok);
+
+  const PrefillMainArgs& l = a.l;
+  const int w = blockIdx.x;
+  if (w >= l.n_work[0]) return;
+  const long lid = l.work[w].x;
+  const int count = l.cnt[lid];
+  int b, g, s;
+  bwd_list_of(l, lid, &b, &g, &s);
+  const int off = l.offs[lid];
+  const int R = l.Hq / l.G;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int kt = wave % KT, rt = wave / KT;
+  const int kb = b * l.B;
+  const int nkey = min(BS, l.T - kb);
+  const size_t kvstride = (size_t)l.G * D;
+  const bf16_t* kblk = l.k + ((size_t)s * l.T + kb) * kvstride + (size_t)g * D;
+  const bf16_t* vblk = l.v + ((size_t)s * l.T + kb) * kvstride + (size_t)g * D;
+  if (tid == 0) a.slot_of[lid] = w;
+
+  // K^T of the block: KTs[d][key]
+  for (int c = tid; c < BS * (D / 8); c += 256) {
+    const int kr = c >> 4, part = c & 15;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (kr < nkey) v = *reinterpret_cast<const u32x4*>(kblk + (size_t)kr * kvstride + part * 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t wd = v[j >> 1];
+      reinterpret_cast<uint16_t*>(KTs)[(part * 8 + j) * KTR + kr] = (uint16_t)((j & 1) ? (wd >> 16) : (wd & 0xffffu));
+    }
+  }
+  // this wave's key tile, rows of K and V as MFMA B operands (k-slots = head dim)
+  bf16x8 kreg[D / 16], vreg[D / 16];
+  {
+    const int kr = 32 * kt + col;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kreg[ks] = kr < nkey ? load_bf16x8(kblk + (size_t)kr * kvstride + 16 * ks + 8 * half) : zero_bf16x8();
+      vreg[ks] = kr < nkey ? load_bf16x8(vblk + (size_t)kr * kvstride + 16 * ks + 8 * half) : zero_bf16x8();
+    }
+  }
+
+  const int nr = count * R;  // (entry, head) rows of the list, row = entry position * R + head
+  const int nsteps = (nr + SR - 1) / SR;
+  const float c2 = l.scale_log2;
+  const float scale = l.scale_log2 * kLn2;
+
+  // Rows of a step travel through registers in parts of CPR chunks per thread.
+  // With one part (steps of up to 64 rows) the next step is fetched while the
+  // current one computes; 128-row steps are fetched part by part in place, as
+  // an early fetch would not fit the register file next to the accumulators.
+  constexpr int CPR = CPT <= 4 ? CPT : 4;
+  constexpr int NPART = CPT / CPR;
+  constexpr bool kAhead = NPART == 1;
+  u32x4 qs[CPR], os[CPR];
+  float lse_v = 0.f, del_v = 0.f;
+  int tok_v = -1;
+  auto fetch = [&](int base, int part0) {
+#pragma unroll
+    for (int i = 0; i < CPR; ++i) {
+      const int c = tid + 256 * (part0 * CPR + i);
+      const int rho = base + (c >> 4), part = c & 15;
+      qs[i] = u32x4{0u, 0u, 0u, 0u};
+      os[i] = u32x4{0u, 0u, 0u, 0u};
+      if (rho < nr) {
+        const int p = rho / R, r = rho - p * R;
+        const int tl = l.entries[off + p] >> l.rank_bits;
+        const size_t grow = ((size_t)s * l.T + l.t0 + tl) * l.Hq + (size_t)g * R + r;
+        qs[i] = *reinterpret_cast<const u32x4*>(l.q + grow * D + part * 8);
+        os[i] = *reinterpret_cast<const u32x4*>(a.dout + grow * D + part * 8);
+      }
+    }
+    if (part0 == 0 && tid < SR) {
+      const int rho = base + tid;
+      tok_v = -1;
+      if (rho < nr) {
+        const int p = rho / R, r = rho - p * R;
+        const int tl = l.entries[off + p] >> l.rank_bits;
+        const size_t grow = ((size_t)s * l.T + l.t0 + tl) * l.Hq + (size_t)g * R + r;
+        lse_v = l.lse[grow] * kLog2e;
+        del_v = a.delta[((size_t)s * l.tc + tl) * l.Hq + (size_t)g * R + r];
+        tok_v = l.t0 + tl;
+      }
+    }
+  };
+  auto store = [&](int part0) {
+#pragma unroll
+    for (int i = 0; i < CPR; ++i) {
+      const int c = tid + 256 * (part0 * CPR + i);
+      const int row = c >> 4, part = c & 15;
+      *reinterpret_cast<u32x4*>(Qr + row * QR + part * 8) = qs[i];
+      *reinterpret_cast<u32x4*>(Or + row * QR + part * 8) = os[i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sh = (j & 1) * 16;
+        reinterpret_cast<uint16_t*>(Qt)[(part * 8 + j) * QTR + row] = (uint16_t)(qs[i][j >> 1] >> sh);
+        reinterpret_cast<uint16_t*>(Ot)[(part * 8 + j) * QTR + row] = (uint16_t)(os[i][j >> 1] >> sh);
+      }
+    }
+    if (part0 == 0 && tid < SR) {
+      rlse[tid] = lse_v;
+      rdel[tid] = del_v;
+      rtok[tid] = tok_v;
+    }
+  };
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+
+  if (kAhead) fetch(0, 0);
+  for (int step = 0; step < nsteps; ++step) {
+    __syncthreads();  // the previous step's LDS reads are done (and KTs is written)
+    if (kAhead) {
+      store(0);
+    } else {
+#pragma unroll 1
+      for (int part0 = 0; part0 < NPART; ++part0) {
+        fetch(step * SR, part0);
+        store(part0);
+      }
+    }
+    __syncthreads();
+    if (kAhead && step + 1 < nsteps) fetch((step + 1) * SR, 0);
+
+    const int r0 = rt * 32;
+    f32x16 S = {}, dP = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      S = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Qr + (r0 + col) * QR + 16 * ks + 8 * half), kreg[ks], S);
+      dP = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Or + (r0 + col) * QR + 16 * ks + 8 * half), vreg[ks], dP);
+    }
+    // lane: key j of its tile, rows r0 + 8*(i/4) + 4*half + (i%4)
+    const int j = kb + 32 * kt + col;
+    bf16x8 p8[2], d8[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = r0 + 8 * (i / 4) + 4 * half + (i % 4);
+      const int t = rtok[row];
+      const bool ok = t >= 0 && j <= t;
+      const float p = ok ? __builtin_amdgcn_exp2f(S[i] * c2 - rlse[row]) : 0.f;
+      const float ds = p * (dP[i] - rdel[row]) * scale;
+      p8[i / 8][i % 8] = (__bf16)p;
+      d8[i / 8][i % 8] = (__bf16)ds;
+      reinterpret_cast<uint16_t*>(DSr)[row * DSR + 32 * kt + col] = bf16_bits(ds);
+    }
+    // dv[key][d] += P^T dO, dk[key][d] += dS^T Q over this row tile (k-slots = rows)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int o0 = (32 * dt + col) * QTR + r0 + 16 * ks + 4 * half;
+        const bf16x8 ob = join_bf16x4(*reinterpret_cast<const u32x2*>(Ot + o0),
+                                      *reinterpret_cast<const u32x2*>(Ot + o0 + 8));
+        const bf16x8 qb = join_bf16x4(*reinterpret_cast<const u32x2*>(Qt + o0),
+                                      *reinterpret_cast<const u32x2*>(Qt + o0 + 8));
+        dv[dt] = mfma32x32x16(p8[ks], ob, dv[dt]);
+        dk[dt] = mfma32x32x16(d8[ks], qb, dk[dt]);
+      }
+    }
+    __syncthreads();  // dS rows of the step complete
+    // dq[row][d] = sum over the block's keys of dS[row][key] K[key][d]
+#pragma unroll 1
+    for (int ii = 0; ii < NRT; ++ii) {
+      const int f = wave * NRT + ii;
+      const int rt2 = f >> 2, dt = f & 3;
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < BS / 16; ++ks)
+        acc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(DSr + (rt2 * 32 + col) * DSR + 16 * ks + 8 * half),
+                           *reinterpret_cast<const bf16x8*>(KTs + (32 * dt + col) * KTR + 16 * ks + 8 * half),
+                           acc);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rho = step * SR + rt2 * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+        if (rho < nr) a.dqp[((size_t)off * R + rho) * D + 32 * dt + col] = bf16_bits(acc[i]);
+      }
+    }
+  }
+
+  // row groups of one key tile add up in a fixed order (group 0 + 1 + ...)
+  if constexpr (NRT > 1) {
+    float* red = reinterpret_cast<float*>(smem);
+    for (int rr = 1; rr < NRT; ++rr) {
+      __syncthreads();
+      if (rt == rr) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            red[(((kt * 2 + 0) * 4 + dt) * 16 + i) * 64 + lane] = dk[dt][i];
+            red[(((kt * 2 + 1) * 4 + dt) * 16 + i) * 64 + lane] = dv[dt][i];
+          }
+      }
+      __syncthreads();
+      if (rt == 0) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            dk[dt][i] += red[(((kt * 2 + 0) * 4 + dt) * 16 + i) * 64 + lane];
+            dv[dt][i] += red[(((kt * 2 + 1) * 4 + dt) * 16 + i) * 64 + lane];
+          }
+      }
+    }
+  }
+  if (rt == 0) {
+    float* pk = a.part + (size_t)w * 2 * BS * D;
+    float* pv = pk + (size_t)BS * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kr = 32 * kt + 8 * (i / 4) + 4 * half + (i % 4);
+        pk[(size_t)kr * D + 32 * dt + col] = dk[dt][i];
+        pv[(size_t)kr * D + 32 * dt + col] = dv[dt][i];
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. dq[s, t, h] = sum over the row's entries, in slot order, of its partials.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+  const PrefillMainArgs& l = a.l;
+  const long nrows = (long)l.batch * l.tc * l.Hq;
+  const long x = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row = x >> 4;
+  const int part = (int)(x & 15);
+  if (row >= nrows) return;
+  const int R = l.Hq / l.G;
+  const long per_b = (long)l.tc * l.Hq;
+  const int s = (int)(row / per_b);
+  const int tl = (int)((row % per_b) / l.Hq);
+  const int h = (int)(row % l.Hq);
+  const int g = h / R, r = h - g * R;
+  const long rowg = ((long)s * l.tc + tl) * l.G + g;
+  const int nv = l.rinfo[rowg] & 0x3fffffff;
+  const int32_t* pos = l.epos + (size_t)rowg * l.KS;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < nv; ++q) {
+    const bf16x8 v = load_bf16x8(a.dqp + ((size_t)pos[q] * R + r) * D + part * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += (float)v[i];
+  }
+  float* dst = a.dq + (((size_t)s * l.T + l.t0 + tl) * l.Hq + h) * D + part * 8;
+  *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+}
+
+// ---------------------------------------------------------------------------
+// 5. dk, dv of a key block of one (sequence, group): its lists' partials in
+//    window order; added onto earlier query chunks.
+// ---------------------------------------------------------------------------
+template <int BS>
+__global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs a) {
+  constexpr int PER = BS * D / 256;
+  const PrefillMainArgs& l = a.l;
+  const int b = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int kb = b * l.B;
+  const int nkey = min(BS, l.T - kb);
+  float ak[PER], av[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    ak[i] = 0.f;
+    av[i] = 0.f;
+  }
+  for (int x = 0; x < l.nwin; ++x) {
+    const size_t lid = (((size_t)s * l.G + g) * l.nwin + x) * l.nbl + b;
+    if (l.cnt[lid] == 0) continue;
+    const float* pk = a.part + (size_t)a.slot_of[lid] * 2 * BS * D;
+    const float* pv = pk + (size_t)BS * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = threadIdx.x + 256 * i;
+      ak[i] += pk[u];
+      av[i] += pv[u];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    const int kr = u / D, dd = u % D;
+    if (kr < nkey) {
+      const size_t o = (((size_t)s * l.T + kb + kr) * l.G + g) * D + dd;
+      a.dk[o] = a.accumulate ? a.dk[o] + ak[i] : ak[i];
+      a.dv[o] = a.accumulate ? a.dv[o] + av[i] : av[i];
+    }
+  }
+}
+
+}  // namespace
+
+// mt for the lists' work list: large enough that every non-empty list is one item
+constexpr int kBwdListTile = 1 << 28;
+
+hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t st) {
+  const PrefillMainArgs& l = a.l;
+  const long nrows = (long)l.batch * l.tc * l.Hq;
+  prof_mark(st, MSA_STAGE_BWD_PREP);
+  bwd_delta_kernel<<<(unsigned)((nrows + 15) / 16), 256, 0, st>>>(a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if ((err = launch_block_lists(l, kBwdListTile, st)) != hipSuccess) return err;
+  if (l.max_work > 0) bwd_sort_kernel<<<(unsigned)l.max_work, 256, 0, st>>>(a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark(st, MSA_STAGE_BWD_LISTS);
+  if (l.max_work > 0) {
+    if (l.B == 128) bwd_list_kernel<128><<<(unsigned)l.max_work, 256, 0, st>>>(a);
+    else if (l.B == 64) bwd_list_kernel<64><<<(unsigned)l.max_work, 256, 0, st>>>(a);
+    else bwd_list_kernel<32><<<(unsigned)l.max_work, 256, 0, st>>>(a);
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  prof_mark(st, MSA_STAGE_BWD_MERGE);
+  bwd_dq_kernel<<<(unsigned)((nrows * 16 + 255) / 256), 256, 0, st>>>(a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const dim3 grid((unsigned)((l.T + l.B - 1) / l.B), (unsigned)l.G, (unsigned)l.batch);
+  if (l.B == 128) bwd_dkv_kernel<128><<<grid, 256, 0, st>>>(a);
+  else if (l.B == 64) bwd_dkv_kernel<64><<<grid, 256, 0, st>>>(a);
+  else bwd_dkv_kernel<32><<<grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -118,6 +118,23 @@ struct IndexerKlArgs {
 };
 hipError_t launch_indexer_kl(const IndexerKlArgs& a, hipStream_t st);
 
+// ---- Main-branch backward (selection held fixed) ----
+struct BwdArgs {
+  PrefillMainArgs l;      // lists of the chunk (include_local = 1); q, k, v, lse, scale used
+  const uint16_t* o;      // [batch][T][Hq][128] forward output
+  const uint16_t* dout;   // [batch][T][Hq][128]
+  float* dq;              // [batch][T][Hq][128]
+  float* dk;              // [batch][T][G][128]
+  float* dv;              // [batch][T][G][128]
+  bool accumulate;        // add dk, dv onto earlier query chunks
+  // workspace
+  float* delta;           // [batch*tc*Hq] dO . out
+  int32_t* slot_of;       // [nlists] work item (partial slot) of a non-empty list
+  uint16_t* dqp;          // [E*R][128] bf16 dq partial rows in list order
+  float* part;            // [max_work][2][B][128] dk, dv partial per list
+};
+hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t st);
+
 // ---- Decode ----
 hipError_t launch_index_blockmax_decode(const uint16_t* idx_q, const uint16_t* idx_k,
                                         const int32_t* lens, float* S, int batch, int Lmax, int G,

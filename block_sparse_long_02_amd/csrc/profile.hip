@@ -105,6 +105,9 @@ const char* msa_stage_name(int32_t stage) {
     case MSA_STAGE_DECODE_ATTN: return "decode_attn_kernel";
     case MSA_STAGE_DECODE_COMBINE: return "decode_combine_kernel";
     case MSA_STAGE_INDEXER_KL: return "indexer KL (lists, stats, entry, list, reduction kernels)";
+    case MSA_STAGE_BWD_PREP: return "backward prep (delta, block lists, list sort kernels)";
+    case MSA_STAGE_BWD_LISTS: return "bwd_list_kernel";
+    case MSA_STAGE_BWD_MERGE: return "backward merge (bwd_dq_kernel, bwd_dkv_kernel)";
     default: return "unknown stage";
   }
 }

@@ -80,6 +80,7 @@ extern "C" {
 #define MSA_OP_PREFILL 1
 #define MSA_OP_DECODE 2
 #define MSA_OP_INDEXER_KL 3
+#define MSA_OP_BACKWARD 4
 
 typedef struct msa_dims {
   int32_t batch;         /* sequences, >= 1 */
@@ -196,6 +197,35 @@ int msa_indexer_kl(const msa_dims* dims, const void* q, const void* k, const voi
                    float* d_idx_q, float* d_idx_k, void* workspace, size_t workspace_bytes,
                    void* hip_stream);
 
+/*
+ * Backward of the main branch: dq, dk, dv of the block-sparse attention with
+ * the selection held fixed.  The selection is a top-k, piecewise constant in
+ * the index inputs, and the index branch learns through msa_indexer_kl only
+ * [Telegram review quant_prune_distill post 751, "Метод": stop-gradient on the
+ * index branch; hyper.ai paper page 2606.13392, 方法 (Method): gradient detach
+ * on the Index Branch inputs, standard scaled dot-product attention over the
+ * gathered Key/Value vectors].  Per (token t, head h), g = h / R, over the
+ * tokens J = {j <= t in the row's selected blocks}, P_j = exp(scale q[t,h].k[j,g]
+ * - lse[t,h]) and dO = dout[t,h]:
+ *   dv[j,g] += P_j dO;   dS_j = scale P_j (dO.v[j,g] - dO.out[t,h])
+ *   dq[t,h]  = sum_j dS_j k[j,g];   dk[j,g] += dS_j q[t,h]
+ *   q, out, dout [batch, T, Hq, d] bf16;  k, v [batch, T, G, d] bf16
+ *   lse        [batch, T, Hq] fp32: the forward's log-sum-exp (msa_prefill's lse)
+ *   block_idx  [batch, T, G, topk] int32: the forward's selection (entries
+ *              outside [0, L(t)] ignored, valid entries distinct)
+ *   dq [batch, T, Hq, d], dk and dv [batch, T, G, d] fp32 OUTPUTS (a row with
+ *              nothing to attend gets dq = 0; keys no row attends get 0)
+ * dims: prefill shapes, flags must be 0, Hq / G <= 128.  bf16 pointers 16-byte
+ * aligned, fp32 and int32 pointers 4-byte aligned.  P and dS enter the
+ * gradient products rounded to bf16, and dq is summed from one bf16 partial
+ * per selected block (fp32 accumulation throughout).  Deterministic:
+ * fixed-order sums, no atomics on values.
+ */
+int msa_prefill_backward(const msa_dims* dims, const void* q, const void* k, const void* v,
+                         const void* out, const float* lse, const void* dout,
+                         const int32_t* block_idx, float* dq, float* dk, float* dv,
+                         void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Workspace bytes needed by op for dims (0 when none is needed).  Returns
    (size_t)-1 when dims are invalid for op. */
 size_t msa_workspace_bytes(int op, const msa_dims* dims);
@@ -236,7 +266,10 @@ int msa_abi_version(void);
 #define MSA_STAGE_DECODE_ATTN 8        /* per-(sequence, group) attention         */
 #define MSA_STAGE_DECODE_COMBINE 9     /* combine of the split partials (dense)   */
 #define MSA_STAGE_INDEXER_KL 10        /* msa_indexer_kl, all of its kernels      */
-#define MSA_STAGE_COUNT 11
+#define MSA_STAGE_BWD_PREP 11          /* backward: dO.out, block lists, list sort */
+#define MSA_STAGE_BWD_LISTS 12         /* backward: per-list dq / dk / dv products */
+#define MSA_STAGE_BWD_MERGE 13         /* backward: fixed-order dq and dk/dv sums  */
+#define MSA_STAGE_COUNT 14
 
 typedef struct msa_stage_time {
   int32_t stage;

@@ -200,3 +200,27 @@ def test_indexer_kl_shape_limits(lib):
     for d in (r3, r64, fl):
         assert lib.msa_workspace_bytes(bd.MSA_OP_INDEXER_KL, ctypes.byref(d)) == ctypes.c_size_t(-1).value
 
+
+
+def test_backward_shape_limits(lib):
+    ok = bd.make_dims(1, 2048, 12, 4, index_dim=64, block_size=64, topk=8)  # R = 3 is fine
+    assert lib.msa_workspace_bytes(bd.MSA_OP_BACKWARD, ctypes.byref(ok)) > 0
+    for fl in (bd.MSA_DENSE, bd.MSA_GIVEN_INDICES, bd.MSA_FORCE_SINK):
+        d = bd.make_dims(1, 2048, 16, 4, index_dim=64, block_size=64, topk=8, flags=fl)
+        assert lib.msa_workspace_bytes(bd.MSA_OP_BACKWARD, ctypes.byref(d)) == ctypes.c_size_t(-1).value
+    # the selection is an input: null pointers and a short workspace are rejected before any launch
+    d = bd.make_dims(1, 256, 8, 2, index_dim=64, block_size=64, topk=2)
+    need = lib.msa_workspace_bytes(bd.MSA_OP_BACKWARD, ctypes.byref(d))
+    buf = ctypes.create_string_buffer(1024)
+    addr = (ctypes.addressof(buf) + 255) // 256 * 256  # every pointer 256-byte aligned
+    p = ctypes.c_void_p(addr)
+    args = [p] * 10
+    assert lib.msa_prefill_backward(ctypes.byref(d), *args[:6], None, *args[7:], p, need, None) == \
+        bd.MSA_ERR_INVALID_ARG
+    assert lib.msa_prefill_backward(ctypes.byref(d), *args, p, need - 1, None) == bd.MSA_ERR_WORKSPACE
+
+
+def test_backward_workspace_fits_128k_in_one_chunk(lib):
+    d = bd.make_dims(1, 131072, 64, 8, index_dim=128, block_size=128, topk=16)
+    ws = lib.msa_workspace_bytes(bd.MSA_OP_BACKWARD, ctypes.byref(d))
+    assert 0 < ws <= 64 << 30

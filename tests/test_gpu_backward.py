@@ -1,0 +1,116 @@
+"""GPU parity of msa_prefill_backward against the oracle's attention_backward.
+
+The forward runs on the GPU (its selection and lse feed the backward, as in
+training); the oracle recomputes the gradients in fp64 from the same bf16
+inputs and the GPU's selection.  Bounds: max-abs <= 1e-2 of the largest
+reference value and mean-relative (sum |diff| / sum |ref|) <= 5e-3 per
+gradient.  P and dS enter the MFMA products rounded to bf16 (2^-9 relative)
+and dq is summed from bf16 partials, one per selected block; over the
+hundreds to thousands of keys of a row these roundings average out to a few
+1e-3 of the values, which is what the bounds allow.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_02_amd import binding as bd
+from block_sparse_long_02_amd import inputs
+from oracle import msa_oracle as orc
+
+from gpu_common import gpu_prefill, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _dout(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g).to(torch.bfloat16)
+
+
+def gpu_backward(inp, out, lse, bidx, dout, B, k, query_chunk=0):
+    b, T, Hq, d = inp.q.shape
+    G = inp.k.shape[2]
+    dims = bd.make_dims(b, T, Hq, G, head_dim=d, index_dim=inp.idx_q.shape[-1], block_size=B, topk=k,
+                        query_chunk=query_chunk)
+    dq = torch.full((b, T, Hq, d), float("nan"), device="cuda")
+    dk = torch.full((b, T, G, d), float("nan"), device="cuda")
+    dv = torch.full((b, T, G, d), float("nan"), device="cuda")
+    bd.msa_prefill_backward(dims, inp.q.cuda(), inp.k.cuda(), inp.v.cuda(), out.cuda(), lse.cuda(), dout.cuda(),
+                            bidx.cuda().to(torch.int32).contiguous(), dq, dk, dv)
+    torch.cuda.synchronize()
+    return dq.cpu().double().numpy(), dk.cpu().double().numpy(), dv.cpu().double().numpy()
+
+
+def check_grad(got, ref, what):
+    assert np.isfinite(got).all(), what
+    err = np.abs(got - ref)
+    scale = np.abs(ref).max()
+    mr = err.sum() / max(np.abs(ref).sum(), 1e-300)
+    say(f"  {what}: max-abs {err.max():.3e} (of {scale:.3e})  mean-rel {mr:.3e}")
+    assert err.max() <= 1e-2 * scale, what
+    assert mr <= 5e-3, what
+
+
+CASES = [
+    # T, Hq, G, B, k, query_chunk, batch
+    (1000, 16, 4, 64, 6, 0, 1),       # R = 4, ragged tail
+    (777, 8, 8, 32, 9, 256, 2),       # R = 1, three query chunks, batch 2
+    (600, 24, 8, 128, 3, 0, 1),       # R = 3, partial last block
+    (700, 64, 8, 128, 4, 0, 1),       # the 128K workload's heads and block size
+    (300, 32, 2, 64, 12, 0, 1),       # R = 16, k beyond the number of blocks (all selected)
+]
+
+
+@pytest.mark.parametrize("T,Hq,G,B,k,chunk,nb", CASES)
+def test_backward_vs_oracle(T, Hq, G, B, k, chunk, nb):
+    say(f"[backward] T={T} Hq={Hq} G={G} B={B} k={k} chunk={chunk} batch={nb}")
+    inp = inputs.make_prefill(T, Hq, G, 128, 64, batch=nb, seed=900 + T)
+    out, lse, bidx = gpu_prefill(inp, B, k)
+    dout = _dout((nb, T, Hq, 128), 901 + T)
+    dq, dk, dv = gpu_backward(inp, out, lse, bidx, dout, B, k, query_chunk=chunk)
+    rq, rk, rv = orc.attention_backward(inp.q, inp.k, inp.v, dout, bidx, B)
+    check_grad(dq, rq, "dq")
+    check_grad(dk, rk, "dk")
+    check_grad(dv, rv, "dv")
+
+
+def test_backward_given_selection_edge_rows():
+    """A given selection with rows missing their local block, out-of-range
+    entries and rows that attend nothing (dq = 0 there)."""
+    T, Hq, G, B, k = 500, 8, 2, 32, 4
+    say("[backward given selection]")
+    inp = inputs.make_prefill(T, Hq, G, 128, 64, seed=911)
+    rng = np.random.default_rng(912)
+    sel = np.full((1, T, G, k), -1, dtype=np.int32)
+    for t in range(T):
+        L = t // B
+        for g in range(G):
+            if t % 11 == 5:
+                continue                                   # nothing to attend
+            c = list(rng.permutation(L)[: k - 1]) if L > 0 else []
+            row = ([] if t % 7 == 3 and c else [L]) + c
+            if len(row) < k and t % 3 == 0:
+                row.append(L + 1 + t % 5)                   # out of range: ignored
+            sel[0, t, g, : len(row)] = rng.permutation(row)
+    bidx = torch.from_numpy(sel)
+    out, lse, _ = gpu_prefill(inp, B, k, flags=bd.MSA_GIVEN_INDICES, block_idx=bidx)
+    dout = _dout((1, T, Hq, 128), 913)
+    dq, dk, dv = gpu_backward(inp, out, lse, bidx, dout, B, k)
+    rq, rk, rv = orc.attention_backward(inp.q, inp.k, inp.v, dout, bidx, B)
+    empty = np.array([t % 11 == 5 for t in range(T)])
+    assert (dq[0, empty] == 0).all()
+    check_grad(dq, rq, "dq")
+    check_grad(dk, rk, "dk")
+    check_grad(dv, rv, "dv")
+
+
+def test_backward_bitwise_deterministic():
+    T, Hq, G, B, k = 2100, 16, 2, 64, 8
+    say("[backward determinism]")
+    inp = inputs.make_prefill(T, Hq, G, 128, 64, seed=921)
+    out, lse, bidx = gpu_prefill(inp, B, k)
+    dout = _dout((1, T, Hq, 128), 922)
+    a = gpu_backward(inp, out, lse, bidx, dout, B, k)
+    b = gpu_backward(inp, out, lse, bidx, dout, B, k)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
