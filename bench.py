@@ -42,7 +42,8 @@ COPY_BYTES = 1 << 30   # calibration copy for the --pmc passes
 
 
 def traffic_file(kernel):
-    workload = "decode_8x1m" if kernel.startswith("decode_") else "prefill_t131072"
+    workload = ("decode_8x1m" if kernel.startswith("decode_") else
+                "backward_t131072" if kernel.startswith("bwd_") else "prefill_t131072")
     return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
 
 
@@ -84,6 +85,88 @@ def indexer_kl_ms(pin, bidx, lse, dev, stream, reps):
     fn()
     ms, _ = timed(fn, reps, stream)
     return ms
+
+
+def backward_flops(T, Hq, d, B, k):
+    """Per (token, head, attended key) the backward's five products (S, dP,
+    dv, dk, dq), 2d flop each."""
+    t = np.arange(T, dtype=np.float64)
+    att = (t % B) + 1 + B * np.minimum(k - 1, np.floor(t / B))
+    return 10.0 * d * Hq * att.sum()
+
+
+def bwd_list_bytes(bidx, T, Hq, G, d, B, window=8192):
+    """Algorithmic bytes of one bwd_list_kernel launch over the whole prefill:
+    per (token, group, selected block) entry, the local block included, the
+    group's R q and dO rows are read and R bf16 dq partial rows written, plus
+    each row's lse and dO.out (8 bytes) and the 4-byte entry; per non-empty
+    (group, 8192-token window, block) list the K/V block is read once and its
+    fp32 dk/dv partial block written."""
+    R = Hq // G
+    t = torch.arange(T, device=bidx.device).view(1, T, 1, 1)
+    sel = bidx.long()
+    valid = (sel >= 0) & (sel <= t // B)
+    entries = int(valid.sum().item())
+    nb = (T + B - 1) // B
+    nwin = (T + window - 1) // window
+    g = torch.arange(G, device=bidx.device).view(1, 1, G, 1)
+    key = ((g * nwin + t // window) * nb + sel)[valid]
+    lists = int(torch.unique(key).numel())
+    per_entry = R * (3 * d * 2 + 8) + 4
+    return entries * per_entry + lists * (2 * B * d * 2 + 2 * B * d * 4), entries, lists
+
+
+def backward_run(pin, pout, plse, pbidx, dev, stream, reps, profile=True):
+    """The main-branch backward on the headline prefill's output, lse and
+    selection with a seeded d out: (mean ms, stage ms, tensors)."""
+    T, Hq, G = PF["T"], PF["Hq"], PF["G"]
+    bdims = bd.make_dims(1, T, Hq, G, index_dim=PF["di"], block_size=PF["B"], topk=PF["k"])
+    gen = torch.Generator(device=dev).manual_seed(77)
+    dout = torch.randn((1, T, Hq, PF["d"]), generator=gen, device=dev).to(torch.bfloat16)
+    dq = torch.empty((1, T, Hq, PF["d"]), dtype=torch.float32, device=dev)
+    dk = torch.empty((1, T, G, PF["d"]), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    ws = torch.empty(bd.msa_workspace_bytes(bd.MSA_OP_BACKWARD, bdims), dtype=torch.uint8, device=dev)
+    fn = lambda: bd.msa_prefill_backward(bdims, pin.q, pin.k, pin.v, pout, plse, dout, pbidx,  # noqa: E731
+                                         dq, dk, dv, workspace=ws)
+    fn()
+    ms, per = timed(fn, reps, stream)
+    stages = None
+    if profile:
+        bd.msa_profile_begin()
+        fn()
+        torch.cuda.synchronize()
+        stages = {n: t_ / c for n, (c, t_) in bd.msa_profile_end().items()}
+    del ws
+    return ms, per, stages, (dout, dq, dk, dv)
+
+
+def backward_checks(pin, pbidx, tensors, n_rows=24):
+    """Full-size checks of the backward: dq on seeded sampled rows against the
+    oracle (row by row), and for dk / dv the properties that hold at any size
+    (per group the key gradients sum to zero, the value gradients to the
+    summed d out, every row attending at least its local block)."""
+    from oracle import msa_oracle as orc
+    dout, dq, dk, dv = tensors
+    T, Hq, G, B = PF["T"], PF["Hq"], PF["G"], PF["B"]
+    rng = np.random.default_rng(78)
+    ts = sorted(set([0, B - 1, B, T - 1] + [int(x) for x in rng.integers(0, T, n_rows - 4)]))
+    rows = [(0, t) for t in ts]
+    bidx_c = pbidx.cpu()
+    ref = orc.attention_backward_dq(pin.q.cpu(), pin.k.cpu(), pin.v.cpu(), dout.cpu(), bidx_c, B, rows)
+    got = dq.cpu().double().numpy()
+    err = sum(float(np.abs(got[r] - ref[r]).sum()) for r in rows)
+    tot = sum(float(np.abs(ref[r]).sum()) for r in rows)
+    mx = max(float(np.abs(got[r] - ref[r]).max()) for r in rows)
+    scale = max(float(np.abs(ref[r]).max()) for r in rows)
+    R = Hq // G
+    dk64, dv64 = dk.double(), dv.double()
+    dsum = dout.double().view(1, T, G, R, -1).sum(dim=(1, 3))        # [1, G, d]
+    inv_k = float((dk64.sum(dim=1).abs().max() / dk64.abs().sum(dim=1).max()).item())
+    inv_v = float(((dv64.sum(dim=1) - dsum).abs().max() / dsum.abs().max()).item())
+    return {"rows": len(rows), "dq_max_abs": mx, "dq_ref_max": scale, "dq_mean_rel": err / max(tot, 1e-300),
+            "dk_sum_rel": inv_k, "dv_sum_minus_dout_rel": inv_v,
+            "ok": bool(mx <= 1e-2 * scale and err / max(tot, 1e-300) <= 5e-3 and inv_k <= 1e-4 and inv_v <= 1e-4)}
 
 
 def dense_prefill_flops(T, Hq, d):
@@ -155,8 +238,9 @@ def measured_peaks(dev):
 
 def profile_kernels_only(args, dev):
     """The 128K prefill's inputs, one calibration copy of COPY_BYTES, then
-    --steps prefills, --steps indexer KL calls on the last prefill's selection
-    (+1 warmup) and --steps decode steps (8 x 1M context), every kernel
+    --steps prefills, --steps indexer KL calls and --steps main-branch
+    backward calls on the last prefill's output (each +1 warmup) and --steps
+    decode steps (8 x 1M context), every kernel
     launched as in the timed steps: the workload of the --pmc counter passes
     and of the kernel-trace summary."""
     stream = torch.cuda.current_stream()
@@ -176,6 +260,8 @@ def profile_kernels_only(args, dev):
                                          block_idx=pbidx, workspace=pws), args.steps, stream)
     del pws
     kms = indexer_kl_ms(pin, pbidx, plse, dev, stream, args.steps)
+    bms, _, _, btens = backward_run(pin, pout, plse, pbidx, dev, stream, args.steps, profile=False)
+    del btens
     dec = inputs.make_decode(DC["batch"], DC["L"], DC["Hq"], DC["G"], DC["d"], DC["di"], seed=DC["seed"],
                              device=dev)
     ddims = bd.make_dims(DC["batch"], DC["L"], DC["Hq"], DC["G"], index_dim=DC["di"], block_size=DC["B"],
@@ -187,7 +273,7 @@ def profile_kernels_only(args, dev):
     dms, _ = timed(dfn, args.steps, stream)
     stages = bd.msa_profile_end()
     print(json.dumps({"profile_steps": args.steps, "prefill_ms": round(ms, 4), "decode_ms": round(dms, 4),
-                      "indexer_kl_ms": round(kms, 4),
+                      "indexer_kl_ms": round(kms, 4), "backward_ms": round(bms, 4),
                       "copy_bytes": COPY_BYTES,
                       "stage_ms": {n: round(t / c, 4) for n, (c, t) in stages.items()}}), flush=True)
 
@@ -275,6 +361,7 @@ def cpu_baseline_and_parity(pin, out_gpu, bidx_gpu, n_tokens, time_budget_s):
         "selection_other": sel_other, "out_max_abs": err_abs,
         "out_mean_rel": err_sum / max(ref_sum, 1e-300), "t_range": [min(used), max(used)],
     }
+    parity["ok"] = bool(sel_other == 0 and err_abs <= 2e-2 and parity["out_mean_rel"] <= 5e-3)
     return cpu, parity
 
 
@@ -316,6 +403,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg (CPU baseline + parity)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the block-size sweep, 32K prefill and forced-sink timings")
+    ap.add_argument("--no-backward", action="store_true", help="skip the main-branch backward at 128K")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--profile-kernels", action="store_true",
@@ -464,12 +552,13 @@ def main():
     if not args.no_variants:
         log("variant workloads")
         variants = {}
+        vbuf = torch.empty_like(pout)  # the headline output stays intact for the checks below
         for B_, k_ in ((64, 32), (32, 64)):
             vd = bd.make_dims(1, PF["T"], PF["Hq"], PF["G"], index_dim=PF["di"], block_size=B_, topk=k_)
             vin = inputs.make_prefill(PF["T"], PF["Hq"], PF["G"], PF["d"], PF["di"], seed=PF["seed"], device=dev,
                                       block_size=B_, skew_std=PF["skew"])
             vws = torch.empty(bd.msa_workspace_bytes(bd.MSA_OP_PREFILL, vd), dtype=torch.uint8, device=dev)
-            fn = lambda: bd.msa_prefill(vd, vin.q, vin.k, vin.v, vin.idx_q, vin.idx_k, pout, workspace=vws)  # noqa: E731
+            fn = lambda: bd.msa_prefill(vd, vin.q, vin.k, vin.v, vin.idx_q, vin.idx_k, vbuf, workspace=vws)  # noqa: E731
             fn()
             ms, _ = timed(fn, 3, stream)
             variants[f"prefill_t131072_b{B_}_k{k_}"] = {"ms": round(ms, 3),
@@ -489,7 +578,7 @@ def main():
         del vin, vout, vws
         sd = bd.make_dims(1, PF["T"], PF["Hq"], PF["G"], index_dim=PF["di"], block_size=PF["B"], topk=PF["k"],
                           flags=bd.MSA_FORCE_SINK)
-        fn = lambda: bd.msa_prefill(sd, pin.q, pin.k, pin.v, pin.idx_q, pin.idx_k, pout, workspace=pws)  # noqa: E731
+        fn = lambda: bd.msa_prefill(sd, pin.q, pin.k, pin.v, pin.idx_q, pin.idx_k, vbuf, workspace=pws)  # noqa: E731
         fn()
         ms, _ = timed(fn, 3, stream)
         variants["prefill_t131072_sink"] = {"ms": round(ms, 3), "tok_s": round(PF["T"] / (ms * 1e-3), 1)}
@@ -506,7 +595,38 @@ def main():
         variants["indexer_kl_t131072"] = {"ms": round(ms, 3), "tok_s": round(PF["T"] / (ms * 1e-3), 1),
                                           "algorithmic_tflop": round(kl_flops / 1e12, 3),
                                           "tflops": round(kl_flops / (ms * 1e-3) / 1e12, 2)}
+        del vbuf
         log(f"variants: {variants}")
+
+    # The main-branch backward (selection held fixed) on the headline
+    # prefill's output: a second workload of the same shapes, not in `value`.
+    backward = None
+    if not args.no_backward:
+        log("main-branch backward at 128K")
+        bms, bper, bst, btens = backward_run(pin, pout, plse, pbidx, dev, stream, 3)
+        bflops = backward_flops(PF["T"], PF["Hq"], PF["d"], PF["B"], PF["k"])
+        bbytes, b_entries, b_lists = bwd_list_bytes(pbidx, PF["T"], PF["Hq"], PF["G"], PF["d"], PF["B"])
+        name_bl = bd.msa_stage_name(bd.MSA_STAGE_BWD_LISTS)
+        bl_ms = bst.get(name_bl)
+        backward = {
+            "workload": "MSA main-branch backward T=131072 (B=128, k=16) on the prefill's own output and "
+                        "selection, seeded d out",
+            "ms": round(bms, 3), "median_ms": round(float(np.median(bper)), 3),
+            "tok_s": round(PF["T"] / (bms * 1e-3), 1),
+            "algorithmic_tflop": round(bflops / 1e12, 3),
+            "tflops": round(bflops / (bms * 1e-3) / 1e12, 2),
+            "stage_ms": {n: round(v, 4) for n, v in bst.items()},
+            "roofline": None if bl_ms is None else {
+                "kernel": name_bl, "bound": "hbm", "achieved": round(bbytes / (bl_ms * 1e-3) / 1e9, 1),
+                "peak": 8000.0, "unit": "GB/s", "frac": round(bbytes / (bl_ms * 1e-3) / PEAK_HBM, 4),
+                "traffic": measured_traffic("bwd_list_kernel"), "launch_ms": round(bl_ms, 4),
+                "algorithmic_gbytes_per_launch": round(bbytes / 1e9, 3), "entries": b_entries, "lists": b_lists,
+                "mfma_tflops": round(bflops / (bl_ms * 1e-3) / 1e12, 1)},
+        }
+        if not args.no_cpu:
+            backward["sampled_check"] = backward_checks(pin, pbidx, btens)
+        del btens
+        log(f"backward: {backward}")
 
     peaks = measured_peaks(dev)
     cpu, parity, dparity = None, None, None
@@ -558,6 +678,7 @@ def main():
         "stage_ms": {n: round(v, 4) for n, v in stage.items()},
         "dense": dense,
         "variants": variants,
+        "backward": backward,
         "measured_peaks": peaks,
         "parity": {"prefill_sampled": parity, "decode_sampled": dparity},
         "cpu_baseline": cpu,

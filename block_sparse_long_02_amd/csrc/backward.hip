@@ -123,15 +123,22 @@ __global__ __launch_bounds__(256) void bwd_sort_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // 3. Per list: dq partial rows, dk / dv partial block.
 // ---------------------------------------------------------------------------
+// Row tiles of 32 (entry, head) rows per wave per step: two for 128-key
+// blocks (each wave owns one key tile), one otherwise (waves also split rows).
+template <int BS>
+constexpr int bwd_rtw() { return BS == 128 ? 2 : 1; }
+
 template <int BS>
 struct BwdLds {
-  static constexpr int KT = BS / 32;     // key tiles of the block = waves per row tile
-  static constexpr int NRT = 4 / KT;     // row tiles per step
-  static constexpr int SR = 32 * NRT;    // (entry, head) rows per step
-  static constexpr int KTR = BS + 8;     // K^T row stride (keys)
-  static constexpr int QR = D + 8;       // row-major q / dO row stride
-  static constexpr int QTR = SR + 4;     // transposed q / dO row stride (rows)
-  static constexpr int DSR = BS + 8;     // dS row stride (keys)
+  static constexpr int KT = BS / 32;          // key tiles of the block
+  static constexpr int NRG = 4 / KT;          // row groups: waves sharing a key tile
+  static constexpr int RTW = bwd_rtw<BS>();   // row tiles per wave per step
+  static constexpr int RT = NRG * RTW;        // row tiles per step
+  static constexpr int SR = 32 * RT;          // (entry, head) rows per step
+  static constexpr int KTR = BS + 8;          // K^T row stride (keys)
+  static constexpr int QR = D + 8;            // row-major q / dO row stride
+  static constexpr int QTR = SR + 4;          // transposed q / dO row stride (rows)
+  static constexpr int DSR = BS + 8;          // dS row stride (keys)
   static constexpr int o_kt = 0;
   static constexpr int o_qr = o_kt + D * KTR * 2;
   static constexpr int o_or = o_qr + SR * QR * 2;
@@ -144,14 +151,14 @@ struct BwdLds {
   static constexpr int bytes = o_tok + SR * 4;
   // after the row loop: dk/dv accumulators of the row groups, KT * 32 keys x 128 x 2
   static constexpr int red_bytes = KT * 32 * D * 2 * 4;
-  static_assert(NRT == 1 || red_bytes <= bytes, "reduction buffer fits the LDS of the loop");
+  static_assert(NRG == 1 || red_bytes <= bytes, "reduction buffer fits the LDS of the loop");
   static_assert(bytes <= 160 * 1024, "LDS of one workgroup");
 };
 
 template <int BS>
 __global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
   using Lds = BwdLds<BS>;
-  constexpr int KT = Lds::KT, NRT = Lds::NRT, SR = Lds::SR;
+  constexpr int KT = Lds::KT, NRG = Lds::NRG, RTW = Lds::RTW, RT = Lds::RT, SR = Lds::SR;
   constexpr int KTR = Lds::KTR, QR = Lds::QR, QTR = Lds::QTR, DSR = Lds::DSR;
   constexpr int CPT = SR * (D / 8) / 256;  // 16-byte chunks of q (and of dO) per thread per step
   __shared__ __attribute__((aligned(16))) unsigned char smem[Lds::bytes];
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
   const int R = l.Hq / l.G;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
-  const int kt = wave % KT, rt = wave / KT;
+  const int kt = wave % KT, rg = wave / KT;
   const int kb = b * l.B;
   const int nkey = min(BS, l.T - kb);
   const size_t kvstride = (size_t)l.G * D;
@@ -212,36 +219,47 @@ __global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
   const float scale = l.scale_log2 * kLn2;
 
   // Rows of a step travel through registers in parts of CPR chunks per thread.
-  // With one part (steps of up to 64 rows) the next step is fetched while the
-  // current one computes; 128-row steps are fetched part by part in place, as
-  // an early fetch would not fit the register file next to the accumulators.
+  // With one part (steps of up to 64 rows) the next step's rows are fetched
+  // while the current one computes; 128-row steps are fetched part by part in
+  // place, as an early fetch would not fit next to the accumulators.  The
+  // entries that address a step's rows are loaded one step earlier still, so
+  // that no row load waits on the entry load just before it.
   constexpr int CPR = CPT <= 4 ? CPT : 4;
   constexpr int NPART = CPT / CPR;
   constexpr bool kAhead = NPART == 1;
+  int pe[CPT];        // entry of each chunk's row, -1 past the list
+  int pr = -1;        // entry of row tid (threads < SR)
   u32x4 qs[CPR], os[CPR];
   float lse_v = 0.f, del_v = 0.f;
   int tok_v = -1;
+  auto load_ent = [&](int base) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int rho = base + ((tid + 256 * i) >> 4);
+      pe[i] = rho < nr ? l.entries[off + rho / R] : -1;
+    }
+    if (tid < SR) pr = base + tid < nr ? l.entries[off + (base + tid) / R] : -1;
+  };
   auto fetch = [&](int base, int part0) {
 #pragma unroll
     for (int i = 0; i < CPR; ++i) {
       const int c = tid + 256 * (part0 * CPR + i);
       const int rho = base + (c >> 4), part = c & 15;
+      const int e = pe[part0 * CPR + i];
       qs[i] = u32x4{0u, 0u, 0u, 0u};
       os[i] = u32x4{0u, 0u, 0u, 0u};
-      if (rho < nr) {
-        const int p = rho / R, r = rho - p * R;
-        const int tl = l.entries[off + p] >> l.rank_bits;
-        const size_t grow = ((size_t)s * l.T + l.t0 + tl) * l.Hq + (size_t)g * R + r;
+      if (e >= 0) {
+        const int r = rho % R;
+        const size_t grow = ((size_t)s * l.T + l.t0 + (e >> l.rank_bits)) * l.Hq + (size_t)g * R + r;
         qs[i] = *reinterpret_cast<const u32x4*>(l.q + grow * D + part * 8);
         os[i] = *reinterpret_cast<const u32x4*>(a.dout + grow * D + part * 8);
       }
     }
     if (part0 == 0 && tid < SR) {
-      const int rho = base + tid;
       tok_v = -1;
-      if (rho < nr) {
-        const int p = rho / R, r = rho - p * R;
-        const int tl = l.entries[off + p] >> l.rank_bits;
+      if (pr >= 0) {
+        const int r = (base + tid) % R;
+        const int tl = pr >> l.rank_bits;
         const size_t grow = ((size_t)s * l.T + l.t0 + tl) * l.Hq + (size_t)g * R + r;
         lse_v = l.lse[grow] * kLog2e;
         del_v = a.delta[((size_t)s * l.tc + tl) * l.Hq + (size_t)g * R + r];
@@ -277,7 +295,11 @@ __global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
     dv[i] = f32x16{};
   }
 
-  if (kAhead) fetch(0, 0);
+  load_ent(0);
+  if (kAhead) {
+    fetch(0, 0);
+    load_ent(SR);
+  }
   for (int step = 0; step < nsteps; ++step) {
     __syncthreads();  // the previous step's LDS reads are done (and KTs is written)
     if (kAhead) {
@@ -288,50 +310,58 @@ __global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
         fetch(step * SR, part0);
         store(part0);
       }
+      load_ent((step + 1) * SR);
     }
     __syncthreads();
-    if (kAhead && step + 1 < nsteps) fetch((step + 1) * SR, 0);
+    if (kAhead && step + 1 < nsteps) {
+      fetch((step + 1) * SR, 0);
+      load_ent((step + 2) * SR);
+    }
 
-    const int r0 = rt * 32;
-    f32x16 S = {}, dP = {};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      S = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Qr + (r0 + col) * QR + 16 * ks + 8 * half), kreg[ks], S);
-      dP = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Or + (r0 + col) * QR + 16 * ks + 8 * half), vreg[ks], dP);
-    }
-    // lane: key j of its tile, rows r0 + 8*(i/4) + 4*half + (i%4)
     const int j = kb + 32 * kt + col;
-    bf16x8 p8[2], d8[2];
+#pragma unroll 1
+    for (int u = 0; u < RTW; ++u) {
+      const int r0 = (rg * RTW + u) * 32;
+      f32x16 S = {}, dP = {};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = r0 + 8 * (i / 4) + 4 * half + (i % 4);
-      const int t = rtok[row];
-      const bool ok = t >= 0 && j <= t;
-      const float p = ok ? __builtin_amdgcn_exp2f(S[i] * c2 - rlse[row]) : 0.f;
-      const float ds = p * (dP[i] - rdel[row]) * scale;
-      p8[i / 8][i % 8] = (__bf16)p;
-      d8[i / 8][i % 8] = (__bf16)ds;
-      reinterpret_cast<uint16_t*>(DSr)[row * DSR + 32 * kt + col] = bf16_bits(ds);
-    }
-    // dv[key][d] += P^T dO, dk[key][d] += dS^T Q over this row tile (k-slots = rows)
+      for (int ks = 0; ks < D / 16; ++ks) {
+        S = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Qr + (r0 + col) * QR + 16 * ks + 8 * half), kreg[ks], S);
+        dP = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Or + (r0 + col) * QR + 16 * ks + 8 * half), vreg[ks],
+                          dP);
+      }
+      // lane: key j of its tile, rows r0 + 8*(i/4) + 4*half + (i%4)
+      bf16x8 p8[2], d8[2];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+      for (int i = 0; i < 16; ++i) {
+        const int row = r0 + 8 * (i / 4) + 4 * half + (i % 4);
+        const int t = rtok[row];
+        const bool ok = t >= 0 && j <= t;
+        const float p = ok ? __builtin_amdgcn_exp2f(S[i] * c2 - rlse[row]) : 0.f;
+        const float ds = p * (dP[i] - rdel[row]) * scale;
+        p8[i / 8][i % 8] = (__bf16)p;
+        d8[i / 8][i % 8] = (__bf16)ds;
+        reinterpret_cast<uint16_t*>(DSr)[row * DSR + 32 * kt + col] = bf16_bits(ds);
+      }
+      // dv[key][d] += P^T dO, dk[key][d] += dS^T Q over this row tile (k-slots = rows)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int o0 = (32 * dt + col) * QTR + r0 + 16 * ks + 4 * half;
-        const bf16x8 ob = join_bf16x4(*reinterpret_cast<const u32x2*>(Ot + o0),
-                                      *reinterpret_cast<const u32x2*>(Ot + o0 + 8));
-        const bf16x8 qb = join_bf16x4(*reinterpret_cast<const u32x2*>(Qt + o0),
-                                      *reinterpret_cast<const u32x2*>(Qt + o0 + 8));
-        dv[dt] = mfma32x32x16(p8[ks], ob, dv[dt]);
-        dk[dt] = mfma32x32x16(d8[ks], qb, dk[dt]);
+      for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int o0 = (32 * dt + col) * QTR + r0 + 16 * ks + 4 * half;
+          const bf16x8 ob = join_bf16x4(*reinterpret_cast<const u32x2*>(Ot + o0),
+                                        *reinterpret_cast<const u32x2*>(Ot + o0 + 8));
+          const bf16x8 qb = join_bf16x4(*reinterpret_cast<const u32x2*>(Qt + o0),
+                                        *reinterpret_cast<const u32x2*>(Qt + o0 + 8));
+          dv[dt] = mfma32x32x16(p8[ks], ob, dv[dt]);
+          dk[dt] = mfma32x32x16(d8[ks], qb, dk[dt]);
+        }
       }
     }
     __syncthreads();  // dS rows of the step complete
     // dq[row][d] = sum over the block's keys of dS[row][key] K[key][d]
 #pragma unroll 1
-    for (int ii = 0; ii < NRT; ++ii) {
-      const int f = wave * NRT + ii;
+    for (int ii = 0; ii < RT; ++ii) {
+      const int f = wave * RT + ii;
       const int rt2 = f >> 2, dt = f & 3;
       f32x16 acc = {};
 #pragma unroll
@@ -348,11 +378,11 @@ __global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
   }
 
   // row groups of one key tile add up in a fixed order (group 0 + 1 + ...)
-  if constexpr (NRT > 1) {
+  if constexpr (NRG > 1) {
     float* red = reinterpret_cast<float*>(smem);
-    for (int rr = 1; rr < NRT; ++rr) {
+    for (int rr = 1; rr < NRG; ++rr) {
       __syncthreads();
-      if (rt == rr) {
+      if (rg == rr) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -362,7 +392,7 @@ __global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
           }
       }
       __syncthreads();
-      if (rt == 0) {
+      if (rg == 0) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -373,7 +403,7 @@ __global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
       }
     }
   }
-  if (rt == 0) {
+  if (rg == 0) {
     float* pk = a.part + (size_t)w * 2 * BS * D;
     float* pv = pk + (size_t)BS * D;
 #pragma unroll

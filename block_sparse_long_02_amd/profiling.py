@@ -35,6 +35,8 @@ KERNEL_SOURCES = {
                             "build.py"],
     "decode_attn_kernel": ["csrc/decode.hip", "csrc/msa_device.h", "csrc/msa_internal.h", "csrc/api.hip",
                            "build.py"],
+    "bwd_list_kernel": ["csrc/backward.hip", "csrc/msa_device.h", "csrc/msa_internal.h", "csrc/api.hip",
+                        "build.py"],
 }
 
 

@@ -330,6 +330,18 @@ def indexer_kl(q, k, idx_q, idx_k, block_idx, B: int, scale: float | None = None
     return res
 
 
+def _backward_row(q_rows, Kg, Vg, dO, scale: float):
+    """One (token, group) row of the backward: R query heads q_rows [R, d]
+    over the gathered keys/values Kg, Vg [n, d], upstream gradient dO [R, d].
+    Returns (dq [R, d], dk [n, d], dv [n, d]) of this row."""
+    x = scale * (q_rows @ Kg.T)                        # [R, n]
+    P = np.exp(x - x.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    dP = dO @ Vg.T                                     # [R, n]
+    dx = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+    return scale * (dx @ Kg), scale * (dx.T @ q_rows), P.T @ dO
+
+
 def attention_backward(q, k, v, dout, block_idx, B: int, scale: float | None = None):
     """Gradient of the main branch's output with respect to q, k and v, the
     selection held fixed.
@@ -371,14 +383,36 @@ def attention_backward(q, k, v, dout, block_idx, B: int, scale: float | None = N
                 if len(toks) == 0:
                     continue
                 heads = slice(g * R, (g + 1) * R)
-                Kg, Vg = k[s, toks, g], v[s, toks, g]          # [n, d]
-                x = scale * (q[s, t, heads] @ Kg.T)            # [R, n]
-                P = np.exp(x - x.max(axis=1, keepdims=True))
-                P /= P.sum(axis=1, keepdims=True)
-                dO = dout[s, t, heads]                         # [R, d]
-                dP = dO @ Vg.T                                 # [R, n]
-                dx = P * (dP - (P * dP).sum(axis=1, keepdims=True))
-                dq[s, t, heads] = scale * (dx @ Kg)
-                np.add.at(dk[s, :, g], toks, scale * (dx.T @ q[s, t, heads]))
-                np.add.at(dv[s, :, g], toks, P.T @ dO)
+                dq_r, dk_r, dv_r = _backward_row(q[s, t, heads], k[s, toks, g], v[s, toks, g],
+                                                 dout[s, t, heads], scale)
+                dq[s, t, heads] = dq_r
+                np.add.at(dk[s, :, g], toks, dk_r)
+                np.add.at(dv[s, :, g], toks, dv_r)
     return dq, dk, dv
+
+
+def attention_backward_dq(q, k, v, dout, block_idx, B: int, rows, scale: float | None = None):
+    """dq of the rows (s, t) given, as attention_backward defines it, reading
+    only those rows and their selected keys (for sampled checks at sizes
+    where the whole gradient does not fit in float64).  Returns
+    {(s, t): dq [Hq, d]}."""
+    nbatch, T, Hq, d = q.shape
+    G = k.shape[2]
+    R = Hq // G
+    if scale is None:
+        scale = default_scale(d)
+    res = {}
+    for s, t in rows:
+        dq_t = np.zeros((Hq, d))
+        sel_t = np.asarray(_f64(block_idx[s, t]), dtype=np.int64)
+        q_t, do_t = _f64(q[s, t]), _f64(dout[s, t])
+        for g in range(G):
+            toks = selected_tokens(sel_t[g], t, B)
+            if len(toks) == 0:
+                continue
+            lo, hi = int(toks.min()), int(toks.max()) + 1
+            Kw, Vw = _f64(k[s, lo:hi, g]), _f64(v[s, lo:hi, g])
+            heads = slice(g * R, (g + 1) * R)
+            dq_t[heads] = _backward_row(q_t[heads], Kw[toks - lo], Vw[toks - lo], do_t[heads], scale)[0]
+        res[(s, t)] = dq_t
+    return res

@@ -649,3 +649,16 @@ def test_backward_invariants():
             rows = [t for t in range(T) if any(0 <= b <= t // B for b in bidx[s, t, g])]
             ref = dout[s, rows][:, g * R:(g + 1) * R].sum(axis=(0, 1))
             np.testing.assert_allclose(dv[s, :, g].sum(axis=0), ref, atol=1e-10)
+
+
+def test_backward_sampled_rows_match_the_whole_gradient():
+    T, Hq, G, d, B, k = 120, 6, 3, 8, 16, 3
+    rng = np.random.default_rng(70)
+    inp = inputs.make_prefill(T, Hq, G, d, 8, seed=71)
+    dout = rng.standard_normal((1, T, Hq, d))
+    bidx = _random_selection(T, G, B, k, rng, drop_local=True, junk=True)
+    dq, _, _ = orc.attention_backward(inp.q, inp.k, inp.v, dout, bidx, B)
+    rows = [(0, t) for t in (0, 3, 15, 16, 64, 119)]
+    got = orc.attention_backward_dq(inp.q, inp.k, inp.v, dout, bidx, B, rows)
+    for r in rows:
+        np.testing.assert_array_equal(got[r], dq[r])
