@@ -28,7 +28,8 @@
 //     MFMA, P and dS in the accumulator layout (one key per lane), dv += P^T dO
 //     and dk += dS^T Q straight from there, and dq = dS K through LDS.  dq
 //     leaves as one bf16 partial row per (entry, head), in list order; dk and
-//     dv as one fp32 partial block per list;
+//     dv as one fp32 partial block per list.  dS is kept without the softmax
+//     scale, which the two merges apply;
 //  4. bwd_dq_kernel: per (token, head), the partials summed in slot order;
 //  5. bwd_dkv_kernel: per (sequence, group, key block), the lists' partials
 //     summed in (window) order.  No atomic touches a value.
@@ -191,9 +192,10 @@ __global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
   const bf16_t* vblk = l.v + ((size_t)s * l.T + kb) * kvstride + (size_t)g * D;
   if (tid == 0) a.slot_of[lid] = w;
 
-  // K^T of the block: KTs[d][key]
+  // K^T of the block: KTs[d][key]; consecutive lanes take consecutive keys,
+  // so that the 2-byte transposed writes of a wave land in distinct banks
   for (int c = tid; c < BS * (D / 8); c += 256) {
-    const int kr = c >> 4, part = c & 15;
+    const int kr = c % BS, part = c / BS;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (kr < nkey) v = *reinterpret_cast<const u32x4*>(kblk + (size_t)kr * kvstride + part * 8);
 #pragma unroll
@@ -216,53 +218,63 @@ __global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
   const int nr = count * R;  // (entry, head) rows of the list, row = entry position * R + head
   const int nsteps = (nr + SR - 1) / SR;
   const float c2 = l.scale_log2;
-  const float scale = l.scale_log2 * kLn2;
 
-  // Rows of a step travel through registers in parts of CPR chunks per thread.
-  // With one part (steps of up to 64 rows) the next step's rows are fetched
-  // while the current one computes; 128-row steps are fetched part by part in
-  // place, as an early fetch would not fit next to the accumulators.  The
-  // entries that address a step's rows are loaded one step earlier still, so
-  // that no row load waits on the entry load just before it.
+  // Staging of a step's rows: thread tid owns row tid % SR of every step and
+  // the 16-byte chunks part = tid / SR + (256 / SR) * i of it (consecutive
+  // lanes take consecutive rows, so the 2-byte transposed LDS writes of a wave
+  // land in distinct banks and the row-major 16-byte writes are spread by the
+  // row padding).  The row's (list position, head) advance by a constant each
+  // step.  With one part (steps of up to 64 rows) the next step's rows are
+  // fetched while the current one computes; 128-row steps are fetched part by
+  // part in place, as an early fetch would not fit next to the accumulators.
+  // The entry that addresses a step's row is loaded one step earlier still.
+  static_assert(256 % SR == 0 && CPT * 256 == SR * (D / 8), "one row per thread");
   constexpr int CPR = CPT <= 4 ? CPT : 4;
   constexpr int NPART = CPT / CPR;
   constexpr bool kAhead = NPART == 1;
-  int pe[CPT];        // entry of each chunk's row, -1 past the list
-  int pr = -1;        // entry of row tid (threads < SR)
+  const int myrow = tid % SR, part_base = tid / SR;
+  const int step_q = SR / R, step_r = SR % R;  // list-position and head advance per step
+  int cur_p = myrow / R, cur_r = myrow % R;     // row of the next entry load
+  int ent = -1, ent_r = 0, ent_rho = 0;         // that load's result and its head / row index
+  int row_e = -1, row_r = 0;                    // entry and head of the rows being fetched
   u32x4 qs[CPR], os[CPR];
   float lse_v = 0.f, del_v = 0.f;
   int tok_v = -1;
-  auto load_ent = [&](int base) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int rho = base + ((tid + 256 * i) >> 4);
-      pe[i] = rho < nr ? l.entries[off + rho / R] : -1;
+  auto load_ent = [&]() {
+    ent_rho = cur_p * R + cur_r;
+    ent_r = cur_r;
+    ent = ent_rho < nr ? l.entries[off + cur_p] : -1;
+    cur_p += step_q;
+    cur_r += step_r;
+    if (cur_r >= R) {
+      cur_r -= R;
+      ++cur_p;
     }
-    if (tid < SR) pr = base + tid < nr ? l.entries[off + (base + tid) / R] : -1;
   };
-  auto fetch = [&](int base, int part0) {
+  auto take_ent = [&]() {
+    row_e = ent;
+    row_r = ent_r;
+  };
+  auto fetch = [&](int part0) {
+    const size_t grow = row_e >= 0 ? ((size_t)s * l.T + l.t0 + (row_e >> l.rank_bits)) * l.Hq +
+                                         (size_t)g * R + row_r
+                                   : 0;
 #pragma unroll
     for (int i = 0; i < CPR; ++i) {
-      const int c = tid + 256 * (part0 * CPR + i);
-      const int rho = base + (c >> 4), part = c & 15;
-      const int e = pe[part0 * CPR + i];
+      const int part = part_base + (256 / SR) * (part0 * CPR + i);
       qs[i] = u32x4{0u, 0u, 0u, 0u};
       os[i] = u32x4{0u, 0u, 0u, 0u};
-      if (e >= 0) {
-        const int r = rho % R;
-        const size_t grow = ((size_t)s * l.T + l.t0 + (e >> l.rank_bits)) * l.Hq + (size_t)g * R + r;
+      if (row_e >= 0) {
         qs[i] = *reinterpret_cast<const u32x4*>(l.q + grow * D + part * 8);
         os[i] = *reinterpret_cast<const u32x4*>(a.dout + grow * D + part * 8);
       }
     }
     if (part0 == 0 && tid < SR) {
       tok_v = -1;
-      if (pr >= 0) {
-        const int r = (base + tid) % R;
-        const int tl = pr >> l.rank_bits;
-        const size_t grow = ((size_t)s * l.T + l.t0 + tl) * l.Hq + (size_t)g * R + r;
+      if (row_e >= 0) {
+        const int tl = row_e >> l.rank_bits;
         lse_v = l.lse[grow] * kLog2e;
-        del_v = a.delta[((size_t)s * l.tc + tl) * l.Hq + (size_t)g * R + r];
+        del_v = a.delta[((size_t)s * l.tc + tl) * l.Hq + (size_t)g * R + row_r];
         tok_v = l.t0 + tl;
       }
     }
@@ -270,15 +282,14 @@ __global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
   auto store = [&](int part0) {
 #pragma unroll
     for (int i = 0; i < CPR; ++i) {
-      const int c = tid + 256 * (part0 * CPR + i);
-      const int row = c >> 4, part = c & 15;
-      *reinterpret_cast<u32x4*>(Qr + row * QR + part * 8) = qs[i];
-      *reinterpret_cast<u32x4*>(Or + row * QR + part * 8) = os[i];
+      const int part = part_base + (256 / SR) * (part0 * CPR + i);
+      *reinterpret_cast<u32x4*>(Qr + myrow * QR + part * 8) = qs[i];
+      *reinterpret_cast<u32x4*>(Or + myrow * QR + part * 8) = os[i];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int sh = (j & 1) * 16;
-        reinterpret_cast<uint16_t*>(Qt)[(part * 8 + j) * QTR + row] = (uint16_t)(qs[i][j >> 1] >> sh);
-        reinterpret_cast<uint16_t*>(Ot)[(part * 8 + j) * QTR + row] = (uint16_t)(os[i][j >> 1] >> sh);
+        reinterpret_cast<uint16_t*>(Qt)[(part * 8 + j) * QTR + myrow] = (uint16_t)(qs[i][j >> 1] >> sh);
+        reinterpret_cast<uint16_t*>(Ot)[(part * 8 + j) * QTR + myrow] = (uint16_t)(os[i][j >> 1] >> sh);
       }
     }
     if (part0 == 0 && tid < SR) {
@@ -295,33 +306,46 @@ __global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
     dv[i] = f32x16{};
   }
 
-  load_ent(0);
+  load_ent();
   if (kAhead) {
-    fetch(0, 0);
-    load_ent(SR);
+    take_ent();
+    fetch(0);
+    load_ent();
   }
   for (int step = 0; step < nsteps; ++step) {
     __syncthreads();  // the previous step's LDS reads are done (and KTs is written)
     if (kAhead) {
       store(0);
     } else {
+      take_ent();
 #pragma unroll 1
       for (int part0 = 0; part0 < NPART; ++part0) {
-        fetch(step * SR, part0);
+        fetch(part0);
         store(part0);
       }
-      load_ent((step + 1) * SR);
+      load_ent();
     }
     __syncthreads();
     if (kAhead && step + 1 < nsteps) {
-      fetch((step + 1) * SR, 0);
-      load_ent((step + 2) * SR);
+      take_ent();
+      fetch(0);
+      load_ent();
     }
 
     const int j = kb + 32 * kt + col;
 #pragma unroll 1
     for (int u = 0; u < RTW; ++u) {
       const int r0 = (rg * RTW + u) * 32;
+      // the lane's 16 rows are 4 runs of 4: their t, lse and Delta in 16-byte reads
+      i32x4 tk[4];
+      f32x4 lv[4], dl[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int rr = r0 + 8 * q4 + 4 * half;
+        tk[q4] = *reinterpret_cast<const i32x4*>(rtok + rr);
+        lv[q4] = *reinterpret_cast<const f32x4*>(rlse + rr);
+        dl[q4] = *reinterpret_cast<const f32x4*>(rdel + rr);
+      }
       f32x16 S = {}, dP = {};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
@@ -334,10 +358,11 @@ __global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = r0 + 8 * (i / 4) + 4 * half + (i % 4);
-        const int t = rtok[row];
-        const bool ok = t >= 0 && j <= t;
-        const float p = ok ? __builtin_amdgcn_exp2f(S[i] * c2 - rlse[row]) : 0.f;
-        const float ds = p * (dP[i] - rdel[row]) * scale;
+        // rows past the list carry t = -1, so one compare masks them and the
+        // keys after t in the local block (exp of a masked entry is finite and dropped)
+        const float e = __builtin_amdgcn_exp2f(S[i] * c2 - lv[i / 4][i % 4]);
+        const float p = j <= tk[i / 4][i % 4] ? e : 0.f;
+        const float ds = p * (dP[i] - dl[i / 4][i % 4]);  // the softmax scale is applied in the merges
         p8[i / 8][i % 8] = (__bf16)p;
         d8[i / 8][i % 8] = (__bf16)ds;
         reinterpret_cast<uint16_t*>(DSr)[row * DSR + 32 * kt + col] = bf16_bits(ds);
@@ -358,7 +383,9 @@ __global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
       }
     }
     __syncthreads();  // dS rows of the step complete
-    // dq[row][d] = sum over the block's keys of dS[row][key] K[key][d]
+    // dq^T[d][row] = sum over the block's keys of K^T[d][key] dS^T[key][row]:
+    // each lane ends with one row and 4 runs of 4 consecutive d, stored as
+    // 8-byte bf16 groups
 #pragma unroll 1
     for (int ii = 0; ii < RT; ++ii) {
       const int f = wave * RT + ii;
@@ -366,13 +393,19 @@ __global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
       f32x16 acc = {};
 #pragma unroll
       for (int ks = 0; ks < BS / 16; ++ks)
-        acc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(DSr + (rt2 * 32 + col) * DSR + 16 * ks + 8 * half),
-                           *reinterpret_cast<const bf16x8*>(KTs + (32 * dt + col) * KTR + 16 * ks + 8 * half),
+        acc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(KTs + (32 * dt + col) * KTR + 16 * ks + 8 * half),
+                           *reinterpret_cast<const bf16x8*>(DSr + (rt2 * 32 + col) * DSR + 16 * ks + 8 * half),
                            acc);
+      const int rho = step * SR + rt2 * 32 + col;
+      if (rho < nr) {
+        uint16_t* dst = a.dqp + ((size_t)off * R + rho) * D + 32 * dt + 4 * half;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rho = step * SR + rt2 * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-        if (rho < nr) a.dqp[((size_t)off * R + rho) * D + 32 * dt + col] = bf16_bits(acc[i]);
+        for (int i4 = 0; i4 < 4; ++i4) {
+          bf16x4 v;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = (__bf16)acc[4 * i4 + u];
+          *reinterpret_cast<bf16x4*>(dst + 8 * i4) = v;
+        }
       }
     }
   }
@@ -442,9 +475,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += (float)v[i];
   }
+  const float sc = l.scale_log2 * kLn2;
   float* dst = a.dq + (((size_t)s * l.T + l.t0 + tl) * l.Hq + h) * D + part * 8;
-  *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-  *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0] * sc, acc[1] * sc, acc[2] * sc, acc[3] * sc};
+  *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4] * sc, acc[5] * sc, acc[6] * sc, acc[7] * sc};
 }
 
 // ---------------------------------------------------------------------------
@@ -476,13 +510,14 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs a) {
       av[i] += pv[u];
     }
   }
+  const float sc = l.scale_log2 * kLn2;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int u = threadIdx.x + 256 * i;
     const int kr = u / D, dd = u % D;
     if (kr < nkey) {
       const size_t o = (((size_t)s * l.T + kb + kr) * l.G + g) * D + dd;
-      a.dk[o] = a.accumulate ? a.dk[o] + ak[i] : ak[i];
+      a.dk[o] = a.accumulate ? a.dk[o] + ak[i] * sc : ak[i] * sc;
       a.dv[o] = a.accumulate ? a.dv[o] + av[i] : av[i];
     }
   }

@@ -27,6 +27,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // structs are not promoted to registers by the compiler and end in scratch.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;  // raw bfloat16 bits in memory
 
 constexpr int kWave = 64;
