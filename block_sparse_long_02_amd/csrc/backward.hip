@@ -126,8 +126,15 @@ __global__ __launch_bounds__(256) void bwd_sort_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Row tiles of 32 (entry, head) rows per wave per step: two for 128-key
 // blocks (each wave owns one key tile), one otherwise (waves also split rows).
+#ifndef MSA_BWD_RTW128
+#define MSA_BWD_RTW128 2
+#endif
+// Workgroups per CU the list kernel is compiled for (register budget).
+#ifndef MSA_BWD_MIN_BLOCKS
+#define MSA_BWD_MIN_BLOCKS 1
+#endif
 template <int BS>
-constexpr int bwd_rtw() { return BS == 128 ? 2 : 1; }
+constexpr int bwd_rtw() { return BS == 128 ? MSA_BWD_RTW128 : 1; }
 
 template <int BS>
 struct BwdLds {
@@ -157,7 +164,7 @@ struct BwdLds {
 };
 
 template <int BS>
-__global__ __launch_bounds__(256, 1) void bwd_list_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdArgs a) {
   using Lds = BwdLds<BS>;
   constexpr int KT = Lds::KT, NRG = Lds::NRG, RTW = Lds::RTW, RT = Lds::RT, SR = Lds::SR;
   constexpr int KTR = Lds::KTR, QR = Lds::QR, QTR = Lds::QTR, DSR = Lds::DSR;
