@@ -18,10 +18,10 @@
 // Work split (block-major, the prefill's (s, g, window, block) lists, here
 // holding every selected block of a row, its local block included):
 //  1. bwd_delta_kernel: Delta per (token, head) row;
-//  2. the lists, then bwd_sort_kernel: each list's entries sorted by
-//     (token, slot), so that the dk/dv sums below run in an order that does
-//     not depend on how the lists were filled (their positions come from
-//     integer atomics);
+//  2. the lists, then each list's entries sorted by (token, slot)
+//     (launch_sort_lists), so that the dk/dv sums below run in an order that
+//     does not depend on how the lists were filled (their positions come
+//     from integer atomics);
 //  3. bwd_list_kernel: one workgroup per list.  K^T of the block sits in LDS,
 //     each wave owns one 32-key tile (its K and V rows in registers) and
 //     steps over the list's (entry, head) rows: S = Q K^T and dP = dO V^T on
@@ -73,52 +73,6 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
 #pragma unroll
   for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
   if (row < nrows && part == 0) a.delta[row] = acc;
-}
-
-// ---------------------------------------------------------------------------
-// 2. Sort each list's entries (tl << rank_bits | slot, all distinct) in LDS
-//    and point every row slot at its entry's new list position.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_sort_kernel(BwdArgs a) {
-  __shared__ uint32_t key[kListWindow];
-  const PrefillMainArgs& l = a.l;
-  const int w = blockIdx.x;
-  if (w >= l.n_work[0]) return;
-  const long lid = l.work[w].x;
-  const int count = l.cnt[lid];
-  // one entry per token of the window when a row's valid entries are
-  // distinct; a longer list (duplicate input) keeps its order
-  if (count > kListWindow) return;
-  int b, g, s;
-  bwd_list_of(l, lid, &b, &g, &s);
-  const int off = l.offs[lid];
-  const int tid = threadIdx.x;
-  int n2 = 1;
-  while (n2 < count) n2 <<= 1;
-  for (int i = tid; i < n2; i += 256) key[i] = i < count ? (uint32_t)l.entries[off + i] : 0xffffffffu;
-  __syncthreads();
-  for (int kk = 2; kk <= n2; kk <<= 1)
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int i = tid; i < n2; i += 256) {
-        const int p = i ^ jj;
-        if (p > i) {
-          const uint32_t x = key[i], y = key[p];
-          const bool up = (i & kk) == 0;
-          if ((x > y) == up) {
-            key[i] = y;
-            key[p] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  const uint32_t mask = (1u << l.rank_bits) - 1u;
-  for (int i = tid; i < count; i += 256) {
-    const uint32_t e = key[i];
-    l.entries[off + i] = (int32_t)e;
-    const long row = ((long)s * l.tc + (long)(e >> l.rank_bits)) * l.G + g;
-    l.epos[(size_t)row * l.KS + (e & mask)] = off + i;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -543,8 +497,7 @@ hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t st) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if ((err = launch_block_lists(l, kBwdListTile, st)) != hipSuccess) return err;
-  if (l.max_work > 0) bwd_sort_kernel<<<(unsigned)l.max_work, 256, 0, st>>>(a);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = launch_sort_lists(l, st)) != hipSuccess) return err;
   prof_mark(st, MSA_STAGE_BWD_LISTS);
   if (l.max_work > 0) {
     if (l.B == 128) bwd_list_kernel<128><<<(unsigned)l.max_work, 256, 0, st>>>(a);

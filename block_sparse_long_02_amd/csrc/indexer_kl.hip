@@ -25,7 +25,8 @@
 //     and the index logits on MFMA, p_M, p_I, the entry's KL term and dS
 //     (bf16, row-major per entry);
 //  4. kl_list_kernel: per list, d idx_q of each entry (dS . idx_k) and the
-//     list's d idx_k partial (dS^T . idx_q) on MFMA;
+//     list's d idx_k partial (dS^T . idx_q) on MFMA, over the entries in
+//     (token, slot) order (the lists are sorted right after they are built);
 //  5. kl_row_out_kernel / kl_dk_reduce_kernel: fixed-order sums per row and
 //     per key block.  No atomic touches a value: results are reproducible.
 #include "msa_device.h"
@@ -282,9 +283,6 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t Dr[EC * DRR];
   __shared__ __attribute__((aligned(16))) bf16_t DT[BS * ER];
   __shared__ __attribute__((aligned(16))) bf16_t QT[DI * ER];
-  // the list's entries sorted by (token, slot): its d idx_k partial is then
-  // accumulated in an order that does not depend on how the list was filled
-  __shared__ uint64_t order[kListWindow];
   const PrefillMainArgs& l = a.l;
   const long lid = blockIdx.x;
   const int count = l.cnt[lid];
@@ -297,32 +295,6 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
   const int kb = b * l.B;
   const int nkey = min(BS, l.T - kb);
 
-  // One entry per token of the list's window when a row's valid selections are
-  // distinct, so count <= kListWindow; otherwise the list order is kept.
-  const bool sorted = count <= kListWindow;
-  if (sorted) {
-    int n2 = 1;
-    while (n2 < count) n2 <<= 1;
-    for (int i = tid; i < n2; i += 256)
-      order[i] = i < count ? ((uint64_t)(uint32_t)l.entries[off + i] << 32) | (uint32_t)i : ~0ull;
-    __syncthreads();
-    for (int kk = 2; kk <= n2; kk <<= 1)
-      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-        for (int i = tid; i < n2; i += 256) {
-          const int p = i ^ jj;
-          if (p > i) {
-            const uint64_t x = order[i], y = order[p];
-            const bool up = (i & kk) == 0;
-            if ((x > y) == up) {
-              order[i] = y;
-              order[p] = x;
-            }
-          }
-        }
-        __syncthreads();
-      }
-  }
-  auto at_rank = [&](int i) -> int { return sorted ? (int)(uint32_t)order[i] : i; };
 
   // idx_k block, transposed: IkT[c][key], in 4 keys x 4 c units
   for (int u = tid; u < (BS / 4) * (DI / 4); u += 256) {
@@ -350,7 +322,7 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
     if (tid < EC) {
       int qr = -1;
       if (tid < n) {
-        const int ent = l.entries[off + at_rank(c0 + tid)];
+        const int ent = l.entries[off + c0 + tid];
         qr = (int)(((size_t)s * l.T + l.t0 + (ent >> l.rank_bits)) * l.G + g);
       }
       qrow[tid] = qr;
@@ -362,7 +334,7 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int en = 4 * e4 + i;
-        r[i] = en < n ? *reinterpret_cast<const u32x2*>(a.ds + (size_t)(off + at_rank(c0 + en)) * BS + 4 * k4)
+        r[i] = en < n ? *reinterpret_cast<const u32x2*>(a.ds + (size_t)(off + c0 + en) * BS + 4 * k4)
                       : u32x2{0u, 0u};
         *reinterpret_cast<u32x2*>(Dr + en * DRR + 4 * k4) = r[i];
       }
@@ -397,7 +369,7 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int en = 8 * (i / 4) + 4 * half + (i % 4);
-        if (en < n) a.dq_e[(size_t)(off + at_rank(c0 + en)) * DI + 32 * wave + col] = acc[i];
+        if (en < n) a.dq_e[(size_t)(off + c0 + en) * DI + 32 * wave + col] = acc[i];
       }
     }
     // d idx_k partial: [key][c] += sum_entry dS[entry][key] idx_q[entry][c]
@@ -512,6 +484,9 @@ hipError_t launch_indexer_kl(const IndexerKlArgs& a, hipStream_t st) {
   const int mt = kAttnRows / R;
   hipError_t err = launch_block_lists(l, mt, st);
   if (err != hipSuccess) return err;
+  // entries in (token, slot) order within each list before any per-entry
+  // value is written: the d idx_k sums then run in a fixed order
+  if ((err = launch_sort_lists(l, st)) != hipSuccess) return err;
   if ((err = launch_list_work(l, 128, a.work_a, a.n_work_a, st)) != hipSuccess) return err;
   const long n_rows = (long)l.batch * l.tc * l.G;
 #define MSA_KL_DISPATCH(KERNEL, GRID, ...)                                                        \

@@ -90,6 +90,9 @@ hipError_t launch_prefill_main_sparse(const PrefillMainArgs& a, hipStream_t st);
 // Block lists of a chunk (cnt, offs, epos -> list positions, entries, rinfo)
 // and the work list of tiles of mt entries (a.work, a.n_work).
 hipError_t launch_block_lists(const PrefillMainArgs& a, int mt, hipStream_t st);
+// Sort every list's entries by (token, slot) and rewrite epos (after
+// launch_block_lists): fixed summation order over a list.
+hipError_t launch_sort_lists(const PrefillMainArgs& a, hipStream_t st);
 // Another work list over the same lists, tiles of mt entries (a.bsum reused).
 hipError_t launch_list_work(const PrefillMainArgs& a, int mt, int2* work, int32_t* n_work, hipStream_t st);
 hipError_t launch_prefill_main_dense(const PrefillMainArgs& a, hipStream_t st);

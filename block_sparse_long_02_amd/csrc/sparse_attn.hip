@@ -828,6 +828,53 @@ hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t value, hipStream_t st) 
   return hipGetLastError();
 }
 
+// Sorts each block list's entries (tl << rank_bits | slot, all distinct) in
+// LDS and points every row slot at its entry's new list position, so that
+// sums over a list run in an order that does not depend on how the integer
+// atomics filled it.  A list longer than kListWindow (only possible with
+// duplicate selections, which are invalid input) keeps its order.
+__global__ __launch_bounds__(256) void lists_sort_kernel(PrefillMainArgs a) {
+  __shared__ uint32_t key[kListWindow];
+  const long lid = blockIdx.x;
+  const int count = a.cnt[lid];
+  if (count < 2 || count > kListWindow) return;
+  const int g = (int)((lid / a.nbl) / a.nwin % a.G);
+  const int s = (int)((lid / a.nbl) / a.nwin / a.G);
+  const int off = a.offs[lid];
+  const int tid = threadIdx.x;
+  int n2 = 1;
+  while (n2 < count) n2 <<= 1;
+  for (int i = tid; i < n2; i += 256) key[i] = i < count ? (uint32_t)a.entries[off + i] : 0xffffffffu;
+  __syncthreads();
+  for (int kk = 2; kk <= n2; kk <<= 1)
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int i = tid; i < n2; i += 256) {
+        const int p = i ^ jj;
+        if (p > i) {
+          const uint32_t x = key[i], y = key[p];
+          const bool up = (i & kk) == 0;
+          if ((x > y) == up) {
+            key[i] = y;
+            key[p] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  const uint32_t mask = (1u << a.rank_bits) - 1u;
+  for (int i = tid; i < count; i += 256) {
+    const uint32_t e = key[i];
+    a.entries[off + i] = (int32_t)e;
+    const long row = ((long)s * a.tc + (long)(e >> a.rank_bits)) * a.G + g;
+    a.epos[(size_t)row * a.KS + (e & mask)] = off + i;
+  }
+}
+
+hipError_t launch_sort_lists(const PrefillMainArgs& a, hipStream_t st) {
+  if (a.nlists > 0) lists_sort_kernel<<<(unsigned)a.nlists, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_list_work(const PrefillMainArgs& a, int mt, int2* work, int32_t* n_work, hipStream_t st) {
   const int nblk = (int)((a.nlists + kScanItems - 1) / kScanItems);
   lists_scan_reduce_kernel<<<nblk, 1024, 0, st>>>(a.cnt, a.bsum, a.nlists, mt);
