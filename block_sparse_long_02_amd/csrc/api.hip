@@ -602,7 +602,7 @@ int msa_indexer_kl(const msa_dims* dims, const void* q, const void* k, const voi
       lse == nullptr || kl == nullptr || d_idx_q == nullptr || d_idx_k == nullptr)
     return MSA_ERR_INVALID_ARG;
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(idx_q, 16) || misaligned(idx_k, 16) ||
-      misaligned(block_idx, 4) || misaligned(lse, 4) || misaligned(kl, 4) || misaligned(d_idx_q, 4) ||
+      misaligned(block_idx, 4) || misaligned(lse, 4) || misaligned(kl, 4) || misaligned(d_idx_q, 16) ||
       misaligned(d_idx_k, 4))
     return MSA_ERR_ALIGNMENT;
   if ((st = check_workspace(p.total, workspace, workspace_bytes)) != MSA_OK) return st;

@@ -444,42 +444,52 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // 5. dk, dv of a key block of one (sequence, group): its lists' partials in
-//    window order; added onto earlier query chunks.
+//    window order; added onto earlier query chunks.  The block's dk and dv
+//    elements are split over kDkvSplit workgroups; the lists' counts are read
+//    in parallel and walked in order by every thread.
 // ---------------------------------------------------------------------------
+constexpr int kDkvSplit = 4;
+
 template <int BS>
 __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs a) {
-  constexpr int PER = BS * D / 256;
+  constexpr int PER = 2 * BS * D / 256 / kDkvSplit;  // elements per thread (dk block, then dv block)
+  __shared__ int slot[256];
   const PrefillMainArgs& l = a.l;
-  const int b = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int b = blockIdx.x, g = blockIdx.y % l.G, s = blockIdx.y / l.G, z = blockIdx.z;
   const int kb = b * l.B;
   const int nkey = min(BS, l.T - kb);
-  float ak[PER], av[PER];
+  const int u0 = z * (2 * BS * D / kDkvSplit);
+  float acc[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    ak[i] = 0.f;
-    av[i] = 0.f;
-  }
-  for (int x = 0; x < l.nwin; ++x) {
-    const size_t lid = (((size_t)s * l.G + g) * l.nwin + x) * l.nbl + b;
-    if (l.cnt[lid] == 0) continue;
-    const float* pk = a.part + (size_t)a.slot_of[lid] * 2 * BS * D;
-    const float* pv = pk + (size_t)BS * D;
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  for (int base = 0; base < l.nwin; base += 256) {
+    __syncthreads();
+    {
+      const int x = base + (int)threadIdx.x;
+      const size_t lid = (((size_t)s * l.G + g) * l.nwin + x) * l.nbl + b;
+      slot[threadIdx.x] = x < l.nwin && l.cnt[lid] > 0 ? a.slot_of[lid] : -1;
+    }
+    __syncthreads();
+    const int n = min(256, l.nwin - base);
+    for (int i = 0; i < n; ++i) {
+      const int sl = slot[i];
+      if (sl < 0) continue;
+      const float* part = a.part + (size_t)sl * 2 * BS * D + u0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int u = threadIdx.x + 256 * i;
-      ak[i] += pk[u];
-      av[i] += pv[u];
+      for (int e = 0; e < PER; ++e) acc[e] += part[threadIdx.x + 256 * e];
     }
   }
-  const float sc = l.scale_log2 * kLn2;
+  const float sc = l.scale_log2 * kLn2;  // dk carries the softmax scale, dv does not
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int u = threadIdx.x + 256 * i;
-    const int kr = u / D, dd = u % D;
+  for (int e = 0; e < PER; ++e) {
+    const int u = u0 + threadIdx.x + 256 * e;
+    const bool is_k = u < BS * D;
+    const int uu = is_k ? u : u - BS * D;
+    const int kr = uu / D, dd = uu % D;
     if (kr < nkey) {
-      const size_t o = (((size_t)s * l.T + kb + kr) * l.G + g) * D + dd;
-      a.dk[o] = a.accumulate ? a.dk[o] + ak[i] * sc : ak[i] * sc;
-      a.dv[o] = a.accumulate ? a.dv[o] + av[i] : av[i];
+      float* dst = (is_k ? a.dk : a.dv) + (((size_t)s * l.T + kb + kr) * l.G + g) * D + dd;
+      const float v = is_k ? acc[e] * sc : acc[e];
+      *dst = a.accumulate ? *dst + v : v;
     }
   }
 }
@@ -508,7 +518,7 @@ hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t st) {
   prof_mark(st, MSA_STAGE_BWD_MERGE);
   bwd_dq_kernel<<<(unsigned)((nrows * 16 + 255) / 256), 256, 0, st>>>(a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  const dim3 grid((unsigned)((l.T + l.B - 1) / l.B), (unsigned)l.G, (unsigned)l.batch);
+  const dim3 grid((unsigned)((l.T + l.B - 1) / l.B), (unsigned)(l.G * l.batch), (unsigned)kDkvSplit);
   if (l.B == 128) bwd_dkv_kernel<128><<<grid, 256, 0, st>>>(a);
   else if (l.B == 64) bwd_dkv_kernel<64><<<grid, 256, 0, st>>>(a);
   else bwd_dkv_kernel<32><<<grid, 256, 0, st>>>(a);

@@ -403,15 +403,16 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 5a. Per row and index dimension: KL and d idx_q, summed in slot order.
+// 5a. Per row and 4 index dimensions: KL and d idx_q, summed in slot order.
 // ---------------------------------------------------------------------------
 __global__ void kl_row_out_kernel(IndexerKlArgs a) {
   const PrefillMainArgs& l = a.l;
-  const long n = (long)l.batch * l.tc * l.G * a.di;
+  const int dq4 = a.di / 4;
+  const long n = (long)l.batch * l.tc * l.G * dq4;
   const long x = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (x >= n) return;
-  const long row = x / a.di;
-  const int cc = (int)(x % a.di);
+  const long row = x / dq4;
+  const int c4 = (int)(x % dq4);
   const long per_b = (long)l.tc * l.G;
   const int s = (int)(row / per_b);
   const int tl = (int)((row % per_b) / l.G);
@@ -419,59 +420,62 @@ __global__ void kl_row_out_kernel(IndexerKlArgs a) {
   const size_t orow = ((size_t)s * l.T + l.t0 + tl) * l.G + g;
   const int nv = l.rinfo[row] & 0x3fffffff;
   const int32_t* pos = l.epos + (size_t)row * l.KS;
-  float dq = 0.f, kl = 0.f;
+  f32x4 dq = {0.f, 0.f, 0.f, 0.f};
+  float kl = 0.f;
   for (int q = 0; q < nv; ++q) {
-    dq += a.dq_e[(size_t)pos[q] * a.di + cc];
-    if (cc == 0) kl += a.kl_e[pos[q]];
+    const int p = pos[q];
+    dq += *reinterpret_cast<const f32x4*>(a.dq_e + (size_t)p * a.di + 4 * c4);
+    if (c4 == 0) kl += a.kl_e[p];
   }
-  a.d_idx_q[orow * a.di + cc] = dq;
-  if (cc == 0) a.kl[orow] = kl;
+  *reinterpret_cast<f32x4*>(a.d_idx_q + orow * a.di + 4 * c4) = dq;
+  if (c4 == 0) a.kl[orow] = kl;
 }
 
 // ---------------------------------------------------------------------------
 // 5b. Per key block: d idx_k = sum over the block's lists (group, window) of
-//     their partials, in that order; added onto earlier query chunks.
+//     their partials, in that order; added onto earlier query chunks.  The
+//     block's elements are split over kDkSplit workgroups; the lists' counts
+//     are read 256 at a time in parallel and walked in order by every thread.
 // ---------------------------------------------------------------------------
+constexpr int kDkSplit = 4;
+
 template <int DI, int BS>
 __global__ __launch_bounds__(256) void kl_dk_reduce_kernel(IndexerKlArgs a) {
-  constexpr int kMaxLists = 1024;  // lists of the block staged at a time
-  __shared__ long lids[kMaxLists];
-  __shared__ int nl;
+  constexpr int PER = BS * DI / 256 / kDkSplit;  // elements per thread
+  __shared__ int live[256];
   const PrefillMainArgs& l = a.l;
-  const int b = blockIdx.x, s = blockIdx.y;
+  const int b = blockIdx.x, s = blockIdx.y, z = blockIdx.z;
   const int kb = b * l.B;
   const int nkey = min(BS, l.T - kb);
   const int nall = l.G * l.nwin;  // lists of this key block, in (group, window) order
-  float acc[(BS * DI + 255) / 256];
+  const int u0 = z * (BS * DI / kDkSplit);
+  float acc[PER];
 #pragma unroll
-  for (int i = 0; i < (BS * DI + 255) / 256; ++i) acc[i] = 0.f;
-  for (int base = 0; base < nall; base += kMaxLists) {
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  for (int base = 0; base < nall; base += 256) {
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int n = 0;
-      for (int x = base; x < min(nall, base + kMaxLists); ++x) {
-        const size_t lid = (((size_t)s * l.G + x / l.nwin) * l.nwin + x % l.nwin) * l.nbl + b;
-        if (l.cnt[lid] > 0) lids[n++] = (long)lid;
-      }
-      nl = n;
+    {
+      const int x = base + (int)threadIdx.x;
+      const size_t lid = (((size_t)s * l.G + x / l.nwin) * l.nwin + x % l.nwin) * l.nbl + b;
+      live[threadIdx.x] = x < nall && l.cnt[lid] > 0;
     }
     __syncthreads();
-    const int n = nl;
-    for (int x = 0; x < n; ++x) {
-      const float* part = a.dk_part + (size_t)lids[x] * BS * DI;
+    const int n = min(256, nall - base);
+    for (int i = 0; i < n; ++i) {
+      if (!live[i]) continue;
+      const int x = base + i;
+      const size_t lid = (((size_t)s * l.G + x / l.nwin) * l.nwin + x % l.nwin) * l.nbl + b;
+      const float* part = a.dk_part + lid * BS * DI + u0;
 #pragma unroll
-      for (int i = 0; i < (BS * DI + 255) / 256; ++i) {
-        const int u = threadIdx.x + 256 * i;
-        if (u < nkey * DI) acc[i] += part[u];
-      }
+      for (int e = 0; e < PER; ++e) acc[e] += part[threadIdx.x + 256 * e];
     }
   }
 #pragma unroll
-  for (int i = 0; i < (BS * DI + 255) / 256; ++i) {
-    const int u = threadIdx.x + 256 * i;
+  for (int e = 0; e < PER; ++e) {
+    const int u = u0 + threadIdx.x + 256 * e;
     if (u < nkey * DI) {
       float* dst = a.d_idx_k + ((size_t)s * l.T + kb) * DI + u;
-      *dst = a.accumulate_dk ? *dst + acc[i] : acc[i];
+      *dst = a.accumulate_dk ? *dst + acc[e] : acc[e];
     }
   }
 }
@@ -509,11 +513,11 @@ hipError_t launch_indexer_kl(const IndexerKlArgs& a, hipStream_t st) {
   if ((err = hipGetLastError()) != hipSuccess) return err;
   MSA_KL_DISPATCH(kl_list_kernel, dim3((unsigned)l.nlists), a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  const long nout = n_rows * a.di;
+  const long nout = n_rows * (a.di / 4);
   kl_row_out_kernel<<<(unsigned)((nout + 255) / 256), 256, 0, st>>>(a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int nb = (l.T + l.B - 1) / l.B;
-  MSA_KL_DISPATCH(kl_dk_reduce_kernel, dim3((unsigned)nb, (unsigned)l.batch), a);
+  MSA_KL_DISPATCH(kl_dk_reduce_kernel, dim3((unsigned)nb, (unsigned)l.batch, (unsigned)kDkSplit), a);
 #undef MSA_KL_DISPATCH
   return hipGetLastError();
 }
