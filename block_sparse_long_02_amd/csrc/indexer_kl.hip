@@ -171,11 +171,20 @@ __global__ void kl_row_lse_kernel(IndexerKlArgs a) {
 //    the group are visited in turn and their exp(x - lse) summed in the lane,
 //    so p_M needs no cross-lane work and the index logits are computed once.
 // ---------------------------------------------------------------------------
+// Key tiles per pass over the R heads' q rows (each pass re-reads them) and
+// workgroups per CU the entry kernel is compiled for.
+#ifndef MSA_KL_ENTRY_KC
+#define MSA_KL_ENTRY_KC 4
+#endif
+#ifndef MSA_KL_ENTRY_MINB
+#define MSA_KL_ENTRY_MINB 1
+#endif
+
 template <int DI, int BS>
-__global__ __launch_bounds__(256, 2) void kl_entry_kernel(IndexerKlArgs a) {
+__global__ __launch_bounds__(256, MSA_KL_ENTRY_MINB) void kl_entry_kernel(IndexerKlArgs a) {
   constexpr int KROW = D + 8, KP = DI + 8;
   constexpr int KT = BS / 32;
-  constexpr int KC = KT < 2 ? KT : 2;
+  constexpr int KC = KT < MSA_KL_ENTRY_KC ? KT : MSA_KL_ENTRY_KC;
   constexpr int MT = 128;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[BS * KROW];
   __shared__ __attribute__((aligned(16))) bf16_t Is[BS * KP];
@@ -215,7 +224,8 @@ __global__ __launch_bounds__(256, 2) void kl_entry_kernel(IndexerKlArgs a) {
     const float lse2_i = a.lse_i[((size_t)s * l.tc + tl) * l.G + g];
     bf16_t* dsrow = a.ds + (size_t)(off + min(pos, count - 1)) * BS;
     float kl = 0.f;
-    // chunks of KC key tiles keep the accumulators few and statically indexed
+    // chunks of KC key tiles: the q rows are read once per chunk (all of the
+    // block's tiles by default, one workgroup per CU for the registers)
 #pragma unroll 1
     for (int k0 = 0; k0 < KT; k0 += KC) {
       float pm[KC][16];  // sum over the heads of exp(x - lse): R * p_M
