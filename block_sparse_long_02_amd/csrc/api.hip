@@ -327,9 +327,6 @@ int make_bwd_plan(const msa_dims* d, BwdPlan* p) {
   const long max_win = (kMaxInt32 - 1) / lists_per_win;
   if (max_win < 1) return MSA_ERR_UNSUPPORTED;
   if (max_win * msa::kListWindow < lim) lim = max_win * msa::kListWindow;
-  // dq partial rows are addressed as (list position * R + head) in int32 arithmetic per list
-  const long lim3 = (kMaxInt32 / 2) / ((long)per_tok_entries * p->R > 0 ? (long)per_tok_entries * p->R : 1);
-  if (lim3 < lim) lim = lim3;
   long tc;
   if (d->query_chunk > 0) {
     tc = d->query_chunk < T ? d->query_chunk : T;

@@ -118,14 +118,16 @@ def test_backward_bitwise_deterministic():
 
 def test_backward_several_list_windows():
     """T beyond two 8192-token list windows: lists of one key block in several
-    windows, their dk/dv partials summed across windows."""
+    windows, their dk/dv partials summed across windows; then the same in four
+    query chunks, dk/dv accumulated across chunks."""
     T, Hq, G, B, k = 16500, 4, 2, 64, 4
-    say(f"[backward multi-window] T={T}")
     inp = inputs.make_prefill(T, Hq, G, 128, 64, seed=931)
     out, lse, bidx = gpu_prefill(inp, B, k)
     dout = _dout((1, T, Hq, 128), 932)
-    dq, dk, dv = gpu_backward(inp, out, lse, bidx, dout, B, k)
     rq, rk, rv = orc.attention_backward(inp.q, inp.k, inp.v, dout, bidx, B)
-    check_grad(dq, rq, "dq")
-    check_grad(dk, rk, "dk")
-    check_grad(dv, rv, "dv")
+    for chunk in (0, 5120):
+        say(f"[backward multi-window] T={T} query_chunk={chunk}")
+        dq, dk, dv = gpu_backward(inp, out, lse, bidx, dout, B, k, query_chunk=chunk)
+        check_grad(dq, rq, "dq")
+        check_grad(dk, rk, "dk")
+        check_grad(dv, rv, "dv")

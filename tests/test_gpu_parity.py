@@ -582,24 +582,25 @@ def test_indexer_kl_several_list_windows():
     """T beyond two 8192-token list windows: d idx_k summed over the lists of
     one key block in several windows."""
     T, Hq, G, di, B, k = 16500, 4, 2, 64, 64, 4
-    say(f"[indexer KL multi-window] T={T}")
     inp = inputs.make_prefill(T, Hq, G, 128, di, seed=941)
     _, lse, bidx = gpu_prefill(inp, B, k)
-    dims = bd.make_dims(1, T, Hq, G, index_dim=di, block_size=B, topk=k)
-    kl = torch.empty((1, T, G), device="cuda")
-    dq = torch.empty((1, T, G, di), device="cuda")
-    dk = torch.empty((1, T, di), device="cuda")
-    bd.msa_indexer_kl(dims, inp.q.cuda(), inp.k.cuda(), inp.idx_q.cuda(), inp.idx_k.cuda(), bidx.cuda(),
-                      lse.cuda(), kl, dq, dk)
-    torch.cuda.synchronize()
     ores = orc.indexer_kl(inp.q, inp.k, inp.idx_q, inp.idx_k, bidx, B)
     kl_ref = np.stack([ores["kl"][(0, t)] for t in range(T)])[None]
     dq_ref = np.stack([ores["d_idx_q"][(0, t)] for t in range(T)])[None]
-    err = np.abs(kl.cpu().double().numpy() - kl_ref)
-    say(f"  kl: max-abs {err.max():.3e}")
-    assert (err <= 1e-3 * np.abs(kl_ref) + 1e-4).all()
-    _rel_close(dq.cpu().numpy(), dq_ref, "d_idx_q")
-    _rel_close(dk.cpu().numpy(), ores["d_idx_k"], "d_idx_k")
+    for chunk in (0, 5120):  # one chunk, then four with d idx_k accumulated across them
+        say(f"[indexer KL multi-window] T={T} query_chunk={chunk}")
+        dims = bd.make_dims(1, T, Hq, G, index_dim=di, block_size=B, topk=k, query_chunk=chunk)
+        kl = torch.empty((1, T, G), device="cuda")
+        dq = torch.empty((1, T, G, di), device="cuda")
+        dk = torch.empty((1, T, di), device="cuda")
+        bd.msa_indexer_kl(dims, inp.q.cuda(), inp.k.cuda(), inp.idx_q.cuda(), inp.idx_k.cuda(), bidx.cuda(),
+                          lse.cuda(), kl, dq, dk)
+        torch.cuda.synchronize()
+        err = np.abs(kl.cpu().double().numpy() - kl_ref)
+        say(f"  kl: max-abs {err.max():.3e}")
+        assert (err <= 1e-3 * np.abs(kl_ref) + 1e-4).all()
+        _rel_close(dq.cpu().numpy(), dq_ref, "d_idx_q")
+        _rel_close(dk.cpu().numpy(), ores["d_idx_k"], "d_idx_k")
 
 
 def test_indexer_kl_deterministic_and_zero_case():
