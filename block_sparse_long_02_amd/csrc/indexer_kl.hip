@@ -233,18 +233,26 @@ __global__ __launch_bounds__(256, MSA_KL_ENTRY_MINB) void kl_entry_kernel(Indexe
       for (int kt = 0; kt < KC; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) pm[kt][i] = 0.f;
+      // head r's q rows are in qop while head r + 1's are fetched into qnx
+      bf16x8 qop[D / 16], qnx[D / 16];
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) qop[ks] = load_bf16x8(l.q + qrow * D + 16 * ks + 8 * half);
+      float lse_nx = a.lse[qrow];
 #pragma unroll 1
       for (int r = 0; r < R; ++r) {
-        bf16x8 qop[D / 16];
+        const float lse2 = lse_nx * kLog2e;
+        const size_t rn = qrow + (r + 1 < R ? r + 1 : r);
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) qop[ks] = load_bf16x8(l.q + (qrow + r) * D + 16 * ks + 8 * half);
-        const float lse2 = a.lse[qrow + r] * kLog2e;
+        for (int ks = 0; ks < D / 16; ++ks) qnx[ks] = load_bf16x8(l.q + rn * D + 16 * ks + 8 * half);
+        lse_nx = a.lse[rn];
 #pragma unroll
         for (int kt = 0; kt < KC; ++kt) {
           const f32x16 x = logit_tile<D>(Ks, KROW, (k0 + kt) * 32, qop, col, half);
 #pragma unroll
           for (int i = 0; i < 16; ++i) pm[kt][i] += __builtin_amdgcn_exp2f(x[i] * c - lse2);
         }
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) qop[ks] = qnx[ks];
       }
 #pragma unroll
       for (int kt = 0; kt < KC; ++kt) {
