@@ -196,15 +196,14 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
   const int myrow = tid % SR, part_base = tid / SR;
   const int step_q = SR / R, step_r = SR % R;  // list-position and head advance per step
   int cur_p = myrow / R, cur_r = myrow % R;     // row of the next entry load
-  int ent = -1, ent_r = 0, ent_rho = 0;         // that load's result and its head / row index
+  int ent = -1, ent_r = 0;                      // that load's result and its head
   int row_e = -1, row_r = 0;                    // entry and head of the rows being fetched
   u32x4 qs[CPR], os[CPR];
   float lse_v = 0.f, del_v = 0.f;
   int tok_v = -1;
   auto load_ent = [&]() {
-    ent_rho = cur_p * R + cur_r;
     ent_r = cur_r;
-    ent = ent_rho < nr ? l.entries[off + cur_p] : -1;
+    ent = cur_p * R + cur_r < nr ? l.entries[off + cur_p] : -1;
     cur_p += step_q;
     cur_r += step_r;
     if (cur_r >= R) {
