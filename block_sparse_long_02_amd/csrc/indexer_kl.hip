@@ -328,53 +328,68 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(IkT + (4 * c4 + j) * IKR + 4 * k4) = o[j];
   }
-  __shared__ int qrow[EC];  // idx_q row offsets of the chunk's entries
-
   f32x16 dk[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) dk[i] = f32x16{};
 
+  // Each thread stages one 4 entries x 4 keys unit of the chunk's dS rows and
+  // one 4 entries x 4 dims unit of its idx_q rows.  The next chunk's units
+  // are fetched into registers while the current chunk computes, and the
+  // entries that address its idx_q rows one chunk earlier still.
+  constexpr int NUD = (EC / 4) * (BS / 4), NUQ = (EC / 4) * (DI / 4);
+  static_assert(NUD <= 256 && NUQ <= 256, "one unit per thread");
+  const bool has_d = tid < NUD, has_q = tid < NUQ;
+  const int de4 = tid / (BS / 4), dk4 = tid % (BS / 4);
+  const int qe4 = tid / (DI / 4), qc4 = tid % (DI / 4);
+  u32x2 dsr[4], qsr[4];
+  int ent4[4];
+  auto load_ent = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int en = c0 + 4 * qe4 + i;
+      ent4[i] = has_q && en < count ? l.entries[off + en] : -1;
+    }
+  };
+  auto load_data = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int en = c0 + 4 * de4 + i;
+      dsr[i] = has_d && en < count ? *reinterpret_cast<const u32x2*>(a.ds + (size_t)(off + en) * BS + 4 * dk4)
+                                   : u32x2{0u, 0u};
+      const int e = ent4[i];
+      qsr[i] = e >= 0 ? *reinterpret_cast<const u32x2*>(
+                            a.idx_q + (((size_t)s * l.T + l.t0 + (e >> l.rank_bits)) * l.G + g) * DI + 4 * qc4)
+                      : u32x2{0u, 0u};
+    }
+  };
+  auto store = [&]() {
+    u32x2 o[4];
+    if (has_d) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x2*>(Dr + (4 * de4 + i) * DRR + 4 * dk4) = dsr[i];
+      transpose4x4(dsr, o);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(DT + (4 * dk4 + j) * ER + 4 * de4) = o[j];
+    }
+    if (has_q) {
+      transpose4x4(qsr, o);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(QT + (4 * qc4 + j) * ER + 4 * qe4) = o[j];
+    }
+  };
+
+  load_ent(0);
+  load_data(0);
+  load_ent(EC);
   for (int c0 = 0; c0 < count; c0 += EC) {
     const int n = min(EC, count - c0);
     __syncthreads();  // the previous chunk's LDS reads are done (and IkT is written)
-    if (tid < EC) {
-      int qr = -1;
-      if (tid < n) {
-        const int ent = l.entries[off + c0 + tid];
-        qr = (int)(((size_t)s * l.T + l.t0 + (ent >> l.rank_bits)) * l.G + g);
-      }
-      qrow[tid] = qr;
-    }
-    // dS rows of the chunk, row-major and transposed, in 4 entries x 4 keys units
-    for (int u = tid; u < (EC / 4) * (BS / 4); u += 256) {
-      const int e4 = u / (BS / 4), k4 = u % (BS / 4);
-      u32x2 r[4], o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int en = 4 * e4 + i;
-        r[i] = en < n ? *reinterpret_cast<const u32x2*>(a.ds + (size_t)(off + c0 + en) * BS + 4 * k4)
-                      : u32x2{0u, 0u};
-        *reinterpret_cast<u32x2*>(Dr + en * DRR + 4 * k4) = r[i];
-      }
-      transpose4x4(r, o);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(DT + (4 * k4 + j) * ER + 4 * e4) = o[j];
-    }
-    __syncthreads();  // qrow
-    // idx_q rows of the chunk, transposed: QT[c][entry]
-    for (int u = tid; u < (EC / 4) * (DI / 4); u += 256) {
-      const int e4 = u / (DI / 4), c4 = u % (DI / 4);
-      u32x2 r[4], o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qr = qrow[4 * e4 + i];
-        r[i] = qr >= 0 ? *reinterpret_cast<const u32x2*>(a.idx_q + (size_t)qr * DI + 4 * c4) : u32x2{0u, 0u};
-      }
-      transpose4x4(r, o);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(QT + (4 * c4 + j) * ER + 4 * e4) = o[j];
-    }
+    store();
     __syncthreads();
+    if (c0 + EC < count) {
+      load_data(c0 + EC);
+      load_ent(c0 + 2 * EC);
+    }
     // d idx_q of the chunk's entries: [entry][c] = sum_key dS[entry][key] idx_k[key][c]
     if (wave < DI / 32) {
       f32x16 acc = {};
