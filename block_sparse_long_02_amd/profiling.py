@@ -7,6 +7,10 @@
       -> per-launch HBM traffic of a kernel from two --pmc passes (FETCH_SIZE,
          WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
          reads for the blit copy kernel of N bytes in the same run
+  python -m block_sparse_long_02_amd.profiling counters --dirs <dir> [<dir> ...]
+         --kernels k1,k2 --title T --command C --out <md>
+      -> per-dispatch SQ counters of the kernels (summed over the shader
+         engines) with instruction mix and MFMA-busy ratios
 
 The traffic file records a hash of the kernel's sources; bench.py reports the
 traffic only while the sources still match.
@@ -95,6 +99,46 @@ def pmc_traffic(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int) ->
             "source_sha256": source_hash(kernel)}
 
 
+# MI355X: 256 CUs in 32 shader engines, 4 SIMDs per CU
+SIMDS_PER_SE = 32
+N_SIMDS = 1024
+
+
+def counters_md(dirs, kernels, title: str, command: str) -> str:
+    rows = []
+    for d in dirs:
+        rows += _counter_rows(d)
+    names = sorted({r["Counter_Name"] for r in rows})
+    per = {}
+    for k in kernels:
+        per[k] = {}
+        for c in names:
+            v = _per_dispatch(rows, k, c)
+            if v:
+                per[k][c] = sum(v) / len(v)
+    out = [f"# {title}", "", "Commands (from the repository root, on one MI355X; one pass per counter set):", "",
+           "```", command, "```", "",
+           "Values are per dispatch, averaged over the dispatches of the kernel, each summed over the shader "
+           "engines (SQ counters).", "",
+           "| counter | " + " | ".join(kernels) + " |", "|---|" + "---:|" * len(kernels)]
+    for c in names:
+        out.append(f"| {c} | " + " | ".join(f"{per[k].get(c, float('nan')):.4g}" for k in kernels) + " |")
+
+    def ratio(k, a, b, scale=1.0):
+        x, y = per[k].get(a), per[k].get(b)
+        return f"{x / (y * scale):.3f}" if x is not None and y else "n/a"
+    out += ["", "Derived:", "", "| ratio | " + " | ".join(kernels) + " |", "|---|" + "---:|" * len(kernels),
+            "| VALU instructions per MFMA instruction | " +
+            " | ".join(ratio(k, "SQ_INSTS_VALU", "SQ_INSTS_MFMA") for k in kernels) + " |",
+            "| LDS instructions per MFMA instruction | " +
+            " | ".join(ratio(k, "SQ_INSTS_LDS", "SQ_INSTS_MFMA") for k in kernels) + " |",
+            f"| MFMA busy / (SQ busy x {SIMDS_PER_SE} SIMDs per engine) | " +
+            " | ".join(ratio(k, "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", SIMDS_PER_SE) for k in kernels) + " |",
+            "| waves' cycles waiting on any instruction / wave cycles | " +
+            " | ".join(ratio(k, "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES") for k in kernels) + " |"]
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -110,7 +154,19 @@ def main():
     s2.add_argument("--copy-bytes", type=int, required=True)
     s2.add_argument("--command", required=True)
     s2.add_argument("--out", required=True)
+    s3 = sub.add_parser("counters")
+    s3.add_argument("--dirs", nargs="+", required=True)
+    s3.add_argument("--kernels", required=True)
+    s3.add_argument("--title", required=True)
+    s3.add_argument("--command", required=True)
+    s3.add_argument("--out")
     a = ap.parse_args()
+    if a.cmd == "counters":
+        md = counters_md(a.dirs, a.kernels.split(","), a.title, a.command)
+        if a.out:
+            open(a.out, "w").write(md)
+        print(md)
+        return
     if a.cmd == "stats":
         md = kernel_stats_md(a.csv, a.title, a.command)
         if a.out:
