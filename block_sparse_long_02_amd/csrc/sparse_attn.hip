@@ -206,7 +206,7 @@ __device__ __forceinline__ void load_sel_chunk(int (&ev)[kSelChunk], const int32
 // attends its local block (a given selection may omit it).
 //
 // Popular blocks gather thousands of entries per list, so one global atomic
-// per entry would serialise on a few addresses.  A workgroup of
+// per entry would serialise on a few addresses.  A workgroup of up to
 // kCountRows rows therefore aggregates in LDS first: each entry's list id is
 // hashed into an LDS table whose counter hands out the entry's local rank;
 // then one global atomicAdd per distinct list reserves the workgroup's range,
@@ -219,7 +219,17 @@ constexpr int kHashSlots = 1 << kHashBits;
 constexpr uint32_t kHashEmpty = 0xffffffffu;
 constexpr uint32_t kDirect = 0x80000000u;
 
-__global__ __launch_bounds__(kCountRows) void lists_count_kernel(PrefillMainArgs a) {
+// At most kCountRows rows per workgroup, fewer when rows carry many slots, so
+// that the hash table stays at most half full (rows_wg * KS <= kHashSlots / 2);
+// a probe gives up after kMaxProbe slots and takes the direct path.
+constexpr int kMaxProbe = 64;
+
+__host__ __device__ inline int count_rows_per_wg(int KS) {
+  const int r = kHashSlots / (2 * (KS > 0 ? KS : 1));
+  return r < 1 ? 1 : (r > kCountRows ? kCountRows : r);
+}
+
+__global__ __launch_bounds__(kCountRows) void lists_count_kernel(PrefillMainArgs a, int rows_wg) {
   __shared__ uint32_t hkey[kHashSlots];
   __shared__ int32_t hval[kHashSlots];  // local counts, then the reserved global bases
   const int tid = threadIdx.x;
@@ -230,11 +240,11 @@ __global__ __launch_bounds__(kCountRows) void lists_count_kernel(PrefillMainArgs
   __syncthreads();
 
   const long n_rows = (long)a.batch * a.tc * a.G;
-  const long row = (long)blockIdx.x * kCountRows + tid;
+  const long row = (long)blockIdx.x * rows_wg + tid;
   // local ranks fit 16 bits while a workgroup holds fewer than 2^16 entries
-  const bool use_lds = (long)kCountRows * a.KS < 65536;
+  const bool use_lds = (long)rows_wg * a.KS < 65536;
   int rank = 0;
-  if (row < n_rows) {
+  if (tid < rows_wg && row < n_rows) {
     const long per_b = (long)a.tc * a.G;
     const int s = (int)(row / per_b);
     const int tl = (int)((row % per_b) / a.G);
@@ -256,7 +266,7 @@ __global__ __launch_bounds__(kCountRows) void lists_count_kernel(PrefillMainArgs
           if (use_lds) {
             const uint32_t key = (uint32_t)lid;
             uint32_t slot = (key * 2654435761u) >> (32 - kHashBits);
-            for (int p = 0; p < kHashSlots; ++p) {
+            for (int p = 0; p < kMaxProbe; ++p) {
               const uint32_t prev = atomicCAS(&hkey[slot], kHashEmpty, key);
               if (prev == kHashEmpty || prev == key) {
                 code = (slot << 16) | (uint32_t)atomicAdd(&hval[slot], 1);
@@ -890,7 +900,8 @@ hipError_t launch_block_lists(const PrefillMainArgs& a, int mt, hipStream_t st) 
   hipError_t err = launch_fill_i32(a.cnt, (size_t)a.nlists, 0, st);
   if (err != hipSuccess) return err;
   const long n_rows = (long)a.batch * a.tc * a.G;
-  lists_count_kernel<<<(unsigned)((n_rows + kCountRows - 1) / kCountRows), kCountRows, 0, st>>>(a);
+  const int rows_wg = count_rows_per_wg(a.KS);
+  lists_count_kernel<<<(unsigned)((n_rows + rows_wg - 1) / rows_wg), kCountRows, 0, st>>>(a, rows_wg);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if ((err = launch_list_work(a, mt, a.work, a.n_work, st)) != hipSuccess) return err;
   lists_scatter_kernel<<<(unsigned)((n_rows + 255) / 256), 256, 0, st>>>(a);
