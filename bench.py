@@ -73,7 +73,9 @@ def indexer_kl_flops(T, Hq, G, d, di, B, k):
     return G * (6.0 * di + 2.0 * d * (Hq // G)) * att.sum()
 
 
-def indexer_kl_ms(pin, bidx, lse, dev, stream, reps):
+def indexer_kl_ms(pin, bidx, lse, dev, stream, reps, keep=False):
+    """Mean ms of the indexer KL on the prefill's selection and lse (and its
+    outputs kl, d_idx_q, d_idx_k when keep)."""
     T, Hq, G, di = PF["T"], PF["Hq"], PF["G"], PF["di"]
     kd = bd.make_dims(1, T, Hq, G, index_dim=di, block_size=PF["B"], topk=PF["k"])
     kl = torch.empty((1, T, G), dtype=torch.float32, device=dev)
@@ -84,7 +86,32 @@ def indexer_kl_ms(pin, bidx, lse, dev, stream, reps):
                                    workspace=kws)
     fn()
     ms, _ = timed(fn, reps, stream)
-    return ms
+    return (ms, (kl, dq, dk)) if keep else ms
+
+
+def indexer_kl_checks(pin, pbidx, tensors, n_rows=24):
+    """Full-size checks of the indexer KL: kl and d idx_q on seeded sampled
+    rows against the oracle (row by row), and for d idx_k the property that
+    holds at any size (summed over all keys it vanishes: each row's
+    p_I - p_M sums to zero)."""
+    from oracle import msa_oracle as orc
+    kl, dq, dk = tensors
+    T, B = PF["T"], PF["B"]
+    rng = np.random.default_rng(79)
+    ts = sorted(set([0, B - 1, B, T - 1] + [int(x) for x in rng.integers(0, T, n_rows - 4)]))
+    rows = [(0, t) for t in ts]
+    ref = orc.indexer_kl_rows(pin.q.cpu(), pin.k.cpu(), pin.idx_q.cpu(), pin.idx_k.cpu(), pbidx.cpu(), B, rows)
+    klg, dqg = kl.cpu().double().numpy(), dq.cpu().double().numpy()
+    kl_ok = all(bool((np.abs(klg[r] - ref["kl"][r]) <= 1e-3 * np.abs(ref["kl"][r]) + 1e-4).all()) for r in rows)
+    err = sum(float(np.abs(dqg[r] - ref["d_idx_q"][r]).sum()) for r in rows)
+    tot = sum(float(np.abs(ref["d_idx_q"][r]).sum()) for r in rows)
+    mx = max(float(np.abs(dqg[r] - ref["d_idx_q"][r]).max()) for r in rows)
+    scale = max(float(np.abs(ref["d_idx_q"][r]).max()) for r in rows)
+    dk64 = dk.double()
+    inv = float((dk64.sum(dim=1).abs().max() / dk64.abs().sum(dim=1).max()).item())
+    return {"rows": len(rows), "kl_within_bound": kl_ok, "d_idx_q_max_abs": mx, "d_idx_q_ref_max": scale,
+            "d_idx_q_mean_rel": err / max(tot, 1e-300), "d_idx_k_sum_rel": inv,
+            "ok": bool(kl_ok and mx <= 1e-2 * scale and err / max(tot, 1e-300) <= 5e-3 and inv <= 1e-4)}
 
 
 def backward_flops(T, Hq, d, B, k):
@@ -590,11 +617,14 @@ def main():
         ms, _ = timed(fn, 10, stream)
         variants["decode_8x1m_sink"] = {"ms": round(ms, 4), "tok_s": round(DC["batch"] / (ms * 1e-3), 1)}
         # indexer KL loss + gradient on the headline prefill's own selection and lse
-        ms = indexer_kl_ms(pin, pbidx, plse, dev, stream, 3)
+        ms, kl_out = indexer_kl_ms(pin, pbidx, plse, dev, stream, 3, keep=True)
         kl_flops = indexer_kl_flops(PF["T"], PF["Hq"], PF["G"], PF["d"], PF["di"], PF["B"], PF["k"])
         variants["indexer_kl_t131072"] = {"ms": round(ms, 3), "tok_s": round(PF["T"] / (ms * 1e-3), 1),
                                           "algorithmic_tflop": round(kl_flops / 1e12, 3),
                                           "tflops": round(kl_flops / (ms * 1e-3) / 1e12, 2)}
+        if not args.no_cpu:
+            variants["indexer_kl_t131072"]["sampled_check"] = indexer_kl_checks(pin, pbidx, kl_out)
+        del kl_out
         del vbuf
         log(f"variants: {variants}")
 

@@ -330,6 +330,47 @@ def indexer_kl(q, k, idx_q, idx_k, block_idx, B: int, scale: float | None = None
     return res
 
 
+def indexer_kl_rows(q, k, idx_q, idx_k, block_idx, B: int, rows, scale: float | None = None):
+    """kl and d idx_q of the rows (s, t) given, as indexer_kl defines them,
+    reading only those rows and their selected keys (for sampled checks at
+    sizes where the whole inputs do not fit in float64).  Returns
+    {'kl': {(s,t): [G]}, 'd_idx_q': {(s,t): [G, di]}}."""
+    nbatch, T, Hq, d = q.shape
+    G = k.shape[2]
+    R = Hq // G
+    if scale is None:
+        scale = default_scale(d)
+    res = {"kl": {}, "d_idx_q": {}}
+    for s, t in rows:
+        L = local_block(t, B)
+        sel_t = np.asarray(_f64(block_idx[s, t]), dtype=np.int64)
+        q_t, iq_t = _f64(q[s, t]), _f64(idx_q[s, t])
+        kl_t = np.zeros(G)
+        dq_t = np.zeros((G, iq_t.shape[-1]))
+        for g in range(G):
+            sel = [b for b in sel_t[g] if 0 <= b <= L]
+            toks = selected_tokens(np.array(sorted(set(sel)), dtype=np.int64), t, B)
+            if len(toks) == 0:
+                continue
+            lo, hi = int(toks.min()), int(toks.max()) + 1
+            Kw = _f64(k[s, lo:hi, g])[toks - lo]
+            IKw = _f64(idx_k[s, lo:hi])[toks - lo]
+            sI = IKw @ iq_t[g]
+            log_pI = sI - (sI.max() + np.log(np.exp(sI - sI.max()).sum()))
+            pM = np.zeros(len(toks))
+            for h in range(g * R, (g + 1) * R):
+                x = scale * (Kw @ q_t[h])
+                a = np.exp(x - x.max())
+                pM += a / a.sum()
+            pM /= R
+            nz = pM > 0
+            kl_t[g] = float((pM[nz] * (np.log(pM[nz]) - log_pI[nz])).sum())
+            dq_t[g] = (np.exp(log_pI) - pM) @ IKw
+        res["kl"][(s, t)] = kl_t
+        res["d_idx_q"][(s, t)] = dq_t
+    return res
+
+
 def _backward_row(q_rows, Kg, Vg, dO, scale: float):
     """One (token, group) row of the backward: R query heads q_rows [R, d]
     over the gathered keys/values Kg, Vg [n, d], upstream gradient dO [R, d].

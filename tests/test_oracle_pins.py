@@ -662,3 +662,14 @@ def test_backward_sampled_rows_match_the_whole_gradient():
     got = orc.attention_backward_dq(inp.q, inp.k, inp.v, dout, bidx, B, rows)
     for r in rows:
         np.testing.assert_array_equal(got[r], dq[r])
+
+
+def test_kl_sampled_rows_match_the_whole_computation():
+    T, Hq, G, d, di, B, k = 90, 4, 2, 8, 8, 8, 3
+    inp, bidx = _kl_inputs(T, Hq, G, d, di, B, k, seed=72)
+    full = orc.indexer_kl(inp.q, inp.k, inp.idx_q, inp.idx_k, bidx, B)
+    rows = [(0, t) for t in (0, 7, 8, 45, 89)]
+    got = orc.indexer_kl_rows(inp.q, inp.k, inp.idx_q, inp.idx_k, bidx, B, rows)
+    for r in rows:
+        np.testing.assert_allclose(got["kl"][r], full["kl"][r], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(got["d_idx_q"][r], full["d_idx_q"][r], rtol=0, atol=1e-14)
