@@ -98,37 +98,47 @@ struct BwdLds {
   static constexpr int RT = NRG * RTW;        // row tiles per step
   static constexpr int SR = 32 * RT;          // (entry, head) rows per step
   static constexpr int KTR = BS + 8;          // K^T row stride (keys)
-  static constexpr int QR = D + 8;            // row-major q / dO row stride
-  static constexpr int QTR = SR + 4;          // transposed q / dO row stride (rows)
+  static constexpr int QR = D + 8;            // q / dO row stride
   static constexpr int DSR = BS + 8;          // dS row stride (keys)
   static constexpr int o_kt = 0;
   static constexpr int o_qr = o_kt + D * KTR * 2;
   static constexpr int o_or = o_qr + SR * QR * 2;
-  static constexpr int o_qt = o_or + SR * QR * 2;
-  static constexpr int o_ot = o_qt + D * QTR * 2;
-  static constexpr int o_ds = o_ot + D * QTR * 2;
+  static constexpr int o_ds = o_or + SR * QR * 2;
   static constexpr int o_lse = o_ds + SR * DSR * 2;
   static constexpr int o_del = o_lse + SR * 4;
   static constexpr int o_tok = o_del + SR * 4;
-  static constexpr int bytes = o_tok + SR * 4;
+  static constexpr int loop_bytes = o_tok + SR * 4;
   // after the row loop: dk/dv accumulators of the row groups, KT * 32 keys x 128 x 2
-  static constexpr int red_bytes = KT * 32 * D * 2 * 4;
-  static_assert(NRG == 1 || red_bytes <= bytes, "reduction buffer fits the LDS of the loop");
+  static constexpr int red_bytes = NRG > 1 ? KT * 32 * D * 2 * 4 : 0;
+  static constexpr int bytes = loop_bytes > red_bytes ? loop_bytes : red_bytes;
   static_assert(bytes <= 160 * 1024, "LDS of one workgroup");
 };
+
+// Transposing LDS read of gfx950 (ds_read_b64_tr_b16).  In each group of 16
+// lanes, lane 4a + c receives element c of the 8-byte words addressed by
+// lanes a, a + 4, a + 8 and a + 12 of the group, in that order.  tr_lane_off
+// places those words so that lane l gets 4 consecutive rows of a row-major
+// bf16 tile (row stride `stride`) at column l % 32, starting 4 (l / 32) rows
+// down: the k-slot layout of an MFMA operand whose k-slots run over rows.
+__device__ __forceinline__ int tr_lane_off(int lane, int stride) {
+  return (4 * (lane >> 5) + ((lane >> 2) & 3)) * stride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+}
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
 
 template <int BS>
 __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdArgs a) {
   using Lds = BwdLds<BS>;
   constexpr int KT = Lds::KT, NRG = Lds::NRG, RTW = Lds::RTW, RT = Lds::RT, SR = Lds::SR;
-  constexpr int KTR = Lds::KTR, QR = Lds::QR, QTR = Lds::QTR, DSR = Lds::DSR;
+  constexpr int KTR = Lds::KTR, QR = Lds::QR, DSR = Lds::DSR;
   constexpr int CPT = SR * (D / 8) / 256;  // 16-byte chunks of q (and of dO) per thread per step
   __shared__ __attribute__((aligned(16))) unsigned char smem[Lds::bytes];
   bf16_t* KTs = reinterpret_cast<bf16_t*>(smem + Lds::o_kt);
   bf16_t* Qr = reinterpret_cast<bf16_t*>(smem + Lds::o_qr);
   bf16_t* Or = reinterpret_cast<bf16_t*>(smem + Lds::o_or);
-  bf16_t* Qt = reinterpret_cast<bf16_t*>(smem + Lds::o_qt);
-  bf16_t* Ot = reinterpret_cast<bf16_t*>(smem + Lds::o_ot);
   bf16_t* DSr = reinterpret_cast<bf16_t*>(smem + Lds::o_ds);
   float* rlse = reinterpret_cast<float*>(smem + Lds::o_lse);
   float* rdel = reinterpret_cast<float*>(smem + Lds::o_del);
@@ -181,14 +191,14 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
   const float c2 = l.scale_log2;
 
   // Staging of a step's rows: thread tid owns row tid % SR of every step and
-  // the 16-byte chunks part = tid / SR + (256 / SR) * i of it (consecutive
-  // lanes take consecutive rows, so the 2-byte transposed LDS writes of a wave
-  // land in distinct banks and the row-major 16-byte writes are spread by the
-  // row padding).  The row's (list position, head) advance by a constant each
-  // step.  With one part (steps of up to 64 rows) the next step's rows are
-  // fetched while the current one computes; 128-row steps are fetched part by
-  // part in place, as an early fetch would not fit next to the accumulators.
-  // The entry that addresses a step's row is loaded one step earlier still.
+  // the 16-byte chunks part = tid / SR + (256 / SR) * i of it, written
+  // row-major (the products that run over rows read them back through the
+  // transposing LDS read).  The row's (list position, head) advance by a
+  // constant each step.  With one part (steps of up to 64 rows) the next
+  // step's rows are fetched while the current one computes; 128-row steps are
+  // fetched part by part in place, as an early fetch would not fit next to
+  // the accumulators.  The entry that addresses a step's row is loaded one
+  // step earlier still.
   static_assert(256 % SR == 0 && CPT * 256 == SR * (D / 8), "one row per thread");
   constexpr int CPR = CPT <= 4 ? CPT : 4;
   constexpr int NPART = CPT / CPR;
@@ -245,12 +255,6 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
       const int part = part_base + (256 / SR) * (part0 * CPR + i);
       *reinterpret_cast<u32x4*>(Qr + myrow * QR + part * 8) = qs[i];
       *reinterpret_cast<u32x4*>(Or + myrow * QR + part * 8) = os[i];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int sh = (j & 1) * 16;
-        reinterpret_cast<uint16_t*>(Qt)[(part * 8 + j) * QTR + myrow] = (uint16_t)(qs[i][j >> 1] >> sh);
-        reinterpret_cast<uint16_t*>(Ot)[(part * 8 + j) * QTR + myrow] = (uint16_t)(os[i][j >> 1] >> sh);
-      }
     }
     if (part0 == 0 && tid < SR) {
       rlse[tid] = lse_v;
@@ -293,6 +297,7 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
     }
 
     const int j = kb + 32 * kt + col;
+    const int tro = tr_lane_off(lane, QR);
 #pragma unroll 1
     for (int u = 0; u < RTW; ++u) {
       const int r0 = (rg * RTW + u) * 32;
@@ -327,16 +332,15 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
         d8[i / 8][i % 8] = (__bf16)ds;
         reinterpret_cast<uint16_t*>(DSr)[row * DSR + 32 * kt + col] = bf16_bits(ds);
       }
-      // dv[key][d] += P^T dO, dk[key][d] += dS^T Q over this row tile (k-slots = rows)
+      // dv[key][d] += P^T dO, dk[key][d] += dS^T Q over this row tile (k-slots =
+      // rows: {0-3, 8-11} + 4 half of each 16-row slice, as in p8 / d8)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int o0 = (32 * dt + col) * QTR + r0 + 16 * ks + 4 * half;
-          const bf16x8 ob = join_bf16x4(*reinterpret_cast<const u32x2*>(Ot + o0),
-                                        *reinterpret_cast<const u32x2*>(Ot + o0 + 8));
-          const bf16x8 qb = join_bf16x4(*reinterpret_cast<const u32x2*>(Qt + o0),
-                                        *reinterpret_cast<const u32x2*>(Qt + o0 + 8));
+          const int o0 = (r0 + 16 * ks) * QR + 32 * dt + tro;
+          const bf16x8 ob = join_bf16x4(lds_read_tr16(Or + o0), lds_read_tr16(Or + o0 + 8 * QR));
+          const bf16x8 qb = join_bf16x4(lds_read_tr16(Qr + o0), lds_read_tr16(Qr + o0 + 8 * QR));
           dv[dt] = mfma32x32x16(p8[ks], ob, dv[dt]);
           dk[dt] = mfma32x32x16(d8[ks], qb, dk[dt]);
         }
