@@ -187,79 +187,118 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
   }
 
   const int nr = count * R;  // (entry, head) rows of the list, row = entry position * R + head
+  const __amdgpu_buffer_rsrc_t dq_rs =
+      __builtin_amdgcn_make_buffer_rsrc(a.dqp + (size_t)off * R * D, (short)0, nr * D * 2, kBufferWord3);
   const int nsteps = (nr + SR - 1) / SR;
   const float c2 = l.scale_log2;
 
-  // Staging of a step's rows: thread tid owns row tid % SR of every step and
-  // the 16-byte chunks part = tid / SR + (256 / SR) * i of it, written
-  // row-major (the products that run over rows read them back through the
-  // transposing LDS read).  The row's (list position, head) advance by a
-  // constant each step.  With one part (steps of up to 64 rows) the next
-  // step's rows are fetched while the current one computes; 128-row steps are
-  // fetched part by part in place, as an early fetch would not fit next to
-  // the accumulators.  The entry that addresses a step's row is loaded one
-  // step earlier still.
-  static_assert(256 % SR == 0 && CPT * 256 == SR * (D / 8), "one row per thread");
-  constexpr int CPR = CPT <= 4 ? CPT : 4;
+  // Staging of a step's rows, 8 lanes per row: thread tid owns rows
+  // tid / 8 + 32 j (j < NRW) of every step and the 16-byte chunks tid % 8 and
+  // 8 + tid % 8 of each, so that one load instruction covers 8 rows x 128
+  // contiguous bytes (whole cache lines) and the 16-byte LDS writes of 8
+  // lanes fill the 8 bank groups of one row (the 16-byte row padding shifts
+  // each row by one group).  Rows are stored row-major; the products that run
+  // over rows read them back through the transposing LDS read.  Each row's
+  // (list position, head) advances by a constant each step.  With 64-row
+  // steps the next step's rows are fetched while the current one computes;
+  // 128-row steps are fetched in two parts in place, as an early fetch would
+  // not fit next to the accumulators.  The entries that address a step's
+  // rows are loaded one step earlier still.
+  // No branch guards a load: rows past the list read a row that exists and
+  // carry t = -1, which zeroes their P and dS; with the same memory
+  // operations on every path, the wait for a step's rows need not also wait
+  // for the previous step's dq stores.
+  constexpr int NRW = SR / 32;                   // rows per thread per step
+  static_assert(CPT == 2 * NRW, "two 16-byte chunks of each row per thread");
+  constexpr int CPR = CPT <= 4 ? CPT : 4;        // chunks per part
   constexpr int NPART = CPT / CPR;
+  constexpr int RPP = CPR / 2;                   // rows per part
   constexpr bool kAhead = NPART == 1;
-  const int myrow = tid % SR, part_base = tid / SR;
+  const int r8 = tid >> 3, c8 = tid & 7;
   const int step_q = SR / R, step_r = SR % R;  // list-position and head advance per step
-  int cur_p = myrow / R, cur_r = myrow % R;     // row of the next entry load
-  int ent = -1, ent_r = 0;                      // that load's result and its head
-  int row_e = -1, row_r = 0;                    // entry and head of the rows being fetched
+  int cur_p[NRW], cur_r[NRW];                   // row of the next entry load, per row slot
+  int ent[NRW], ent_r[NRW];                     // that load's result and its head
+  bool ent_ok[NRW];                             // whether that row is in the list
+  int row_e[NRW], row_r[NRW];                   // entry (-1: none) and head of the rows being fetched
+#pragma unroll
+  for (int j = 0; j < NRW; ++j) {
+    cur_p[j] = (r8 + 32 * j) / R;
+    cur_r[j] = (r8 + 32 * j) % R;
+    ent[j] = 0;
+    ent_r[j] = 0;
+    ent_ok[j] = false;
+    row_e[j] = -1;
+    row_r[j] = 0;
+  }
   u32x4 qs[CPR], os[CPR];
+  // t, lse and Delta of row r8 + 32 c8 (lanes with c8 < NRW)
   float lse_v = 0.f, del_v = 0.f;
   int tok_v = -1;
   auto load_ent = [&]() {
-    ent_r = cur_r;
-    ent = cur_p * R + cur_r < nr ? l.entries[off + cur_p] : -1;
-    cur_p += step_q;
-    cur_r += step_r;
-    if (cur_r >= R) {
-      cur_r -= R;
-      ++cur_p;
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) {
+      ent_r[j] = cur_r[j];
+      ent_ok[j] = cur_p[j] * R + cur_r[j] < nr;
+      ent[j] = l.entries[off + min(cur_p[j], count - 1)];
+      cur_p[j] += step_q;
+      cur_r[j] += step_r;
+      if (cur_r[j] >= R) {
+        cur_r[j] -= R;
+        ++cur_p[j];
+      }
     }
   };
   auto take_ent = [&]() {
-    row_e = ent;
-    row_r = ent_r;
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) {
+      row_e[j] = ent_ok[j] ? ent[j] : -1;
+      row_r[j] = ent_r[j];
+    }
+  };
+  auto row_of = [&](int e, int r) {  // (sequence row of the token, head) -> row of q / dO / lse
+    const int tl = e >= 0 ? e >> l.rank_bits : 0;
+    return ((size_t)s * l.T + l.t0 + tl) * l.Hq + (size_t)g * R + r;
   };
   auto fetch = [&](int part0) {
-    const size_t grow = row_e >= 0 ? ((size_t)s * l.T + l.t0 + (row_e >> l.rank_bits)) * l.Hq +
-                                         (size_t)g * R + row_r
-                                   : 0;
 #pragma unroll
-    for (int i = 0; i < CPR; ++i) {
-      const int part = part_base + (256 / SR) * (part0 * CPR + i);
-      qs[i] = u32x4{0u, 0u, 0u, 0u};
-      os[i] = u32x4{0u, 0u, 0u, 0u};
-      if (row_e >= 0) {
-        qs[i] = *reinterpret_cast<const u32x4*>(l.q + grow * D + part * 8);
-        os[i] = *reinterpret_cast<const u32x4*>(a.dout + grow * D + part * 8);
+    for (int jj = 0; jj < RPP; ++jj) {
+      const int j = part0 * RPP + jj;
+      const size_t grow = row_of(row_e[j], row_r[j]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        qs[2 * jj + h] = *reinterpret_cast<const u32x4*>(l.q + grow * D + (c8 + 8 * h) * 8);
+        os[2 * jj + h] = *reinterpret_cast<const u32x4*>(a.dout + grow * D + (c8 + 8 * h) * 8);
       }
     }
-    if (part0 == 0 && tid < SR) {
-      tok_v = -1;
-      if (row_e >= 0) {
-        const int tl = row_e >> l.rank_bits;
-        lse_v = l.lse[grow] * kLog2e;
-        del_v = a.delta[((size_t)s * l.tc + tl) * l.Hq + (size_t)g * R + row_r];
-        tok_v = l.t0 + tl;
-      }
+    if (part0 == 0) {
+      int e = row_e[0], r = row_r[0];
+#pragma unroll
+      for (int j = 1; j < NRW; ++j)
+        if (c8 == j) {
+          e = row_e[j];
+          r = row_r[j];
+        }
+      const int tl = e >= 0 ? e >> l.rank_bits : 0;
+      lse_v = l.lse[row_of(e, r)];  // scaled when stored: arithmetic on it here would wait for the step's loads
+      del_v = a.delta[((size_t)s * l.tc + tl) * l.Hq + (size_t)g * R + r];
+      tok_v = e >= 0 ? l.t0 + tl : -1;
     }
   };
   auto store = [&](int part0) {
 #pragma unroll
-    for (int i = 0; i < CPR; ++i) {
-      const int part = part_base + (256 / SR) * (part0 * CPR + i);
-      *reinterpret_cast<u32x4*>(Qr + myrow * QR + part * 8) = qs[i];
-      *reinterpret_cast<u32x4*>(Or + myrow * QR + part * 8) = os[i];
+    for (int jj = 0; jj < RPP; ++jj) {
+      const int row = r8 + 32 * (part0 * RPP + jj);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        *reinterpret_cast<u32x4*>(Qr + row * QR + (c8 + 8 * h) * 8) = qs[2 * jj + h];
+        *reinterpret_cast<u32x4*>(Or + row * QR + (c8 + 8 * h) * 8) = os[2 * jj + h];
+      }
     }
-    if (part0 == 0 && tid < SR) {
-      rlse[tid] = lse_v;
-      rdel[tid] = del_v;
-      rtok[tid] = tok_v;
+    if (part0 == 0 && c8 < NRW) {
+      const int row = r8 + 32 * c8;
+      rlse[row] = lse_v * kLog2e;
+      rdel[row] = del_v;
+      rtok[row] = tok_v;
     }
   };
 
@@ -275,6 +314,13 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
     take_ent();
     fetch(0);
     load_ent();
+    // Each later step's rows are waited for with the previous step's RT * 4
+    // dq stores issued after them.  The same number of stores here, at an
+    // offset past the resource (dropped by the range check), gives the path
+    // into the loop the same count, so the wait need not cover the stores.
+#pragma unroll
+    for (int i = 0; i < RT * 4; ++i)
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, dq_rs, nr * D * 2 + 16 * i, 0, 0);
   }
   for (int step = 0; step < nsteps; ++step) {
     __syncthreads();  // the previous step's LDS reads are done (and KTs is written)
@@ -282,7 +328,7 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
       store(0);
     } else {
       take_ent();
-#pragma unroll 1
+#pragma unroll
       for (int part0 = 0; part0 < NPART; ++part0) {
         fetch(part0);
         store(part0);
@@ -298,7 +344,24 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
 
     const int j = kb + 32 * kt + col;
     const int tro = tr_lane_off(lane, QR);
-#pragma unroll 1
+    // S = Q K^T and dP = dO V^T of all the wave's row tiles first: the next
+    // tile's products run on the matrix unit while the vector unit takes the
+    // current tile's exps and dS
+    f32x16 S[RTW], dP[RTW];
+#pragma unroll
+    for (int u = 0; u < RTW; ++u) {
+      const int r0 = (rg * RTW + u) * 32;
+      S[u] = f32x16{};
+      dP[u] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        S[u] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Qr + (r0 + col) * QR + 16 * ks + 8 * half), kreg[ks],
+                            S[u]);
+        dP[u] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Or + (r0 + col) * QR + 16 * ks + 8 * half), vreg[ks],
+                             dP[u]);
+      }
+    }
+#pragma unroll
     for (int u = 0; u < RTW; ++u) {
       const int r0 = (rg * RTW + u) * 32;
       // the lane's 16 rows are 4 runs of 4: their t, lse and Delta in 16-byte reads
@@ -311,13 +374,6 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
         lv[q4] = *reinterpret_cast<const f32x4*>(rlse + rr);
         dl[q4] = *reinterpret_cast<const f32x4*>(rdel + rr);
       }
-      f32x16 S = {}, dP = {};
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        S = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Qr + (r0 + col) * QR + 16 * ks + 8 * half), kreg[ks], S);
-        dP = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Or + (r0 + col) * QR + 16 * ks + 8 * half), vreg[ks],
-                          dP);
-      }
       // lane: key j of its tile, rows r0 + 8*(i/4) + 4*half + (i%4)
       bf16x8 p8[2], d8[2];
 #pragma unroll
@@ -325,9 +381,9 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
         const int row = r0 + 8 * (i / 4) + 4 * half + (i % 4);
         // rows past the list carry t = -1, so one compare masks them and the
         // keys after t in the local block (exp of a masked entry is finite and dropped)
-        const float e = __builtin_amdgcn_exp2f(S[i] * c2 - lv[i / 4][i % 4]);
+        const float e = __builtin_amdgcn_exp2f(S[u][i] * c2 - lv[i / 4][i % 4]);
         const float p = j <= tk[i / 4][i % 4] ? e : 0.f;
-        const float ds = p * (dP[i] - dl[i / 4][i % 4]);  // the softmax scale is applied in the merges
+        const float ds = p * (dP[u][i] - dl[i / 4][i % 4]);  // the softmax scale is applied in the merges
         p8[i / 8][i % 8] = (__bf16)p;
         d8[i / 8][i % 8] = (__bf16)ds;
         reinterpret_cast<uint16_t*>(DSr)[row * DSR + 32 * kt + col] = bf16_bits(ds);
@@ -349,8 +405,9 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
     __syncthreads();  // dS rows of the step complete
     // dq^T[d][row] = sum over the block's keys of K^T[d][key] dS^T[key][row]:
     // each lane ends with one row and 4 runs of 4 consecutive d, stored as
-    // 8-byte bf16 groups
-#pragma unroll 1
+    // 8-byte bf16 groups.  Unrolled (where registers allow) so that the
+    // compiler can count the stores when the next step waits for its rows.
+#pragma unroll(RT <= 2 ? RT : 1)
     for (int ii = 0; ii < RT; ++ii) {
       const int f = wave * RT + ii;
       const int rt2 = f >> 2, dt = f & 3;
@@ -360,16 +417,15 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
         acc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(KTs + (32 * dt + col) * KTR + 16 * ks + 8 * half),
                            *reinterpret_cast<const bf16x8*>(DSr + (rt2 * 32 + col) * DSR + 16 * ks + 8 * half),
                            acc);
+      // rows past the list fall outside the resource and their stores are dropped
       const int rho = step * SR + rt2 * 32 + col;
-      if (rho < nr) {
-        uint16_t* dst = a.dqp + ((size_t)off * R + rho) * D + 32 * dt + 4 * half;
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          bf16x4 v;
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 v;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] = (__bf16)acc[4 * i4 + u];
-          *reinterpret_cast<bf16x4*>(dst + 8 * i4) = v;
-        }
+        for (int u = 0; u < 4; ++u) v[u] = (__bf16)acc[4 * i4 + u];
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), dq_rs,
+                                              (rho * D + 32 * dt + 4 * half + 8 * i4) * 2, 0, 0);
       }
     }
   }

@@ -31,6 +31,10 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;  // raw bfloat16 bits in memory
 
 constexpr int kWave = 64;
+// Fourth word of a raw (unswizzled, stride 0) buffer resource on gfx9-family
+// chips: 32-bit data format, no index stride; byte offsets >= the record count
+// are out of range (loads return 0, stores are dropped).
+constexpr int kBufferWord3 = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -34,10 +34,6 @@ namespace msa {
 namespace {
 
 constexpr int D = 128;          // head_dim
-// Fourth word of a raw (unswizzled, stride 0) buffer resource on gfx9-family
-// chips: 32-bit data format, no index stride; byte offsets >= the record count
-// are out of range (loads return 0, stores are dropped).
-constexpr int kBufferWord3 = 0x00020000;
 constexpr int KROW = D + 8;     // LDS row stride of K tiles (bf16)
 
 // ---------------------------------------------------------------------------
