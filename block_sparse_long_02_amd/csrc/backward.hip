@@ -22,7 +22,7 @@
 //     (launch_sort_lists), so that the dk/dv sums below run in an order that
 //     does not depend on how the lists were filled (their positions come
 //     from integer atomics);
-//  3. bwd_list_kernel: one workgroup per list.  K^T of the block sits in LDS,
+//  3. bwd_list_kernel: one workgroup per list.  K of the block sits in LDS,
 //     each wave owns one 32-key tile (its K and V rows in registers) and
 //     steps over the list's (entry, head) rows: S = Q K^T and dP = dO V^T on
 //     MFMA, P and dS in the accumulator layout (one key per lane), dv += P^T dO
@@ -97,11 +97,11 @@ struct BwdLds {
   static constexpr int RTW = bwd_rtw<BS>();   // row tiles per wave per step
   static constexpr int RT = NRG * RTW;        // row tiles per step
   static constexpr int SR = 32 * RT;          // (entry, head) rows per step
-  static constexpr int KTR = BS + 8;          // K^T row stride (keys)
+  static constexpr int KR = D + 8;            // K row stride
   static constexpr int QR = D + 8;            // q / dO row stride
   static constexpr int DSR = BS + 8;          // dS row stride (keys)
-  static constexpr int o_kt = 0;
-  static constexpr int o_qr = o_kt + D * KTR * 2;
+  static constexpr int o_k = 0;
+  static constexpr int o_qr = o_k + BS * KR * 2;
   static constexpr int o_or = o_qr + SR * QR * 2;
   static constexpr int o_ds = o_or + SR * QR * 2;
   static constexpr int o_lse = o_ds + SR * DSR * 2;
@@ -133,10 +133,10 @@ template <int BS>
 __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdArgs a) {
   using Lds = BwdLds<BS>;
   constexpr int KT = Lds::KT, NRG = Lds::NRG, RTW = Lds::RTW, RT = Lds::RT, SR = Lds::SR;
-  constexpr int KTR = Lds::KTR, QR = Lds::QR, DSR = Lds::DSR;
+  constexpr int KR = Lds::KR, QR = Lds::QR, DSR = Lds::DSR;
   constexpr int CPT = SR * (D / 8) / 256;  // 16-byte chunks of q (and of dO) per thread per step
   __shared__ __attribute__((aligned(16))) unsigned char smem[Lds::bytes];
-  bf16_t* KTs = reinterpret_cast<bf16_t*>(smem + Lds::o_kt);
+  bf16_t* Ks = reinterpret_cast<bf16_t*>(smem + Lds::o_k);
   bf16_t* Qr = reinterpret_cast<bf16_t*>(smem + Lds::o_qr);
   bf16_t* Or = reinterpret_cast<bf16_t*>(smem + Lds::o_or);
   bf16_t* DSr = reinterpret_cast<bf16_t*>(smem + Lds::o_ds);
@@ -163,27 +163,32 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
   const bf16_t* vblk = l.v + ((size_t)s * l.T + kb) * kvstride + (size_t)g * D;
   if (tid == 0) a.slot_of[lid] = w;
 
-  // K^T of the block: KTs[d][key]; consecutive lanes take consecutive keys,
-  // so that the 2-byte transposed writes of a wave land in distinct banks
-  for (int c = tid; c < BS * (D / 8); c += 256) {
-    const int kr = c % BS, part = c / BS;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (kr < nkey) v = *reinterpret_cast<const u32x4*>(kblk + (size_t)kr * kvstride + part * 8);
+  // K of the block row-major in LDS (the dq product reads it through the
+  // transposing LDS read) and this wave's 32-key tile of K and V in registers
+  // (B operands of S = Q K^T and dP = dO V^T, k-slots = head dim).  Every load
+  // is issued before the first LDS write.  Keys past the sequence read its
+  // last key: every row masks them (key > t), so their P and dS are zero.
+  constexpr int NKC = BS * (D / 8) / 256;  // 16-byte chunks of K per thread
+  const int klast = nkey - 1;
+  u32x4 kc[NKC];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t wd = v[j >> 1];
-      reinterpret_cast<uint16_t*>(KTs)[(part * 8 + j) * KTR + kr] = (uint16_t)((j & 1) ? (wd >> 16) : (wd & 0xffffu));
-    }
+  for (int i = 0; i < NKC; ++i) {
+    const int c = tid + 256 * i;
+    kc[i] = *reinterpret_cast<const u32x4*>(kblk + (size_t)min(c >> 4, klast) * kvstride + (c & 15) * 8);
   }
-  // this wave's key tile, rows of K and V as MFMA B operands (k-slots = head dim)
   bf16x8 kreg[D / 16], vreg[D / 16];
   {
-    const int kr = 32 * kt + col;
+    const int kr = min(32 * kt + col, klast);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      kreg[ks] = kr < nkey ? load_bf16x8(kblk + (size_t)kr * kvstride + 16 * ks + 8 * half) : zero_bf16x8();
-      vreg[ks] = kr < nkey ? load_bf16x8(vblk + (size_t)kr * kvstride + 16 * ks + 8 * half) : zero_bf16x8();
+      kreg[ks] = load_bf16x8(kblk + (size_t)kr * kvstride + 16 * ks + 8 * half);
+      vreg[ks] = load_bf16x8(vblk + (size_t)kr * kvstride + 16 * ks + 8 * half);
     }
+  }
+#pragma unroll
+  for (int i = 0; i < NKC; ++i) {
+    const int c = tid + 256 * i;
+    *reinterpret_cast<u32x4*>(Ks + (c >> 4) * KR + (c & 15) * 8) = kc[i];
   }
 
   const int nr = count * R;  // (entry, head) rows of the list, row = entry position * R + head
@@ -323,7 +328,7 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
       __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, dq_rs, nr * D * 2 + 16 * i, 0, 0);
   }
   for (int step = 0; step < nsteps; ++step) {
-    __syncthreads();  // the previous step's LDS reads are done (and KTs is written)
+    __syncthreads();  // the previous step's LDS reads are done (and Ks is written)
     if (kAhead) {
       store(0);
     } else {
@@ -344,6 +349,10 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
 
     const int j = kb + 32 * kt + col;
     const int tro = tr_lane_off(lane, QR);
+    // dS rows keep each 16-key group in the order 0-3, 8-11, 4-7, 12-15 (bits
+    // 2 and 3 of the key swapped), the k-slot order of K read through the
+    // transposing LDS read: lane half h then reads its 8 keys contiguously
+    const int dscol = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
     // S = Q K^T and dP = dO V^T of all the wave's row tiles first: the next
     // tile's products run on the matrix unit while the vector unit takes the
     // current tile's exps and dS
@@ -386,7 +395,7 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
         const float ds = p * (dP[u][i] - dl[i / 4][i % 4]);  // the softmax scale is applied in the merges
         p8[i / 8][i % 8] = (__bf16)p;
         d8[i / 8][i % 8] = (__bf16)ds;
-        reinterpret_cast<uint16_t*>(DSr)[row * DSR + 32 * kt + col] = bf16_bits(ds);
+        reinterpret_cast<uint16_t*>(DSr)[row * DSR + 32 * kt + dscol] = bf16_bits(ds);
       }
       // dv[key][d] += P^T dO, dk[key][d] += dS^T Q over this row tile (k-slots =
       // rows: {0-3, 8-11} + 4 half of each 16-row slice, as in p8 / d8)
@@ -403,6 +412,7 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
       }
     }
     __syncthreads();  // dS rows of the step complete
+    const int trk = tr_lane_off(lane, KR);
     // dq^T[d][row] = sum over the block's keys of K^T[d][key] dS^T[key][row]:
     // each lane ends with one row and 4 runs of 4 consecutive d, stored as
     // 8-byte bf16 groups.  Unrolled (where registers allow) so that the
@@ -413,10 +423,12 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
       const int rt2 = f >> 2, dt = f & 3;
       f32x16 acc = {};
 #pragma unroll
-      for (int ks = 0; ks < BS / 16; ++ks)
-        acc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(KTs + (32 * dt + col) * KTR + 16 * ks + 8 * half),
+      for (int ks = 0; ks < BS / 16; ++ks) {
+        const int o0 = 16 * ks * KR + 32 * dt + trk;
+        acc = mfma32x32x16(join_bf16x4(lds_read_tr16(Ks + o0), lds_read_tr16(Ks + o0 + 8 * KR)),
                            *reinterpret_cast<const bf16x8*>(DSr + (rt2 * 32 + col) * DSR + 16 * ks + 8 * half),
                            acc);
+      }
       // rows past the list fall outside the resource and their stores are dropped
       const int rho = step * SR + rt2 * 32 + col;
 #pragma unroll

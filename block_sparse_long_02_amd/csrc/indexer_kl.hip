@@ -47,17 +47,27 @@ __device__ __forceinline__ size_t kl_list_of(const PrefillMainArgs& l, long lid,
   return (size_t)lid;
 }
 
-// Rows [0, nrows) of a B x C bf16 block (row stride `stride` elements) into
-// LDS with row stride ldsr; rows >= nvalid are zero-filled.
-template <int C>
+// Rows [0, NR) of an NR x C bf16 block (row stride `stride` elements) into
+// LDS with row stride ldsr; rows >= nvalid are zero-filled.  16 lanes per
+// 256-byte row; every load is issued before the first store, so the staging
+// costs one memory latency.
+template <int C, int NR>
 __device__ __forceinline__ void stage_rows(bf16_t* dst, int ldsr, const bf16_t* __restrict__ src, size_t stride,
-                                           int nrows, int nvalid, int tid, int nthr) {
+                                           int nvalid, int tid) {
   constexpr int CPR = C / 8;
-  for (int c = tid; c < nrows * CPR; c += nthr) {
-    const int r = c / CPR, part = c % CPR;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < nvalid) v = *reinterpret_cast<const u32x4*>(src + (size_t)r * stride + part * 8);
-    *reinterpret_cast<u32x4*>(dst + r * ldsr + part * 8) = v;
+  constexpr int N = NR * CPR / 256;  // chunks per thread
+  static_assert(N >= 1 && N * 256 == NR * CPR, "whole chunks per thread");
+  u32x4 v[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int c = tid + 256 * i, r = c / CPR, part = c % CPR;
+    v[i] = *reinterpret_cast<const u32x4*>(src + (size_t)min(r, nvalid - 1) * stride + part * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int c = tid + 256 * i, r = c / CPR, part = c % CPR;
+    if (r >= nvalid) v[i] = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(dst + r * ldsr + part * 8) = v[i];
   }
 }
 
@@ -106,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void kl_index_stats_kernel(IndexerKlArgs a)
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
   const int kb = b * l.B;
-  stage_rows<DI>(Is, KP, a.idx_k + ((size_t)s * l.T + kb) * DI, DI, BS, min(BS, l.T - kb), tid, 256);
+  stage_rows<DI, BS>(Is, KP, a.idx_k + ((size_t)s * l.T + kb) * DI, DI, min(BS, l.T - kb), tid);
   __syncthreads();
   for (int it = 0; it < ntile; ++it) {
     const int pos = (tile0 + it) * MT + wave * 32 + col;
@@ -204,8 +214,8 @@ __global__ __launch_bounds__(256, MSA_KL_ENTRY_MINB) void kl_entry_kernel(Indexe
   const int kb = b * l.B;
   const size_t kvstride = (size_t)l.G * D;
   const int nkey = min(BS, l.T - kb);
-  stage_rows<D>(Ks, KROW, l.k + ((size_t)s * l.T + kb) * kvstride + (size_t)g * D, kvstride, BS, nkey, tid, 256);
-  stage_rows<DI>(Is, KP, a.idx_k + ((size_t)s * l.T + kb) * DI, DI, BS, nkey, tid, 256);
+  stage_rows<D, BS>(Ks, KROW, l.k + ((size_t)s * l.T + kb) * kvstride + (size_t)g * D, kvstride, nkey, tid);
+  stage_rows<DI, BS>(Is, KP, a.idx_k + ((size_t)s * l.T + kb) * DI, DI, nkey, tid);
   __syncthreads();
   const float c = l.scale_log2;
   const float invR = 1.0f / (float)R;
