@@ -37,20 +37,29 @@ constexpr int D = 128;          // head_dim
 constexpr int KROW = D + 8;     // LDS row stride of K tiles (bf16)
 
 // ---------------------------------------------------------------------------
-// LDS staging helpers (256 threads).
+// LDS staging helpers (256 threads) for tiles of NK keys.
 // K tile: rows [key][D] -> Ks[key*KROW + d]
 // V tile: transposed -> Vt[d*VROW + key], so that a lane can fetch 4
 // consecutive keys of one d with one 8-byte read (PV operand layout).
-// Keys >= nvalid are zero-filled.
+// Keys >= nvalid (>= 1) are zero-filled.  Every load of a tile is issued
+// before its first LDS write, so a tile costs one memory latency.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void stage_k(bf16_t* Ks, const bf16_t* __restrict__ kbase, size_t kstride,
-                                        int nkeys, int nvalid, int tid) {
-  const int nch = nkeys * (D / 8);
-  for (int c = tid; c < nch; c += 256) {
-    const int key = c >> 4, part = c & 15;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (key < nvalid) val = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * kstride + part * 8);
-    *reinterpret_cast<u32x4*>(Ks + key * KROW + part * 8) = val;
+template <int NK>
+__device__ __forceinline__ void stage_k(bf16_t* Ks, const bf16_t* __restrict__ kbase, size_t kstride, int nvalid,
+                                        int tid) {
+  constexpr int N = NK * (D / 8) / 256;  // 16-byte chunks per thread
+  static_assert(N * 256 == NK * (D / 8), "whole chunks per thread");
+  u32x4 v[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int c = tid + 256 * i;
+    v[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)min(c >> 4, nvalid - 1) * kstride + (c & 15) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int c = tid + 256 * i;
+    if ((c >> 4) >= nvalid) v[i] = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(Ks + (c >> 4) * KROW + (c & 15) * 8) = v[i];
   }
 }
 
@@ -63,29 +72,39 @@ __device__ __forceinline__ void vt_unit(int u, int& k4, int& dq) {
   k4 = (u >> 7) * 4 + ((u >> 3) & 3);
 }
 
-__device__ __forceinline__ void stage_vt(bf16_t* Vt, int vrow, const bf16_t* __restrict__ vbase,
-                                         size_t vstride, int nkeys, int nvalid, int tid) {
-  // unit = 4 keys x 4 d; 32 units per 4-key group
-  const int nunits = (nkeys / 4) * (D / 4);
-  for (int u = tid; u < nunits; u += 256) {
+// 4x4 transpose of 16-bit lanes: o[j] = (r0[j], r1[j], r2[j], r3[j])
+__device__ __forceinline__ void transpose_4x4(const u32x2 (&r)[4], u32x2 (&o)[4]) {
+  o[0] = u32x2{(r[0][0] & 0xffffu) | (r[1][0] << 16), (r[2][0] & 0xffffu) | (r[3][0] << 16)};
+  o[1] = u32x2{(r[0][0] >> 16) | (r[1][0] & 0xffff0000u), (r[2][0] >> 16) | (r[3][0] & 0xffff0000u)};
+  o[2] = u32x2{(r[0][1] & 0xffffu) | (r[1][1] << 16), (r[2][1] & 0xffffu) | (r[3][1] << 16)};
+  o[3] = u32x2{(r[0][1] >> 16) | (r[1][1] & 0xffff0000u), (r[2][1] >> 16) | (r[3][1] & 0xffff0000u)};
+}
+
+template <int NK>
+__device__ __forceinline__ void stage_vt(bf16_t* Vt, int vrow, const bf16_t* __restrict__ vbase, size_t vstride,
+                                         int nvalid, int tid) {
+  constexpr int N = (NK / 4) * (D / 4) / 256;  // units of 4 keys x 4 d per thread
+  static_assert(N * 256 == (NK / 4) * (D / 4), "whole units per thread");
+  u32x2 r[N][4];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
     int k4, dq;
-    vt_unit(u, k4, dq);
-    u32x2 r[4];
+    vt_unit(tid + 256 * n, k4, dq);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = k4 * 4 + i;
-      r[i] = u32x2{0u, 0u};
-      if (key < nvalid) r[i] = *reinterpret_cast<const u32x2*>(vbase + (size_t)key * vstride + dq * 4);
-    }
-    // 4x4 transpose of 16-bit lanes: o[j] = (r0[j], r1[j], r2[j], r3[j])
+    for (int i = 0; i < 4; ++i)
+      r[n][i] = *reinterpret_cast<const u32x2*>(vbase + (size_t)min(k4 * 4 + i, nvalid - 1) * vstride + dq * 4);
+  }
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    int k4, dq;
+    vt_unit(tid + 256 * n, k4, dq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (k4 * 4 + i >= nvalid) r[n][i] = u32x2{0u, 0u};
     u32x2 o[4];
-    o[0] = u32x2{(r[0][0] & 0xffffu) | (r[1][0] << 16), (r[2][0] & 0xffffu) | (r[3][0] << 16)};
-    o[1] = u32x2{(r[0][0] >> 16) | (r[1][0] & 0xffff0000u), (r[2][0] >> 16) | (r[3][0] & 0xffff0000u)};
-    o[2] = u32x2{(r[0][1] & 0xffffu) | (r[1][1] << 16), (r[2][1] & 0xffffu) | (r[3][1] << 16)};
-    o[3] = u32x2{(r[0][1] >> 16) | (r[1][1] & 0xffff0000u), (r[2][1] >> 16) | (r[3][1] & 0xffff0000u)};
+    transpose_4x4(r[n], o);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x2*>(Vt + (dq * 4 + j) * vrow + k4 * 4) = o[j];
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(Vt + (dq * 4 + j) * vrow + k4 * 4) = o[j];
   }
 }
 
@@ -128,12 +147,8 @@ __device__ __forceinline__ void block_store(const BlockRegs<BS>& r, bf16_t* Ks, 
     const int u = tid + 256 * i;
     int k4, dq;
     vt_unit(u, k4, dq);
-    const u32x2* x = r.v[i];
     u32x2 o[4];
-    o[0] = u32x2{(x[0][0] & 0xffffu) | (x[1][0] << 16), (x[2][0] & 0xffffu) | (x[3][0] << 16)};
-    o[1] = u32x2{(x[0][0] >> 16) | (x[1][0] & 0xffff0000u), (x[2][0] >> 16) | (x[3][0] & 0xffff0000u)};
-    o[2] = u32x2{(x[0][1] & 0xffffu) | (x[1][1] << 16), (x[2][1] & 0xffffu) | (x[3][1] << 16)};
-    o[3] = u32x2{(x[0][1] >> 16) | (x[1][1] & 0xffff0000u), (x[2][1] >> 16) | (x[3][1] & 0xffff0000u)};
+    transpose_4x4(r.v[i], o);
 #pragma unroll
     for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(Vt + (dq * 4 + j) * vrow + k4 * 4) = o[j];
   }
@@ -710,8 +725,8 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
   for (int kb = k_lo; kb <= k_hi; kb += KTILE) {
     const int nvalid = min(KTILE, k_hi + 1 - kb);
     __syncthreads();
-    stage_k(Ks, kseq + (size_t)kb * kvstride, kvstride, KTILE, nvalid, tid);
-    stage_vt(Vt, VROW, vseq + (size_t)kb * kvstride, kvstride, KTILE, nvalid, tid);
+    stage_k<KTILE>(Ks, kseq + (size_t)kb * kvstride, kvstride, nvalid, tid);
+    stage_vt<KTILE>(Vt, VROW, vseq + (size_t)kb * kvstride, kvstride, nvalid, tid);
     __syncthreads();
 
     f32x16 sacc[KT];
@@ -771,10 +786,19 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
     const int nv = info & 0x3fffffff;  // partial slots 0..nv-1
     // list positions of the row's partials; rows pos*R + r of pO / pS
     const int32_t* pos = a.epos + (((size_t)s * a.tc + tl) * a.G + g) * a.KS;
-    // pass 1: the largest log-weight
-    for (int q = 0; q < nv; ++q) {
-      const float2 st = a.pS[(size_t)pos[q] * R + r];
-      M2 = fmaxf(M2, st.x + __log2f(st.y));
+    // pass 1: the largest log-weight.  Both passes take the slots in groups
+    // whose position and statistics loads are issued together (slots past nv
+    // read the last one again and get weight 0).
+    constexpr int QG = 16;
+    for (int q0 = 0; q0 < nv; q0 += QG) {
+      int pq[QG];
+#pragma unroll
+      for (int u = 0; u < QG; ++u) pq[u] = pos[min(q0 + u, nv - 1)];
+      float2 st[QG];
+#pragma unroll
+      for (int u = 0; u < QG; ++u) st[u] = a.pS[(size_t)pq[u] * R + r];
+#pragma unroll
+      for (int u = 0; u < QG; ++u) M2 = fmaxf(M2, st[u].x + __log2f(st[u].y));
     }
     const float M2u = (M2 == -INFINITY) ? 0.f : M2;
     const float wl = (l > 0.f) ? __builtin_amdgcn_exp2f(m * c - M2u) : 0.f;
@@ -783,17 +807,20 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[dt][i] = oacc[dt][i] * wl;
-    // pass 2: weighted partials in slot order
-#ifndef MSA_COMBINE_UNROLL
-#define MSA_COMBINE_UNROLL 2
-#endif
-#pragma unroll MSA_COMBINE_UNROLL
-    for (int q = 0; q < nv; ++q) {
-      const size_t prow = (size_t)pos[q] * R + r;
-      const float2 st = a.pS[prow];
-      const float w = __builtin_amdgcn_exp2f(st.x - M2u);
-      sumw += w * st.y;
-      accumulate_partial_row(o, a.pO + prow * D, w, half);
+    // pass 2: weighted partials in slot order, in groups of QG2 (registers)
+    constexpr int QG2 = 8;
+    for (int q0 = 0; q0 < nv; q0 += QG2) {
+      int pq[QG2];
+#pragma unroll
+      for (int u = 0; u < QG2; ++u) pq[u] = pos[min(q0 + u, nv - 1)];
+#pragma unroll
+      for (int u = 0; u < QG2; ++u) {
+        const size_t prow = (size_t)pq[u] * R + r;
+        const float2 st = a.pS[prow];
+        const float w = q0 + u < nv ? __builtin_amdgcn_exp2f(st.x - M2u) : 0.f;
+        sumw += w * st.y;
+        accumulate_partial_row(o, a.pO + prow * D, w, half);
+      }
     }
     M2 = M2u;
   } else {
