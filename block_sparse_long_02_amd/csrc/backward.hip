@@ -502,10 +502,19 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int nv = l.rinfo[rowg] & 0x3fffffff;
   const int32_t* pos = l.epos + (size_t)rowg * l.KS;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int q = 0; q < nv; ++q) {
-    const bf16x8 v = load_bf16x8(a.dqp + ((size_t)pos[q] * R + r) * D + part * 8);
+  // slots in groups of 8 whose position and partial loads are issued together
+  for (int q0 = 0; q0 < nv; q0 += 8) {
+    int pq[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += (float)v[i];
+    for (int u = 0; u < 8; ++u) pq[u] = pos[min(q0 + u, nv - 1)];
+    bf16x8 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = load_bf16x8(a.dqp + ((size_t)pq[u] * R + r) * D + part * 8);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (q0 + u < nv)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += (float)v[u][i];
   }
   const float sc = l.scale_log2 * kLn2;
   float* dst = a.dq + (((size_t)s * l.T + l.t0 + tl) * l.Hq + h) * D + part * 8;

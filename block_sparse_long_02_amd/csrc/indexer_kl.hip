@@ -164,12 +164,23 @@ __global__ void kl_row_lse_kernel(IndexerKlArgs a) {
   if (row >= n_rows) return;
   const int nv = l.rinfo[row] & 0x3fffffff;
   const int32_t* pos = l.epos + (size_t)row * l.KS;
+  // slots in groups of 8 whose position and statistics loads are issued together
   float M = -INFINITY;
-  for (int q = 0; q < nv; ++q) M = fmaxf(M, a.stat[pos[q]].x);
+  for (int q0 = 0; q0 < nv; q0 += 8) {
+    float2 st[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) st[u] = a.stat[pos[min(q0 + u, nv - 1)]];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) M = fmaxf(M, st[u].x);
+  }
   float sum = 0.f;
-  for (int q = 0; q < nv; ++q) {
-    const float2 st = a.stat[pos[q]];
-    sum += st.y * __builtin_amdgcn_exp2f(st.x - M);
+  for (int q0 = 0; q0 < nv; q0 += 8) {
+    float2 st[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) st[u] = a.stat[pos[min(q0 + u, nv - 1)]];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (q0 + u < nv) sum += st[u].y * __builtin_amdgcn_exp2f(st[u].x - M);
   }
   a.lse_i[row] = nv > 0 ? M + __log2f(sum) : -INFINITY;
 }
@@ -465,10 +476,24 @@ __global__ void kl_row_out_kernel(IndexerKlArgs a) {
   const int32_t* pos = l.epos + (size_t)row * l.KS;
   f32x4 dq = {0.f, 0.f, 0.f, 0.f};
   float kl = 0.f;
-  for (int q = 0; q < nv; ++q) {
-    const int p = pos[q];
-    dq += *reinterpret_cast<const f32x4*>(a.dq_e + (size_t)p * a.di + 4 * c4);
-    if (c4 == 0) kl += a.kl_e[p];
+  // slots in groups of 8 whose position and term loads are issued together
+  for (int q0 = 0; q0 < nv; q0 += 8) {
+    int pq[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pq[u] = pos[min(q0 + u, nv - 1)];
+    f32x4 v[8];
+    float ke[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v[u] = *reinterpret_cast<const f32x4*>(a.dq_e + (size_t)pq[u] * a.di + 4 * c4);
+      ke[u] = a.kl_e[pq[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (q0 + u < nv) {
+        dq += v[u];
+        kl += ke[u];
+      }
   }
   *reinterpret_cast<f32x4*>(a.d_idx_q + orow * a.di + 4 * c4) = dq;
   if (c4 == 0) a.kl[orow] = kl;
