@@ -414,21 +414,29 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
     __syncthreads();  // dS rows of the step complete
     const int trk = tr_lane_off(lane, KR);
     // dq^T[d][row] = sum over the block's keys of K^T[d][key] dS^T[key][row]:
-    // each lane ends with one row and 4 runs of 4 consecutive d, stored as
-    // 8-byte bf16 groups.  Unrolled (where registers allow) so that the
-    // compiler can count the stores when the next step waits for its rows.
+    // the wave's RT (row tile, d tile) pairs share one row tile, whose dS
+    // operands are read once; each d tile's K^T operands are read before its
+    // products.  Each lane ends with one row and 4 runs of 4 consecutive d,
+    // stored as 8-byte bf16 groups.  Unrolled (where registers allow) so that
+    // the compiler can count the stores when the next step waits for its rows.
+    static_assert(4 % RT == 0, "a wave's pairs share one row tile");
+    const int rt2 = (wave * RT) >> 2;
+    bf16x8 dsb[BS / 16];
+#pragma unroll
+    for (int ks = 0; ks < BS / 16; ++ks)
+      dsb[ks] = *reinterpret_cast<const bf16x8*>(DSr + (rt2 * 32 + col) * DSR + 16 * ks + 8 * half);
 #pragma unroll(RT <= 2 ? RT : 1)
     for (int ii = 0; ii < RT; ++ii) {
-      const int f = wave * RT + ii;
-      const int rt2 = f >> 2, dt = f & 3;
-      f32x16 acc = {};
+      const int dt = (wave * RT + ii) & 3;
+      bf16x8 ka[BS / 16];
 #pragma unroll
       for (int ks = 0; ks < BS / 16; ++ks) {
         const int o0 = 16 * ks * KR + 32 * dt + trk;
-        acc = mfma32x32x16(join_bf16x4(lds_read_tr16(Ks + o0), lds_read_tr16(Ks + o0 + 8 * KR)),
-                           *reinterpret_cast<const bf16x8*>(DSr + (rt2 * 32 + col) * DSR + 16 * ks + 8 * half),
-                           acc);
+        ka[ks] = join_bf16x4(lds_read_tr16(Ks + o0), lds_read_tr16(Ks + o0 + 8 * KR));
       }
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < BS / 16; ++ks) acc = mfma32x32x16(ka[ks], dsb[ks], acc);
       // rows past the list fall outside the resource and their stores are dropped
       const int rho = step * SR + rt2 * 32 + col;
 #pragma unroll
