@@ -120,7 +120,7 @@ int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
     const long lists_per_win = (long)d->batch * G * p->nb;
     const long max_win = (kMaxInt32 - 1) / lists_per_win;
     if (max_win < 1) return MSA_ERR_UNSUPPORTED;
-    if ((tc_max + msa::kListWindow - 1) / msa::kListWindow > max_win) tc_max = max_win * msa::kListWindow;
+    if ((tc_max + msa::kFwdListWindow - 1) / msa::kFwdListWindow > max_win) tc_max = max_win * msa::kFwdListWindow;
     if (tc_max < B) return MSA_ERR_UNSUPPORTED;
   }
   if (tc_max >= T) {
@@ -141,7 +141,7 @@ int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
     p->off_bidx = L.add(nb_ * Tc * G_ * (size_t)d->topk * 4);
   }
   if (p->with_main) {
-    const size_t nwin = ((size_t)p->Tc + msa::kListWindow - 1) / msa::kListWindow;
+    const size_t nwin = ((size_t)p->Tc + msa::kFwdListWindow - 1) / msa::kFwdListWindow;
     const size_t nlists = nb_ * G_ * nwin * (size_t)p->nb;
     const size_t nscan = (nlists + msa::kScanItems - 1) / msa::kScanItems;
     const size_t emax = nb_ * Tc * G_ * (size_t)p->KS;
@@ -579,7 +579,8 @@ int msa_prefill(const msa_dims* dims, const void* q, const void* k, const void* 
     a.t0 = t0;
     a.tc = tc;
     const long emax = (long)dims->batch * tc * dims->num_kv_heads * p.KS;
-    a.nwin = (tc + msa::kListWindow - 1) / msa::kListWindow;
+    a.window = msa::kFwdListWindow;
+    a.nwin = (tc + msa::kFwdListWindow - 1) / msa::kFwdListWindow;
     a.nlists = (long)dims->batch * dims->num_kv_heads * a.nwin * p.nb;
     a.max_work = (emax + p.mt - 1) / p.mt + a.nlists;
     hipError_t e = msa::launch_prefill_main_sparse(a, s);
@@ -652,6 +653,7 @@ int msa_indexer_kl(const msa_dims* dims, const void* q, const void* k, const voi
     const long emax = (long)dims->batch * tc * dims->num_kv_heads * p.KS;
     l.t0 = t0;
     l.tc = tc;
+    l.window = msa::kListWindow;
     l.nwin = (tc + msa::kListWindow - 1) / msa::kListWindow;
     l.nlists = (long)dims->batch * dims->num_kv_heads * l.nwin * p.nb;
     l.max_work = (emax + p.mt - 1) / p.mt + l.nlists;
@@ -721,6 +723,7 @@ int msa_prefill_backward(const msa_dims* dims, const void* q, const void* k, con
     const int tc = (dims->seqlen - t0) < p.Tc ? dims->seqlen - t0 : p.Tc;
     l.t0 = t0;
     l.tc = tc;
+    l.window = msa::kListWindow;
     l.nwin = (tc + msa::kListWindow - 1) / msa::kListWindow;
     l.nlists = (long)dims->batch * dims->num_kv_heads * l.nwin * p.nb;
     l.max_work = p.max_lists;

@@ -8,7 +8,9 @@
 //    block 0..L-1 for all G groups at once: each 16-key x 32-dim slice is the
 //    MFMA A operand and the G index queries form the B operand (columns), so
 //    every idx_k byte read feeds all groups.  Grid: sequences x block ranges;
-//    each wave owns a few consecutive blocks.
+//    each wave owns one block (at 8 x 1M, two blocks per wave streamed the
+//    cache 6 % slower: fewer, longer waves leave more of it idle between
+//    their load bursts).
 // 2. the shared top-k kernel selects the blocks (local block forced).
 // 3. decode_attn_kernel: 8 waves per (sequence, group) share its selected
 //    blocks (or, in dense mode, runs of consecutive blocks), attend them on
@@ -25,7 +27,7 @@ namespace {
 
 constexpr int D = 128;
 constexpr int kDecMaxR = 16;     // query heads per group handled by the decode kernels (<= 32 MFMA columns)
-constexpr int kDecBlocksPerWave = 2;
+constexpr int kDecBlocksPerWave = 1;
 
 template <int DI, int BS>
 __global__ __launch_bounds__(256) void decode_index_kernel(const bf16_t* __restrict__ idx_q,

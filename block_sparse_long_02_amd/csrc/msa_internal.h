@@ -38,13 +38,20 @@ hipError_t launch_topk_decode(const float* S, int s_stride, int32_t* bidx, const
                               int Lmax, int batch, int G, int B, int k, bool sink, hipStream_t st);
 
 // ---- Main Branch, prefill ----
-// Query tokens per window of the block lists: the lists of non-local
-// (token, slot) pairs are kept per (sequence, group, window, block), so that
-// consecutive block-major workgroups touch the q rows of one window.
+// Query tokens per window of the block lists: the lists of (token, slot)
+// pairs are kept per (sequence, group, window, block), so that consecutive
+// block-major workgroups touch the q rows of one window.  The forward uses
+// 4096-token windows (at 128K its lists build in 0.97 ms against 1.5 ms with
+// 8192, 3.2 ms with 16384); the indexer KL and the backward keep 8192, which
+// halves their per-list partial blocks and bounds the list sort's LDS keys.
 #ifndef MSA_LIST_WINDOW
 #define MSA_LIST_WINDOW 8192
 #endif
 constexpr int kListWindow = MSA_LIST_WINDOW;
+#ifndef MSA_FWD_LIST_WINDOW
+#define MSA_FWD_LIST_WINDOW 4096
+#endif
+constexpr int kFwdListWindow = MSA_FWD_LIST_WINDOW;
 // Workgroup size of the multi-workgroup scans over the lists.
 constexpr int kScanItems = 4096;
 // Tiles of one block list served by one block-major workgroup (the K/V
@@ -69,7 +76,8 @@ struct PrefillMainArgs {
   int rank_bits;          // list entry = local token << rank_bits | slot; 2^rank_bits >= KS
   int include_local;      // lists also hold each row's local block (entries b <= L(t))
   int nbl;                // block lists per (batch, group, window) = nb
-  int nwin;               // windows in this chunk = ceil(tc / kListWindow)
+  int window;             // query tokens per list window
+  int nwin;               // windows in this chunk = ceil(tc / window)
   long nlists;            // batch * G * nwin * nbl
   float scale_log2;       // softmax_scale * log2(e)
   // workspace

@@ -198,7 +198,7 @@ __global__ void fill_i32_kernel(int32_t* p, size_t n, int32_t v) {
 }
 
 __device__ __forceinline__ size_t list_id(const PrefillMainArgs& a, int s, int g, int tl, int b) {
-  const int w = tl / kListWindow;
+  const int w = tl / a.window;
   return (((size_t)s * a.G + g) * a.nwin + w) * a.nbl + b;
 }
 
