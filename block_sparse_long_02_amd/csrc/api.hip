@@ -347,8 +347,12 @@ int make_bwd_plan(const msa_dims* d, BwdPlan* p) {
 // ---------------------------------------------------------------------------
 // Decode plan
 // ---------------------------------------------------------------------------
+#ifndef MSA_DEC_SPLIT_BLOCKS
+#define MSA_DEC_SPLIT_BLOCKS 1
+#endif
+
 struct DecodePlan {
-  int nbmax = 0, R = 0, s_stride = 0, nsplit = 0, bps = 0;
+  int nbmax = 0, R = 0, s_stride = 0, nsplit = 0, bps = 0, sub = 1;
   bool with_scores = false;
   size_t off_S = 0, off_bidx = 0, off_pO = 0, off_pS = 0, total = 0;
 };
@@ -364,10 +368,12 @@ int make_decode_plan(const msa_dims* d, DecodePlan* p) {
   if (d->flags & MSA_DENSE) {
     p->bps = 2048 / B;  // 2048 keys per work item
     p->nsplit = (p->nbmax + p->bps - 1) / p->bps;
-  } else if (d->flags & MSA_GIVEN_INDICES) {
-    p->nsplit = d->topk;
   } else {
-    p->nsplit = d->topk < p->nbmax ? d->topk : p->nbmax;
+    // 128-key blocks are split into two 64-key work items: one key tile per
+    // wave, so no wave waits for two block loads in turn
+    p->sub = (B == 128 && MSA_DEC_SPLIT_BLOCKS) ? 2 : 1;
+    const int sel = (d->flags & MSA_GIVEN_INDICES) ? d->topk : (d->topk < p->nbmax ? d->topk : p->nbmax);
+    p->nsplit = sel * p->sub;
   }
   Layout L;
   const size_t nb_ = (size_t)d->batch, G_ = (size_t)G;
@@ -786,6 +792,7 @@ int msa_decode(const msa_dims* dims, const void* q, const void* k_cache, const v
   a.topk = dims->topk;
   a.dense = dense;
   a.nsplit = p.nsplit;
+  a.sub = p.sub;
   a.blocks_per_split = p.bps;
   a.scale_log2 = log2_scale(dims);
   a.pO = at<float>(workspace, p.off_pO);

@@ -92,7 +92,10 @@ __global__ __launch_bounds__(256) void decode_index_kernel(const bf16_t* __restr
 constexpr int kDecAttnWaves = 8;
 // (s, g) rows below which a decode step splits each row over several
 // workgroups: one per CU of the 256 on MI355X.
-constexpr long kDecFillRows = 256;
+#ifndef MSA_DEC_FILL_ROWS
+#define MSA_DEC_FILL_ROWS 256
+#endif
+constexpr long kDecFillRows = MSA_DEC_FILL_ROWS;
 
 template <int BS>
 struct DecTile {
@@ -145,18 +148,22 @@ __global__ __launch_bounds__(kDecAttnWaves * 64) void decode_attn_kernel(DecodeM
   for (int i = 0; i < ipw; ++i) {
     const int item = x * kDecAttnWaves * ipw + wave + kDecAttnWaves * i;
     if (item >= a.nsplit) break;
-    int blk_lo, blk_hi;
+    int k_lo, k_end;  // keys [k_lo, k_end) of this item
     if (a.dense) {
-      blk_lo = item * a.blocks_per_split;
-      blk_hi = min(blk_lo + a.blocks_per_split - 1, L);
+      const int blk_lo = item * a.blocks_per_split;
+      const int blk_hi = min(blk_lo + a.blocks_per_split - 1, L);
+      k_lo = blk_lo * a.B;
+      k_end = min((blk_hi + 1) * a.B, len);
     } else {
-      const int e = a.bidx[((size_t)s * a.G + g) * a.topk + item];
-      blk_lo = e;
-      blk_hi = (e >= 0 && e <= L) ? e : e - 1;
+      // item = selected entry * sub + part: part `part` of the block's keys
+      const int e = a.bidx[((size_t)s * a.G + g) * a.topk + item / a.sub];
+      if (e < 0 || e > L) continue;  // -1 padding
+      const int span = a.B / a.sub;
+      k_lo = e * a.B + (item % a.sub) * span;
+      k_end = min(k_lo + span, len);
     }
-    if (blk_lo < 0 || blk_lo > blk_hi) continue;
-    const int k_end = min((blk_hi + 1) * a.B, len);  // exclusive
-    for (int kb = blk_lo * a.B; kb < k_end; kb += NK) {
+    if (k_lo >= k_end) continue;
+    for (int kb = k_lo; kb < k_end; kb += NK) {
       // K rows as MFMA A operands, V units for the transposed LDS tile
       bf16x8 kop[KTL][D / 16];
 #pragma unroll
@@ -307,29 +314,31 @@ __global__ __launch_bounds__(kDecAttnWaves * 64) void decode_attn_kernel(DecodeM
   }
 }
 
-// Merges the nparts partials of every (s, g) in fixed order.
+// Merges the nparts partials of one (s, g, head r) in fixed order; one
+// workgroup per (r, g, s), one thread per output dimension.  The loads of a
+// pass do not depend on each other, so four are kept in flight.
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeMainArgs a, int nparts) {
-  const int g = blockIdx.x, s = blockIdx.y;
+  const int r = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int R = a.Hq / a.G;
   const int d = threadIdx.x;
-  for (int r = 0; r < R; ++r) {
-    const size_t base = ((size_t)s * a.G + g) * nparts;
-    float M2 = -INFINITY;
-    for (int j = 0; j < nparts; ++j) M2 = fmaxf(M2, a.pS[(base + j) * R + r]);
-    const float Mu = (M2 == -INFINITY) ? 0.f : M2;
-    float sw = 0.f, acc = 0.f;
-    for (int j = 0; j < nparts; ++j) {
-      const size_t prow = (base + j) * R + r;
-      const float w = __builtin_amdgcn_exp2f(a.pS[prow] - Mu);
-      sw += w;
-      acc += w * a.pO[prow * D + d];
-    }
-    const int h = g * R + r;
-    const float ov = (sw > 0.f) ? acc / sw : 0.f;
-    a.out[((size_t)s * a.Hq + h) * D + d] = __builtin_bit_cast(bf16_t, (__bf16)ov);
-    if (a.lse != nullptr && d == 0)
-      a.lse[(size_t)s * a.Hq + h] = (sw > 0.f) ? (Mu + __log2f(sw)) * kLn2 : -INFINITY;
+  const size_t base = ((size_t)s * a.G + g) * nparts;
+  float M2 = -INFINITY;
+#pragma unroll 4
+  for (int j = 0; j < nparts; ++j) M2 = fmaxf(M2, a.pS[(base + j) * R + r]);
+  const float Mu = (M2 == -INFINITY) ? 0.f : M2;
+  float sw = 0.f, acc = 0.f;
+#pragma unroll 4
+  for (int j = 0; j < nparts; ++j) {
+    const size_t prow = (base + j) * R + r;
+    const float w = __builtin_amdgcn_exp2f(a.pS[prow] - Mu);
+    sw += w;
+    acc += w * a.pO[prow * D + d];
   }
+  const int h = g * R + r;
+  const float ov = (sw > 0.f) ? acc / sw : 0.f;
+  a.out[((size_t)s * a.Hq + h) * D + d] = __builtin_bit_cast(bf16_t, (__bf16)ov);
+  if (a.lse != nullptr && d == 0)
+    a.lse[(size_t)s * a.Hq + h] = (sw > 0.f) ? (Mu + __log2f(sw)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -385,7 +394,7 @@ hipError_t launch_decode_main(const DecodeMainArgs& a, hipStream_t st) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nparts == 1) return err;
   prof_mark(st, MSA_STAGE_DECODE_COMBINE);
-  decode_combine_kernel<<<dim3(a.G, a.batch), 128, 0, st>>>(a, nparts);
+  decode_combine_kernel<<<dim3(a.Hq / a.G, a.G, a.batch), 128, 0, st>>>(a, nparts);
   return hipGetLastError();
 }
 

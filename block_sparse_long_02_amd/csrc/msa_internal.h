@@ -161,6 +161,7 @@ struct DecodeMainArgs {
   int batch, Lmax, Hq, G, B, topk;
   bool dense;
   int nsplit;             // work items per (s, g)
+  int sub;                // sparse / given: work items per selected block (each covers B / sub keys)
   int blocks_per_split;   // dense: consecutive blocks per work item
   float scale_log2;
   float* pO;              // [batch*G*nsplit*R*128]
