@@ -63,18 +63,24 @@ float log2_scale(const msa_dims* d) {
 struct PrefillPlan {
   int nb = 0, KS = 0, R = 0, mt = 0, rank_bits = 0;
   int Tc = 0, nchunks = 0;
-  int s_stride_max = 0;
+  int s_stride_max = 0, sm_stride_max = 0;
   long max_work = 0;
   bool with_scores = false, with_main = false;
-  size_t off_S = 0, off_bidx = 0, off_cnt = 0, off_offs = 0, off_bsum = 0, off_rinfo = 0, off_epos = 0,
+  size_t off_S = 0, off_SM = 0, off_bidx = 0, off_cnt = 0, off_offs = 0, off_bsum = 0, off_rinfo = 0, off_epos = 0,
          off_entries = 0, off_work = 0, off_nwork = 0, off_pO = 0, off_pS = 0;
   size_t total = 0;
 };
 
+// superblock maxima per row: ceil(L / 16) floats, padded to a multiple of 4
+int sm_stride_for(int L) {
+  const int n = (L + msa::kSuperBlock - 1) / msa::kSuperBlock;
+  return (int)round_up((size_t)(n > 1 ? n : 1), 4);
+}
+
 size_t per_token_bytes(const msa_dims* d, const PrefillPlan& p) {
   const size_t G = (size_t)d->num_kv_heads;
   size_t b = 0;
-  if (p.with_scores) b += G * (size_t)p.s_stride_max * 4 + G * (size_t)d->topk * 4;
+  if (p.with_scores) b += G * ((size_t)p.s_stride_max + (size_t)p.sm_stride_max) * 4 + G * (size_t)d->topk * 4;
   if (p.with_main) b += G * 4 + G * (size_t)p.KS * (4 + 4 + (size_t)p.R * (128 * 2 + 8));
   return b;
 }
@@ -93,6 +99,7 @@ int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
   p->with_main = !index_only && !(d->flags & MSA_DENSE);
   const int Lmax = (T - 1) / B;
   p->s_stride_max = (int)round_up((size_t)(Lmax > 1 ? Lmax : 1), 4);
+  p->sm_stride_max = sm_stride_for(Lmax);
   if (!p->with_scores && !p->with_main) {  // dense prefill needs no workspace
     p->Tc = T;
     p->nchunks = 1;
@@ -138,6 +145,7 @@ int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
   const size_t nb_ = (size_t)d->batch, Tc = (size_t)p->Tc, G_ = (size_t)G;
   if (p->with_scores) {
     p->off_S = L.add(nb_ * Tc * G_ * (size_t)p->s_stride_max * 4);
+    p->off_SM = L.add(nb_ * Tc * G_ * (size_t)p->sm_stride_max * 4);
     p->off_bidx = L.add(nb_ * Tc * G_ * (size_t)d->topk * 4);
   }
   if (p->with_main) {
@@ -414,14 +422,16 @@ hipError_t run_index_chunk(const msa_dims* d, const PrefillPlan& p, const void* 
   const int B = d->block_size;
   const int Lc = (t0 + tc - 1) / B;
   const int s_stride = (int)round_up((size_t)(Lc > 1 ? Lc : 1), 4);
+  const int sm_stride = sm_stride_for(Lc);
   float* S = at<float>(ws, p.off_S);
+  float* SM = Lc > msa::kSbMinCandidates ? at<float>(ws, p.off_SM) : nullptr;
   msa::prof_mark(st, MSA_STAGE_INDEX_PREFILL);
   hipError_t e = msa::launch_index_blockmax_prefill(
       static_cast<const uint16_t*>(idx_q), static_cast<const uint16_t*>(idx_k), S, d->batch,
-      d->seqlen, d->num_kv_heads, d->index_dim, B, t0, tc, s_stride, st);
+      d->seqlen, d->num_kv_heads, d->index_dim, B, t0, tc, s_stride, SM, sm_stride, st);
   if (e != hipSuccess) return e;
   msa::prof_mark(st, MSA_STAGE_TOPK_PREFILL);
-  return msa::launch_topk_prefill(S, s_stride, bidx, bidx_rows, t_off, d->batch, d->num_kv_heads, B,
+  return msa::launch_topk_prefill(S, s_stride, SM, sm_stride, bidx, bidx_rows, t_off, d->batch, d->num_kv_heads, B,
                                   d->topk, (d->flags & MSA_FORCE_SINK) != 0, t0, tc, st);
 }
 
@@ -502,7 +512,8 @@ int msa_index_scores(const msa_dims* dims, const void* idx_q, const void* idx_k,
   msa::prof_mark(s, MSA_STAGE_INDEX_PREFILL);
   hipError_t e = msa::launch_index_blockmax_prefill(
       static_cast<const uint16_t*>(idx_q), static_cast<const uint16_t*>(idx_k), scores, dims->batch,
-      dims->seqlen, dims->num_kv_heads, dims->index_dim, dims->block_size, t0, t1 - t0, row_stride, s);
+      dims->seqlen, dims->num_kv_heads, dims->index_dim, dims->block_size, t0, t1 - t0, row_stride, nullptr, 0,
+      s);
   msa::prof_mark(s, -1);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }

@@ -18,6 +18,9 @@
 // a time through double-buffered LDS as the A operand, so each idx_k byte
 // fetched feeds 128*NT rows and each A operand read from LDS feeds NT MFMAs.
 // Workgroups are issued longest-first (latest tokens have the most blocks).
+// Beside S, each row gets the maximum of every run of 16 of its candidate
+// blocks (a superblock), so the top-k can skip the runs that cannot hold a
+// selected block.
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -30,10 +33,12 @@ namespace {
 template <int DI>
 constexpr int idx_nt() { return DI == 128 ? 3 : 4; }
 
-template <int DI, int B, int NT>
+// WITH_SM: also write the superblock maxima SM (chunks with rows of more
+// than kSbMinCandidates candidate blocks).
+template <int DI, int B, int NT, bool WITH_SM>
 __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
     const bf16_t* __restrict__ idx_q, const bf16_t* __restrict__ idx_k, float* __restrict__ S,
-    int T, int G, int t0, int tc, int s_stride, int n_tiles) {
+    int T, int G, int t0, int tc, int s_stride, float* __restrict__ SM, int sm_stride, int n_tiles) {
   constexpr int ROWS = 128 * NT;
   constexpr int KPAD = DI + 8;            // LDS row stride (bf16): +16 B against bank conflicts
   constexpr int KSTEPS = DI / 16;         // MFMA k-steps per 32x32 tile
@@ -57,13 +62,14 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
 
   // B operands: idx_q rows of this wave's NT 32-row column tiles.
   bf16x8 qop[NT][KSTEPS];
-  int row_idx[NT];
+  int row_idx[NT], row_L[NT];
   bool row_ok[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = r0 + wave * 32 * NT + nt * 32 + col;
     row_idx[nt] = r;
     row_ok[nt] = r < rows_chunk;
+    row_L[nt] = (t0 + r / G) / B;  // the row's candidate blocks are 0 .. row_L - 1
     const bf16_t* qp = idx_q + ((size_t)s * T * G + (size_t)t0 * G + (size_t)(row_ok[nt] ? r : 0)) * DI;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
@@ -97,8 +103,14 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
 
   // block maxima of 4 consecutive blocks are buffered and written as float4
   f32x4 sb[NT];
+  float smx[NT];   // running superblock maximum over the row's candidate blocks
+  f32x4 smb[NT];   // maxima of 4 consecutive superblocks, written as float4
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) sb[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < NT; ++nt) {
+    sb[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    smx[nt] = -INFINITY;
+    smb[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   for (int b = 0; b < nblk; ++b) {
     const int cur = b & 1;
@@ -133,6 +145,27 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
       else if (slot == 1) sb[nt][1] = v;
       else if (slot == 2) sb[nt][2] = v;
       else sb[nt][3] = v;
+      if (WITH_SM && b < row_L[nt]) smx[nt] = fmaxf(smx[nt], v);
+    }
+    if (WITH_SM && (b % kSuperBlock == kSuperBlock - 1 || b == nblk - 1)) {  // uniform
+      const int sbi = b / kSuperBlock, sslot = sbi & 3;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (sslot == 0) smb[nt][0] = smx[nt];
+        else if (sslot == 1) smb[nt][1] = smx[nt];
+        else if (sslot == 2) smb[nt][2] = smx[nt];
+        else smb[nt][3] = smx[nt];
+        smx[nt] = -INFINITY;
+      }
+      if ((sslot == 3 || b == nblk - 1) && half == 0) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          if (row_ok[nt]) {
+            float* dst = SM + ((size_t)s * rows_chunk + (size_t)row_idx[nt]) * sm_stride + (sbi & ~3);
+            *reinterpret_cast<f32x4*>(dst) = smb[nt];
+          }
+        }
+      }
     }
     if ((slot == 3 || b == nblk - 1) && half == 0) {
 #pragma unroll
@@ -155,14 +188,20 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
 
 hipError_t launch_index_blockmax_prefill(const uint16_t* idx_q, const uint16_t* idx_k, float* S,
                                          int batch, int T, int G, int di, int B, int t0, int tc,
-                                         int s_stride, hipStream_t st) {
+                                         int s_stride, float* SM, int sm_stride, hipStream_t st) {
   const long rows = (long)tc * G;
   const int rows_per_wg = 128 * (di == 128 ? idx_nt<128>() : idx_nt<64>());
   const int n_tiles = (int)((rows + rows_per_wg - 1) / rows_per_wg);
   dim3 grid(n_tiles, batch);
-#define MSA_IDX_LAUNCH(DI_, B_)                                                                   \
-  index_blockmax_prefill_kernel<DI_, B_, idx_nt<DI_>()><<<grid, 256, 0, st>>>(idx_q, idx_k, S, T, G, t0, tc,     \
-                                                               s_stride, n_tiles)
+#define MSA_IDX_LAUNCH(DI_, B_)                                                                         \
+  do {                                                                                                  \
+    if (SM != nullptr)                                                                                  \
+      index_blockmax_prefill_kernel<DI_, B_, idx_nt<DI_>(), true><<<grid, 256, 0, st>>>(                \
+          idx_q, idx_k, S, T, G, t0, tc, s_stride, SM, sm_stride, n_tiles);                             \
+    else                                                                                                \
+      index_blockmax_prefill_kernel<DI_, B_, idx_nt<DI_>(), false><<<grid, 256, 0, st>>>(               \
+          idx_q, idx_k, S, T, G, t0, tc, s_stride, SM, sm_stride, n_tiles);                             \
+  } while (0)
   if (di == 128) {
     if (B == 128) MSA_IDX_LAUNCH(128, 128);
     else if (B == 64) MSA_IDX_LAUNCH(128, 64);

@@ -22,15 +22,25 @@ void prof_mark(hipStream_t st, int stage);
 
 // ---- Index Branch, prefill: scores + Block-Max for query tokens [t0, t0+tc) ----
 // S is [batch][tc*G][s_stride] fp32; row (t-t0)*G+g holds blocks 0..L(t)-1.
+// Superblocks are runs of kSuperBlock consecutive blocks; SM (nullable) is
+// [batch][tc*G][sm_stride] fp32 and SM[row][i] is the largest S[row][b] over
+// the row's candidate blocks b in [16 i, 16 i + 16) with b < L(t), for
+// i < ceil(L(t) / 16): the top-k reads only the superblocks that can hold
+// a selected block.
+constexpr int kSuperBlock = 16;
+// Rows with more candidate blocks than this take the superblock path; SM is
+// only needed (and only computed) when a chunk has such rows.
+constexpr int kSbMinCandidates = 1024;
 hipError_t launch_index_blockmax_prefill(const uint16_t* idx_q, const uint16_t* idx_k, float* S,
                                          int batch, int T, int G, int di, int B, int t0, int tc,
-                                         int s_stride, hipStream_t st);
+                                         int s_stride, float* SM, int sm_stride, hipStream_t st);
 
 // ---- Top-k with the forced local block ----
 // prefill rows: (s, t in [t0, t0+tc), g); output row address
 //   bidx + ((s*bidx_rows + (t - bidx_t_off))*G + g)*k
 // sink: block 0 is forced too when a row keeps at least two blocks.
-hipError_t launch_topk_prefill(const float* S, int s_stride, int32_t* bidx, long bidx_rows,
+hipError_t launch_topk_prefill(const float* S, int s_stride, const float* SM, int sm_stride,
+                               int32_t* bidx, long bidx_rows,
                                int bidx_t_off, int batch, int G, int B, int k, bool sink, int t0, int tc,
                                hipStream_t st);
 // decode rows: (s, g); query position cache_lens[s]-1; output bidx + (s*G+g)*k

@@ -27,6 +27,14 @@
 //     them out in ascending order, followed by L and the -1 padding.
 // When more than kCap candidates survive (many exact ties, e.g. integer
 // inputs), steps 3-4 run directly over all candidates in global memory.
+//
+// Prefill rows also come with superblock maxima (the largest score of every
+// run of 16 candidate blocks).  The want-th largest superblock maximum lb is
+// a lower bound of the want-th largest candidate score: want superblocks
+// each hold a candidate scoring >= lb.  So every block that can be selected,
+// ties at the threshold included, lies in a superblock whose maximum is
+// >= lb, and step 2 reads only those superblocks (at 1M tokens a row has up
+// to 512 superblocks, of which a few dozen pass).
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -215,6 +223,91 @@ __device__ __forceinline__ int compact_candidates(const float* __restrict__ srow
   return cnt;
 }
 
+// Superblock-pruned form of compact_candidates for the candidates c0..L-1:
+// sm[i] is the largest candidate score in blocks [16 i, 16 i + 16).  With
+// c0 = 1 (block 0 forced), superblock 0 also covers block 0, so it is left
+// out of the bound and always read.  Survivors (keys >= lb) are compacted in
+// ascending block order; the passing superblock ids go through slist (LDS,
+// kCap entries).  Returns the survivor count (entries beyond kCap are counted
+// but not stored), or -1 when the row has too few or too many superblocks
+// for this path.
+static_assert(kSuperBlock == 16, "the superblock gather maps 4 superblocks of 16 blocks onto a wave");
+static_assert(kSbMinCandidates == kWave * kRegKeys, "superblock rows start where the register path ends");
+__device__ __forceinline__ int compact_candidates_sb(const float* __restrict__ srow, const float* __restrict__ sm,
+                                                     int c0, int L, int want, uint32_t* skey, int32_t* sblk,
+                                                     int32_t* slist, int lane) {
+  const int nsb = (L + kSuperBlock - 1) / kSuperBlock;
+  const int s_lo = c0 > 0 ? 1 : 0;
+  // rows that compact_candidates reads once into registers are cheaper there
+  if (L - c0 <= kSbMinCandidates || nsb - s_lo <= want || nsb > kCap) return -1;  // wave-uniform
+  const uint64_t lt = lanemask_lt();
+  constexpr int kSbRegs = kCap / kWave;
+  uint32_t key[kSbRegs];
+#pragma unroll
+  for (int i = 0; i < kSbRegs; ++i) {
+    const int j = i * kWave + lane;
+    key[i] = (j >= s_lo && j < nsb) ? order_key(sm[j]) : 0u;
+  }
+  const int nch = (nsb + kWave - 1) / kWave;
+  // lb = want-th largest bound key (exact bitwise search, counts by ballots)
+  uint32_t lb = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = lb | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kSbRegs; ++i)
+      if (i < nch) cnt += popc(__ballot(key[i] >= c));
+    if (cnt >= want) lb = c;
+  }
+  // passing superblocks, ascending
+  int P = 0;
+#pragma unroll
+  for (int i = 0; i < kSbRegs; ++i) {
+    if (i < nch) {  // wave-uniform
+      const int j = i * kWave + lane;
+      const bool pass = j < nsb && (j < s_lo || key[i] >= lb);
+      const uint64_t bal = __ballot(pass);
+      if (pass) slist[P + popc(bal & lt)] = j;
+      P += popc(bal);
+    }
+  }
+  wave_lds_sync();
+  // gather the passing superblocks, 4 per step (16 lanes each), 4 steps of
+  // loads in flight before their compaction
+  const int sub = lane >> 4, off = lane & (kSuperBlock - 1);
+  int cnt = 0;
+  for (int i0 = 0; i0 < P; i0 += 16) {
+    uint32_t kk[4];
+    int bl[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int si = i0 + 4 * u + sub;
+      bl[u] = -1;
+      kk[u] = 0u;
+      if (si < P) {
+        const int b = slist[si] * kSuperBlock + off;
+        if (b >= c0 && b < L) {
+          bl[u] = b;
+          kk[u] = order_key(srow[b]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool sv = bl[u] >= 0 && kk[u] >= lb;
+      const uint64_t bal = __ballot(sv);
+      const int pos = cnt + popc(bal & lt);
+      if (sv && pos < kCap) {
+        skey[pos] = kk[u];
+        sblk[pos] = bl[u];
+      }
+      cnt += popc(bal);
+    }
+  }
+  wave_lds_sync();
+  return cnt;
+}
+
 __device__ __forceinline__ void write_trivial(int L, int mp, int k, int32_t* out, int lane) {
   if (mp == L) {  // every visible block is kept (covers L == 0)
     for (int j = lane; j < k; j += kWave) out[j] = (j <= L) ? j : -1;
@@ -242,7 +335,8 @@ __device__ __forceinline__ RowPlan row_plan(int L, int k, bool sink) {
 }
 
 __device__ __forceinline__ void select_row(const float* __restrict__ srow, int L, int k, bool sink,
-                                           int32_t* __restrict__ out, uint32_t* skey, int32_t* sblk, int lane) {
+                                           int32_t* __restrict__ out, uint32_t* skey, int32_t* sblk, int lane,
+                                           const float* __restrict__ smrow = nullptr, int32_t* slist = nullptr) {
   const RowPlan rp = row_plan(L, k, sink);
   const int mp = rp.m - 1;
   if (mp == L || mp == 0) {  // every visible block, or the local block alone
@@ -251,7 +345,9 @@ __device__ __forceinline__ void select_row(const float* __restrict__ srow, int L
   }
   if (rp.want > 0) {
     const int off = rp.fs ? 1 : 0;
-    const int n = compact_candidates(srow, rp.c0, L - rp.c0, rp.want, skey, sblk, lane);
+    int n = -1;
+    if (smrow != nullptr) n = compact_candidates_sb(srow, smrow, rp.c0, L, rp.want, skey, sblk, slist, lane);
+    if (n < 0) n = compact_candidates(srow, rp.c0, L - rp.c0, rp.want, skey, sblk, lane);
     auto emit = [&](int pos, uint32_t, int32_t blk) { out[off + pos] = blk; };
     if (n <= kCap) select_best(LdsList{skey, sblk}, n, rp.want, lane, emit);
     else select_best(RowList{srow + rp.c0, rp.c0}, L - rp.c0, rp.want, lane, emit);
@@ -263,12 +359,17 @@ __device__ __forceinline__ void select_row(const float* __restrict__ srow, int L
   for (int j = mp + 1 + lane; j < k; j += kWave) out[j] = -1;
 }
 
+// SB: the chunk has rows long enough for the superblock path (SM given);
+// without it the kernel carries neither that path nor its LDS list.
+template <bool SB>
 __global__ __launch_bounds__(256) void topk_prefill_kernel(const float* __restrict__ S, int s_stride,
+                                                           const float* __restrict__ SM, int sm_stride,
                                                            int32_t* __restrict__ bidx, long bidx_rows,
                                                            int bidx_t_off, int G, int B, int k, bool sink,
                                                            int t0, int tc, long n_rows) {
   __shared__ uint32_t skey[kTopkWaves][kCap];
   __shared__ int32_t sblk[kTopkWaves][kCap];
+  __shared__ int32_t slist[SB ? kTopkWaves : 1][SB ? kCap : 1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * kTopkWaves + wave;
   if (row >= n_rows) return;
@@ -279,7 +380,11 @@ __global__ __launch_bounds__(256) void topk_prefill_kernel(const float* __restri
   const int g = (int)(r % G);
   const float* srow = S + (size_t)row * s_stride;
   int32_t* out = bidx + ((size_t)(s * bidx_rows + (t - bidx_t_off)) * G + g) * (size_t)k;
-  select_row(srow, t / B, k, sink, out, skey[wave], sblk[wave], lane);
+  if constexpr (SB) {
+    select_row(srow, t / B, k, sink, out, skey[wave], sblk[wave], lane, SM + (size_t)row * sm_stride, slist[wave]);
+  } else {
+    select_row(srow, t / B, k, sink, out, skey[wave], sblk[wave], lane);
+  }
 }
 
 // Decode rows are few (batch x G) and long (up to Lmax / B candidates): one
@@ -356,12 +461,18 @@ __global__ __launch_bounds__(1024) void topk_decode_kernel(const float* __restri
 
 }  // namespace
 
-hipError_t launch_topk_prefill(const float* S, int s_stride, int32_t* bidx, long bidx_rows,
+hipError_t launch_topk_prefill(const float* S, int s_stride, const float* SM, int sm_stride,
+                               int32_t* bidx, long bidx_rows,
                                int bidx_t_off, int batch, int G, int B, int k, bool sink, int t0, int tc,
                                hipStream_t st) {
   const long n_rows = (long)batch * tc * G;
   const long grid = (n_rows + kTopkWaves - 1) / kTopkWaves;
-  topk_prefill_kernel<<<dim3((unsigned)grid), 256, 0, st>>>(S, s_stride, bidx, bidx_rows, bidx_t_off,
+  if (SM != nullptr)
+    topk_prefill_kernel<true><<<dim3((unsigned)grid), 256, 0, st>>>(S, s_stride, SM, sm_stride, bidx, bidx_rows,
+                                                                    bidx_t_off, G, B, k, sink, t0, tc, n_rows);
+  else
+    topk_prefill_kernel<false><<<dim3((unsigned)grid), 256, 0, st>>>(S, s_stride, SM, sm_stride, bidx, bidx_rows,
+                                                                     bidx_t_off,
                                                             G, B, k, sink, t0, tc, n_rows);
   return hipGetLastError();
 }
