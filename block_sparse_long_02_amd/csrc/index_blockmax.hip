@@ -101,7 +101,10 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
   MSA_IDX_LSTORE(0);
   __syncthreads();
 
-  // block maxima of 4 consecutive blocks are buffered and written as float4
+  // Block maxima are written in groups of 8 consecutive blocks, 32 bytes
+  // per row: both halves of the wave hold every row maximum (after the
+  // cross-half shuffle), so half h keeps blocks 4h..4h+3 of the group and one
+  // store instruction covers 32 rows x 32 contiguous bytes.
   f32x4 sb[NT];
   float smx[NT];   // running superblock maximum over the row's candidate blocks
   f32x4 smb[NT];   // maxima of 4 consecutive superblocks, written as float4
@@ -137,14 +140,17 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
 #pragma unroll
         for (int i = 0; i < 16; i += 2) mx[nt] = fmaxf(mx[nt], fmaxf(acc[nt][i], acc[nt][i + 1]));
     }
-    const int slot = b & 3;
+    const int slot8 = b & 7, slot = b & 3;
+    const bool mine = (slot8 >> 2) == half;  // this half keeps block b
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float v = fmaxf(mx[nt], __shfl_xor(mx[nt], 32, kWave));
-      if (slot == 0) sb[nt][0] = v;
-      else if (slot == 1) sb[nt][1] = v;
-      else if (slot == 2) sb[nt][2] = v;
-      else sb[nt][3] = v;
+      if (mine) {
+        if (slot == 0) sb[nt][0] = v;
+        else if (slot == 1) sb[nt][1] = v;
+        else if (slot == 2) sb[nt][2] = v;
+        else sb[nt][3] = v;
+      }
       if (WITH_SM && b < row_L[nt]) smx[nt] = fmaxf(smx[nt], v);
     }
     if (WITH_SM && (b % kSuperBlock == kSuperBlock - 1 || b == nblk - 1)) {  // uniform
@@ -167,11 +173,15 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
         }
       }
     }
-    if ((slot == 3 || b == nblk - 1) && half == 0) {
+    // At the group's end both halves store; at the row range's end only the
+    // halves that hold blocks of the last group (half 1 holds none when the
+    // group ends before its fifth block), so every store stays below
+    // round_up(nblk, 4) <= s_stride.
+    if (slot8 == 7 || (b == nblk - 1 && (half == 0 || slot8 >= 4))) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         if (row_ok[nt]) {
-          float* dst = S + ((size_t)s * rows_chunk + (size_t)row_idx[nt]) * s_stride + (b & ~3);
+          float* dst = S + ((size_t)s * rows_chunk + (size_t)row_idx[nt]) * s_stride + (b & ~7) + 4 * half;
           *reinterpret_cast<f32x4*>(dst) = sb[nt];
         }
       }

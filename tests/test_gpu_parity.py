@@ -100,6 +100,63 @@ def test_index_topk_all_ties_fallback():
             assert got[0, t, g].tolist() == exp, (t, g)
 
 
+
+def _index_topk_flags(inp, B, k, flags):
+    b, T, G, di = inp.idx_q.shape
+    dims = bd.make_dims(b, T, G, G, index_dim=di, block_size=B, topk=k, flags=flags)
+    bidx = torch.full((b, T, G, k), -7, dtype=torch.int32, device="cuda")
+    bd.msa_index_topk(dims, inp.idx_q.cuda(), inp.idx_k.cuda(), bidx)
+    torch.cuda.synchronize()
+    return bidx.cpu()
+
+
+def _exact_rows(inp, got, B, k, rows, sink):
+    iq = inp.idx_q.to(torch.float64).numpy()
+    ik = inp.idx_k.to(torch.float64).numpy()
+    G = iq.shape[2]
+    for t in rows:
+        for g in range(G):
+            S = orc.block_max(orc.index_scores(iq[0, t, g], ik[0], t), t, B)
+            exp = orc.select_blocks(S, t, B, k, sink=sink)
+            assert got[0, t, g].tolist() == exp.tolist(), (t, g, sink)
+
+
+@pytest.mark.parametrize("sink", [False, True])
+def test_index_topk_long_rows_integer_exact(sink):
+    # Rows of more than 1024 candidate blocks (here t >= 32800 at B = 32) take
+    # the superblock-pruned top-k; integer index inputs make the block maxima
+    # exact and tie often, so the tie rule is checked on that path too.
+    T, G, di, B, k = 36000, 2, 64, 32, 16
+    say(f"[index_topk long rows integer] T={T} B={B} k={k} sink={sink}")
+    inp = inputs.make_prefill(T, G, G, 8, di, seed=901, idx_mode="integer")
+    got = _index_topk_flags(inp, B, k, bd.MSA_FORCE_SINK if sink else 0)
+    if not sink:
+        check_selection_invariants(got, T, G, B, k)
+    rng = np.random.default_rng(901)
+    rows = sorted(set(int(t) for t in rng.integers(32800, T, 60)) | {T - 1, 32799, 32800, 5000, 20000})
+    _exact_rows(inp, got, B, k, rows, sink)
+
+
+def test_index_topk_long_rows_dominant_first_block():
+    # Every row scores key 0 far above all others, so block 0 heads superblock
+    # 0.  With the sink rule block 0 is forced and is not a candidate: the
+    # superblock bound must leave superblock 0 out (it would otherwise lift the
+    # bound past the threshold); without it block 0 is an ordinary winner.
+    T, G, di, B, k = 36000, 2, 64, 32, 16
+    say(f"[index_topk long rows, dominant block 0] T={T} B={B} k={k}")
+    base = inputs.make_prefill(T, G, G, 8, di, seed=902, idx_mode="integer")
+    u = base.idx_q[0, 0, 0].clone()
+    idx_q = u.expand_as(base.idx_q).contiguous()
+    idx_k = base.idx_k.clone()
+    idx_k[0, 0] = (3.0 * torch.sign(u.float())).to(idx_k.dtype)
+    inp = inputs.PrefillInputs(base.q, base.k, base.v, idx_q, idx_k)
+    rng = np.random.default_rng(902)
+    rows = sorted(set(int(t) for t in rng.integers(32800, T, 40)) | {T - 1, 33000})
+    for sink in (True, False):
+        got = _index_topk_flags(inp, B, k, bd.MSA_FORCE_SINK if sink else 0)
+        _exact_rows(inp, got, B, k, rows, sink)
+
+
 PREFILL_CASES = [
     # T, Hq, G, di, B, k, chunk, batch
     (2048, 16, 4, 64, 128, 4, 0, 1),     # tiny prefill workload
