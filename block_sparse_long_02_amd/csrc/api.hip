@@ -98,9 +98,9 @@ int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
   p->with_scores = index_only || !(d->flags & (MSA_DENSE | MSA_GIVEN_INDICES));
   p->with_main = !index_only && !(d->flags & MSA_DENSE);
   const int Lmax = (T - 1) / B;
-  // rows of the block-score table start 32-byte aligned (the index kernel
-  // stores 8 block maxima per row at a time)
-  p->s_stride_max = (int)round_up((size_t)(Lmax > 1 ? Lmax : 1), 8);
+  // rows of the block-score table start 64-byte aligned (the index kernel
+  // stores 16 block maxima per row at a time)
+  p->s_stride_max = (int)round_up((size_t)(Lmax > 1 ? Lmax : 1), 16);
   p->sm_stride_max = sm_stride_for(Lmax);
   if (!p->with_scores && !p->with_main) {  // dense prefill needs no workspace
     p->Tc = T;
@@ -423,7 +423,7 @@ hipError_t run_index_chunk(const msa_dims* d, const PrefillPlan& p, const void* 
                            int t_off, hipStream_t st) {
   const int B = d->block_size;
   const int Lc = (t0 + tc - 1) / B;
-  const int s_stride = (int)round_up((size_t)(Lc > 1 ? Lc : 1), 8);
+  const int s_stride = (int)round_up((size_t)(Lc > 1 ? Lc : 1), 16);
   const int sm_stride = sm_stride_for(Lc);
   float* S = at<float>(ws, p.off_S);
   float* SM = Lc > msa::kSbMinCandidates ? at<float>(ws, p.off_SM) : nullptr;

@@ -101,18 +101,17 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
   MSA_IDX_LSTORE(0);
   __syncthreads();
 
-  // Block maxima are written in groups of 8 consecutive blocks, 32 bytes
+  // Block maxima are written in groups of 16 consecutive blocks, 64 bytes
   // per row: both halves of the wave hold every row maximum (after the
-  // cross-half shuffle), so half h keeps blocks 4h..4h+3 of the group and one
-  // store instruction covers 32 rows x 32 contiguous bytes.
-  f32x4 sb[NT];
+  // cross-half shuffle), so half h keeps blocks 8h..8h+7 of the group (two
+  // float4) and each row receives 64 contiguous bytes per group.
+  f32x4 sb[NT], sb2[NT];
   float smx[NT];   // running superblock maximum over the row's candidate blocks
-  f32x4 smb[NT];   // maxima of 4 consecutive superblocks, written as float4
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     sb[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sb2[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     smx[nt] = -INFINITY;
-    smb[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   for (int b = 0; b < nblk; ++b) {
@@ -140,49 +139,43 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
 #pragma unroll
         for (int i = 0; i < 16; i += 2) mx[nt] = fmaxf(mx[nt], fmaxf(acc[nt][i], acc[nt][i + 1]));
     }
-    const int slot8 = b & 7, slot = b & 3;
-    const bool mine = (slot8 >> 2) == half;  // this half keeps block b
+    const int slot16 = b & 15, slot = b & 3;
+    const bool mine = (slot16 >> 3) == half;  // this half keeps block b
+    const bool second = (slot16 & 4) != 0;    // ... in its second float4
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float v = fmaxf(mx[nt], __shfl_xor(mx[nt], 32, kWave));
       if (mine) {
-        if (slot == 0) sb[nt][0] = v;
-        else if (slot == 1) sb[nt][1] = v;
-        else if (slot == 2) sb[nt][2] = v;
-        else sb[nt][3] = v;
+        f32x4& dv = second ? sb2[nt] : sb[nt];
+        if (slot == 0) dv[0] = v;
+        else if (slot == 1) dv[1] = v;
+        else if (slot == 2) dv[2] = v;
+        else dv[3] = v;
       }
       if (WITH_SM && b < row_L[nt]) smx[nt] = fmaxf(smx[nt], v);
     }
+    // a superblock is one 16-block store group: its maximum leaves with it
     if (WITH_SM && (b % kSuperBlock == kSuperBlock - 1 || b == nblk - 1)) {  // uniform
-      const int sbi = b / kSuperBlock, sslot = sbi & 3;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        if (sslot == 0) smb[nt][0] = smx[nt];
-        else if (sslot == 1) smb[nt][1] = smx[nt];
-        else if (sslot == 2) smb[nt][2] = smx[nt];
-        else smb[nt][3] = smx[nt];
+        if (row_ok[nt] && half == 0)
+          SM[((size_t)s * rows_chunk + (size_t)row_idx[nt]) * sm_stride + b / kSuperBlock] = smx[nt];
         smx[nt] = -INFINITY;
       }
-      if ((sslot == 3 || b == nblk - 1) && half == 0) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          if (row_ok[nt]) {
-            float* dst = SM + ((size_t)s * rows_chunk + (size_t)row_idx[nt]) * sm_stride + (sbi & ~3);
-            *reinterpret_cast<f32x4*>(dst) = smb[nt];
-          }
-        }
-      }
     }
-    // At the group's end both halves store; at the row range's end only the
-    // halves that hold blocks of the last group (half 1 holds none when the
-    // group ends before its fifth block), so every store stays below
-    // round_up(nblk, 4) <= s_stride.
-    if (slot8 == 7 || (b == nblk - 1 && (half == 0 || slot8 >= 4))) {
+    // At the group's end every float4 is stored; at the row range's end only
+    // the float4s holding blocks of the last group (those starting at or
+    // before block b), so every store stays below round_up(nblk, 4) <= s_stride.
+    if (slot16 == 15 || b == nblk - 1) {  // uniform
+      const int first = 8 * half;         // group offset of this half's first float4
+      const bool w1 = slot16 == 15 || first <= slot16;
+      const bool w2 = slot16 == 15 || first + 4 <= slot16;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         if (row_ok[nt]) {
-          float* dst = S + ((size_t)s * rows_chunk + (size_t)row_idx[nt]) * s_stride + (b & ~7) + 4 * half;
-          *reinterpret_cast<f32x4*>(dst) = sb[nt];
+          float* dst = S + ((size_t)s * rows_chunk + (size_t)row_idx[nt]) * s_stride + (b & ~15) + first;
+          if (w1) *reinterpret_cast<f32x4*>(dst) = sb[nt];
+          if (w2) *reinterpret_cast<f32x4*>(dst + 4) = sb2[nt];
         }
       }
     }
