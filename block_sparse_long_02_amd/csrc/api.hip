@@ -357,8 +357,8 @@ int make_bwd_plan(const msa_dims* d, BwdPlan* p) {
 // ---------------------------------------------------------------------------
 // Decode plan
 // ---------------------------------------------------------------------------
-#ifndef MSA_DEC_SPLIT_BLOCKS
-#define MSA_DEC_SPLIT_BLOCKS 1
+#ifndef MSA_DEC_ITEM_KEYS
+#define MSA_DEC_ITEM_KEYS 64
 #endif
 
 struct DecodePlan {
@@ -379,9 +379,9 @@ int make_decode_plan(const msa_dims* d, DecodePlan* p) {
     p->bps = 2048 / B;  // 2048 keys per work item
     p->nsplit = (p->nbmax + p->bps - 1) / p->bps;
   } else {
-    // 128-key blocks are split into two 64-key work items: one key tile per
-    // wave, so no wave waits for two block loads in turn
-    p->sub = (B == 128 && MSA_DEC_SPLIT_BLOCKS) ? 2 : 1;
+    // blocks are split into work items of MSA_DEC_ITEM_KEYS keys: one key
+    // tile per wave, so no wave waits for two loads in turn
+    p->sub = B > MSA_DEC_ITEM_KEYS ? B / MSA_DEC_ITEM_KEYS : 1;
     const int sel = (d->flags & MSA_GIVEN_INDICES) ? d->topk : (d->topk < p->nbmax ? d->topk : p->nbmax);
     p->nsplit = sel * p->sub;
   }

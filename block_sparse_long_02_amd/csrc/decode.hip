@@ -387,8 +387,10 @@ hipError_t launch_decode_main(const DecodeMainArgs& a, hipStream_t st) {
   prof_mark(st, MSA_STAGE_DECODE_ATTN);
 #define MSA_DEC_ATTN(BS_)                                                                          \
   decode_attn_kernel<BS_><<<grid, kDecAttnWaves * 64, 0, st>>>(a, ipw, nparts)
-  if (a.B == 128) MSA_DEC_ATTN(128);
-  else if (a.B == 64) MSA_DEC_ATTN(64);
+  // the kernel's tile shape follows the keys of one work item
+  const int span = a.dense ? a.B : a.B / a.sub;
+  if (span == 128) MSA_DEC_ATTN(128);
+  else if (span == 64) MSA_DEC_ATTN(64);
   else MSA_DEC_ATTN(32);
 #undef MSA_DEC_ATTN
   hipError_t err = hipGetLastError();
