@@ -137,6 +137,24 @@ def test_index_topk_long_rows_integer_exact(sink):
     _exact_rows(inp, got, B, k, rows, sink)
 
 
+
+def test_index_topk_long_rows_batch_and_chunks():
+    # Batch 2 in three query chunks: the first chunk's rows have at most 561
+    # candidate blocks (no superblock maxima), the later ones up to 1124 (the
+    # superblock path); integer inputs, exact against the oracle in both
+    # sequences and every chunk.
+    T, G, di, B, k, chunk = 36000, 2, 64, 32, 16, 17984
+    say(f"[index_topk long rows batch 2, chunks] T={T} B={B} k={k} chunk={chunk}")
+    inp = inputs.make_prefill(T, G, G, 8, di, batch=2, seed=903, idx_mode="integer")
+    got = gpu_index_topk(inp, B, k, query_chunk=chunk)
+    check_selection_invariants(got, T, G, B, k)
+    rng = np.random.default_rng(903)
+    rows = sorted(set([(s, int(t)) for s in range(2) for t in rng.integers(0, T, 25)]
+                      + [(s, t) for s in range(2) for t in (17983, 17984, 32900, 35967, 35968, T - 1)]))
+    ores = oracle_selection(inp, B, k, rows)
+    compare_selection(got, ores, B, k, exact=True)
+
+
 def test_index_topk_long_rows_dominant_first_block():
     # Every row scores key 0 far above all others, so block 0 heads superblock
     # 0.  With the sink rule block 0 is forced and is not a candidate: the
