@@ -87,13 +87,13 @@ constexpr int kRegKeys = 16;
 // list order, pos = 0 .. want-1.  Wave-uniform control flow.  Lists of up to
 // 64 * kRegKeys entries are read once into registers; the 32-step threshold
 // search then needs only ballots.
-template <class List, class Emit>
+template <int NR = kRegKeys, class List, class Emit>
 __device__ __forceinline__ void select_best(const List& lst, int n, int want, int lane, Emit emit) {
   const uint64_t lt = lanemask_lt();
-  if (n <= kWave * kRegKeys) {
-    uint32_t key[kRegKeys];
+  if (n <= kWave * NR) {
+    uint32_t key[NR];
 #pragma unroll
-    for (int i = 0; i < kRegKeys; ++i) {
+    for (int i = 0; i < NR; ++i) {
       const int j = i * kWave + lane;
       key[i] = j < n ? lst.k(j) : 0u;
     }
@@ -106,19 +106,19 @@ __device__ __forceinline__ void select_best(const List& lst, int n, int want, in
         const uint32_t c = tau | (1u << bit);
         int cnt = 0;
 #pragma unroll
-        for (int i = 0; i < kRegKeys; ++i)
+        for (int i = 0; i < NR; ++i)
           if (i < nch) cnt += popc(__ballot(key[i] >= c));
         if (cnt >= want) tau = c;
       }
     }
     int cgt = 0;
 #pragma unroll
-    for (int i = 0; i < kRegKeys; ++i)
+    for (int i = 0; i < NR; ++i)
       if (i < nch) cgt += popc(__ballot(key[i] > tau));
     const int need = want - cgt;  // >= 1 by construction of tau
     int base = 0, eq_seen = 0;
 #pragma unroll
-    for (int i = 0; i < kRegKeys; ++i) {
+    for (int i = 0; i < NR; ++i) {
       if (i < nch) {  // wave-uniform
         const int j = i * kWave + lane;
         const bool in = j < n;
@@ -173,23 +173,24 @@ __device__ __forceinline__ void select_best(const List& lst, int n, int want, in
 // skey/sblk in block order; returns the number of survivors (entries beyond
 // kCap are counted but not stored).  Rows of up to 64 * kRegKeys candidates
 // are read once, all loads in flight together, and compacted from registers.
+template <int NR = kRegKeys>
 __device__ __forceinline__ int compact_candidates(const float* __restrict__ srow, int b0, int n, int want, uint32_t* skey,
                                   int32_t* sblk, int lane) {
   const uint64_t lt = lanemask_lt();
   int cnt = 0;
-  if (n <= kWave * kRegKeys) {
-    uint32_t key[kRegKeys];
+  if (n <= kWave * NR) {
+    uint32_t key[NR];
 #pragma unroll
-    for (int i = 0; i < kRegKeys; ++i) {
+    for (int i = 0; i < NR; ++i) {
       const int j = i * kWave + lane;
       key[i] = j < n ? order_key(srow[b0 + j]) : 0u;
     }
     uint32_t lmax = 0;
 #pragma unroll
-    for (int i = 0; i < kRegKeys; ++i) lmax = max(lmax, key[i]);
+    for (int i = 0; i < NR; ++i) lmax = max(lmax, key[i]);
     const uint32_t lb = (want <= kWave) ? kth_largest_lanes(lmax, want) : 0u;
 #pragma unroll
-    for (int i = 0; i < kRegKeys; ++i) {
+    for (int i = 0; i < NR; ++i) {
       if (i * kWave < n) {  // wave-uniform
         const int j = i * kWave + lane;
         const bool sv = j < n && key[i] >= lb;
@@ -402,7 +403,6 @@ __global__ __launch_bounds__(1024) void topk_decode_kernel(const float* __restri
   __shared__ int32_t sblk[kDecWaves][kCap];
   __shared__ uint32_t mkey[kDecWaves * kDecMaxKeep];
   __shared__ int32_t mblk[kDecWaves * kDecMaxKeep];
-  __shared__ int mcnt[kDecWaves];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const long row = blockIdx.x;
@@ -419,38 +419,38 @@ __global__ __launch_bounds__(1024) void topk_decode_kernel(const float* __restri
     if (wave == 0) select_row(srow, L, k, sink, out, skey[0], sblk[0], lane);
     return;
   }
-  // level 1: per-wave partitions of the candidates c0..L-1
+  // level 1: per-wave partitions of the candidates c0..L-1.  Wave w keeps
+  // min(want, its candidates) and writes them, in block order, straight into
+  // the combined list at the sum of the earlier waves' counts (known without
+  // communication), so the combined list is in block order too.
   const int per = (ncand + kDecWaves - 1) / kDecWaves;
+  auto kept_of = [&](int w) { return min(rp.want, max(0, min(per, L - (rp.c0 + w * per)))); };
+  int off_w = 0, total = 0;
+  for (int w = 0; w < kDecWaves; ++w) {  // uniform scalar arithmetic
+    if (w == wave) off_w = total;
+    total += kept_of(w);
+  }
   const int b0 = rp.c0 + wave * per;
   const int nw = max(0, min(per, L - b0));
-  int kept = 0;
   if (nw > 0) {
     const int want = min(rp.want, nw);
-    const int n = compact_candidates(srow, b0, nw, want, skey[wave], sblk[wave], lane);
-    uint32_t* ok = mkey + wave * kDecMaxKeep;
-    int32_t* ob = mblk + wave * kDecMaxKeep;
-    auto emit = [&](int pos, uint32_t key, int32_t blk) { ok[pos] = key; ob[pos] = blk; };
-    if (n <= kCap) select_best(LdsList{skey[wave], sblk[wave]}, n, want, lane, emit);
+    const int n = nw <= kWave * 8 ? compact_candidates<8>(srow, b0, nw, want, skey[wave], sblk[wave], lane)
+                                  : compact_candidates(srow, b0, nw, want, skey[wave], sblk[wave], lane);
+    auto emit = [&](int pos, uint32_t key, int32_t blk) {
+      mkey[off_w + pos] = key;
+      mblk[off_w + pos] = blk;
+    };
+    if (n <= kWave) select_best<1>(LdsList{skey[wave], sblk[wave]}, n, want, lane, emit);
+    else if (n <= kCap) select_best(LdsList{skey[wave], sblk[wave]}, n, want, lane, emit);
     else select_best(RowList{srow + b0, b0}, nw, want, lane, emit);
-    kept = want;
   }
-  if (lane == 0) mcnt[wave] = kept;
   __syncthreads();
-  // level 2: wave 0 compacts the per-wave lists (block order) and selects
+  // level 2: wave 0 selects among the combined list
   if (wave == 0) {
-    int n = 0;
-    for (int w = 0; w < kDecWaves; ++w) {
-      const int c = mcnt[w];
-      for (int i = lane; i < c; i += kWave) {
-        skey[0][n + i] = mkey[w * kDecMaxKeep + i];
-        sblk[0][n + i] = mblk[w * kDecMaxKeep + i];
-      }
-      n += c;
-    }
-    wave_lds_sync();
     const int off = rp.fs ? 1 : 0;
     auto emit = [&](int pos, uint32_t, int32_t blk) { out[off + pos] = blk; };
-    select_best(LdsList{skey[0], sblk[0]}, n, rp.want, lane, emit);
+    if (total <= kWave * 4) select_best<4>(LdsList{mkey, mblk}, total, rp.want, lane, emit);
+    else select_best(LdsList{mkey, mblk}, total, rp.want, lane, emit);
     if (lane == 0) {
       if (rp.fs) out[0] = 0;
       out[mp] = L;
