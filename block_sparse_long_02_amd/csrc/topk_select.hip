@@ -350,7 +350,8 @@ __device__ __forceinline__ void select_row(const float* __restrict__ srow, int L
     if (smrow != nullptr) n = compact_candidates_sb(srow, smrow, rp.c0, L, rp.want, skey, sblk, slist, lane);
     if (n < 0) n = compact_candidates(srow, rp.c0, L - rp.c0, rp.want, skey, sblk, lane);
     auto emit = [&](int pos, uint32_t, int32_t blk) { out[off + pos] = blk; };
-    if (n <= kCap) select_best(LdsList{skey, sblk}, n, rp.want, lane, emit);
+    if (n <= kWave) select_best<1>(LdsList{skey, sblk}, n, rp.want, lane, emit);
+    else if (n <= kCap) select_best(LdsList{skey, sblk}, n, rp.want, lane, emit);
     else select_best(RowList{srow + rp.c0, rp.c0}, L - rp.c0, rp.want, lane, emit);
   }
   if (lane == 0) {
