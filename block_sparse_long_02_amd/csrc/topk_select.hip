@@ -348,7 +348,12 @@ __device__ __forceinline__ void select_row(const float* __restrict__ srow, int L
     const int off = rp.fs ? 1 : 0;
     int n = -1;
     if (smrow != nullptr) n = compact_candidates_sb(srow, smrow, rp.c0, L, rp.want, skey, sblk, slist, lane);
-    if (n < 0) n = compact_candidates(srow, rp.c0, L - rp.c0, rp.want, skey, sblk, lane);
+    if (n < 0) {
+      const int nc = L - rp.c0;
+      n = nc <= kWave * 4 ? compact_candidates<4>(srow, rp.c0, nc, rp.want, skey, sblk, lane)
+        : nc <= kWave * 8 ? compact_candidates<8>(srow, rp.c0, nc, rp.want, skey, sblk, lane)
+                          : compact_candidates(srow, rp.c0, nc, rp.want, skey, sblk, lane);
+    }
     auto emit = [&](int pos, uint32_t, int32_t blk) { out[off + pos] = blk; };
     if (n <= kWave) select_best<1>(LdsList{skey, sblk}, n, rp.want, lane, emit);
     else if (n <= kCap) select_best(LdsList{skey, sblk}, n, rp.want, lane, emit);
