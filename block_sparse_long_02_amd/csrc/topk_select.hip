@@ -350,9 +350,11 @@ __device__ __forceinline__ void select_row(const float* __restrict__ srow, int L
     if (smrow != nullptr) n = compact_candidates_sb(srow, smrow, rp.c0, L, rp.want, skey, sblk, slist, lane);
     if (n < 0) {
       const int nc = L - rp.c0;
-      n = nc <= kWave * 4 ? compact_candidates<4>(srow, rp.c0, nc, rp.want, skey, sblk, lane)
-        : nc <= kWave * 8 ? compact_candidates<8>(srow, rp.c0, nc, rp.want, skey, sblk, lane)
-                          : compact_candidates(srow, rp.c0, nc, rp.want, skey, sblk, lane);
+      n = nc <= kWave * 2   ? compact_candidates<2>(srow, rp.c0, nc, rp.want, skey, sblk, lane)
+        : nc <= kWave * 4   ? compact_candidates<4>(srow, rp.c0, nc, rp.want, skey, sblk, lane)
+        : nc <= kWave * 8   ? compact_candidates<8>(srow, rp.c0, nc, rp.want, skey, sblk, lane)
+        : nc <= kWave * 12  ? compact_candidates<12>(srow, rp.c0, nc, rp.want, skey, sblk, lane)
+                            : compact_candidates(srow, rp.c0, nc, rp.want, skey, sblk, lane);
     }
     auto emit = [&](int pos, uint32_t, int32_t blk) { out[off + pos] = blk; };
     if (n <= kWave) select_best<1>(LdsList{skey, sblk}, n, rp.want, lane, emit);
