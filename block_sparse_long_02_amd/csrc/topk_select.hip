@@ -234,15 +234,15 @@ __device__ __forceinline__ int compact_candidates(const float* __restrict__ srow
 // for this path.
 static_assert(kSuperBlock == 16, "the superblock gather maps 4 superblocks of 16 blocks onto a wave");
 static_assert(kSbMinCandidates == kWave * kRegKeys, "superblock rows start where the register path ends");
+template <int kSbRegs>  // superblock maxima per lane held in registers (rows of up to 64 * kSbRegs superblocks)
 __device__ __forceinline__ int compact_candidates_sb(const float* __restrict__ srow, const float* __restrict__ sm,
                                                      int c0, int L, int want, uint32_t* skey, int32_t* sblk,
                                                      int32_t* slist, int lane) {
   const int nsb = (L + kSuperBlock - 1) / kSuperBlock;
   const int s_lo = c0 > 0 ? 1 : 0;
   // rows that compact_candidates reads once into registers are cheaper there
-  if (L - c0 <= kSbMinCandidates || nsb - s_lo <= want || nsb > kCap) return -1;  // wave-uniform
+  if (L - c0 <= kSbMinCandidates || nsb - s_lo <= want || nsb > kWave * kSbRegs) return -1;  // wave-uniform
   const uint64_t lt = lanemask_lt();
-  constexpr int kSbRegs = kCap / kWave;
   uint32_t key[kSbRegs];
 #pragma unroll
   for (int i = 0; i < kSbRegs; ++i) {
@@ -347,7 +347,12 @@ __device__ __forceinline__ void select_row(const float* __restrict__ srow, int L
   if (rp.want > 0) {
     const int off = rp.fs ? 1 : 0;
     int n = -1;
-    if (smrow != nullptr) n = compact_candidates_sb(srow, smrow, rp.c0, L, rp.want, skey, sblk, slist, lane);
+    if (smrow != nullptr) {  // register arrays sized to the row's superblocks
+      const int nsb = (L + kSuperBlock - 1) / kSuperBlock;
+      n = nsb <= kWave * 2 ? compact_candidates_sb<2>(srow, smrow, rp.c0, L, rp.want, skey, sblk, slist, lane)
+        : nsb <= kWave * 4 ? compact_candidates_sb<4>(srow, smrow, rp.c0, L, rp.want, skey, sblk, slist, lane)
+                           : compact_candidates_sb<kCap / kWave>(srow, smrow, rp.c0, L, rp.want, skey, sblk, slist, lane);
+    }
     if (n < 0) {
       const int nc = L - rp.c0;
       n = nc <= kWave * 2   ? compact_candidates<2>(srow, rp.c0, nc, rp.want, skey, sblk, lane)
