@@ -114,21 +114,6 @@ struct BwdLds {
   static_assert(bytes <= 160 * 1024, "LDS of one workgroup");
 };
 
-// Transposing LDS read of gfx950 (ds_read_b64_tr_b16).  In each group of 16
-// lanes, lane 4a + c receives element c of the 8-byte words addressed by
-// lanes a, a + 4, a + 8 and a + 12 of the group, in that order.  tr_lane_off
-// places those words so that lane l gets 4 consecutive rows of a row-major
-// bf16 tile (row stride `stride`) at column l % 32, starting 4 (l / 32) rows
-// down: the k-slot layout of an MFMA operand whose k-slots run over rows.
-__device__ __forceinline__ int tr_lane_off(int lane, int stride) {
-  return (4 * (lane >> 5) + ((lane >> 2) & 3)) * stride + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-}
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t* p) {
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
-  return __builtin_bit_cast(u32x2, v);
-}
-
 template <int BS>
 __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdArgs a) {
   using Lds = BwdLds<BS>;

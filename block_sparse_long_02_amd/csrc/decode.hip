@@ -81,11 +81,12 @@ __global__ __launch_bounds__(256) void decode_index_kernel(const bf16_t* __restr
 // ---------------------------------------------------------------------------
 // Decode attention.  A workgroup of kDecAttnWaves waves owns (s, g, part x)
 // and work items part*W*ipw .. ; wave w takes items x*W*ipw + w + W*i,
-// i < ipw.  A work item is one selected block (sparse / given) or a run of
-// blocks_per_split consecutive blocks (dense).  Each wave attends its keys
-// in sub-tiles of up to 64 with online softmax: S^T = K.Q^T on MFMA with the
-// K rows loaded straight into the A operand, V transposed through the
-// wave's own LDS area for the P.V product.  The waves then merge in LDS in
+// i < ipw.  A work item is a part of a selected block (sparse / given; 64
+// keys) or a run of blocks_per_split consecutive blocks (dense).  Each wave
+// attends its keys in sub-tiles of up to 64 with online softmax: S^T =
+// K.Q^T on MFMA with the K rows loaded straight into the A operand; the V
+// rows go unchanged into the wave's own LDS area and come back as the P.V
+// operand through the transposing LDS read.  The waves then merge in LDS in
 // fixed order; with one part per (s, g) the merge writes the output, else a
 // normalised partial that decode_combine_kernel merges.
 // ---------------------------------------------------------------------------
@@ -100,8 +101,8 @@ constexpr long kDecFillRows = MSA_DEC_FILL_ROWS;
 template <int BS>
 struct DecTile {
   static constexpr int NK = BS < 64 ? BS : 64;   // keys per sub-tile
-  static constexpr int VROW = NK + 4;
-  static constexpr int VT_BYTES = D * VROW * 2;  // per wave
+  static constexpr int VR = D + 8;               // row stride (bf16) of the staged key-major V tile
+  static constexpr int VT_BYTES = NK * VR * 2;   // per wave
   static constexpr int CMB_BYTES = (64 * 64 + 2 * 64) * 4;
   static constexpr int AREA = VT_BYTES > CMB_BYTES ? VT_BYTES : CMB_BYTES;
 };
@@ -115,18 +116,19 @@ __device__ __forceinline__ void dec_wave_sync() {
 template <int BS>
 __global__ __launch_bounds__(kDecAttnWaves * 64) void decode_attn_kernel(DecodeMainArgs a, int ipw, int nparts) {
   using Tl = DecTile<BS>;
-  constexpr int NK = Tl::NK, VROW = Tl::VROW, KTL = NK / 32;
+  constexpr int NK = Tl::NK, KTL = NK / 32;
   __shared__ __attribute__((aligned(16))) unsigned char dec_smem[kDecAttnWaves * Tl::AREA];
 
   const int x = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int R = a.Hq / a.G;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31, half = lane >> 5;
   unsigned char* area = dec_smem + (size_t)wave * Tl::AREA;
-  bf16_t* Vt = reinterpret_cast<bf16_t*>(area);
+  bf16_t* Vt = reinterpret_cast<bf16_t*>(area);  // key-major V sub-tile, row stride Tl::VR
   const int len = min(max(a.lens[s], 1), a.Lmax);
   const int t = len - 1;
   const int L = t / a.B;
   const float c = a.scale_log2;
+  const int tro = tr_lane_off(lane, Tl::VR);  // transposing-read offset of this lane (row-major V)
 
   // B operand: Q^T, column = head (col < R)
   const bool hv = col < R;
@@ -174,32 +176,22 @@ __global__ __launch_bounds__(kDecAttnWaves * 64) void decode_attn_kernel(DecodeM
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) kop[kt][ks] = kv ? load_bf16x8(kr + 16 * ks) : zero_bf16x8();
       }
-      constexpr int UNITS = (NK / 4) * (D / 4) / 64;  // 4x4 units per lane
-      u32x2 vr[UNITS][4];
+      // V rows as they are in memory, 16 bytes per lane per load; the P.V
+      // operands are read back transposed by the gfx950 transposing LDS read
+      constexpr int VP = NK * (D / 8) / 64;  // 16-byte pieces per lane
+      u32x4 vv[VP];
 #pragma unroll
-      for (int u = 0; u < UNITS; ++u) {
-        const int unit = lane + 64 * u;
-        const int k4 = unit >> 5, dq = unit & 31;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = kb + k4 * 4 + j;
-          vr[u][j] = key < k_end ? *reinterpret_cast<const u32x2*>(vseq + (size_t)key * kvstride + dq * 4)
-                                 : u32x2{0u, 0u};
-        }
+      for (int u = 0; u < VP; ++u) {
+        const int p = lane + 64 * u;
+        const int key = kb + (p >> 4);
+        vv[u] = key < k_end ? *reinterpret_cast<const u32x4*>(vseq + (size_t)key * kvstride + (p & 15) * 8)
+                            : u32x4{0u, 0u, 0u, 0u};
       }
       dec_wave_sync();  // previous sub-tile's V reads are done
 #pragma unroll
-      for (int u = 0; u < UNITS; ++u) {
-        const int unit = lane + 64 * u;
-        const int k4 = unit >> 5, dq = unit & 31;
-        const u32x2* xx = vr[u];
-        u32x2 o[4];
-        o[0] = u32x2{(xx[0][0] & 0xffffu) | (xx[1][0] << 16), (xx[2][0] & 0xffffu) | (xx[3][0] << 16)};
-        o[1] = u32x2{(xx[0][0] >> 16) | (xx[1][0] & 0xffff0000u), (xx[2][0] >> 16) | (xx[3][0] & 0xffff0000u)};
-        o[2] = u32x2{(xx[0][1] & 0xffffu) | (xx[1][1] << 16), (xx[2][1] & 0xffffu) | (xx[3][1] << 16)};
-        o[3] = u32x2{(xx[0][1] >> 16) | (xx[1][1] & 0xffff0000u), (xx[2][1] >> 16) | (xx[3][1] & 0xffff0000u)};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(Vt + (dq * 4 + j) * VROW + k4 * 4) = o[j];
+      for (int u = 0; u < VP; ++u) {
+        const int p = lane + 64 * u;
+        *reinterpret_cast<u32x4*>(Vt + (p >> 4) * Tl::VR + (p & 15) * 8) = vv[u];
       }
       dec_wave_sync();
 
@@ -247,11 +239,11 @@ __global__ __launch_bounds__(kDecAttnWaves * 64) void decode_attn_kernel(DecodeM
             p0[e] = (__bf16)sacc[kt][e];
             p1[e] = (__bf16)sacc[kt][8 + e];
           }
-          const bf16_t* vr0 = Vt + (dt * 32 + col) * VROW + kt * 32 + 4 * half;
-          oacc[dt] = mfma32x32x16(join_bf16x4(*reinterpret_cast<const u32x2*>(vr0),
-                                              *reinterpret_cast<const u32x2*>(vr0 + 8)), p0, oacc[dt]);
-          oacc[dt] = mfma32x32x16(join_bf16x4(*reinterpret_cast<const u32x2*>(vr0 + 16),
-                                              *reinterpret_cast<const u32x2*>(vr0 + 24)), p1, oacc[dt]);
+          // keys kt*32 + {0-3, 8-11} + 4 half (p0) and + 16 (p1), at column d
+          const bf16_t* vb = Vt + kt * 32 * Tl::VR + dt * 32 + tro;
+          oacc[dt] = mfma32x32x16(join_bf16x4(lds_read_tr16(vb), lds_read_tr16(vb + 8 * Tl::VR)), p0, oacc[dt]);
+          oacc[dt] = mfma32x32x16(join_bf16x4(lds_read_tr16(vb + 16 * Tl::VR), lds_read_tr16(vb + 24 * Tl::VR)), p1,
+                                  oacc[dt]);
         }
       }
     }
