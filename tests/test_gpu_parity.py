@@ -445,10 +445,15 @@ def test_decode_bitwise_deterministic():
 
 
 @pytest.mark.parametrize("mode", ["integer", "gaussian"])
-def test_decode_many_candidates(mode):
+@pytest.mark.parametrize("L,k,lens", [
+    (70000, 20, [70000, 40001]),
+    # k = 64, 1025-1026 candidates: the last of the 16 partitions holds fewer
+    # candidates (50-51) than the row keeps (63), and level 2 selects among ~1000
+    (33000, 64, [32833, 32801]),
+])
+def test_decode_many_candidates(mode, L, k, lens):
     # more than 16 x 64 candidate blocks: the workgroup-per-row two-level top-k
-    L, Hq, G, di, B, k = 70000, 16, 4, 64, 32, 20
-    lens = [70000, 40001]
+    Hq, G, di, B = 16, 4, 64, 32
     say(f"[decode many candidates {mode}] L={L} B={B} k={k}")
     dec = inputs.make_decode(len(lens), L, Hq, G, 128, di, seed=61, cache_lens=lens, idx_mode=mode)
     out, lse, bidx = gpu_decode(dec, B, k)
@@ -587,7 +592,8 @@ def test_sink_prefill_end_to_end():
 
 
 @pytest.mark.parametrize("mode", ["integer", "gaussian"])
-@pytest.mark.parametrize("L,B,k,lens", [(9000, 64, 6, [9000, 1, 64, 65, 4321]), (70000, 32, 20, [70000, 40001])])
+@pytest.mark.parametrize("L,B,k,lens", [(9000, 64, 6, [9000, 1, 64, 65, 4321]), (70000, 32, 20, [70000, 40001]),
+                                       (33000, 32, 64, [32833, 32801])])
 def test_sink_decode(mode, L, B, k, lens):
     Hq, G, di = 16, 4, 64
     say(f"[sink decode {mode}] L={L} B={B} k={k}")
