@@ -16,8 +16,9 @@
 // The selection is exp-free and exact (it compares the same fp32 maxima the
 // index kernel produced, mapped to order-preserving uint32 keys):
 //  1. each lane takes the max key over its strided share of the candidates;
-//     the (m-1)-th largest of the 64 lane maxima is a lower bound lb of the
-//     (m-1)-th largest key overall (valid while m-1 <= 64);
+//     any lb that m-1 lane maxima reach is a lower bound of the (m-1)-th
+//     largest key overall (valid while m-1 <= 64); lb is taken on the keys'
+//     top 16 bits only, a 16-step search;
 //  2. candidates with key >= lb are compacted, in ascending block order, into
 //     a per-wave LDS list (ballot + prefix popcount);
 //  3. the exact threshold tau = (m-1)-th largest key is found by a 32-step
@@ -52,6 +53,18 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 __device__ __forceinline__ int popc(uint64_t x) { return __popcll(x); }
+
+// A lower bound of the kth (>= 1) largest key among at most one key per lane
+// (0 = no key): the largest multiple of 2^16 that kth keys reach, found on
+// the top 16 bits only (sign, exponent and 7 mantissa bits of the scores).
+__device__ __forceinline__ uint32_t kth_largest_lanes_hi16(uint32_t key, int kth) {
+  uint32_t tau = 0;
+  for (int bit = 31; bit >= 16; --bit) {
+    const uint32_t c = tau | (1u << bit);
+    if (popc(__ballot(key >= c)) >= kth) tau = c;
+  }
+  return tau;
+}
 
 // kth (>= 1) largest key among at most one key per lane (0 = no key).
 __device__ __forceinline__ uint32_t kth_largest_lanes(uint32_t key, int kth) {
@@ -188,7 +201,7 @@ __device__ __forceinline__ int compact_candidates(const float* __restrict__ srow
     uint32_t lmax = 0;
 #pragma unroll
     for (int i = 0; i < NR; ++i) lmax = max(lmax, key[i]);
-    const uint32_t lb = (want <= kWave) ? kth_largest_lanes(lmax, want) : 0u;
+    const uint32_t lb = (want <= kWave) ? kth_largest_lanes_hi16(lmax, want) : 0u;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       if (i * kWave < n) {  // wave-uniform
@@ -206,7 +219,7 @@ __device__ __forceinline__ int compact_candidates(const float* __restrict__ srow
   } else {
     uint32_t lmax = 0;
     for (int j = lane; j < n; j += kWave) lmax = max(lmax, order_key(srow[b0 + j]));
-    const uint32_t lb = (want <= kWave) ? kth_largest_lanes(lmax, want) : 0u;
+    const uint32_t lb = (want <= kWave) ? kth_largest_lanes_hi16(lmax, want) : 0u;
     for (int j0 = 0; j0 < n; j0 += kWave) {
       const int j = j0 + lane;
       const uint32_t key = j < n ? order_key(srow[b0 + j]) : 0u;
