@@ -263,9 +263,10 @@ __device__ __forceinline__ int compact_candidates_sb(const float* __restrict__ s
     key[i] = (j >= s_lo && j < nsb) ? order_key(sm[j]) : 0u;
   }
   const int nch = (nsb + kWave - 1) / kWave;
-  // lb = want-th largest bound key (exact bitwise search, counts by ballots)
+  // lb: the largest multiple of 2^16 that want bound keys reach (a lower
+  // bound of the want-th largest, found on the top 16 bits; counts by ballots)
   uint32_t lb = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int bit = 31; bit >= 16; --bit) {
     const uint32_t c = lb | (1u << bit);
     int cnt = 0;
 #pragma unroll
