@@ -305,6 +305,34 @@ def profile_kernels_only(args, dev):
                       "stage_ms": {n: round(t / c, 4) for n, (c, t) in stages.items()}}), flush=True)
 
 
+def prefill_1m_run(dev, stream):
+    """The long prefill of the pages' 1M-token setting: T = 1,048,576, 64 q heads
+    in 8 groups, block 128, top-k 16, with 64 needle blocks (separable preset);
+    one warmup, the mean of 2 timed calls, and the per-prefill stage totals of a
+    third (the call runs in query chunks, so stages launch several times)."""
+    T = 1 << 20
+    pin = inputs.make_prefill(T, PF["Hq"], PF["G"], PF["d"], PF["di"], seed=5, device=dev, block_size=PF["B"],
+                              needles=64)
+    dims = bd.make_dims(1, T, PF["Hq"], PF["G"], index_dim=PF["di"], block_size=PF["B"], topk=PF["k"])
+    out = torch.empty_like(pin.q)
+    ws = torch.empty(bd.msa_workspace_bytes(bd.MSA_OP_PREFILL, dims), dtype=torch.uint8, device=dev)
+    fn = lambda: bd.msa_prefill(dims, pin.q, pin.k, pin.v, pin.idx_q, pin.idx_k, out, workspace=ws)  # noqa: E731
+    fn()
+    ms, _ = timed(fn, 2, stream)
+    bd.msa_profile_begin()
+    fn()
+    torch.cuda.synchronize()
+    stages = {n: {"launches": c, "ms": round(t, 3)} for n, (c, t) in bd.msa_profile_end().items()}
+    f_index, f_main = prefill_flops(T, PF["Hq"], PF["G"], PF["d"], PF["di"], PF["B"], PF["k"])
+    res = {"ms": round(ms, 2), "tok_s": round(T / (ms * 1e-3), 1),
+           "algorithmic_tflop": round((f_index + f_main) / 1e12, 2),
+           "tflops": round((f_index + f_main) / (ms * 1e-3) / 1e12, 2),
+           "needles": 64, "workspace_gbytes": round(ws.numel() / 1e9, 2), "stages_per_prefill": stages}
+    del pin, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def timed(fn, reps, stream):
     """Mean ms of reps launches of fn, HIP events on the launch stream."""
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
@@ -664,6 +692,15 @@ def main():
         log("oracle leg on host cores")
         cpu, parity = cpu_baseline_and_parity(pin, pout, pbidx, args.cpu_tokens, args.cpu_seconds)
         dparity = decode_parity(dec, dout, dbidx, seqs=[0, 5])
+
+    if variants is not None:
+        # the 1M-token prefill last, after the decode caches and the 128K
+        # workspace are released
+        del dec, dws, pws
+        torch.cuda.empty_cache()
+        log("prefill at T=1,048,576 (64 needle blocks)")
+        variants["prefill_t1048576_b128_k16_needles"] = prefill_1m_run(dev, stream)
+        log(f"1M prefill: {variants['prefill_t1048576_b128_k16_needles']}")
 
     prefill_tok_s = PF["T"] / (p_ms * 1e-3)
     decode_tok_s = DC["batch"] / (d_ms * 1e-3)
