@@ -461,6 +461,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the main-branch backward at 128K")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
+    ap.add_argument("--profile-1m", action="store_true",
+                    help="run only the 1M-token prefill (one warmup, two timed, one staged) for a rocprofv3 pass")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="run only prefills and decode steps (plus a calibration copy) for rocprofv3 passes")
     args = ap.parse_args()
@@ -476,6 +478,10 @@ def main():
     stream = torch.cuda.current_stream()
     if args.profile_kernels:
         profile_kernels_only(args, dev)
+        return
+    if args.profile_1m:
+        print(json.dumps({"prefill_t1048576_b128_k16_needles": prefill_1m_run(dev, torch.cuda.current_stream())}),
+              flush=True)
         return
 
     log("generating prefill inputs (T=131072)")
