@@ -499,8 +499,7 @@ hipError_t launch_topk_prefill(const float* S, int s_stride, const float* SM, in
                                                                     bidx_t_off, G, B, k, sink, t0, tc, n_rows);
   else
     topk_prefill_kernel<false><<<dim3((unsigned)grid), 256, 0, st>>>(S, s_stride, SM, sm_stride, bidx, bidx_rows,
-                                                                     bidx_t_off,
-                                                            G, B, k, sink, t0, tc, n_rows);
+                                                                     bidx_t_off, G, B, k, sink, t0, tc, n_rows);
   return hipGetLastError();
 }
 
