@@ -133,7 +133,11 @@ def attention_row(q_t: np.ndarray, K: np.ndarray, V: np.ndarray, toks: np.ndarra
     """Exact softmax attention of query rows q_t [R, d] over the gathered
     keys/values K[toks], V[toks] ([n, d]) [HA 方法: standard scaled dot-product
     attention over the Key/Value vectors gathered from the selected blocks].
-    Returns (o [R, d], lse [R]) with lse = ln sum_j exp(x_j)."""
+    Returns (o [R, d], lse [R]) with lse = ln sum_j exp(x_j).  A row with no
+    key to attend (a given selection that keeps none of its visible blocks)
+    is defined as o = 0, lse = -inf."""
+    if len(toks) == 0:
+        return np.zeros((q_t.shape[0], V.shape[-1])), np.full(q_t.shape[0], -np.inf)
     Kg, Vg = K[toks], V[toks]
     x = scale * (q_t @ Kg.T)                      # [R, n]
     mx = x.max(axis=1, keepdims=True)

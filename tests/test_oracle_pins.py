@@ -288,6 +288,173 @@ def test_decode_equals_prefill_row():
 
 
 # --------------------------------------------------------------------------
+# P7 (decode branches): dense, given-selection and forced-sink decode, each
+# against a reference that is not the oracle's decode code.
+# --------------------------------------------------------------------------
+def _row_mask_from_selection(sel, t, B, Hq, G, n):
+    """Boolean [Hq, n] mask over cache positions 0..n-1 of the tokens of the
+    selected blocks that are <= t (entries outside [0, L(t)] ignored)."""
+    R = Hq // G
+    m = torch.zeros(Hq, n, dtype=torch.bool)
+    for g in range(G):
+        for b in np.asarray(sel[g]).tolist():
+            if 0 <= b <= t // B:
+                m[g * R:(g + 1) * R, b * B:min((b + 1) * B, t + 1)] = True
+    return m
+
+
+def _sdpa_row(q_row, kc, vc, n, mask=None):
+    """torch SDPA (fp64, GQA) of one query token against cache positions
+    0..n-1; mask [Hq, n] bool or None (all visible).  Returns (out [Hq, d],
+    lse [Hq]) with lse from torch.logsumexp of the masked logits."""
+    q = q_row.to(torch.float64)[None, :, None, :]                 # [1, Hq, 1, d]
+    k = kc[:n].to(torch.float64).permute(1, 0, 2)[None]           # [1, G, n, d]
+    v = vc[:n].to(torch.float64).permute(1, 0, 2)[None]
+    am = None if mask is None else mask[None, :, None, :]
+    o = F.scaled_dot_product_attention(q, k, v, attn_mask=am, enable_gqa=True)
+    Hq, G = q.shape[1], k.shape[1]
+    kk = k.repeat_interleave(Hq // G, dim=1)
+    x = (q @ kk.transpose(-1, -2))[0, :, 0, :] / math.sqrt(q.shape[-1])
+    if mask is not None:
+        x = x.masked_fill(~mask, float("-inf"))
+    return _np(o[0, :, 0, :]), _np(torch.logsumexp(x, dim=-1))
+
+
+def test_decode_dense_equals_sdpa_over_the_cache_prefix():
+    """dense=True: every visible block, i.e. plain GQA attention of the token
+    at len-1 over cache positions 0..len-1 (lengths 1, 16, 57, 200)."""
+    L, Hq, G, d, di, B, k = 200, 6, 3, 16, 8, 16, 2
+    lens = [200, 57, 16, 1]
+    dec = inputs.make_decode(len(lens), L, Hq, G, d, di, seed=71, cache_lens=lens)
+    res = orc.decode(dec.q, dec.k_cache, dec.v_cache, dec.idx_q, dec.idx_k_cache, lens, B, k, dense=True)
+    assert res["block_idx"] is None
+    for s, n in enumerate(lens):
+        o, lse = _sdpa_row(dec.q[s], dec.k_cache[s], dec.v_cache[s], n)
+        np.testing.assert_allclose(res["out"][s], o, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(res["lse"][s], lse, rtol=0, atol=1e-12)
+
+
+def test_decode_given_selection_equals_masked_sdpa():
+    """block_idx given: attention over exactly the listed blocks <= len-1
+    (shuffled entries, a row without its local block, out-of-range entries
+    ignored, -1 padding), against SDPA with that selection as a mask; a row
+    listing no visible block gives zero output and lse = -inf."""
+    L, Hq, G, d, di, B, k = 160, 4, 2, 8, 8, 16, 4
+    lens = [160, 70, 33, 16]
+    dec = inputs.make_decode(len(lens), L, Hq, G, d, di, seed=72, cache_lens=lens)
+    given = np.full((len(lens), G, k), -1, dtype=np.int64)
+    given[0, 0] = [3, 9, 0, 7]          # local block 9 last-but-one, shuffled
+    given[0, 1] = [2, 5, -1, -1]        # no local block
+    given[1, 0] = [4, 0, 11, -1]        # 11 > L(69) = 4: ignored
+    given[1, 1] = [1, -1, -1, -1]
+    given[2, 0] = [2, 1, 0, -1]         # L(32) = 2, the partial local block
+    given[2, 1] = [0, 2, -1, -1]
+    given[3, 0] = [0, -1, -1, -1]       # len 16: one full block
+    given[3, 1] = [5, 7, -1, -1]        # nothing visible: empty row
+    res = orc.decode(dec.q, dec.k_cache, dec.v_cache, dec.idx_q, dec.idx_k_cache, lens, B, k,
+                     block_idx=given)
+    R = Hq // G
+    for s, n in enumerate(lens):
+        mask = _row_mask_from_selection(given[s], n - 1, B, Hq, G, n)
+        empty = ~mask.any(dim=-1)
+        safe = mask.clone()
+        safe[empty, 0] = True                       # keep SDPA finite on empty rows
+        o, lse = _sdpa_row(dec.q[s], dec.k_cache[s], dec.v_cache[s], n, safe)
+        for h in range(Hq):
+            if empty[h]:
+                assert (res["out"][s, h] == 0).all() and res["lse"][s, h] == -np.inf
+            else:
+                np.testing.assert_allclose(res["out"][s, h], o[h], rtol=0, atol=1e-12)
+                np.testing.assert_allclose(res["lse"][s, h], lse[h], rtol=0, atol=1e-12)
+    assert empty.sum() == R                         # the last sequence's group 1
+
+
+def test_prefill_given_selection_equals_masked_sdpa():
+    """Prefill with block_idx given (rows without their local block and with
+    out-of-range entries) against SDPA with the selection as a mask."""
+    T, Hq, G, d, B, k = 80, 4, 2, 8, 8, 3
+    rng = np.random.default_rng(73)
+    inp = inputs.make_prefill(T, Hq, G, d, 8, seed=74)
+    bidx = _random_selection(T, G, B, k, rng, drop_local=True, junk=True)
+    mask = _sel_mask(bidx, T, Hq, G, B)
+    empty = ~mask.any(dim=-1)
+    safe = mask.clone()
+    safe[empty.unsqueeze(-1).expand_as(safe) & (torch.arange(T) == 0)] = True
+    res = _run_all(inp, B, k, block_idx=bidx)
+    out, lse = _stack(res, "out", 1, T), _stack(res, "lse", 1, T)
+    q = inp.q.to(torch.float64).transpose(1, 2)
+    kk = inp.k.to(torch.float64).transpose(1, 2)
+    vv = inp.v.to(torch.float64).transpose(1, 2)
+    ref = _np(F.scaled_dot_product_attention(q, kk, vv, attn_mask=safe, enable_gqa=True).transpose(1, 2))
+    x = (q @ kk.repeat_interleave(Hq // G, dim=1).transpose(-1, -2)) / math.sqrt(d)
+    rlse = _np(torch.logsumexp(x.masked_fill(~safe, float("-inf")), dim=-1).transpose(1, 2))
+    em = empty.transpose(1, 2).numpy()              # [1, T, Hq]
+    assert em.any()
+    np.testing.assert_allclose(out[~em], ref[~em], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[~em], rlse[~em], rtol=0, atol=1e-12)
+    assert (out[em] == 0).all() and (lse[em] == -np.inf).all()
+
+
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_decode_sink_exhaustive_and_masked_sdpa(k):
+    """sink=True decode on integer index inputs: the selection equals the
+    brute-force sink rule ({0, L} plus the max-sum subset of blocks 1..L-1,
+    ties to the lexicographically first tuple; only L when m = 1), and the
+    output equals SDPA masked to that selection."""
+    L, Hq, G, d, di, B = 150, 4, 2, 8, 6, 10
+    lens = [150, 101, 31, 10]
+    dec = inputs.make_decode(len(lens), L, Hq, G, d, di, seed=75 + k, cache_lens=lens, idx_mode="integer")
+    res = orc.decode(dec.q, dec.k_cache, dec.v_cache, dec.idx_q, dec.idx_k_cache, lens, B, k, sink=True)
+    iq = dec.idx_q.to(torch.int64).numpy()
+    ik = dec.idx_k_cache.to(torch.int64).numpy()
+    for s, n in enumerate(lens):
+        t = n - 1
+        Lb = t // B
+        m = min(k, Lb + 1)
+        for g in range(G):
+            S = _brute_block_max(iq[s, g], ik[s], t, B)
+            if m >= 2 and Lb >= 1:
+                best, best_sum = None, None
+                for comb in itertools.combinations(range(1, Lb), m - 2):
+                    sm = sum(S[b] for b in comb)
+                    if best_sum is None or sm > best_sum:
+                        best, best_sum = comb, sm
+                expect = sorted([0] + list(best) + [Lb])
+            else:
+                expect = [Lb]
+            assert res["block_idx"][s, g].tolist() == expect + [-1] * (k - m), (s, g)
+        mask = _row_mask_from_selection(res["block_idx"][s], t, B, Hq, G, n)
+        o, lse = _sdpa_row(dec.q[s], dec.k_cache[s], dec.v_cache[s], n, mask)
+        np.testing.assert_allclose(res["out"][s], o, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(res["lse"][s], lse, rtol=0, atol=1e-12)
+
+
+def test_decode_modes_equal_prefill_rows():
+    """Each decode mode equals the same mode's prefill row len-1 (dense,
+    given, sink), on caches that hold the prefill tensors."""
+    T, Hq, G, d, di, B, k = 120, 4, 2, 8, 8, 16, 3
+    inp = inputs.make_prefill(T, Hq, G, d, di, batch=2, seed=76)
+    lens = [120, 45]
+    q_dec = torch.stack([inp.q[s, lens[s] - 1] for s in range(2)])
+    iq_dec = torch.stack([inp.idx_q[s, lens[s] - 1] for s in range(2)])
+    rows = [(s, lens[s] - 1) for s in range(2)]
+    given = np.full((2, T, G, k), -1, dtype=np.int64)
+    given[0, lens[0] - 1] = [[0, 4, 7], [2, 7, -1]]
+    given[1, lens[1] - 1] = [[1, 2, -1], [0, -1, -1]]
+    for kw in ({"dense": True}, {"sink": True}, {"block_idx": given}):
+        dkw = dict(kw)
+        if "block_idx" in kw:
+            dkw["block_idx"] = np.stack([given[s, lens[s] - 1] for s in range(2)])
+        dres = orc.decode(q_dec, inp.k, inp.v, iq_dec, inp.idx_k, lens, B, k, **dkw)
+        pres = _run_all(inp, B, k, rows=rows, **kw)
+        for s, t in rows:
+            np.testing.assert_allclose(dres["out"][s], pres["out"][(s, t)], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(dres["lse"][s], pres["lse"][(s, t)], rtol=0, atol=1e-13)
+            if "sink" in kw:
+                np.testing.assert_array_equal(dres["block_idx"][s], pres["block_idx"][(s, t)])
+
+
+# --------------------------------------------------------------------------
 # P8 needle invariant (separable preset): every row's non-local selections
 # contain min(k-1, visible non-local needles) needle blocks.
 # --------------------------------------------------------------------------
