@@ -100,7 +100,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     pd = ctypes.POINTER(msa_dims)
-    lib.msa_index_scores.argtypes = [pd, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
+    lib.msa_index_scores.argtypes = [pd, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp,
+                                      ctypes.c_int32, vp]
     lib.msa_index_scores.restype = i32
     lib.msa_index_topk.argtypes = [pd, vp, vp, vp, vp, sz, vp]
     lib.msa_index_topk.restype = i32
@@ -199,13 +200,17 @@ def scores_row_stride(dims: msa_dims, t1: int) -> int:
 
 
 def msa_index_scores(dims: msa_dims, idx_q, idx_k, scores, t0: int, t1: int, row_stride: int,
-                     stream=None):
+                     superblock_max=None, stream=None):
     lib = load_library()
     b, T, G, di = dims.batch, dims.seqlen, dims.num_kv_heads, dims.index_dim
     p_iq = _ptr(idx_q, "idx_q", torch.bfloat16, (b, T, G, di))
     p_ik = _ptr(idx_k, "idx_k", torch.bfloat16, (b, T, di))
     p_s = _ptr(scores, "scores", torch.float32, (b, t1 - t0, G, row_stride))
-    _check(lib, lib.msa_index_scores(ctypes.byref(dims), p_iq, p_ik, p_s, t0, t1, row_stride,
+    sb_stride = 0
+    if superblock_max is not None:
+        sb_stride = int(superblock_max.shape[-1])
+    p_sm = _ptr(superblock_max, "superblock_max", torch.float32, (b, t1 - t0, G, sb_stride), optional=True)
+    _check(lib, lib.msa_index_scores(ctypes.byref(dims), p_iq, p_ik, p_s, t0, t1, row_stride, p_sm, sb_stride,
                                      _stream(stream)))
     return scores
 

@@ -501,7 +501,8 @@ int msa_index_topk(const msa_dims* dims, const void* idx_q, const void* idx_k, i
 }
 
 int msa_index_scores(const msa_dims* dims, const void* idx_q, const void* idx_k, float* scores,
-                     int32_t t0, int32_t t1, int32_t row_stride, void* hip_stream) {
+                     int32_t t0, int32_t t1, int32_t row_stride, float* superblock_max,
+                     int32_t sb_stride, void* hip_stream) {
   int st = check_dims(dims, false);
   if (st != MSA_OK) return st;
   if ((dims->flags & ~MSA_FORCE_SINK) != 0) return MSA_ERR_INVALID_ARG;  // scores do not depend on it
@@ -509,13 +510,16 @@ int msa_index_scores(const msa_dims* dims, const void* idx_q, const void* idx_k,
   if (t0 < 0 || t1 <= t0 || t1 > dims->seqlen) return MSA_ERR_INVALID_ARG;
   const int Lc = (t1 - 1) / dims->block_size;
   if (row_stride < 4 || row_stride % 4 != 0 || row_stride < Lc) return MSA_ERR_INVALID_ARG;
-  if (misaligned(idx_q, 16) || misaligned(idx_k, 16) || misaligned(scores, 16)) return MSA_ERR_ALIGNMENT;
+  if (superblock_max != nullptr && (sb_stride < (Lc + msa::kSuperBlock - 1) / msa::kSuperBlock || sb_stride < 1))
+    return MSA_ERR_INVALID_ARG;
+  if (misaligned(idx_q, 16) || misaligned(idx_k, 16) || misaligned(scores, 16) || misaligned(superblock_max, 4))
+    return MSA_ERR_ALIGNMENT;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   msa::prof_mark(s, MSA_STAGE_INDEX_PREFILL);
   hipError_t e = msa::launch_index_blockmax_prefill(
       static_cast<const uint16_t*>(idx_q), static_cast<const uint16_t*>(idx_k), scores, dims->batch,
-      dims->seqlen, dims->num_kv_heads, dims->index_dim, dims->block_size, t0, t1 - t0, row_stride, nullptr, 0,
-      s);
+      dims->seqlen, dims->num_kv_heads, dims->index_dim, dims->block_size, t0, t1 - t0, row_stride,
+      superblock_max, superblock_max != nullptr ? sb_stride : 0, s);
   msa::prof_mark(s, -1);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }

@@ -120,10 +120,19 @@ int msa_index_topk(const msa_dims* dims, const void* idx_q, const void* idx_k,
  * for every candidate block b < L(t) = t / block_size, in fp32 (products of
  * bf16 values accumulated in fp32).  scores is [batch, t1 - t0, G, row_stride]
  * fp32 with row_stride a multiple of 4 and >= L(t1 - 1); entries b >= L(t) of
- * a row are unspecified.  No workspace.  Flags must be 0 or MSA_FORCE_SINK (scores do not depend on it).
+ * a row are unspecified.
+ * superblock_max (nullable): [batch, t1 - t0, G, sb_stride] fp32 OUTPUT with
+ * sb_stride >= ceil(L(t1 - 1) / 16); entry i of a row is the largest score of
+ * the row's candidate blocks b in [16 i, 16 i + 16), b < L(t), for
+ * i < ceil(L(t) / 16) (later entries unspecified).  The selection reads these
+ * run maxima to skip runs of rows with more than 1024 candidates that cannot
+ * hold a selected block; with superblock_max non-NULL the kernel variant that
+ * writes them runs, so both variants can be checked.  4-byte aligned.
+ * No workspace.  Flags must be 0 or MSA_FORCE_SINK (scores do not depend on it).
  */
 int msa_index_scores(const msa_dims* dims, const void* idx_q, const void* idx_k, float* scores,
-                     int32_t t0, int32_t t1, int32_t row_stride, void* hip_stream);
+                     int32_t t0, int32_t t1, int32_t row_stride, float* superblock_max,
+                     int32_t sb_stride, void* hip_stream);
 
 /*
  * Prefill: Index Branch + Main Branch over a whole causal sequence.

@@ -224,3 +224,23 @@ def test_backward_workspace_fits_128k_in_one_chunk(lib):
     d = bd.make_dims(1, 131072, 64, 8, index_dim=128, block_size=128, topk=16)
     ws = lib.msa_workspace_bytes(bd.MSA_OP_BACKWARD, ctypes.byref(d))
     assert 0 < ws <= 64 << 30
+
+
+def test_index_scores_rejects_bad_ranges(lib):
+    """msa_index_scores validates the token range, the row strides and the
+    alignment before any launch."""
+    d = _dims()                                   # T 2048, B 128: L(2047) = 15
+    fake = 0x10000
+    call = lambda t0, t1, rs, sm, sbs, sc=fake: lib.msa_index_scores(ctypes.byref(d), fake, fake, sc, t0, t1, rs,
+                                                                      sm, sbs, None)
+    assert call(0, 0, 16, None, 0) == bd.MSA_ERR_INVALID_ARG        # empty range
+    assert call(-1, 100, 16, None, 0) == bd.MSA_ERR_INVALID_ARG
+    assert call(0, 2049, 16, None, 0) == bd.MSA_ERR_INVALID_ARG     # past T
+    assert call(0, 2048, 12, None, 0) == bd.MSA_ERR_INVALID_ARG     # row_stride < L(t1 - 1)
+    assert call(0, 2048, 18, None, 0) == bd.MSA_ERR_INVALID_ARG     # not a multiple of 4
+    assert call(0, 2048, 16, fake, 0) == bd.MSA_ERR_INVALID_ARG     # sb_stride < ceil(15 / 16)
+    assert call(0, 2048, 16, None, 0, sc=fake + 4) == bd.MSA_ERR_ALIGNMENT
+    assert call(0, 2048, 16, fake + 2, 1) == bd.MSA_ERR_ALIGNMENT
+    dd = _dims(flags=bd.MSA_DENSE)
+    assert lib.msa_index_scores(ctypes.byref(dd), fake, fake, fake, 0, 2048, 16, None, 0, None) == \
+        bd.MSA_ERR_INVALID_ARG

@@ -63,3 +63,18 @@ def test_kv_outer_and_query_major_bytes_count_entries():
     qm = bench.query_major_bytes(entries, T, Hq, G, d, B)
     nb = (T + B - 1) // B
     assert qm == T * Hq * (4 * d + 4) + entries * (R * (2 * d + 8) + 4) + G * nb * 4 * B * d
+
+
+def test_compulsory_bytes_and_kv_outer_flops():
+    # every input read once and every output written once, tensor by tensor
+    T, Hq, G, d, di, k = 131072, 64, 8, 128, 128, 16
+    tensors = {"q": T * Hq * d * 2, "k": T * G * d * 2, "v": T * G * d * 2, "idx_q": T * G * di * 2,
+               "idx_k": T * di * 2, "out": T * Hq * d * 2, "lse": T * Hq * 4, "block_idx": T * G * k * 4}
+    assert bench.compulsory_prefill_bytes(T, Hq, G, d, di, k) == sum(tensors.values())
+    assert abs(sum(tensors.values()) - 5.23e9) / 5.23e9 < 5e-3
+    # one entry: a 128-key block against R = 8 heads, QK^T and PV, 2 flops per MAC
+    assert bench.kv_outer_flops(1, 64, 8, 128, 128) == 2 * 2 * 128 * 128 * 8
+    # local blocks: brute force over a small case
+    T, Hq, d, B = 300, 4, 16, 32
+    ref = sum(4.0 * Hq * d * len(range((t // B) * B, t + 1)) for t in range(T))
+    assert bench.local_block_flops(T, Hq, d, B) == ref

@@ -75,6 +75,22 @@ def test_prefill_128k_block_sweep(B, k):
     torch.cuda.empty_cache()
 
 
+def test_prefill_32k():
+    """The 32K prefill workload: 64 q heads in 8 groups, d 128, d_idx 128,
+    B 128, k 16 (2048 attended tokens), all tensors N(0,1), scale 1/sqrt(128)."""
+    T, B, k = 32768, 128, 16
+    say(f"[prefill 32K] B={B} k={k}")
+    dev = torch.device("cuda")
+    pin = inputs.make_prefill(T, 64, 8, 128, 128, seed=2, device=dev)
+    out, bidx = run_prefill(pin, B, k)
+    invariants_all_rows(bidx, T, B, k)
+    rng = np.random.default_rng(32)
+    rows = sorted(set(int(t) for t in rng.integers(0, T, 48)) | {0, B - 1, B, 2 * B + 5, T - B, T - 1})
+    sampled_check(pin, out, bidx, B, k, rows)
+    del pin, out, bidx
+    torch.cuda.empty_cache()
+
+
 def test_prefill_1m_needles():
     T, B, k, nneedle = 1 << 20, 128, 16, 64
     say("[prefill 1M needles]")
@@ -114,7 +130,7 @@ def test_decode_1m_context():
     bd.msa_decode(dims, dec.q, dec.k_cache, dec.v_cache, dec.idx_q, dec.idx_k_cache, dec.cache_lens, out,
                   block_idx=bidx)
     torch.cuda.synchronize()
-    for s in (0, 2, 4, 7):
+    for s in range(batch):
         t = lens[s] - 1
         IK = dec.idx_k_cache[s, : t + 1].cpu().double().numpy()
         IQ = dec.idx_q[s].cpu().double().numpy()
