@@ -49,7 +49,8 @@ MSA_STAGE_BWD_LISTS = 12
 MSA_STAGE_BWD_MERGE = 13
 MSA_STAGE_COUNT = 14
 
-EXPORTED = ("msa_index_scores", "msa_index_topk", "msa_prefill", "msa_decode", "msa_workspace_bytes",
+EXPORTED = ("msa_index_scores", "msa_index_topk", "msa_prefill", "msa_decode", "msa_decode_noalloc",
+            "msa_decode_noalloc_limit", "msa_workspace_bytes",
             "msa_status_string", "msa_last_hip_error", "msa_abi_version", "msa_profile_begin",
             "msa_profile_end", "msa_stage_name", "msa_indexer_kl", "msa_prefill_backward")
 
@@ -109,6 +110,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_prefill.restype = i32
     lib.msa_decode.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_decode.restype = i32
+    lib.msa_decode_noalloc.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.msa_decode_noalloc.restype = i32
+    lib.msa_decode_noalloc_limit.argtypes = []
+    lib.msa_decode_noalloc_limit.restype = sz
     lib.msa_workspace_bytes.argtypes = [i32, pd]
     lib.msa_workspace_bytes.restype = sz
     lib.msa_status_string.argtypes = [i32]
@@ -309,6 +314,29 @@ def msa_decode(dims: msa_dims, q, k_cache, v_cache, idx_q, idx_k_cache, cache_le
     ws, nws = _workspace(MSA_OP_DECODE, dims, workspace, q.device)
     _check(lib, lib.msa_decode(ctypes.byref(dims), p_q, p_k, p_v, p_iq, p_ik, p_len, p_o, p_l, p_bi,
                                ws, nws, _stream(stream)))
+    return out
+
+
+def msa_decode_noalloc(dims: msa_dims, q, k_cache, v_cache, idx_q, idx_k_cache, cache_lens, out,
+                       lse=None, block_idx=None, stream=None):
+    """msa_decode on the library's own per-GPU scratch array: no workspace
+    argument and no allocation (shapes beyond msa_decode_noalloc_limit()
+    bytes of workspace are rejected)."""
+    lib = load_library()
+    b, L, Hq, G, d, di, kk = (dims.batch, dims.seqlen, dims.num_q_heads, dims.num_kv_heads,
+                             dims.head_dim, dims.index_dim, dims.topk)
+    idx_needed = not (dims.flags & (MSA_DENSE | MSA_GIVEN_INDICES))
+    p_q = _ptr(q, "q", torch.bfloat16, (b, Hq, d))
+    p_k = _ptr(k_cache, "k_cache", torch.bfloat16, (b, L, G, d))
+    p_v = _ptr(v_cache, "v_cache", torch.bfloat16, (b, L, G, d))
+    p_iq = _ptr(idx_q, "idx_q", torch.bfloat16, (b, G, di), optional=not idx_needed)
+    p_ik = _ptr(idx_k_cache, "idx_k_cache", torch.bfloat16, (b, L, di), optional=not idx_needed)
+    p_len = _ptr(cache_lens, "cache_lens", torch.int32, (b,))
+    p_o = _ptr(out, "out", torch.bfloat16, (b, Hq, d))
+    p_l = _ptr(lse, "lse", torch.float32, (b, Hq), optional=True)
+    p_bi = _ptr(block_idx, "block_idx", torch.int32, (b, G, kk), optional=True)
+    _check(lib, lib.msa_decode_noalloc(ctypes.byref(dims), p_q, p_k, p_v, p_iq, p_ik, p_len, p_o, p_l, p_bi,
+                                       _stream(stream)))
     return out
 
 

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "msa.h"
 #include "msa_internal.h"
 
@@ -437,6 +439,40 @@ hipError_t run_index_chunk(const msa_dims* d, const PrefillPlan& p, const void* 
                                   d->topk, (d->flags & MSA_FORCE_SINK) != 0, t0, tc, st);
 }
 
+// ---------------------------------------------------------------------------
+// Library-owned decode scratch for msa_decode_noalloc: a fixed device array
+// (one copy per GPU, held until the process ends) whose device address is
+// looked up once per device.  Host code never passes the array's own name to
+// a kernel: that name is a host-side stand-in, not a device address.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = 32ull << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return MSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (ptr == nullptr || misaligned(ptr, kAlignWs)) return MSA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
+int run_decode(const msa_dims* dims, const DecodePlan& p, const void* q, const void* k_cache, const void* v_cache,
+               const void* idx_q, const void* idx_k_cache, const int32_t* cache_lens, void* out, float* lse,
+               int32_t* block_idx, void* workspace, size_t workspace_bytes, void* hip_stream);
+
 }  // namespace
 
 extern "C" {
@@ -765,6 +801,33 @@ int msa_decode(const msa_dims* dims, const void* q, const void* k_cache, const v
   DecodePlan p;
   int st = make_decode_plan(dims, &p);
   if (st != MSA_OK) return st;
+  return run_decode(dims, p, q, k_cache, v_cache, idx_q, idx_k_cache, cache_lens, out, lse, block_idx, workspace,
+                    workspace_bytes, hip_stream);
+}
+
+int msa_decode_noalloc(const msa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                       const void* idx_q, const void* idx_k_cache, const int32_t* cache_lens, void* out,
+                       float* lse, int32_t* block_idx, void* hip_stream) {
+  DecodePlan p;
+  int st = make_decode_plan(dims, &p);
+  if (st != MSA_OK) return st;
+  if (p.total > kScratchBytes) return MSA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws)) != MSA_OK) return st;
+  return run_decode(dims, p, q, k_cache, v_cache, idx_q, idx_k_cache, cache_lens, out, lse, block_idx, ws,
+                    kScratchBytes, hip_stream);
+}
+
+size_t msa_decode_noalloc_limit(void) { return kScratchBytes; }
+
+}  // extern "C"
+
+namespace {
+
+int run_decode(const msa_dims* dims, const DecodePlan& p, const void* q, const void* k_cache, const void* v_cache,
+               const void* idx_q, const void* idx_k_cache, const int32_t* cache_lens, void* out, float* lse,
+               int32_t* block_idx, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  int st = MSA_OK;
   const bool dense = dims->flags & MSA_DENSE, given = dims->flags & MSA_GIVEN_INDICES;
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || cache_lens == nullptr || out == nullptr)
     return MSA_ERR_INVALID_ARG;
@@ -819,4 +882,4 @@ int msa_decode(const msa_dims* dims, const void* q, const void* k_cache, const v
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
-}  // extern "C"
+}  // namespace

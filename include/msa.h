@@ -172,6 +172,27 @@ int msa_decode(const msa_dims* dims, const void* q, const void* k_cache,
                void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * msa_decode without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, kernels and results as msa_decode;
+ * the workspace is a library-owned device array of msa_decode_noalloc_limit()
+ * bytes (32 MiB), one per GPU, held until the process ends.  Shapes whose
+ * msa_workspace_bytes(MSA_OP_DECODE, dims) exceeds that limit return
+ * MSA_ERR_WORKSPACE before any launch (8 sequences at 1M context, block 128,
+ * top-k 16 need about 10 MiB; all-blocks mode at that context does not fit).
+ * The call allocates nothing; it looks up the array's device address once per
+ * GPU (hipGetSymbolAddress, on the first call with that GPU current).  Every
+ * call on one GPU shares that GPU's array: calls that overlap in time on one
+ * GPU (on different streams, or from different threads) race; calls ordered
+ * on one stream do not.
+ */
+int msa_decode_noalloc(const msa_dims* dims, const void* q, const void* k_cache,
+                       const void* v_cache, const void* idx_q, const void* idx_k_cache,
+                       const int32_t* cache_lens, void* out, float* lse, int32_t* block_idx,
+                       void* hip_stream);
+size_t msa_decode_noalloc_limit(void);
+
+/*
  * Indexer KL loss and its gradient into the index-branch inputs: the signal
  * that trains the Index Branch [Telegram review quant_prune_distill post 751,
  * "Метод": KL between the index branch and the head-averaged main branch,
