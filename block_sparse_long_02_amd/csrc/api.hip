@@ -166,7 +166,8 @@ int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
     p->off_entries = L.add(emax * 4);
     p->off_work = L.add((size_t)p->max_work * 8);
     p->off_nwork = L.add(4);
-    p->off_pO = L.add(emax * (size_t)p->R * 128 * 2);
+    // partial rows are stored in blocks of 32 rows (8 KiB)
+    p->off_pO = L.add(round_up(emax * (size_t)p->R, 32) * 128 * 2);
     p->off_pS = L.add(emax * (size_t)p->R * 8);
   }
   p->total = L.total;

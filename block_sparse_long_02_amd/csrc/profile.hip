@@ -99,7 +99,7 @@ const char* msa_stage_name(int32_t stage) {
     case MSA_STAGE_BLOCK_LISTS: return "block lists (count, scan, scatter kernels)";
     case MSA_STAGE_KV_OUTER: return "kv_outer_kernel";
     case MSA_STAGE_QUERY_MAJOR: return "query_major_kernel<false>";
-    case MSA_STAGE_QUERY_MAJOR_DENSE: return "query_major_kernel<true>";
+    case MSA_STAGE_QUERY_MAJOR_DENSE: return "dense_attn_kernel";
     case MSA_STAGE_INDEX_DECODE: return "decode_index_kernel";
     case MSA_STAGE_TOPK_DECODE: return "topk_decode_kernel";
     case MSA_STAGE_DECODE_ATTN: return "decode_attn_kernel";

@@ -154,24 +154,57 @@ __device__ __forceinline__ void block_store(const BlockRegs<BS>& r, bf16_t* Ks, 
   }
 }
 
-// S^T tile (32 keys x 32 query rows) = K[32 x D] . Q^T, A operand from LDS.
-__device__ __forceinline__ f32x16 qk_tile(const bf16_t* Ks, int key0, const bf16x8* qop, int col,
-                                          int half) {
-  f32x16 acc = {};
-  const bf16_t* arow = Ks + (key0 + col) * KROW + 8 * half;
+// S^T tiles of KT consecutive 32-key tiles at once: acc[kt] = K[32 kt ..][D] . Q^T.
+// The KT A operands of a k-step are read from LDS together and the next
+// k-step's are read before the current k-step's products, so one LDS
+// latency is paid per tile set instead of one per product.  Every
+// accumulator still sums its k-steps in order 0..D/16-1 (the same products
+// in the same order as one tile at a time).
+template <int KT>
+__device__ __forceinline__ void qk_tiles(const bf16_t* Ks, const bf16x8* qop, f32x16 (&acc)[KT], int col, int half) {
+  constexpr int KS = D / 16;
+  const bf16_t* arow = Ks + col * KROW + 8 * half;
+  bf16x8 a[2][KT];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    acc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(arow + 16 * ks), qop[ks], acc);
-  return acc;
+  for (int kt = 0; kt < KT; ++kt) a[0][kt] = *reinterpret_cast<const bf16x8*>(arow + kt * 32 * KROW);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int cur = ks & 1;
+    if (ks + 1 < KS) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+        a[cur ^ 1][kt] = *reinterpret_cast<const bf16x8*>(arow + kt * 32 * KROW + 16 * (ks + 1));
+    }
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) acc[kt] = mfma32x32x16(a[cur][kt], qop[ks], ks == 0 ? f32x16{} : acc[kt]);
+  }
 }
 
-// O^T[d-tile] += V^T[32 d x 16 keys] . P^T, for the 16-key slice starting at key0.
-__device__ __forceinline__ f32x16 pv_step(const bf16_t* Vt, int vrow, int dt, int key0, bf16x8 p,
-                                          f32x16 acc, int col, int half) {
-  const bf16_t* vr = Vt + (dt * 32 + col) * vrow + key0 + 4 * half;
-  const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-  const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
-  return mfma32x32x16(join_bf16x4(lo, hi), p, acc);
+// O^T[4 d-tiles] += V^T . P^T over the 2 KT 16-key slices of KT key tiles;
+// the four d-tiles' A operands of a slice are read together and the next
+// slice's before the current slice's products.  Each d-tile accumulates its
+// slices in key order (as one pv_step after another would).
+template <int KT>
+__device__ __forceinline__ void pv_tiles(const bf16_t* Vt, int vrow, const bf16x8 (*p)[2], f32x16 (&o)[4], int col,
+                                         int half) {
+  constexpr int NS = 2 * KT;
+  const bf16_t* vr = Vt + col * vrow + 4 * half;
+  bf16x8 a[2][4];
+  auto load = [&](int sl, bf16x8 (&dst)[4]) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const bf16_t* r = vr + dt * 32 * vrow + 16 * sl;
+      dst[dt] = join_bf16x4(*reinterpret_cast<const u32x2*>(r), *reinterpret_cast<const u32x2*>(r + 8));
+    }
+  };
+  load(0, a[0]);
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+    const int cur = sl & 1;
+    if (sl + 1 < NS) load(sl + 1, a[cur ^ 1]);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32x32x16(a[cur][dt], p[sl >> 1][sl & 1], o[dt]);
+  }
 }
 
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& a, int base) {
@@ -447,18 +480,29 @@ __global__ void lists_scatter_kernel(PrefillMainArgs a) {
 
 // ---------------------------------------------------------------------------
 // fp16 partial rows, stored in list order: the R rows of the list entry at
-// position p are rows p*R .. p*R+R-1, so that a block-major tile writes one
-// contiguous range.  A row holds 128 values in a lane-native order: value i
-// (= 8*h8 + j) of d-tile dt of lane half h sits at dt*32 + h8*16 + h*8 + j
-// and has d = 32*dt + 8*(i/4) + 4*h + (i%4), so one store instruction covers
-// 32 contiguous bytes of every row.
+// position p are rows p*R .. p*R+R-1.  Rows are grouped in blocks of 32
+// consecutive rows (8 KiB); inside a block, chunk c (0..7, 16 bytes: values
+// 8*h8 .. 8*h8+7 of d-tile dt, c = 2 dt + h8) of lane half h of the block's
+// row j sits at byte 1024 c + 512 h + 16 j.  Value i (= 8*h8 + j') of d-tile
+// dt of half h has d = 32*dt + 8*(i/4) + 4*h + (i%4) (the MFMA output layout).
+// So the 64 lanes of a wave holding 32 consecutive rows store (and a merge
+// lane group of one entry's R rows reads) whole 512-byte runs per
+// instruction, where a row-major layout would touch 32 scattered 32-byte
+// pieces.
 // The row is the unnormalised sum O = sum_j p_j v_j over one block's keys
 // (p_j <= 1 after subtracting the row maximum), scaled by 2^-e with e chosen
 // per K/V block from max|V|: |O| <= BS * max|V| * 2^-e < 2^15, so the fp16
-// store cannot overflow for any finite input.  e = 0 (no multiply) whenever
-// max|V| lies in [2^-6, 2^8), where values too small for fp16 normals are
-// below 2^-8 max|V| and their absolute error is negligible.
+// store cannot overflow for any finite input.  e = 0 whenever max|V| lies in
+// [2^-6, 2^8), where values too small for fp16 normals are below 2^-8 max|V|
+// and their absolute error is negligible.
 // ---------------------------------------------------------------------------
+constexpr int kPartBlockRows = 32;
+constexpr int kPartBlockBytes = kPartBlockRows * D * 2;   // 8 KiB
+
+// Byte offset of chunk 0 of half `half` of global partial row `row`.
+__device__ __forceinline__ size_t partial_row_byte(size_t row, int half) {
+  return (row / kPartBlockRows) * kPartBlockBytes + (row % kPartBlockRows) * 16 + half * 512;
+}
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int block_scale_exp(float vmax) {
@@ -469,32 +513,29 @@ __device__ __forceinline__ int block_scale_exp(float vmax) {
   return e < -100 ? -100 : (e > 126 ? 126 : e);
 }
 
-__device__ __forceinline__ int partial_pos(int dt, int h8, int half) { return dt * 32 + h8 * 16 + half * 8; }
-
 // Stores a lane's half of a row through a buffer resource; byte offsets at or
 // beyond the resource's size (lanes without a list entry) are dropped by the
 // hardware range check.
-template <bool SCALED>
-__device__ __forceinline__ void store_partial_row(__amdgpu_buffer_rsrc_t rs, int row_byte, const f32x16* o,
-                                                  float mul, int half) {
+__device__ __forceinline__ void store_partial_row(__amdgpu_buffer_rsrc_t rs, int row_byte, const f32x16* o) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int h8 = 0; h8 < 2; ++h8) {
       f16x8 v;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = (_Float16)(SCALED ? o[dt][8 * h8 + j] * mul : o[dt][8 * h8 + j]);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs,
-                                             row_byte + 2 * partial_pos(dt, h8, half), 0, 0);
+      for (int j = 0; j < 8; ++j) v[j] = (_Float16)o[dt][8 * h8 + j];
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, row_byte + 1024 * (2 * dt + h8), 0,
+                                             0);
     }
 }
 
-__device__ __forceinline__ void accumulate_partial_row(float (*acc)[16], const uint16_t* row, float w, int half) {
+// p: chunk 0 of the lane's half row (partial_row_byte)
+__device__ __forceinline__ void accumulate_partial_row(float (*acc)[16], const uint8_t* p, float w) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int h8 = 0; h8 < 2; ++h8) {
-      const f16x8 v = *reinterpret_cast<const f16x8*>(row + partial_pos(dt, h8, half));
+      const f16x8 v = *reinterpret_cast<const f16x8*>(p + 1024 * (2 * dt + h8));
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[dt][8 * h8 + j] += w * (float)v[j];
     }
@@ -587,81 +628,78 @@ __global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
     if (lane == 0) vmax_w[wave] = vm;
   }
   __syncthreads();
-  // per-block power-of-two scale of the stored partials
+  // Per-block power-of-two scale of the stored partials, folded into the
+  // exponent: p' = 2^(x c - m c - ex) = p 2^-ex, so O' = sum p' v = O 2^-ex and
+  // l' = l 2^-ex come out of the products already scaled (a power-of-two
+  // factor is exact in fp32 and bf16), and the statistics hold m c + ex.
   const int ex = block_scale_exp(fmaxf(fmaxf(vmax_w[0], vmax_w[1]), fmaxf(vmax_w[2], vmax_w[3])));
-  const float emul = ldexpf(1.0f, -ex);
-  const int row_byte = (e * R + r) * (D * 2);                 // >= the range for e >= mt
   const int stat_byte = half == 0 ? (e * R + r) * 8 : 0x40000000;
 
-  auto run = [&](auto scaled) {
-    constexpr bool SCALED = decltype(scaled)::value;
-    for (int it = 0; it < ntile; ++it) {
-      // The K/V tile is loop-invariant; an opaque zero offset keeps its LDS
-      // operand reads inside the loop instead of hoisting them into registers
-      // (the offset, not the pointer, is opaque, so the reads stay LDS reads).
-      int lds_off = 0;
-      asm volatile("" : "+s"(lds_off));
-      const bf16_t* ks_ = Ks + lds_off;
-      const bf16_t* vt_ = Vt + lds_off;
+  for (int it = 0; it < ntile; ++it) {
+    // The K/V tile is loop-invariant; an opaque zero offset keeps its LDS
+    // operand reads inside the loop instead of hoisting them into registers
+    // (the offset, not the pointer, is opaque, so the reads stay LDS reads).
+    int lds_off = 0;
+    asm volatile("" : "+s"(lds_off));
+    const bf16_t* ks_ = Ks + lds_off;
+    const bf16_t* vt_ = Vt + lds_off;
 
-      f32x16 sacc[KT];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) sacc[kt] = qk_tile(ks_, kt * 32, qop, col, half);
+    f32x16 sacc[KT];
+    qk_tiles<KT>(ks_, qop, sacc, col, half);
 
-      // q of this tile is dead: fetch the next tile's rows into the same
-      // registers (the last tile re-reads its own), and the entries after it
-      load_q(qop, q_row(ent_n), true, half);
-      ent_n = entry_at(tile0 + min(it + 2, ntile - 1));
+    // q of this tile is dead: fetch the next tile's rows into the same
+    // registers (the last tile re-reads its own), and the entries after it
+    load_q(qop, q_row(ent_n), true, half);
+    ent_n = entry_at(tile0 + min(it + 2, ntile - 1));
 
-      float mx = -INFINITY;
+    float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float mc = mx * c;
-      bf16x8 pop[KT][2];
-      float l0 = 0.f, l1 = 0.f;
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float mce = mx * c + (float)ex;
+    bf16x8 pop[KT][2];
+    float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          sacc[kt][i] = __builtin_amdgcn_exp2f(sacc[kt][i] * c - mc);
-          sacc[kt][i + 1] = __builtin_amdgcn_exp2f(sacc[kt][i + 1] * c - mc);
-          l0 += sacc[kt][i];
-          l1 += sacc[kt][i + 1];
-        }
-        pop[kt][0] = to_bf16x8(sacc[kt], 0);
-        pop[kt][1] = to_bf16x8(sacc[kt], 8);
+      for (int i = 0; i < 16; i += 2) {
+        sacc[kt][i] = __builtin_amdgcn_exp2f(sacc[kt][i] * c - mce);
+        sacc[kt][i + 1] = __builtin_amdgcn_exp2f(sacc[kt][i + 1] * c - mce);
+        l0 += sacc[kt][i];
+        l1 += sacc[kt][i + 1];
       }
-      float l = l0 + l1;
-      l += __shfl_xor(l, 32, kWave);
-
-      f32x16 oacc[4];
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        oacc[dt] = f32x16{};
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-          oacc[dt] = pv_step(vt_, VROW, dt, kt * 32, pop[kt][0], oacc[dt], col, half);
-          oacc[dt] = pv_step(vt_, VROW, dt, kt * 32 + 16, pop[kt][1], oacc[dt], col, half);
-        }
-      }
-
-      // rows of this tile: list positions off + (tile0+it)*mt ... + nrow - 1
-      const int p0 = off + (tile0 + it) * mt;
-      const int nrow = min(mt, count - (tile0 + it) * mt);
-      const __amdgpu_buffer_rsrc_t ro =
-          __builtin_amdgcn_make_buffer_rsrc(a.pO + (size_t)p0 * R * D, (short)0, nrow * R * D * 2, kBufferWord3);
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(a.pS + (size_t)p0 * R, (short)0, nrow * R * 8, kBufferWord3);
-      store_partial_row<SCALED>(ro, row_byte, oacc, emul, half);
-      const float2 st = make_float2(mc + (float)ex, l * emul);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, st), rs, stat_byte, 0, 0);
+      pop[kt][0] = to_bf16x8(sacc[kt], 0);
+      pop[kt][1] = to_bf16x8(sacc[kt], 8);
     }
-  };
-  if (ex == 0) run(std::false_type{});
-  else run(std::true_type{});
+    float l = l0 + l1;
+    l += __shfl_xor(l, 32, kWave);
+
+    f32x16 oacc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
+    pv_tiles<KT>(vt_, VROW, pop, oacc, col, half);
+
+    // rows of this tile: list positions off + (tile0+it)*mt ... + nrow - 1
+    const int p0 = off + (tile0 + it) * mt;
+    const int nrow = min(mt, count - (tile0 + it) * mt);
+    // partial rows p0*R .. (p0+nrow)*R - 1 through a resource starting at
+    // their first 32-row block; lanes past the tile's rows get an offset
+    // beyond the resource and are dropped
+    const size_t g0 = (size_t)p0 * R;
+    const size_t blk0 = g0 / kPartBlockRows;
+    const size_t blk1 = (g0 + (size_t)nrow * R - 1) / kPartBlockRows;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<uint8_t*>(a.pO) + blk0 * kPartBlockBytes, (short)0,
+        (int)((blk1 - blk0 + 1) * kPartBlockBytes), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(a.pS + (size_t)p0 * R, (short)0, nrow * R * 8, kBufferWord3);
+    const int row_byte = e < nrow ? (int)(partial_row_byte(g0 + row, half) - blk0 * kPartBlockBytes) : 0x7ff00000;
+    store_partial_row(ro, row_byte, oacc);
+    const float2 st = make_float2(mce, l);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, st), rs, stat_byte, 0, 0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -730,8 +768,7 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
     __syncthreads();
 
     f32x16 sacc[KT];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) sacc[kt] = qk_tile(Ks, kt * 32, qop, col, half);
+    qk_tiles<KT>(Ks, qop, sacc, col, half);
     float tmx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
@@ -763,15 +800,10 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
     l = l * alpha + ps;
     m = m_new;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        oacc[dt] = pv_step(Vt, VROW, dt, kt * 32, pop[kt][0], oacc[dt], col, half);
-        oacc[dt] = pv_step(Vt, VROW, dt, kt * 32 + 16, pop[kt][1], oacc[dt], col, half);
-      }
-    }
+    pv_tiles<KT>(Vt, VROW, pop, oacc, col, half);
   }
   if (!valid) return;
 
@@ -819,7 +851,7 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
         const float2 st = a.pS[prow];
         const float w = q0 + u < nv ? __builtin_amdgcn_exp2f(st.x - M2u) : 0.f;
         sumw += w * st.y;
-        accumulate_partial_row(o, a.pO + prow * D, w, half);
+        accumulate_partial_row(o, reinterpret_cast<const uint8_t*>(a.pO) + partial_row_byte(prow, half), w);
       }
     }
     M2 = M2u;
@@ -849,6 +881,156 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
     const float lse2 = (sumw > 0.f) ? M2 + __log2f(sumw) : -INFINITY;
     a.lse[((size_t)s * a.T + t) * a.Hq + h] = lse2 * kLn2;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Dense (all visible blocks) causal attention: the all-blocks comparison
+// mode.  A workgroup owns 128/R consecutive tokens of one (s, g) with the R
+// heads of the group (128 query rows, 32 per wave) and runs online-softmax
+// attention over 64-key tiles of [0, t_last].  K/V tiles are double-buffered
+// in LDS: the next tile's loads are issued before the current tile's
+// products and written to the other buffer after them, so one barrier per
+// tile separates the two and the load latency hides behind the products.
+// Only tiles that reach past the first token of the workgroup are masked
+// (keys j > t); the others are wholly visible to every row.  Workgroups are
+// issued longest-first.
+// ---------------------------------------------------------------------------
+template <int NK>
+__device__ __forceinline__ void block_load_clamped(BlockRegs<NK>& r, const bf16_t* __restrict__ kbase,
+                                                   const bf16_t* __restrict__ vbase, size_t stride, int nvalid,
+                                                   int tid) {
+#pragma unroll
+  for (int i = 0; i < NK / 16; ++i) {
+    const int c = tid + 256 * i;
+    r.k[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)min(c >> 4, nvalid - 1) * stride + (c & 15) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < NK / 32; ++i) {
+    int k4, dq;
+    vt_unit(tid + 256 * i, k4, dq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      r.v[i][j] = *reinterpret_cast<const u32x2*>(vbase + (size_t)min(k4 * 4 + j, nvalid - 1) * stride + dq * 4);
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void dense_attn_kernel(PrefillMainArgs a) {
+  constexpr int KTILE = 64;
+  constexpr int VROW = KTILE + 4;
+  constexpr int KT = KTILE / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KTILE * KROW];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][D * VROW];
+
+  const int R = a.Hq / a.G;
+  const int mt = kAttnRows / R;
+  const int g = blockIdx.y, s = blockIdx.z;
+  const int tl0 = ((int)gridDim.x - 1 - (int)blockIdx.x) * mt;   // longest rows first
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int row = wave * 32 + col;
+  const int e = row / R, r = row % R;
+  const int tl = tl0 + e;
+  const bool valid = e < mt && tl < a.tc;
+  const int t = a.t0 + min(tl, a.tc - 1);
+  const int h = g * R + r;
+  const int hi = valid ? t : -1;   // rows without a token see no key
+
+  const int t_first = a.t0 + tl0;
+  const int t_last = a.t0 + min(tl0 + mt, a.tc) - 1;
+  const int ntiles = t_last / KTILE + 1;
+
+  bf16x8 qop[D / 16];
+  load_q(qop, a.q + (((size_t)s * a.T + t) * a.Hq + h) * D, valid, half);
+
+  const size_t kvstride = (size_t)a.G * D;
+  const bf16_t* kseq = a.k + (size_t)s * a.T * kvstride + (size_t)g * D;
+  const bf16_t* vseq = a.v + (size_t)s * a.T * kvstride + (size_t)g * D;
+  const float c = a.scale_log2;
+
+  BlockRegs<KTILE> regs;
+  block_load_clamped<KTILE>(regs, kseq, vseq, kvstride, min(KTILE, t_last + 1), tid);
+  block_store<KTILE>(regs, Ks[0], Vt[0], VROW, tid);
+  __syncthreads();
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int cur = it & 1;
+    const int kb = it * KTILE;
+    if (it + 1 < ntiles) {  // uniform
+      const int kn = kb + KTILE;
+      block_load_clamped<KTILE>(regs, kseq + (size_t)kn * kvstride, vseq + (size_t)kn * kvstride, kvstride,
+                                min(KTILE, t_last + 1 - kn), tid);
+    }
+    f32x16 sacc[KT];
+    qk_tiles<KT>(Ks[cur], qop, sacc, col, half);
+    float tmx = -INFINITY;
+    if (kb + KTILE - 1 > t_first) {  // uniform: a tile on the diagonal
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = kb + kt * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+          sacc[kt][i] = j <= hi ? sacc[kt][i] : -INFINITY;
+          tmx = fmaxf(tmx, sacc[kt][i]);
+        }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmx = fmaxf(tmx, sacc[kt][i]);
+    }
+    tmx = fmaxf(tmx, __shfl_xor(tmx, 32, kWave));
+    const float m_new = fmaxf(m, tmx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f((m - m_use) * c);
+    const float muc = m_use * c;
+    bf16x8 pop[KT][2];
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        sacc[kt][i] = __builtin_amdgcn_exp2f(sacc[kt][i] * c - muc);
+        sacc[kt][i + 1] = __builtin_amdgcn_exp2f(sacc[kt][i + 1] * c - muc);
+        ps0 += sacc[kt][i];
+        ps1 += sacc[kt][i + 1];
+      }
+      pop[kt][0] = to_bf16x8(sacc[kt], 0);
+      pop[kt][1] = to_bf16x8(sacc[kt], 8);
+    }
+    float ps = ps0 + ps1;
+    ps += __shfl_xor(ps, 32, kWave);
+    l = l * alpha + ps;
+    m = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    pv_tiles<KT>(Vt[cur], VROW, pop, oacc, col, half);
+    if (it + 1 < ntiles) block_store<KTILE>(regs, Ks[cur ^ 1], Vt[cur ^ 1], VROW, tid);
+    __syncthreads();
+  }
+  if (!valid) return;
+
+  const float inv_l = (l > 0.f) ? 1.0f / l : 0.f;
+  bf16_t* dst = a.out + (((size_t)s * a.T + t) * a.Hq + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      bf16x4 v4;
+      v4[0] = (__bf16)(oacc[dt][4 * i4] * inv_l);
+      v4[1] = (__bf16)(oacc[dt][4 * i4 + 1] * inv_l);
+      v4[2] = (__bf16)(oacc[dt][4 * i4 + 2] * inv_l);
+      v4[3] = (__bf16)(oacc[dt][4 * i4 + 3] * inv_l);
+      *reinterpret_cast<bf16x4*>(dst + dt * 32 + i4 * 8 + 4 * half) = v4;
+    }
+  if (a.lse != nullptr && half == 0)
+    a.lse[((size_t)s * a.T + t) * a.Hq + h] = (l > 0.f) ? (m * c + __log2f(l)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -955,7 +1137,7 @@ hipError_t launch_prefill_main_dense(const PrefillMainArgs& a, hipStream_t st) {
   const int R = a.Hq / a.G;
   const int mt = kAttnRows / R;
   const dim3 qgrid((unsigned)((a.tc + mt - 1) / mt), a.G, a.batch);
-  query_major_kernel<true><<<qgrid, 256, 0, st>>>(a);
+  dense_attn_kernel<<<qgrid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
