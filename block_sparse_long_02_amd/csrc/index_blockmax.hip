@@ -121,18 +121,32 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
     float mx[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) mx[nt] = -INFINITY;
-    // one key tile at a time keeps NT accumulators live (no spills)
+    // One key tile at a time keeps NT accumulators live (no spills).  The A
+    // operand of k-step ks + 2 is read right after the products of k-step ks
+    // issue (two operand registers in turn; the last two k-steps of a key
+    // tile read the first two of the next), and scheduling groups keep that
+    // order, so each read has two k-steps of products to land.
+    const bf16_t* abase = &kbuf[cur][col * KPAD + 8 * half];
+    bf16x8 aop[2];
+    aop[0] = *reinterpret_cast<const bf16x8*>(abase);
+    aop[1] = *reinterpret_cast<const bf16x8*>(abase + 16);
 #pragma unroll 1
     for (int kt = 0; kt < KTILES; ++kt) {
       f32x16 acc[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
-      const bf16_t* arow = &kbuf[cur][(kt * 32 + col) * KPAD + 8 * half];
+      const bf16_t* arow = abase + kt * 32 * KPAD;
+      const bf16_t* anext = abase + min(kt + 1, KTILES - 1) * 32 * KPAD;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 16 * ks);
+        const bf16x8 a = aop[ks & 1];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma32x32x16(a, qop[nt][ks], acc[nt]);
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma32x32x16(a, qop[nt][ks], ks == 0 ? f32x16{} : acc[nt]);
+        aop[ks & 1] = *reinterpret_cast<const bf16x8*>(ks + 2 < KSTEPS ? arow + 16 * (ks + 2)
+                                                                        : anext + 16 * (ks + 2 - KSTEPS));
+      }
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);   // the k-step's products
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // then the read two k-steps ahead
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)

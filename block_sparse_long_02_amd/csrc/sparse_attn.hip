@@ -110,23 +110,23 @@ __device__ __forceinline__ void stage_vt(bf16_t* Vt, int vrow, const bf16_t* __r
 
 // Whole-block K/V staging through registers with compile-time trip counts:
 // every global load of the block is issued before the first LDS write.
-template <int BS>
+template <int BS, int NTH = 256>
 struct BlockRegs {
-  u32x4 k[BS / 16];     // 16-byte chunks of K rows: chunk c = tid + 256 i
-  u32x2 v[BS / 32][4];  // 4 keys x 4 d units of V: unit u = tid + 256 i
+  u32x4 k[BS * 16 / NTH];     // 16-byte chunks of K rows: chunk c = tid + NTH i
+  u32x2 v[BS * 8 / NTH][4];   // 4 keys x 4 d units of V: unit u = tid + NTH i
 };
 
-template <int BS>
-__device__ __forceinline__ void block_load(BlockRegs<BS>& r, const bf16_t* __restrict__ kbase,
+template <int BS, int NTH = 256>
+__device__ __forceinline__ void block_load(BlockRegs<BS, NTH>& r, const bf16_t* __restrict__ kbase,
                                            const bf16_t* __restrict__ vbase, size_t stride, int tid) {
 #pragma unroll
-  for (int i = 0; i < BS / 16; ++i) {
-    const int c = tid + 256 * i;
+  for (int i = 0; i < BS * 16 / NTH; ++i) {
+    const int c = tid + NTH * i;
     r.k[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(c >> 4) * stride + (c & 15) * 8);
   }
 #pragma unroll
-  for (int i = 0; i < BS / 32; ++i) {
-    const int u = tid + 256 * i;
+  for (int i = 0; i < BS * 8 / NTH; ++i) {
+    const int u = tid + NTH * i;
     int k4, dq;
     vt_unit(u, k4, dq);
 #pragma unroll
@@ -135,16 +135,16 @@ __device__ __forceinline__ void block_load(BlockRegs<BS>& r, const bf16_t* __res
   }
 }
 
-template <int BS>
-__device__ __forceinline__ void block_store(const BlockRegs<BS>& r, bf16_t* Ks, bf16_t* Vt, int vrow, int tid) {
+template <int BS, int NTH = 256>
+__device__ __forceinline__ void block_store(const BlockRegs<BS, NTH>& r, bf16_t* Ks, bf16_t* Vt, int vrow, int tid) {
 #pragma unroll
-  for (int i = 0; i < BS / 16; ++i) {
-    const int c = tid + 256 * i;
+  for (int i = 0; i < BS * 16 / NTH; ++i) {
+    const int c = tid + NTH * i;
     *reinterpret_cast<u32x4*>(Ks + (c >> 4) * KROW + (c & 15) * 8) = r.k[i];
   }
 #pragma unroll
-  for (int i = 0; i < BS / 32; ++i) {
-    const int u = tid + 256 * i;
+  for (int i = 0; i < BS * 8 / NTH; ++i) {
+    const int u = tid + NTH * i;
     int k4, dq;
     vt_unit(u, k4, dq);
     u32x2 o[4];
@@ -545,7 +545,7 @@ __device__ __forceinline__ void accumulate_partial_row(float (*acc)[16], const u
 // the magnitude order of non-NaN bf16 equals the unsigned order of their
 // low 15 bits).
 template <int BS>
-__device__ __forceinline__ float block_vmax_part(const BlockRegs<BS>& r) {
+__device__ __forceinline__ float block_vmax_part(const BlockRegs<BS, 256>& r) {
   uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < BS / 32; ++i)
@@ -895,34 +895,39 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
 // (keys j > t); the others are wholly visible to every row.  Workgroups are
 // issued longest-first.
 // ---------------------------------------------------------------------------
-template <int NK>
-__device__ __forceinline__ void block_load_clamped(BlockRegs<NK>& r, const bf16_t* __restrict__ kbase,
+template <int NK, int NTH>
+__device__ __forceinline__ void block_load_clamped(BlockRegs<NK, NTH>& r, const bf16_t* __restrict__ kbase,
                                                    const bf16_t* __restrict__ vbase, size_t stride, int nvalid,
                                                    int tid) {
 #pragma unroll
-  for (int i = 0; i < NK / 16; ++i) {
-    const int c = tid + 256 * i;
+  for (int i = 0; i < NK * 16 / NTH; ++i) {
+    const int c = tid + NTH * i;
     r.k[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)min(c >> 4, nvalid - 1) * stride + (c & 15) * 8);
   }
 #pragma unroll
-  for (int i = 0; i < NK / 32; ++i) {
+  for (int i = 0; i < NK * 8 / NTH; ++i) {
     int k4, dq;
-    vt_unit(tid + 256 * i, k4, dq);
+    vt_unit(tid + NTH * i, k4, dq);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       r.v[i][j] = *reinterpret_cast<const u32x2*>(vbase + (size_t)min(k4 * 4 + j, nvalid - 1) * stride + dq * 4);
   }
 }
 
-__global__ __launch_bounds__(256, 2) void dense_attn_kernel(PrefillMainArgs a) {
-  constexpr int KTILE = 64;
+// 8 waves (two per SIMD, one workgroup per CU): 256 query rows share every
+// staged 128-key tile; tiles are double-buffered in LDS (137 KB).
+constexpr int kDenseRows = 256;
+constexpr int kDenseThreads = 512;
+
+__global__ __launch_bounds__(kDenseThreads, 1) void dense_attn_kernel(PrefillMainArgs a) {
+  constexpr int KTILE = 128;
   constexpr int VROW = KTILE + 4;
   constexpr int KT = KTILE / 32;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KTILE * KROW];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[2][D * VROW];
 
   const int R = a.Hq / a.G;
-  const int mt = kAttnRows / R;
+  const int mt = kDenseRows / R;
   const int g = blockIdx.y, s = blockIdx.z;
   const int tl0 = ((int)gridDim.x - 1 - (int)blockIdx.x) * mt;   // longest rows first
   const int tid = threadIdx.x;
@@ -947,9 +952,9 @@ __global__ __launch_bounds__(256, 2) void dense_attn_kernel(PrefillMainArgs a) {
   const bf16_t* vseq = a.v + (size_t)s * a.T * kvstride + (size_t)g * D;
   const float c = a.scale_log2;
 
-  BlockRegs<KTILE> regs;
-  block_load_clamped<KTILE>(regs, kseq, vseq, kvstride, min(KTILE, t_last + 1), tid);
-  block_store<KTILE>(regs, Ks[0], Vt[0], VROW, tid);
+  BlockRegs<KTILE, kDenseThreads> regs;
+  block_load_clamped<KTILE, kDenseThreads>(regs, kseq, vseq, kvstride, min(KTILE, t_last + 1), tid);
+  block_store<KTILE, kDenseThreads>(regs, Ks[0], Vt[0], VROW, tid);
   __syncthreads();
 
   float m = -INFINITY, l = 0.f;
@@ -962,8 +967,8 @@ __global__ __launch_bounds__(256, 2) void dense_attn_kernel(PrefillMainArgs a) {
     const int kb = it * KTILE;
     if (it + 1 < ntiles) {  // uniform
       const int kn = kb + KTILE;
-      block_load_clamped<KTILE>(regs, kseq + (size_t)kn * kvstride, vseq + (size_t)kn * kvstride, kvstride,
-                                min(KTILE, t_last + 1 - kn), tid);
+      block_load_clamped<KTILE, kDenseThreads>(regs, kseq + (size_t)kn * kvstride, vseq + (size_t)kn * kvstride,
+                                               kvstride, min(KTILE, t_last + 1 - kn), tid);
     }
     f32x16 sacc[KT];
     qk_tiles<KT>(Ks[cur], qop, sacc, col, half);
@@ -984,10 +989,23 @@ __global__ __launch_bounds__(256, 2) void dense_attn_kernel(PrefillMainArgs a) {
         for (int i = 0; i < 16; ++i) tmx = fmaxf(tmx, sacc[kt][i]);
     }
     tmx = fmaxf(tmx, __shfl_xor(tmx, 32, kWave));
-    const float m_new = fmaxf(m, tmx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m - m_use) * c);
-    const float muc = m_use * c;
+    // Lazy rescaling: the reference maximum m moves only when a tile's
+    // maximum exceeds it by more than 8 in the base-2 exponent, so most tiles
+    // skip rescaling the accumulators; probabilities stay below 2^8 (exact
+    // softmax is shift-invariant, and fp32 / bf16 keep their relative
+    // precision there).  A row's first keys always set m (m = -inf before).
+    const bool grow = (tmx - m) * c > 8.0f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // uniform
+      const float m_new = grow ? tmx : m;
+      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+      m = m_new;
+    }
+    const float muc = (m == -INFINITY) ? 0.f : m * c;
     bf16x8 pop[KT][2];
     float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
@@ -1004,14 +1022,9 @@ __global__ __launch_bounds__(256, 2) void dense_attn_kernel(PrefillMainArgs a) {
     }
     float ps = ps0 + ps1;
     ps += __shfl_xor(ps, 32, kWave);
-    l = l * alpha + ps;
-    m = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    l += ps;
     pv_tiles<KT>(Vt[cur], VROW, pop, oacc, col, half);
-    if (it + 1 < ntiles) block_store<KTILE>(regs, Ks[cur ^ 1], Vt[cur ^ 1], VROW, tid);
+    if (it + 1 < ntiles) block_store<KTILE, kDenseThreads>(regs, Ks[cur ^ 1], Vt[cur ^ 1], VROW, tid);
     __syncthreads();
   }
   if (!valid) return;
@@ -1135,9 +1148,9 @@ hipError_t launch_prefill_main_sparse(const PrefillMainArgs& a, hipStream_t st) 
 
 hipError_t launch_prefill_main_dense(const PrefillMainArgs& a, hipStream_t st) {
   const int R = a.Hq / a.G;
-  const int mt = kAttnRows / R;
-  const dim3 qgrid((unsigned)((a.tc + mt - 1) / mt), a.G, a.batch);
-  dense_attn_kernel<<<qgrid, 256, 0, st>>>(a);
+  const int mtd = kDenseRows / R;
+  const dim3 qgrid((unsigned)((a.tc + mtd - 1) / mtd), a.G, a.batch);
+  dense_attn_kernel<<<qgrid, kDenseThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
