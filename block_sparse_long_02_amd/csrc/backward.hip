@@ -97,8 +97,12 @@ struct BwdLds {
   static constexpr int RTW = bwd_rtw<BS>();   // row tiles per wave per step
   static constexpr int RT = NRG * RTW;        // row tiles per step
   static constexpr int SR = 32 * RT;          // (entry, head) rows per step
-  static constexpr int KR = D + 8;            // K row stride
-  static constexpr int QR = D + 8;            // q / dO row stride
+  // K, q and dO rows are read both one row per lane (16 bytes) and through
+  // the transposing LDS read (4 rows x 32 bytes per 16 lanes); a 304-byte
+  // stride (48 mod 256) keeps both patterns free of bank conflicts, where
+  // 272 bytes let the transposing read's rows overlap
+  static constexpr int KR = D + 24;           // K row stride
+  static constexpr int QR = D + 24;           // q / dO row stride
   static constexpr int DSR = BS + 8;          // dS row stride (keys)
   static constexpr int o_k = 0;
   static constexpr int o_qr = o_k + BS * KR * 2;
@@ -370,9 +374,9 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
       }
       // lane: key j of its tile, rows r0 + 8*(i/4) + 4*half + (i%4)
       bf16x8 p8[2], d8[2];
+      uint32_t dsbits[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int row = r0 + 8 * (i / 4) + 4 * half + (i % 4);
         // rows past the list carry t = -1, so one compare masks them and the
         // keys after t in the local block (exp of a masked entry is finite and dropped)
         const float e = __builtin_amdgcn_exp2f(S[u][i] * c2 - lv[i / 4][i % 4]);
@@ -380,7 +384,20 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
         const float ds = p * (dP[u][i] - dl[i / 4][i % 4]);  // the softmax scale is applied in the merges
         p8[i / 8][i % 8] = (__bf16)p;
         d8[i / 8][i % 8] = (__bf16)ds;
-        reinterpret_cast<uint16_t*>(DSr)[row * DSR + 32 * kt + dscol] = bf16_bits(ds);
+        dsbits[i] = bf16_bits(ds);
+      }
+      // dS rows in 4-byte words: lanes 2m and 2m+1 hold adjacent keys (the
+      // column swap keeps bit 0), so for rows i, i+1 the even lane writes
+      // row i's pair and the odd lane row i+1's, each taking the other half
+      // from its neighbour (a DPP swap of adjacent lanes)
+      const bool odd = col & 1;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const uint32_t lo = dsbits[i], hi = dsbits[i + 1];
+        const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? lo : hi), 0xB1, 0xF, 0xF, false);
+        const int row = r0 + 8 * (i / 4) + 4 * half + (i % 4) + (odd ? 1 : 0);
+        const uint32_t word = odd ? ((hi << 16) | recv) : ((recv << 16) | lo);
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(DSr) + row * DSR + 32 * kt + (dscol & ~1)) = word;
       }
       // dv[key][d] += P^T dO, dk[key][d] += dS^T Q over this row tile (k-slots =
       // rows: {0-3, 8-11} + 4 half of each 16-row slice, as in p8 / d8)

@@ -574,15 +574,10 @@ __device__ __forceinline__ float block_vmax_part(const BlockRegs<BS, 256>& r) {
 // for the previous tile's partial stores.
 // ---------------------------------------------------------------------------
 template <int BS>
-__global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
+__device__ __forceinline__ void kv_outer_item(const PrefillMainArgs& a, int w, bf16_t* Ks, bf16_t* Vt,
+                                              float* vmax_w) {
   constexpr int VROW = BS + 4;
   constexpr int KT = BS / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[BS * KROW];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[D * VROW];
-  __shared__ float vmax_w[4];
-
-  const int w = blockIdx.x;
-  if (w >= a.n_work[0]) return;
   const int2 wk = a.work[w];
   const long lid = wk.x;
   const int b = (int)(lid % a.nbl);
@@ -700,6 +695,16 @@ __global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
     const float2 st = make_float2(mce, l);
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, st), rs, stat_byte, 0, 0);
   }
+}
+
+template <int BS>
+__global__ __launch_bounds__(256, 2) void kv_outer_kernel(PrefillMainArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[BS * KROW];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[D * (BS + 4)];
+  __shared__ float vmax_w[4];
+  const int w = blockIdx.x;
+  if (w >= a.n_work[0]) return;
+  kv_outer_item<BS>(a, w, Ks, Vt, vmax_w);
 }
 
 // ---------------------------------------------------------------------------
