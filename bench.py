@@ -287,7 +287,8 @@ def measured_peaks(dev):
 def profile_kernels_only(args, dev):
     """The 128K prefill's inputs, one calibration copy of COPY_BYTES, then
     --steps prefills, --steps indexer KL calls and --steps main-branch
-    backward calls on the last prefill's output (each +1 warmup) and --steps
+    backward calls on the last prefill's output (each +1 warmup), --steps
+    all-blocks prefills of the same inputs (+1 warmup) and --steps
     decode steps (8 x 1M context), every kernel
     launched as in the timed steps: the workload of the --pmc counter passes
     and of the kernel-trace summary."""
@@ -310,6 +311,13 @@ def profile_kernels_only(args, dev):
     kms = indexer_kl_ms(pin, pbidx, plse, dev, stream, args.steps)
     bms, _, _, btens = backward_run(pin, pout, plse, pbidx, dev, stream, args.steps, profile=False)
     del btens
+    # the all-blocks (dense) prefill of the same inputs
+    ddn = bd.make_dims(1, PF["T"], PF["Hq"], PF["G"], index_dim=PF["di"], block_size=PF["B"], topk=PF["k"],
+                       flags=bd.MSA_DENSE)
+    dense_out = torch.empty_like(pin.q)
+    bd.msa_prefill(ddn, pin.q, pin.k, pin.v, None, None, dense_out)
+    dnms, _ = timed(lambda: bd.msa_prefill(ddn, pin.q, pin.k, pin.v, None, None, dense_out), args.steps, stream)
+    del dense_out
     dec = inputs.make_decode(DC["batch"], DC["L"], DC["Hq"], DC["G"], DC["d"], DC["di"], seed=DC["seed"],
                              device=dev)
     ddims = bd.make_dims(DC["batch"], DC["L"], DC["Hq"], DC["G"], index_dim=DC["di"], block_size=DC["B"],
@@ -321,7 +329,7 @@ def profile_kernels_only(args, dev):
     dms, _ = timed(dfn, args.steps, stream)
     stages = bd.msa_profile_end()
     print(json.dumps({"profile_steps": args.steps, "prefill_ms": round(ms, 4), "decode_ms": round(dms, 4),
-                      "indexer_kl_ms": round(kms, 4), "backward_ms": round(bms, 4),
+                      "indexer_kl_ms": round(kms, 4), "backward_ms": round(bms, 4), "dense_ms": round(dnms, 4),
                       "copy_bytes": COPY_BYTES,
                       "stage_ms": {n: round(t / c, 4) for n, (c, t) in stages.items()}}), flush=True)
 

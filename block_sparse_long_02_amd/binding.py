@@ -26,6 +26,7 @@ MSA_ERR_HIP = 5
 MSA_DENSE = 0x1
 MSA_GIVEN_INDICES = 0x2
 MSA_FORCE_SINK = 0x4
+MSA_CHECK_LENS = 0x8
 
 MSA_OP_INDEX_TOPK = 0
 MSA_OP_PREFILL = 1

@@ -40,8 +40,9 @@ int check_dims(const msa_dims* d, bool decode) {
   if (d->num_q_heads % d->num_kv_heads != 0) return MSA_ERR_INVALID_ARG;
   if (d->reserved != 0 || d->query_chunk < 0) return MSA_ERR_INVALID_ARG;
   if (!isfinite(d->softmax_scale)) return MSA_ERR_INVALID_ARG;
-  const uint32_t known = MSA_DENSE | MSA_GIVEN_INDICES | MSA_FORCE_SINK;
+  const uint32_t known = MSA_DENSE | MSA_GIVEN_INDICES | MSA_FORCE_SINK | MSA_CHECK_LENS;
   if ((d->flags & ~known) != 0) return MSA_ERR_INVALID_ARG;
+  if ((d->flags & MSA_CHECK_LENS) && !decode) return MSA_ERR_INVALID_ARG;  // a decode-only option
   if ((d->flags & MSA_DENSE) && (d->flags & MSA_GIVEN_INDICES)) return MSA_ERR_INVALID_ARG;
   // the sink is a rule of the index branch's selection
   if ((d->flags & MSA_FORCE_SINK) && (d->flags & (MSA_DENSE | MSA_GIVEN_INDICES))) return MSA_ERR_INVALID_ARG;
@@ -812,6 +813,7 @@ int msa_decode_noalloc(const msa_dims* dims, const void* q, const void* k_cache,
   DecodePlan p;
   int st = make_decode_plan(dims, &p);
   if (st != MSA_OK) return st;
+  if (dims->flags & MSA_CHECK_LENS) return MSA_ERR_INVALID_ARG;  // it would synchronize the stream
   if (p.total > kScratchBytes) return MSA_ERR_WORKSPACE;
   void* ws = nullptr;
   if ((st = scratch_for_current_device(&ws)) != MSA_OK) return st;
@@ -841,6 +843,18 @@ int run_decode(const msa_dims* dims, const DecodePlan& p, const void* q, const v
     return MSA_ERR_ALIGNMENT;
   if ((st = check_workspace(p.total, workspace, workspace_bytes)) != MSA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (dims->flags & MSA_CHECK_LENS) {
+    // opt-in host check of the lengths: one small copy and a wait on the stream
+    int32_t lens_h[256];
+    for (int s0 = 0; s0 < dims->batch; s0 += 256) {
+      const int n = dims->batch - s0 < 256 ? dims->batch - s0 : 256;
+      hipError_t e = hipMemcpyAsync(lens_h, cache_lens + s0, (size_t)n * 4, hipMemcpyDeviceToHost, s);
+      if (e == hipSuccess) e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return hip_fail(e);
+      for (int i = 0; i < n; ++i)
+        if (lens_h[i] < 1 || lens_h[i] > dims->seqlen) return MSA_ERR_INVALID_ARG;
+    }
+  }
 
   int32_t* bidx = block_idx;
   if (!dense && !given) {

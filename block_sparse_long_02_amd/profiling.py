@@ -41,6 +41,8 @@ KERNEL_SOURCES = {
                            "build.py"],
     "bwd_list_kernel": ["csrc/backward.hip", "csrc/msa_device.h", "csrc/msa_internal.h", "csrc/api.hip",
                         "build.py"],
+    "dense_attn_kernel": ["csrc/sparse_attn.hip", "csrc/msa_device.h", "csrc/msa_internal.h", "csrc/api.hip",
+                          "build.py"],
 }
 
 

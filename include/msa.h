@@ -74,6 +74,13 @@ extern "C" {
    local window].  A rule of the index branch: invalid with MSA_DENSE or
    MSA_GIVEN_INDICES. */
 #define MSA_FORCE_SINK 0x4u
+/* Decode only: validate cache_lens before any launch.  The call copies the
+   batch lengths to the host on hip_stream and waits for that stream, then
+   returns MSA_ERR_INVALID_ARG if any length lies outside [1, Lmax].  Without
+   this flag msa_decode stays fully asynchronous and clamps out-of-range
+   lengths to [1, Lmax] on the device.  Invalid with every other operation and
+   with msa_decode_noalloc (which must not synchronize). */
+#define MSA_CHECK_LENS 0x8u
 
 /* ---- operations for msa_workspace_bytes ---- */
 #define MSA_OP_INDEX_TOPK 0
@@ -93,7 +100,7 @@ typedef struct msa_dims {
   int32_t topk;          /* k >= 1, counts the forced local block; k > number of
                             visible blocks selects all of them */
   float softmax_scale;   /* <= 0 selects 1/sqrt(head_dim) */
-  uint32_t flags;        /* MSA_DENSE, MSA_GIVEN_INDICES, MSA_FORCE_SINK */
+  uint32_t flags;        /* MSA_DENSE, MSA_GIVEN_INDICES, MSA_FORCE_SINK, MSA_CHECK_LENS */
   int32_t query_chunk;   /* prefill: query tokens per internal pass, a multiple of
                             block_size; 0 = the library's default (bounds the
                             workspace).  Ignored by decode. */
@@ -160,8 +167,10 @@ int msa_prefill(const msa_dims* dims, const void* q, const void* k, const void* 
  *   idx_k_cache [batch, Lmax, index_dim] bf16    MSA_GIVEN_INDICES; may be NULL)
  *   cache_lens  [batch] int32, DEVICE: tokens in each cache INCLUDING the new
  *               one (the query sits at position cache_lens[s]-1); each value
- *               must lie in [1, Lmax] -- out-of-range values are clamped to
- *               that range on the device
+ *               must lie in [1, Lmax].  Out-of-range values are clamped to
+ *               that range on the device, unless dims->flags holds
+ *               MSA_CHECK_LENS: then the call returns MSA_ERR_INVALID_ARG
+ *               before any launch (and synchronizes hip_stream to read them)
  *   out         [batch, Hq, d] bf16 OUTPUT;  lse [batch, Hq] fp32 OUTPUT or NULL
  *   block_idx   [batch, G, topk] int32: OUTPUT (may be NULL), INPUT with
  *               MSA_GIVEN_INDICES, must be NULL with MSA_DENSE

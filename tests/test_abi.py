@@ -244,3 +244,18 @@ def test_index_scores_rejects_bad_ranges(lib):
     dd = _dims(flags=bd.MSA_DENSE)
     assert lib.msa_index_scores(ctypes.byref(dd), fake, fake, fake, 0, 2048, 16, None, 0, None) == \
         bd.MSA_ERR_INVALID_ARG
+
+
+def test_check_lens_flag_is_decode_only(lib):
+    """MSA_CHECK_LENS is accepted by decode (same workspace) and rejected by
+    every prefill-shaped operation and by the allocation-free decode."""
+    plain = _dims()
+    chk = _dims(flags=bd.MSA_CHECK_LENS)
+    assert _ws(lib, bd.MSA_OP_DECODE, chk) == _ws(lib, bd.MSA_OP_DECODE, plain)
+    for op in (bd.MSA_OP_INDEX_TOPK, bd.MSA_OP_PREFILL, bd.MSA_OP_INDEXER_KL, bd.MSA_OP_BACKWARD):
+        assert _ws(lib, op, chk) == BAD
+    fake = 0x10000
+    assert lib.msa_prefill(ctypes.byref(chk), fake, fake, fake, fake, fake, fake, None, None, fake, 1 << 40,
+                           None) == bd.MSA_ERR_INVALID_ARG
+    assert lib.msa_decode_noalloc(ctypes.byref(chk), fake, fake, fake, fake, fake, fake, fake, None, None,
+                                  None) == bd.MSA_ERR_INVALID_ARG

@@ -415,6 +415,28 @@ def test_decode_dense_and_given():
     check_attention(out2.to(torch.float64).numpy(), ores2["out"], "decode given out")
 
 
+def test_decode_check_lens():
+    """MSA_CHECK_LENS: valid lengths give the same output as without the flag;
+    a length of 0 or above the cache capacity is rejected before any launch
+    (the output buffer stays untouched)."""
+    L, Hq, G, di, B, k = 3000, 16, 4, 64, 64, 6
+    lens = [3000, 1, 777]
+    say(f"[decode check lens] L={L}")
+    dec = inputs.make_decode(len(lens), L, Hq, G, 128, di, seed=44, cache_lens=lens)
+    out, lse, bidx = gpu_decode(dec, B, k)
+    out2, lse2, bidx2 = gpu_decode(dec, B, k, flags=bd.MSA_CHECK_LENS)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(bidx, bidx2)
+    for bad in ([3000, 0, 777], [3001, 5, 6]):
+        dims = bd.make_dims(len(bad), L, Hq, G, index_dim=di, block_size=B, topk=k, flags=bd.MSA_CHECK_LENS)
+        o = torch.full((len(bad), Hq, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(bd.MSAError) as ei:
+            bd.msa_decode(dims, dec.q.cuda(), dec.k_cache.cuda(), dec.v_cache.cuda(), dec.idx_q.cuda(),
+                          dec.idx_k_cache.cuda(), torch.tensor(bad, dtype=torch.int32, device="cuda"), o)
+        assert ei.value.status == bd.MSA_ERR_INVALID_ARG
+        torch.cuda.synchronize()
+        assert (o.float() == 7.0).all()
+
+
 def test_decode_equals_prefill_row():
     T, Hq, G, di, B, k = 2048, 16, 4, 64, 128, 4
     say("[decode == prefill row]")
