@@ -33,6 +33,11 @@ namespace {
 template <int DI>
 constexpr int idx_nt() { return DI == 128 ? 3 : 4; }
 
+__device__ __forceinline__ void shift_in(f32x4& lo, f32x4& hi, float v) {
+  lo[0] = lo[1]; lo[1] = lo[2]; lo[2] = lo[3]; lo[3] = hi[0];
+  hi[0] = hi[1]; hi[1] = hi[2]; hi[2] = hi[3]; hi[3] = v;
+}
+
 // WITH_SM: also write the superblock maxima SM (chunks with rows of more
 // than kSbMinCandidates candidate blocks).
 template <int DI, int B, int NT, bool WITH_SM>
@@ -104,7 +109,9 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
   // Block maxima are written in groups of 16 consecutive blocks, 64 bytes
   // per row: both halves of the wave hold every row maximum (after the
   // cross-half shuffle), so half h keeps blocks 8h..8h+7 of the group (two
-  // float4) and each row receives 64 contiguous bytes per group.
+  // float4, filled as a shift register: each of the half's blocks enters at
+  // the end, so after its eighth the oldest sits first) and each row
+  // receives 64 contiguous bytes per group.
   f32x4 sb[NT], sb2[NT];
   float smx[NT];   // running superblock maximum over the row's candidate blocks
 #pragma unroll
@@ -148,24 +155,18 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
         __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);   // the k-step's products
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // then the read two k-steps ahead
       }
+      // a chain of three-input maxima: one VALU instruction per two scores
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) mx[nt] = fmaxf(mx[nt], fmaxf(acc[nt][i], acc[nt][i + 1]));
+        for (int i = 0; i < 16; i += 2) mx[nt] = fmaxf(fmaxf(mx[nt], acc[nt][i]), acc[nt][i + 1]);
     }
-    const int slot16 = b & 15, slot = b & 3;
+    const int slot16 = b & 15;
     const bool mine = (slot16 >> 3) == half;  // this half keeps block b
-    const bool second = (slot16 & 4) != 0;    // ... in its second float4
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float v = fmaxf(mx[nt], __shfl_xor(mx[nt], 32, kWave));
-      if (mine) {
-        f32x4& dv = second ? sb2[nt] : sb[nt];
-        if (slot == 0) dv[0] = v;
-        else if (slot == 1) dv[1] = v;
-        else if (slot == 2) dv[2] = v;
-        else dv[3] = v;
-      }
+      if (mine) shift_in(sb[nt], sb2[nt], v);
       if (WITH_SM && b < row_L[nt]) smx[nt] = fmaxf(smx[nt], v);
     }
     // a superblock is one 16-block store group: its maximum leaves with it
@@ -181,6 +182,12 @@ __global__ __launch_bounds__(256, 2) void index_blockmax_prefill_kernel(
     // the float4s holding blocks of the last group (those starting at or
     // before block b), so every store stays below round_up(nblk, 4) <= s_stride.
     if (slot16 == 15 || b == nblk - 1) {  // uniform
+      // a last, partial group: shift this half's entries into their places
+      for (int j = slot16 + 1; j < 16; ++j)
+        if ((j >> 3) == half) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) shift_in(sb[nt], sb2[nt], 0.f);
+        }
       const int first = 8 * half;         // group offset of this half's first float4
       const bool w1 = slot16 == 15 || first <= slot16;
       const bool w2 = slot16 == 15 || first + 4 <= slot16;

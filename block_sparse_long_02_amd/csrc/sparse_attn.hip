@@ -72,6 +72,24 @@ __device__ __forceinline__ void vt_unit(int u, int& k4, int& dq) {
   k4 = (u >> 7) * 4 + ((u >> 3) & 3);
 }
 
+// The all-blocks kernel's V^T tiles: each 16-key group of a row holds its
+// 4-key quads in the order 0, 2, 1, 3, so the 8 keys a lane feeds to a 16-key
+// PV slice ({4h..4h+3} and {8+4h..8+4h+3} for half h) sit in 16 contiguous
+// bytes (one 16-byte read); rows are 8 keys longer than the tile (272-byte
+// rows at 128 keys: 16 lanes reading 16 bytes at one column touch 64
+// distinct banks).
+constexpr int kVtPadQ = 8;
+__device__ __forceinline__ int vt_quad_pos(int k4) { return (k4 & ~3) | ((k4 & 1) << 1) | ((k4 >> 1) & 1); }
+
+// Its staging units: in a half-wave 8 d-quads (64 contiguous bytes of a V
+// row) x 4 key-quads, the key-quads offset by 4 for the upper 4 d-quads, so
+// the 8-byte writes at the 4 (mod 64) dword row stride fall on 32 distinct
+// bank pairs.
+__device__ __forceinline__ void vt_unit_q(int u, int& k4, int& dq) {
+  dq = (u & 7) + 8 * ((u >> 5) & 3);
+  k4 = ((u >> 3) & 3) + 4 * (((u >> 2) ^ (u >> 7)) & 1) + 8 * (u >> 8);
+}
+
 // 4x4 transpose of 16-bit lanes: o[j] = (r0[j], r1[j], r2[j], r3[j])
 __device__ __forceinline__ void transpose_4x4(const u32x2 (&r)[4], u32x2 (&o)[4]) {
   o[0] = u32x2{(r[0][0] & 0xffffu) | (r[1][0] << 16), (r[2][0] & 0xffffu) | (r[3][0] << 16)};
@@ -135,7 +153,8 @@ __device__ __forceinline__ void block_load(BlockRegs<BS, NTH>& r, const bf16_t* 
   }
 }
 
-template <int BS, int NTH = 256>
+// QUADS: the all-blocks kernel's V^T layout (vt_unit_q, vt_quad_pos).
+template <int BS, int NTH = 256, bool QUADS = false>
 __device__ __forceinline__ void block_store(const BlockRegs<BS, NTH>& r, bf16_t* Ks, bf16_t* Vt, int vrow, int tid) {
 #pragma unroll
   for (int i = 0; i < BS * 16 / NTH; ++i) {
@@ -146,11 +165,13 @@ __device__ __forceinline__ void block_store(const BlockRegs<BS, NTH>& r, bf16_t*
   for (int i = 0; i < BS * 8 / NTH; ++i) {
     const int u = tid + NTH * i;
     int k4, dq;
-    vt_unit(u, k4, dq);
+    if (QUADS) vt_unit_q(u, k4, dq);
+    else vt_unit(u, k4, dq);
     u32x2 o[4];
     transpose_4x4(r.v[i], o);
+    const int kpos = QUADS ? vt_quad_pos(k4) : k4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(Vt + (dq * 4 + j) * vrow + k4 * 4) = o[j];
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(Vt + (dq * 4 + j) * vrow + kpos * 4) = o[j];
   }
 }
 
@@ -184,17 +205,18 @@ __device__ __forceinline__ void qk_tiles(const bf16_t* Ks, const bf16x8* qop, f3
 // the four d-tiles' A operands of a slice are read together and the next
 // slice's before the current slice's products.  Each d-tile accumulates its
 // slices in key order (as one pv_step after another would).
-template <int KT>
+template <int KT, bool QUADS = false>
 __device__ __forceinline__ void pv_tiles(const bf16_t* Vt, int vrow, const bf16x8 (*p)[2], f32x16 (&o)[4], int col,
                                          int half) {
   constexpr int NS = 2 * KT;
-  const bf16_t* vr = Vt + col * vrow + 4 * half;
+  const bf16_t* vr = Vt + col * vrow + (QUADS ? 8 : 4) * half;
   bf16x8 a[2][4];
   auto load = [&](int sl, bf16x8 (&dst)[4]) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const bf16_t* r = vr + dt * 32 * vrow + 16 * sl;
-      dst[dt] = join_bf16x4(*reinterpret_cast<const u32x2*>(r), *reinterpret_cast<const u32x2*>(r + 8));
+      dst[dt] = QUADS ? *reinterpret_cast<const bf16x8*>(r)
+                      : join_bf16x4(*reinterpret_cast<const u32x2*>(r), *reinterpret_cast<const u32x2*>(r + 8));
     }
   };
   load(0, a[0]);
@@ -890,33 +912,33 @@ __global__ __launch_bounds__(256, 2) void query_major_kernel(PrefillMainArgs a) 
 
 // ---------------------------------------------------------------------------
 // Dense (all visible blocks) causal attention: the all-blocks comparison
-// mode.  A workgroup owns 128/R consecutive tokens of one (s, g) with the R
-// heads of the group (128 query rows, 32 per wave) and runs online-softmax
-// attention over 64-key tiles of [0, t_last].  K/V tiles are double-buffered
-// in LDS: the next tile's loads are issued before the current tile's
-// products and written to the other buffer after them, so one barrier per
-// tile separates the two and the load latency hides behind the products.
+// mode.  A workgroup owns 256/R consecutive tokens of one (s, g) with the R
+// heads of the group (256 query rows, 32 per wave, 8 waves) and runs
+// online-softmax attention over 128-key tiles of [0, t_last].  K/V tiles are
+// double-buffered in LDS: the next tile's loads are issued before the current
+// tile's products and written to the other buffer after them, so one barrier
+// per tile separates the two and the load latency hides behind the products.
 // Only tiles that reach past the first token of the workgroup are masked
 // (keys j > t); the others are wholly visible to every row.  Workgroups are
 // issued longest-first.
 // ---------------------------------------------------------------------------
+// Loads of one K/V tile through buffer resources whose base is the tile's
+// first row and whose size ends at the sequence's last row: the lanes' byte
+// offsets are computed once (tile-invariant), the row steps between a
+// thread's chunks are scalar offsets, and rows past the sequence read as 0.
+// Rows past the last query row of the workgroup are read as they are: the
+// causal mask gives them probability 0.
 template <int NK, int NTH>
-__device__ __forceinline__ void block_load_clamped(BlockRegs<NK, NTH>& r, const bf16_t* __restrict__ kbase,
-                                                   const bf16_t* __restrict__ vbase, size_t stride, int nvalid,
-                                                   int tid) {
+__device__ __forceinline__ void block_load_buf(BlockRegs<NK, NTH>& r, __amdgpu_buffer_rsrc_t rk,
+                                               __amdgpu_buffer_rsrc_t rv, int koff, const int* voff, int rowbytes) {
 #pragma unroll
-  for (int i = 0; i < NK * 16 / NTH; ++i) {
-    const int c = tid + NTH * i;
-    r.k[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)min(c >> 4, nvalid - 1) * stride + (c & 15) * 8);
-  }
+  for (int i = 0; i < NK * 16 / NTH; ++i)
+    r.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, i * (NTH / 16) * rowbytes, 0));
 #pragma unroll
-  for (int i = 0; i < NK * 8 / NTH; ++i) {
-    int k4, dq;
-    vt_unit(tid + NTH * i, k4, dq);
+  for (int i = 0; i < NK * 8 / NTH; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      r.v[i][j] = *reinterpret_cast<const u32x2*>(vbase + (size_t)min(k4 * 4 + j, nvalid - 1) * stride + dq * 4);
-  }
+      r.v[i][j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff[i], j * rowbytes, 0));
 }
 
 // 8 waves (two per SIMD, one workgroup per CU): 256 query rows share every
@@ -926,7 +948,7 @@ constexpr int kDenseThreads = 512;
 
 __global__ __launch_bounds__(kDenseThreads, 1) void dense_attn_kernel(PrefillMainArgs a) {
   constexpr int KTILE = 128;
-  constexpr int VROW = KTILE + 4;
+  constexpr int VROW = KTILE + kVtPadQ;
   constexpr int KT = KTILE / 32;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KTILE * KROW];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[2][D * VROW];
@@ -958,8 +980,25 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_attn_kernel(PrefillMai
   const float c = a.scale_log2;
 
   BlockRegs<KTILE, kDenseThreads> regs;
-  block_load_clamped<KTILE, kDenseThreads>(regs, kseq, vseq, kvstride, min(KTILE, t_last + 1), tid);
-  block_store<KTILE, kDenseThreads>(regs, Ks[0], Vt[0], VROW, tid);
+  const int rowbytes = (int)(kvstride * 2);
+  const int koff = (tid >> 4) * rowbytes + (tid & 15) * 16;
+  int voff[KTILE * 8 / kDenseThreads];
+#pragma unroll
+  for (int i = 0; i < KTILE * 8 / kDenseThreads; ++i) {
+    int k4, dq;
+    vt_unit_q(tid + kDenseThreads * i, k4, dq);
+    voff[i] = k4 * 4 * rowbytes + dq * 8;
+  }
+  auto load_tile = [&](int kn) {
+    const int nrows = min(KTILE, a.T - kn);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(kseq + (size_t)kn * kvstride), (short)0, nrows * rowbytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(vseq + (size_t)kn * kvstride), (short)0, nrows * rowbytes, kBufferWord3);
+    block_load_buf<KTILE, kDenseThreads>(regs, rk, rv, koff, voff, rowbytes);
+  };
+  load_tile(0);
+  block_store<KTILE, kDenseThreads, true>(regs, Ks[0], Vt[0], VROW, tid);
   __syncthreads();
 
   float m = -INFINITY, l = 0.f;
@@ -970,11 +1009,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_attn_kernel(PrefillMai
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
     const int kb = it * KTILE;
-    if (it + 1 < ntiles) {  // uniform
-      const int kn = kb + KTILE;
-      block_load_clamped<KTILE, kDenseThreads>(regs, kseq + (size_t)kn * kvstride, vseq + (size_t)kn * kvstride,
-                                               kvstride, min(KTILE, t_last + 1 - kn), tid);
-    }
+    if (it + 1 < ntiles) load_tile(kb + KTILE);  // uniform
     f32x16 sacc[KT];
     qk_tiles<KT>(Ks[cur], qop, sacc, col, half);
     float tmx = -INFINITY;
@@ -1028,8 +1063,8 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_attn_kernel(PrefillMai
     float ps = ps0 + ps1;
     ps += __shfl_xor(ps, 32, kWave);
     l += ps;
-    pv_tiles<KT>(Vt[cur], VROW, pop, oacc, col, half);
-    if (it + 1 < ntiles) block_store<KTILE, kDenseThreads>(regs, Ks[cur ^ 1], Vt[cur ^ 1], VROW, tid);
+    pv_tiles<KT, true>(Vt[cur], VROW, pop, oacc, col, half);
+    if (it + 1 < ntiles) block_store<KTILE, kDenseThreads, true>(regs, Ks[cur ^ 1], Vt[cur ^ 1], VROW, tid);
     __syncthreads();
   }
   if (!valid) return;
