@@ -90,6 +90,25 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
 template <int BS>
 constexpr int bwd_rtw() { return BS == 128 ? MSA_BWD_RTW128 : 1; }
 
+// K, q and dO rows in LDS are 256 bytes with 16-byte chunk c of row r stored
+// at chunk position c ^ bwd_swz(r).  They are read one row per lane (16
+// consecutive rows, one chunk: 16 distinct positions, as bwd_swz is a
+// bijection of r mod 16) and through the transposing read, whose 32 lanes
+// take 64 bytes (chunks 4m .. 4m+3) of 4 rows 4n .. 4n+3: the positions
+// 4 (m ^ (r & 3)) + ((c & 3) ^ (r >> 2 & 3)) are 16 distinct, so all 64 banks
+// are hit once.  (A padded row stride satisfies only one of the two
+// patterns: 304 bytes left the transposing read 2-way conflicted.)
+__device__ __forceinline__ int bwd_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// Element offset of the lane's 8-byte word for the transposing read of the
+// rows row0 + 0..7 at d tile dt (row0 a multiple of 8): the lane's row is
+// row0 + 4 (lane / 32) + (lane / 4) % 4, its 8 bytes the (lane % 4)-th of the
+// row's 32 bytes at column 32 dt + 16 ((lane / 16) % 2).
+__device__ __forceinline__ int bwd_tr_off(int lane, int row0, int dt) {
+  const int r = row0 + 4 * (lane >> 5) + ((lane >> 2) & 3);
+  const int c = 4 * dt + 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
+  return r * D + ((c ^ bwd_swz(r)) * 8) + 4 * (lane & 1);
+}
+
 template <int BS>
 struct BwdLds {
   static constexpr int KT = BS / 32;          // key tiles of the block
@@ -97,12 +116,9 @@ struct BwdLds {
   static constexpr int RTW = bwd_rtw<BS>();   // row tiles per wave per step
   static constexpr int RT = NRG * RTW;        // row tiles per step
   static constexpr int SR = 32 * RT;          // (entry, head) rows per step
-  // K, q and dO rows are read both one row per lane (16 bytes) and through
-  // the transposing LDS read (4 rows x 32 bytes per 16 lanes); a 304-byte
-  // stride (48 mod 256) keeps both patterns free of bank conflicts, where
-  // 272 bytes let the transposing read's rows overlap
-  static constexpr int KR = D + 24;           // K row stride
-  static constexpr int QR = D + 24;           // q / dO row stride
+  // K, q and dO rows: 256 bytes, swizzled by chunk (bwd_swz)
+  static constexpr int KR = D;                // K row stride
+  static constexpr int QR = D;                // q / dO row stride
   static constexpr int DSR = BS + 8;          // dS row stride (keys)
   static constexpr int o_k = 0;
   static constexpr int o_qr = o_k + BS * KR * 2;
@@ -177,7 +193,7 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
 #pragma unroll
   for (int i = 0; i < NKC; ++i) {
     const int c = tid + 256 * i;
-    *reinterpret_cast<u32x4*>(Ks + (c >> 4) * KR + (c & 15) * 8) = kc[i];
+    *reinterpret_cast<u32x4*>(Ks + (c >> 4) * KR + (((c & 15) ^ bwd_swz(c >> 4)) * 8)) = kc[i];
   }
 
   const int nr = count * R;  // (entry, head) rows of the list, row = entry position * R + head
@@ -209,6 +225,11 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
   constexpr int RPP = CPR / 2;                   // rows per part
   constexpr bool kAhead = NPART == 1;
   const int r8 = tid >> 3, c8 = tid & 7;
+  // a thread's rows r8 + 32 j share r8 mod 16: its first instruction takes
+  // the chunk half that puts rows r8 and r8 + 1 (one 16-lane group) on
+  // different position halves
+  const int hsel = ((bwd_swz(r8) >> 3) ^ r8) & 1;
+  const int pos8 = c8 ^ (bwd_swz(r8) & 7);  // position of chunk c8 (+8) within its half
   const int step_q = SR / R, step_r = SR % R;  // list-position and head advance per step
   int cur_p[NRW], cur_r[NRW];                   // row of the next entry load, per row slot
   int ent[NRW], ent_r[NRW];                     // that load's result and its head
@@ -260,8 +281,8 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
       const size_t grow = row_of(row_e[j], row_r[j]);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        qs[2 * jj + h] = *reinterpret_cast<const u32x4*>(l.q + grow * D + (c8 + 8 * h) * 8);
-        os[2 * jj + h] = *reinterpret_cast<const u32x4*>(a.dout + grow * D + (c8 + 8 * h) * 8);
+        qs[2 * jj + h] = *reinterpret_cast<const u32x4*>(l.q + grow * D + (c8 + 8 * (h ^ hsel)) * 8);
+        os[2 * jj + h] = *reinterpret_cast<const u32x4*>(a.dout + grow * D + (c8 + 8 * (h ^ hsel)) * 8);
       }
     }
     if (part0 == 0) {
@@ -284,8 +305,10 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
       const int row = r8 + 32 * (part0 * RPP + jj);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        *reinterpret_cast<u32x4*>(Qr + row * QR + (c8 + 8 * h) * 8) = qs[2 * jj + h];
-        *reinterpret_cast<u32x4*>(Or + row * QR + (c8 + 8 * h) * 8) = os[2 * jj + h];
+        // chunk c8 + 8 (h ^ hsel) sits at position (c8 + 8 (h ^ hsel)) ^ bwd_swz(row)
+        const int pos = pos8 + 8 * ((h ^ hsel) ^ (bwd_swz(r8) >> 3));
+        *reinterpret_cast<u32x4*>(Qr + row * QR + pos * 8) = qs[2 * jj + h];
+        *reinterpret_cast<u32x4*>(Or + row * QR + pos * 8) = os[2 * jj + h];
       }
     }
     if (part0 == 0 && c8 < NRW) {
@@ -337,7 +360,7 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
     }
 
     const int j = kb + 32 * kt + col;
-    const int tro = tr_lane_off(lane, QR);
+    const int fcol = bwd_swz(col);  // rows r0 + col, r0 a multiple of 32
     // dS rows keep each 16-key group in the order 0-3, 8-11, 4-7, 12-15 (bits
     // 2 and 3 of the key swapped), the k-slot order of K read through the
     // transposing LDS read: lane half h then reads its 8 keys contiguously
@@ -353,10 +376,9 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
       dP[u] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        S[u] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Qr + (r0 + col) * QR + 16 * ks + 8 * half), kreg[ks],
-                            S[u]);
-        dP[u] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Or + (r0 + col) * QR + 16 * ks + 8 * half), vreg[ks],
-                             dP[u]);
+        const int qo = (r0 + col) * QR + (((2 * ks + half) ^ fcol) * 8);
+        S[u] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Qr + qo), kreg[ks], S[u]);
+        dP[u] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Or + qo), vreg[ks], dP[u]);
       }
     }
 #pragma unroll
@@ -405,16 +427,15 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
       for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int o0 = (r0 + 16 * ks) * QR + 32 * dt + tro;
-          const bf16x8 ob = join_bf16x4(lds_read_tr16(Or + o0), lds_read_tr16(Or + o0 + 8 * QR));
-          const bf16x8 qb = join_bf16x4(lds_read_tr16(Qr + o0), lds_read_tr16(Qr + o0 + 8 * QR));
+          const int o0 = bwd_tr_off(lane, r0 + 16 * ks, dt), o1 = bwd_tr_off(lane, r0 + 16 * ks + 8, dt);
+          const bf16x8 ob = join_bf16x4(lds_read_tr16(Or + o0), lds_read_tr16(Or + o1));
+          const bf16x8 qb = join_bf16x4(lds_read_tr16(Qr + o0), lds_read_tr16(Qr + o1));
           dv[dt] = mfma32x32x16(p8[ks], ob, dv[dt]);
           dk[dt] = mfma32x32x16(d8[ks], qb, dk[dt]);
         }
       }
     }
     __syncthreads();  // dS rows of the step complete
-    const int trk = tr_lane_off(lane, KR);
     // dq^T[d][row] = sum over the block's keys of K^T[d][key] dS^T[key][row]:
     // the wave's RT (row tile, d tile) pairs share one row tile, whose dS
     // operands are read once; each d tile's K^T operands are read before its
@@ -433,8 +454,8 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
       bf16x8 ka[BS / 16];
 #pragma unroll
       for (int ks = 0; ks < BS / 16; ++ks) {
-        const int o0 = 16 * ks * KR + 32 * dt + trk;
-        ka[ks] = join_bf16x4(lds_read_tr16(Ks + o0), lds_read_tr16(Ks + o0 + 8 * KR));
+        ka[ks] = join_bf16x4(lds_read_tr16(Ks + bwd_tr_off(lane, 16 * ks, dt)),
+                             lds_read_tr16(Ks + bwd_tr_off(lane, 16 * ks + 8, dt)));
       }
       f32x16 acc = {};
 #pragma unroll
