@@ -91,6 +91,41 @@ def test_prefill_32k():
     torch.cuda.empty_cache()
 
 
+def test_dense_32k_sampled():
+    """The all-blocks mode at the 32K workload's shape (64 q heads, 8 groups,
+    d 128): sampled rows against the oracle's attention over every visible
+    key, t in [0, 32767] including the first and last rows of key tiles."""
+    T = 32768
+    say("[dense 32K] sampled rows")
+    dev = torch.device("cuda")
+    pin = inputs.make_prefill(T, 64, 8, 128, 128, seed=3, device=dev)
+    dims = bd.make_dims(1, T, 64, 8, index_dim=128, block_size=128, topk=1, flags=bd.MSA_DENSE)
+    out = torch.empty_like(pin.q)
+    lse = torch.empty((1, T, 64), dtype=torch.float32, device=dev)
+    bd.msa_prefill(dims, pin.q, pin.k, pin.v, None, None, out, lse=lse)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(33)
+    rows = sorted(set(int(t) for t in rng.integers(0, T, 10)) | {0, 127, 128, 255, 256, T - 129, T - 1})
+    K = pin.k[0].cpu().to(torch.float64).numpy()
+    V = pin.v[0].cpu().to(torch.float64).numpy()
+    scale = orc.default_scale(128)
+    o_ref, l_ref = [], []
+    for t in rows:
+        Q = pin.q[0, t].cpu().to(torch.float64).numpy()
+        o_t, l_t = np.zeros((64, 128)), np.zeros(64)
+        for g in range(8):
+            o_t[8 * g:8 * g + 8], l_t[8 * g:8 * g + 8] = orc.attention_row(
+                Q[8 * g:8 * g + 8], K[:, g], V[:, g], np.arange(t + 1), scale)
+        o_ref.append(o_t)
+        l_ref.append(l_t)
+    o_got = np.stack([out[0, t].cpu().double().numpy() for t in rows])
+    check_attention(o_got, np.stack(o_ref), "dense 32K sampled rows")
+    l_got = np.stack([lse[0, t].cpu().double().numpy() for t in rows])
+    assert np.abs(l_got - np.stack(l_ref)).max() < 1e-3
+    del pin, out, lse
+    torch.cuda.empty_cache()
+
+
 def test_prefill_1m_needles():
     T, B, k, nneedle = 1 << 20, 128, 16, 64
     say("[prefill 1M needles]")

@@ -269,6 +269,24 @@ def test_dense_mode(T, Hq, G, B):
     assert np.abs(l_got - l_ref).max() < 1e-3
 
 
+def test_dense_mode_batch2_chunked():
+    """All-blocks mode with two sequences, a ragged length and query chunks of
+    512 tokens: each sequence's key tiles are addressed from its own base and
+    rows past the sequence end read as zeros (T = 1100 ends inside a tile)."""
+    T, Hq, G, B = 1100, 16, 2, 64
+    say(f"[prefill dense batch 2, chunks] T={T} Hq={Hq} G={G}")
+    inp = inputs.make_prefill(T, Hq, G, 128, 64, batch=2, seed=13)
+    out, lse, _ = gpu_prefill(inp, B, 1, flags=bd.MSA_DENSE, query_chunk=512)
+    rows = [(s, t) for s in range(2) for t in list(range(0, T, 37)) + [511, 512, T - 1]]
+    ores = orc.prefill(inp.q, inp.k, inp.v, inp.idx_q, inp.idx_k, B, 1, rows=rows, dense=True)
+    o_ref = np.stack([ores["out"][r] for r in rows])
+    o_got = np.stack([out[s, t].to(torch.float64).numpy() for s, t in rows])
+    check_attention(o_got, o_ref, "dense out, batch 2")
+    l_ref = np.stack([ores["lse"][r] for r in rows])
+    l_got = np.stack([lse[s, t].to(torch.float64).numpy() for s, t in rows])
+    assert np.abs(l_got - l_ref).max() < 1e-3
+
+
 def test_all_blocks_selected_matches_dense_mode():
     T, Hq, G, B = 900, 16, 4, 64
     say(f"[prefill k>=nb vs dense] T={T}")
