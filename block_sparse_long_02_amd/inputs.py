@@ -82,7 +82,8 @@ class DecodeInputs:
 def make_prefill(T: int, Hq: int, G: int, d: int, di: int, *, batch: int = 1,
                  seed: int = 0, device="cpu", idx_mode: str = "gaussian",
                  block_size: int | None = None, skew_std: float = 0.0,
-                 needles: int = 0, needle_preset: str = "separable") -> PrefillInputs:
+                 needles: int = 0, needle_preset: str = "separable",
+                 needle_q_mean: float = 8.0) -> PrefillInputs:
     """Prefill tensors.
 
     idx_mode   'gaussian' (iid N(0,1)) or 'integer' (uniform in [-3, 3]; exact
@@ -92,9 +93,10 @@ def make_prefill(T: int, Hq: int, G: int, d: int, di: int, *, batch: int = 1,
                popularity).  Needs block_size.
     needles    number of distinct aligned blocks whose idx_k rows are shifted
                along a direction u.  'separable': u is a seeded unit vector,
-               idx_q = N(0,1) + 8u (so u is idx_q's mean direction, and every
-               row's projection q.u = 8 + N(0,1) stays well above 0 even over
-               millions of rows) and needle keys = N(0,1) + 2 sqrt(di) u.
+               idx_q = N(0,1) + needle_q_mean u (so u is idx_q's mean direction;
+               at the default 8 every row's projection q.u = 8 + N(0,1) stays
+               well above 0 even over millions of rows, at 4 about 1 row in
+               4 000 falls below 0.5) and needle keys = N(0,1) + 2 sqrt(di) u.
                'literal': idx_q iid N(0,1), u = normalised mean of the drawn
                idx_q rows, needle keys += 2u.
     """
@@ -120,8 +122,9 @@ def make_prefill(T: int, Hq: int, G: int, d: int, di: int, *, batch: int = 1,
         for r0 in range(0, fq.shape[0], step):
             r1 = min(fq.shape[0], r0 + step)
             x = torch.randn((r1 - r0, di), generator=gen, device=device, dtype=torch.float32)
-            fq[r0:r1].copy_(x + 8.0 * u)
+            fq[r0:r1].copy_(x + needle_q_mean * u)
         meta["needle_dir"] = u.cpu()
+        meta["needle_q_mean"] = needle_q_mean
     else:
         idx_q = gaussian_bf16((batch, T, G, di), gen, device)
 
