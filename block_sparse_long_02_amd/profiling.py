@@ -11,6 +11,10 @@
          --kernels k1,k2 --title T --command C --out <md>
       -> per-dispatch SQ counters of the kernels (summed over the shader
          engines) with instruction mix and MFMA-busy ratios
+  python -m block_sparse_long_02_amd.profiling clocks --dir <dir> --kernels k1,k2
+         --title T --command C --out <md>
+      -> the clock each kernel ran at (GRBM_GUI_ACTIVE per XCD over the
+         dispatch's duration) and its MFMA-busy share of those cycles
 
 The traffic file records a hash of the kernel's sources; bench.py reports the
 traffic only while the sources still match.
@@ -141,6 +145,45 @@ def counters_md(dirs, kernels, title: str, command: str) -> str:
     return "\n".join(out) + "\n"
 
 
+N_XCDS = 8
+
+
+def _dispatch_clocks(rows, kernel: str):
+    """Per dispatch of `kernel`: (seconds, GRBM_GUI_ACTIVE per XCD, MFMA busy cycles per SIMD)."""
+    per = {}
+    for r in rows:
+        if kernel not in r["Kernel_Name"]:
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        d = per.setdefault(key, {"dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    out = []
+    for d in per.values():
+        if d["dur"] > 0 and "GRBM_GUI_ACTIVE" in d:
+            out.append((d["dur"], d["GRBM_GUI_ACTIVE"] / N_XCDS, d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / N_SIMDS))
+    return out
+
+
+def clocks_md(d: str, kernels, title: str, command: str) -> str:
+    rows = _counter_rows(d)
+    out = [f"# {title}", "", "Command (from the repository root, on one MI355X):", "", "```", command, "```", "",
+           f"Clock = GRBM_GUI_ACTIVE / {N_XCDS} XCDs / dispatch duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+           f"{N_SIMDS} SIMDs / those cycles; MFMA peak at that clock = 1024 flop per SIMD per cycle x {N_SIMDS} "
+           "SIMDs. Averages over the kernel's dispatches.", "",
+           "| kernel | dispatches | avg ms | clock GHz | MFMA busy | bf16 MFMA peak at that clock, PFLOP/s |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for k in kernels:
+        v = _dispatch_clocks(rows, k)
+        if not v:
+            continue
+        dur = sum(x[0] for x in v) / len(v)
+        clk = sum(x[1] / x[0] for x in v) / len(v)
+        busy = sum(x[2] / x[1] for x in v) / len(v)
+        out.append(f"| {k} | {len(v)} | {dur * 1e3:.3f} | {clk / 1e9:.3f} | {busy:.3f} | "
+                   f"{clk * 1024 * N_SIMDS / 1e15:.3f} |")
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -162,7 +205,19 @@ def main():
     s3.add_argument("--title", required=True)
     s3.add_argument("--command", required=True)
     s3.add_argument("--out")
+    s4 = sub.add_parser("clocks")
+    s4.add_argument("--dir", required=True)
+    s4.add_argument("--kernels", required=True)
+    s4.add_argument("--title", required=True)
+    s4.add_argument("--command", required=True)
+    s4.add_argument("--out")
     a = ap.parse_args()
+    if a.cmd == "clocks":
+        md = clocks_md(a.dir, a.kernels.split(","), a.title, a.command)
+        if a.out:
+            open(a.out, "w").write(md)
+        print(md)
+        return
     if a.cmd == "counters":
         md = counters_md(a.dirs, a.kernels.split(","), a.title, a.command)
         if a.out:
