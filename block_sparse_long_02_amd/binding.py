@@ -27,6 +27,7 @@ MSA_DENSE = 0x1
 MSA_GIVEN_INDICES = 0x2
 MSA_FORCE_SINK = 0x4
 MSA_CHECK_LENS = 0x8
+MSA_ONE_PASS_INDEX = 0x10
 
 MSA_OP_INDEX_TOPK = 0
 MSA_OP_PREFILL = 1

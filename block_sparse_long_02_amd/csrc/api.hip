@@ -40,9 +40,12 @@ int check_dims(const msa_dims* d, bool decode) {
   if (d->num_q_heads % d->num_kv_heads != 0) return MSA_ERR_INVALID_ARG;
   if (d->reserved != 0 || d->query_chunk < 0) return MSA_ERR_INVALID_ARG;
   if (!isfinite(d->softmax_scale)) return MSA_ERR_INVALID_ARG;
-  const uint32_t known = MSA_DENSE | MSA_GIVEN_INDICES | MSA_FORCE_SINK | MSA_CHECK_LENS;
+  const uint32_t known = MSA_DENSE | MSA_GIVEN_INDICES | MSA_FORCE_SINK | MSA_CHECK_LENS | MSA_ONE_PASS_INDEX;
   if ((d->flags & ~known) != 0) return MSA_ERR_INVALID_ARG;
   if ((d->flags & MSA_CHECK_LENS) && !decode) return MSA_ERR_INVALID_ARG;  // a decode-only option
+  // a prefill form of the index branch
+  if ((d->flags & MSA_ONE_PASS_INDEX) && (decode || (d->flags & (MSA_DENSE | MSA_GIVEN_INDICES))))
+    return MSA_ERR_INVALID_ARG;
   if ((d->flags & MSA_DENSE) && (d->flags & MSA_GIVEN_INDICES)) return MSA_ERR_INVALID_ARG;
   // the sink is a rule of the index branch's selection
   if ((d->flags & MSA_FORCE_SINK) && (d->flags & (MSA_DENSE | MSA_GIVEN_INDICES))) return MSA_ERR_INVALID_ARG;
@@ -52,6 +55,7 @@ int check_dims(const msa_dims* d, bool decode) {
   const int R = d->num_q_heads / d->num_kv_heads;
   if (R > (decode ? 16 : msa::kAttnRows)) return MSA_ERR_UNSUPPORTED;
   if (!decode && d->query_chunk > 0 && d->query_chunk % d->block_size != 0) return MSA_ERR_INVALID_ARG;
+  if ((d->flags & MSA_ONE_PASS_INDEX) && d->topk > msa::kOnePassMaxTopk) return MSA_ERR_UNSUPPORTED;
   return MSA_OK;
 }
 
@@ -69,6 +73,7 @@ struct PrefillPlan {
   int s_stride_max = 0, sm_stride_max = 0;
   long max_work = 0;
   bool with_scores = false, with_main = false;
+  bool one_pass = false;  // MSA_ONE_PASS_INDEX: the index branch writes no score table
   size_t off_S = 0, off_SM = 0, off_bidx = 0, off_cnt = 0, off_offs = 0, off_bsum = 0, off_rinfo = 0, off_epos = 0,
          off_entries = 0, off_work = 0, off_nwork = 0, off_pO = 0, off_pS = 0;
   size_t total = 0;
@@ -83,7 +88,8 @@ int sm_stride_for(int L) {
 size_t per_token_bytes(const msa_dims* d, const PrefillPlan& p) {
   const size_t G = (size_t)d->num_kv_heads;
   size_t b = 0;
-  if (p.with_scores) b += G * ((size_t)p.s_stride_max + (size_t)p.sm_stride_max) * 4 + G * (size_t)d->topk * 4;
+  if (p.with_scores && !p.one_pass) b += G * ((size_t)p.s_stride_max + (size_t)p.sm_stride_max) * 4;
+  if (p.with_scores && !(p.one_pass && !p.with_main)) b += G * (size_t)d->topk * 4;
   if (p.with_main) b += G * 4 + G * (size_t)p.KS * (4 + 4 + (size_t)p.R * (128 * 2 + 8));
   return b;
 }
@@ -91,7 +97,7 @@ size_t per_token_bytes(const msa_dims* d, const PrefillPlan& p) {
 int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
   int st = check_dims(d, false);
   if (st != MSA_OK) return st;
-  if (index_only && (d->flags & ~MSA_FORCE_SINK) != 0) return MSA_ERR_INVALID_ARG;
+  if (index_only && (d->flags & ~(MSA_FORCE_SINK | MSA_ONE_PASS_INDEX)) != 0) return MSA_ERR_INVALID_ARG;
   const int T = d->seqlen, B = d->block_size, G = d->num_kv_heads;
   p->nb = (T + B - 1) / B;
   p->KS = d->topk < p->nb ? d->topk : p->nb;
@@ -100,6 +106,7 @@ int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
   p->mt = msa::kAttnRows / p->R;
   p->with_scores = index_only || !(d->flags & (MSA_DENSE | MSA_GIVEN_INDICES));
   p->with_main = !index_only && !(d->flags & MSA_DENSE);
+  p->one_pass = (d->flags & MSA_ONE_PASS_INDEX) != 0;
   const int Lmax = (T - 1) / B;
   // rows of the block-score table start 64-byte aligned (the index kernel
   // stores 16 block maxima per row at a time)
@@ -149,9 +156,12 @@ int make_prefill_plan(const msa_dims* d, bool index_only, PrefillPlan* p) {
   Layout L;
   const size_t nb_ = (size_t)d->batch, Tc = (size_t)p->Tc, G_ = (size_t)G;
   if (p->with_scores) {
-    p->off_S = L.add(nb_ * Tc * G_ * (size_t)p->s_stride_max * 4);
-    p->off_SM = L.add(nb_ * Tc * G_ * (size_t)p->sm_stride_max * 4);
-    p->off_bidx = L.add(nb_ * Tc * G_ * (size_t)d->topk * 4);
+    if (!p->one_pass) {
+      p->off_S = L.add(nb_ * Tc * G_ * (size_t)p->s_stride_max * 4);
+      p->off_SM = L.add(nb_ * Tc * G_ * (size_t)p->sm_stride_max * 4);
+    }
+    // the one-pass msa_index_topk needs no workspace at all
+    if (!(p->one_pass && index_only)) p->off_bidx = L.add(nb_ * Tc * G_ * (size_t)d->topk * 4);
   }
   if (p->with_main) {
     const size_t nwin = ((size_t)p->Tc + msa::kFwdListWindow - 1) / msa::kFwdListWindow;
@@ -426,6 +436,12 @@ hipError_t run_index_chunk(const msa_dims* d, const PrefillPlan& p, const void* 
                            const void* idx_k, void* ws, int t0, int tc, int32_t* bidx, long bidx_rows,
                            int t_off, hipStream_t st) {
   const int B = d->block_size;
+  if (p.one_pass) {
+    msa::prof_mark(st, MSA_STAGE_INDEX_PREFILL);
+    return msa::launch_index_topk_one_pass(static_cast<const uint16_t*>(idx_q), static_cast<const uint16_t*>(idx_k),
+                                           bidx, bidx_rows, t_off, d->batch, d->seqlen, d->num_kv_heads,
+                                           d->index_dim, B, d->topk, (d->flags & MSA_FORCE_SINK) != 0, t0, tc, st);
+  }
   const int Lc = (t0 + tc - 1) / B;
   const int s_stride = (int)round_up((size_t)(Lc > 1 ? Lc : 1), 16);
   const int sm_stride = sm_stride_for(Lc);

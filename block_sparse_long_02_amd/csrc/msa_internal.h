@@ -35,6 +35,15 @@ hipError_t launch_index_blockmax_prefill(const uint16_t* idx_q, const uint16_t* 
                                          int batch, int T, int G, int di, int B, int t0, int tc,
                                          int s_stride, float* SM, int sm_stride, hipStream_t st);
 
+// ---- Index Branch in one pass (scores, Block-Max, Top-k; no score table) ----
+// Each row keeps its best want = m - 1 (less the forced sink) candidates in
+// 16 register slots, so topk is at most kOnePassMaxTopk.  Output rows as in
+// launch_topk_prefill.
+constexpr int kOnePassMaxTopk = 17;
+hipError_t launch_index_topk_one_pass(const uint16_t* idx_q, const uint16_t* idx_k, int32_t* bidx, long bidx_rows,
+                                      int bidx_t_off, int batch, int T, int G, int di, int B, int k, bool sink,
+                                      int t0, int tc, hipStream_t st);
+
 // ---- Top-k with the forced local block ----
 // prefill rows: (s, t in [t0, t0+tc), g); output row address
 //   bidx + ((s*bidx_rows + (t - bidx_t_off))*G + g)*k

@@ -81,6 +81,19 @@ extern "C" {
    lengths to [1, Lmax] on the device.  Invalid with every other operation and
    with msa_decode_noalloc (which must not synchronize). */
 #define MSA_CHECK_LENS 0x8u
+/* Index Branch in one pass, for msa_index_topk and msa_prefill: every key
+   block's maximum score is offered at once to a running list of the row's
+   best candidates held in registers, so no block-score table is written and
+   no separate top-k launch runs [hyper.ai paper page 2606.13392, 方法
+   (Method): the index scores, Block-Max and Top-k with the forced local
+   block].  The selection is bit-identical to the default two-pass path,
+   which writes a table of one fp32 per row and candidate block (about 2.2 GB
+   for 128K tokens, 8 groups, B = 128) and is the faster of the two; this path
+   trades that speed for a smaller workspace (msa_index_topk needs none).
+   topk must be <= 17, else MSA_ERR_UNSUPPORTED.  Invalid with MSA_DENSE,
+   MSA_GIVEN_INDICES, decode, msa_index_scores, msa_indexer_kl and
+   msa_prefill_backward. */
+#define MSA_ONE_PASS_INDEX 0x10u
 
 /* ---- operations for msa_workspace_bytes ---- */
 #define MSA_OP_INDEX_TOPK 0
@@ -100,7 +113,8 @@ typedef struct msa_dims {
   int32_t topk;          /* k >= 1, counts the forced local block; k > number of
                             visible blocks selects all of them */
   float softmax_scale;   /* <= 0 selects 1/sqrt(head_dim) */
-  uint32_t flags;        /* MSA_DENSE, MSA_GIVEN_INDICES, MSA_FORCE_SINK, MSA_CHECK_LENS */
+  uint32_t flags;        /* MSA_DENSE, MSA_GIVEN_INDICES, MSA_FORCE_SINK, MSA_CHECK_LENS,
+                            MSA_ONE_PASS_INDEX */
   int32_t query_chunk;   /* prefill: query tokens per internal pass, a multiple of
                             block_size; 0 = the library's default (bounds the
                             workspace).  Ignored by decode. */
@@ -112,7 +126,7 @@ typedef struct msa_dims {
  *   idx_q     [batch, T, G, index_dim] bf16
  *   idx_k     [batch, T, index_dim]    bf16
  *   block_idx [batch, T, G, topk]      int32, OUTPUT
- * Flags must be 0 or MSA_FORCE_SINK.  Integer-valued idx inputs whose dot
+ * Flags: MSA_FORCE_SINK and MSA_ONE_PASS_INDEX, or 0.  Integer-valued idx inputs whose dot
  * products stay below 2^24 in magnitude give exact scores, hence a unique,
  * exact selection.
  */

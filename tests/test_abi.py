@@ -259,3 +259,34 @@ def test_check_lens_flag_is_decode_only(lib):
                            None) == bd.MSA_ERR_INVALID_ARG
     assert lib.msa_decode_noalloc(ctypes.byref(chk), fake, fake, fake, fake, fake, fake, fake, None, None,
                                   None) == bd.MSA_ERR_INVALID_ARG
+
+
+def test_one_pass_index_flag(lib):
+    """MSA_ONE_PASS_INDEX: msa_index_topk needs no workspace and prefill a
+    smaller one (no score table); topk above 17 is unsupported; the flag is
+    rejected by decode, the KL loss, the backward, msa_index_scores and
+    together with MSA_DENSE or MSA_GIVEN_INDICES."""
+    one = bd.MSA_ONE_PASS_INDEX
+    plain = _dims(topk=16)
+    fused = _dims(topk=16, flags=one)
+    assert _ws(lib, bd.MSA_OP_INDEX_TOPK, fused) == 0 < _ws(lib, bd.MSA_OP_INDEX_TOPK, plain)
+    assert 0 < _ws(lib, bd.MSA_OP_PREFILL, fused) < _ws(lib, bd.MSA_OP_PREFILL, plain)
+    assert _ws(lib, bd.MSA_OP_PREFILL, _dims(topk=16, flags=one | bd.MSA_FORCE_SINK)) == \
+        _ws(lib, bd.MSA_OP_PREFILL, fused)
+    # at 128K the table is most of the index branch's share of the prefill workspace
+    big = dict(seqlen=131072, num_q_heads=64, num_kv_heads=8, index_dim=128, topk=16)
+    assert _ws(lib, bd.MSA_OP_INDEX_TOPK, _dims(**big, flags=one)) == 0
+    assert _ws(lib, bd.MSA_OP_INDEX_TOPK, _dims(**big)) > (4 << 30)
+    assert _ws(lib, bd.MSA_OP_INDEX_TOPK, _dims(topk=17, flags=one)) == 0
+    assert _ws(lib, bd.MSA_OP_INDEX_TOPK, _dims(topk=18, flags=one)) == BAD
+    for op in (bd.MSA_OP_DECODE, bd.MSA_OP_INDEXER_KL, bd.MSA_OP_BACKWARD):
+        assert _ws(lib, op, fused) == BAD
+    for fl in (bd.MSA_DENSE, bd.MSA_GIVEN_INDICES, bd.MSA_CHECK_LENS):
+        assert _ws(lib, bd.MSA_OP_PREFILL, _dims(topk=16, flags=one | fl)) == BAD
+    fake = 0x10000
+    assert lib.msa_index_topk(ctypes.byref(_dims(topk=18, flags=one)), fake, fake, fake, None, 0, None) == \
+        bd.MSA_ERR_UNSUPPORTED
+    assert lib.msa_index_scores(ctypes.byref(fused), fake, fake, fake, 0, 2048, 16, None, 0, None) == \
+        bd.MSA_ERR_INVALID_ARG
+    assert lib.msa_decode_noalloc(ctypes.byref(fused), fake, fake, fake, fake, fake, fake, fake, None, None,
+                                  None) == bd.MSA_ERR_INVALID_ARG
