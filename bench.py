@@ -286,7 +286,8 @@ def measured_peaks(dev):
 
 def profile_kernels_only(args, dev):
     """The 128K prefill's inputs, one calibration copy of COPY_BYTES, then
-    --steps prefills, --steps indexer KL calls and --steps main-branch
+    --steps prefills, --steps indexer KL calls, --steps msa_index_topk calls
+    in each of its two forms (two-pass, one-pass) and --steps main-branch
     backward calls on the last prefill's output (each +1 warmup), --steps
     all-blocks prefills of the same inputs (+1 warmup) and --steps
     decode steps (8 x 1M context), every kernel
@@ -309,6 +310,7 @@ def profile_kernels_only(args, dev):
                                          block_idx=pbidx, workspace=pws), args.steps, stream)
     del pws
     kms = indexer_kl_ms(pin, pbidx, plse, dev, stream, args.steps)
+    iforms = index_topk_forms(pin, pbidx, dev, stream, args.steps)
     bms, _, _, btens = backward_run(pin, pout, plse, pbidx, dev, stream, args.steps, profile=False)
     del btens
     # the all-blocks (dense) prefill of the same inputs
@@ -330,6 +332,7 @@ def profile_kernels_only(args, dev):
     stages = bd.msa_profile_end()
     print(json.dumps({"profile_steps": args.steps, "prefill_ms": round(ms, 4), "decode_ms": round(dms, 4),
                       "indexer_kl_ms": round(kms, 4), "backward_ms": round(bms, 4), "dense_ms": round(dnms, 4),
+                      "index_topk": iforms,
                       "copy_bytes": COPY_BYTES,
                       "stage_ms": {n: round(t / c, 4) for n, (c, t) in stages.items()}}), flush=True)
 
@@ -359,6 +362,28 @@ def prefill_1m_run(dev, stream):
            "needles": 64, "workspace_gbytes": round(ws.numel() / 1e9, 2), "stages_per_prefill": stages}
     del pin, out, ws
     torch.cuda.empty_cache()
+    return res
+
+
+def index_topk_forms(pin, pbidx, dev, stream, reps):
+    """The Index Branch alone on the headline inputs, in its default two-pass
+    form (score table, then top-k) and as the one-pass option
+    (MSA_ONE_PASS_INDEX, no table): ms per call (one warmup, then reps),
+    workspace bytes, and whether both selections equal the prefill's."""
+    res = {}
+    for name, fl in (("two_pass", 0), ("one_pass", bd.MSA_ONE_PASS_INDEX)):
+        idd = bd.make_dims(1, PF["T"], PF["G"], PF["G"], index_dim=PF["di"], block_size=PF["B"], topk=PF["k"],
+                           flags=fl)
+        nws = bd.msa_workspace_bytes(bd.MSA_OP_INDEX_TOPK, idd)
+        iws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+        ib = torch.empty((1, PF["T"], PF["G"], PF["k"]), dtype=torch.int32, device=dev)
+        fn = lambda: bd.msa_index_topk(idd, pin.idx_q, pin.idx_k, ib, workspace=iws)  # noqa: E731
+        fn()
+        ms, _ = timed(fn, reps, stream)
+        res[f"{name}_ms"] = round(ms, 3)
+        res[f"{name}_workspace_bytes"] = int(nws)
+        res[f"{name}_equals_prefill_selection"] = bool(torch.equal(ib, pbidx))
+        del iws, ib
     return res
 
 
@@ -706,6 +731,8 @@ def main():
         if not args.no_cpu:
             variants["indexer_kl_t131072"]["sampled_check"] = indexer_kl_checks(pin, pbidx, kl_out)
         del kl_out
+        # the Index Branch alone, two-pass (default) and one-pass
+        variants["index_topk_t131072"] = index_topk_forms(pin, pbidx, dev, stream, 3)
         del vbuf
         log(f"variants: {variants}")
 

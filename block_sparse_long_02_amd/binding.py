@@ -49,7 +49,8 @@ MSA_STAGE_INDEXER_KL = 10
 MSA_STAGE_BWD_PREP = 11
 MSA_STAGE_BWD_LISTS = 12
 MSA_STAGE_BWD_MERGE = 13
-MSA_STAGE_COUNT = 14
+MSA_STAGE_INDEX_ONE_PASS = 14
+MSA_STAGE_COUNT = 15
 
 EXPORTED = ("msa_index_scores", "msa_index_topk", "msa_prefill", "msa_decode", "msa_decode_noalloc",
             "msa_decode_noalloc_limit", "msa_workspace_bytes",

@@ -437,7 +437,7 @@ hipError_t run_index_chunk(const msa_dims* d, const PrefillPlan& p, const void* 
                            int t_off, hipStream_t st) {
   const int B = d->block_size;
   if (p.one_pass) {
-    msa::prof_mark(st, MSA_STAGE_INDEX_PREFILL);
+    msa::prof_mark(st, MSA_STAGE_INDEX_ONE_PASS);
     return msa::launch_index_topk_one_pass(static_cast<const uint16_t*>(idx_q), static_cast<const uint16_t*>(idx_k),
                                            bidx, bidx_rows, t_off, d->batch, d->seqlen, d->num_kv_heads,
                                            d->index_dim, B, d->topk, (d->flags & MSA_FORCE_SINK) != 0, t0, tc, st);

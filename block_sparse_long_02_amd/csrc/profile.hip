@@ -108,6 +108,7 @@ const char* msa_stage_name(int32_t stage) {
     case MSA_STAGE_BWD_PREP: return "backward prep (delta, block lists, list sort kernels)";
     case MSA_STAGE_BWD_LISTS: return "bwd_list_kernel";
     case MSA_STAGE_BWD_MERGE: return "backward merge (bwd_dq_kernel, bwd_dkv_kernel)";
+    case MSA_STAGE_INDEX_ONE_PASS: return "index_topk_one_pass_kernel";
     default: return "unknown stage";
   }
 }

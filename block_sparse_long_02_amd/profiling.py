@@ -47,6 +47,8 @@ KERNEL_SOURCES = {
                         "build.py"],
     "dense_attn_kernel": ["csrc/sparse_attn.hip", "csrc/msa_device.h", "csrc/msa_internal.h", "csrc/api.hip",
                           "build.py"],
+    "index_topk_one_pass_kernel": ["csrc/index_blockmax.hip", "csrc/msa_device.h", "csrc/msa_internal.h",
+                                   "csrc/api.hip", "build.py"],
 }
 
 

@@ -323,7 +323,8 @@ int msa_abi_version(void);
 #define MSA_STAGE_BWD_PREP 11          /* backward: dO.out, block lists, list sort */
 #define MSA_STAGE_BWD_LISTS 12         /* backward: per-list dq / dk / dv products */
 #define MSA_STAGE_BWD_MERGE 13         /* backward: fixed-order dq and dk/dv sums  */
-#define MSA_STAGE_COUNT 14
+#define MSA_STAGE_INDEX_ONE_PASS 14    /* Index Branch in one pass (MSA_ONE_PASS_INDEX) */
+#define MSA_STAGE_COUNT 15
 
 typedef struct msa_stage_time {
   int32_t stage;
