@@ -133,6 +133,14 @@ def test_prefill_1m_needles():
     pin = inputs.make_prefill(T, 64, 8, 128, 128, seed=5, device=dev, block_size=B, needles=nneedle)
     out, bidx = run_prefill(pin, B, k)
     invariants_all_rows(bidx, T, B, k)
+    # the one-pass Index Branch (no score table, one launch over all 1M tokens)
+    # selects exactly what the prefill's chunked two-pass path selected
+    one = torch.full_like(bidx, -7)
+    bd.msa_index_topk(bd.make_dims(1, T, 8, 8, index_dim=128, block_size=B, topk=k, flags=bd.MSA_ONE_PASS_INDEX),
+                      pin.idx_q, pin.idx_k, one)
+    torch.cuda.synchronize()
+    assert torch.equal(one, bidx), "one-pass selection"
+    del one
     # P8: needles among the non-local selections = min(k-1, visible non-local needles), every row
     needles = pin.meta["needle_blocks"].numpy()
     is_needle = np.zeros(T // B + 1, dtype=bool)
