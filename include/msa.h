@@ -37,6 +37,11 @@
  *    waiting.  Outputs are bitwise reproducible run to run.
  *  - Calls on different streams with disjoint workspaces may run
  *    concurrently; calls sharing a workspace must be ordered by the caller.
+ *  - A call only launches kernels on hip_stream (no allocation, no memset,
+ *    no host synchronisation), so it can be captured into a HIP graph and
+ *    replayed; replays read the tensors' current contents, cache_lens
+ *    included.  Exceptions: msa_decode with MSA_CHECK_LENS (it waits for the
+ *    stream) and calls made while msa_profile_begin is active.
  *  - Inputs must be finite; NaN or Inf inputs give unspecified outputs.
  */
 #ifndef MSA_H_
