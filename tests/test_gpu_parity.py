@@ -182,6 +182,9 @@ PREFILL_CASES = [
     (640, 32, 2, 128, 64, 3, 0, 1),      # R = 16
     (100, 8, 2, 64, 128, 4, 0, 1),       # T < B: one partial block
     (1536, 12, 4, 128, 64, 30, 0, 1),    # R = 3, k beyond the block count
+    (1, 8, 2, 64, 128, 4, 0, 1),         # one token: its local block of one key
+    (300, 128, 1, 64, 32, 5, 0, 1),      # R = 128, the largest heads per group (one token per row tile)
+    (450, 64, 1, 128, 64, 4, 128, 3),    # R = 64, odd batch, query chunks of 128
 ]
 
 
@@ -193,7 +196,7 @@ def test_prefill_integer_idx_end_to_end(T, Hq, G, di, B, k, chunk, nb):
     check_selection_invariants(bidx, T, G, B, k)
     rng = np.random.default_rng(T)
     rows = sorted(set([(s, int(t)) for s in range(nb) for t in rng.integers(0, T, 300)]
-                      + [(s, t) for s in range(nb) for t in (0, 1, T - 1, min(B, T - 1))]))
+                      + [(s, t) for s in range(nb) for t in (0, min(1, T - 1), T - 1, min(B, T - 1))]))
     ores = orc.prefill(inp.q, inp.k, inp.v, inp.idx_q, inp.idx_k, B, k, rows=rows)
     compare_selection(bidx, ores, B, k, exact=True)
     o_ref = np.stack([ores["out"][r] for r in rows])
