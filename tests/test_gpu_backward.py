@@ -58,7 +58,42 @@ CASES = [
     (600, 24, 8, 128, 3, 0, 1),       # R = 3, partial last block
     (700, 64, 8, 128, 4, 0, 1),       # the 128K workload's heads and block size
     (300, 32, 2, 64, 12, 0, 1),       # R = 16, k beyond the number of blocks (all selected)
+    (200, 128, 1, 32, 5, 0, 1),       # R = 128, the largest heads per group
 ]
+
+
+def test_backward_one_token():
+    """T = 1: each head attends to one key with P = 1, so dv = the sum of the
+    group's dO rows and, exactly, dS = P (dP - Delta) = 0, hence dq = dk = 0.
+    On the GPU dP (an MFMA dot product) and Delta (dO . out, out = v exactly)
+    are two fp32 sums of the same 128 exact bf16 products in different orders,
+    each within 128 * 2^-24 * sum_i |dO_i v_i| of the exact value, so |dS| is at
+    most twice that, and dq, dk are bounded by the softmax scale times |dS|
+    times |k| or |q| (plus the bf16 rounding of the dq partial)."""
+    T, Hq, G, B, k, d = 1, 8, 2, 128, 4, 128
+    say("[backward one token]")
+    inp = inputs.make_prefill(T, Hq, G, d, 64, seed=77)
+    out, lse, bidx = gpu_prefill(inp, B, k)
+    dout = _dout((1, T, Hq, d), 78)
+    dq, dk, dv = gpu_backward(inp, out, lse, bidx, dout, B, k)
+    rq, rk, rv = orc.attention_backward(inp.q, inp.k, inp.v, dout, bidx, B)
+    check_grad(dv, rv, "dv")
+    assert np.abs(rq).max() == 0.0 and np.abs(rk).max() == 0.0
+    R = Hq // G
+    scale = 1.0 / np.sqrt(d)
+    q64 = inp.q[0, 0].double().numpy()               # [Hq, d]
+    k64 = inp.k[0, 0].double().numpy()               # [G, d]
+    v64 = inp.v[0, 0].double().numpy()
+    do64 = dout[0, 0].double().numpy()
+    for h in range(Hq):
+        g = h // R
+        ds_bound = 2 * d * 2.0 ** -24 * np.abs(do64[h] * v64[g]).sum()
+        assert (np.abs(dq[0, 0, h]) <= scale * ds_bound * np.abs(k64[g]) * (1 + 2.0 ** -8) + 1e-30).all(), h
+    for g in range(G):
+        ds_bounds = np.array([2 * d * 2.0 ** -24 * np.abs(do64[h] * v64[g]).sum() for h in range(g * R, g * R + R)])
+        bound = scale * (ds_bounds[:, None] * np.abs(q64[g * R:(g + 1) * R])).sum(0)
+        assert (np.abs(dk[0, 0, g]) <= bound * (1 + 1e-6) + 1e-30).all(), g
+    say(f"  dq max {np.abs(dq).max():.2e}, dk max {np.abs(dk).max():.2e} (exact 0)")
 
 
 @pytest.mark.parametrize("T,Hq,G,B,k,chunk,nb", CASES)
