@@ -702,6 +702,44 @@ def test_indexer_kl_vs_oracle(T, Hq, G, di, B, k, chunk, nb):
     _rel_close(dk.cpu().numpy(), ores["d_idx_k"], "d_idx_k")
 
 
+def test_indexer_kl_one_token():
+    """T = 1: one key, so p_I = p_M = 1 and, exactly, kl = 0, dS = 0 and both
+    gradients are 0.  On the GPU p_M = exp2(x c - lse log2 e) with the
+    forward's fp32 lse, whose exponent is x c up to three fp32 roundings of
+    products of size |x c|, and p_I = exp2 of a difference that is exact;
+    with exp2 within two ulps, |dS| <= 8 * 2^-24 * (1 + max_h |x_h c|).  The
+    gradients are dS times idx_k (d idx_q) and idx_q (d idx_k), dS rounded to
+    bf16 on the way, and |kl| <= 2 |dS| near p = 1."""
+    T, Hq, G, di, B, k = 1, 8, 2, 64, 64, 4
+    say("[indexer KL one token]")
+    inp = inputs.make_prefill(T, Hq, G, 128, di, seed=850)
+    _, lse, bidx = gpu_prefill(inp, B, k)
+    dims = bd.make_dims(1, T, Hq, G, index_dim=di, block_size=B, topk=k)
+    kl = torch.full((1, T, G), float("nan"), device="cuda")
+    dq = torch.full((1, T, G, di), float("nan"), device="cuda")
+    dk = torch.full((1, T, di), float("nan"), device="cuda")
+    bd.msa_indexer_kl(dims, inp.q.cuda(), inp.k.cuda(), inp.idx_q.cuda(), inp.idx_k.cuda(), bidx.cuda(),
+                      lse.cuda(), kl, dq, dk)
+    torch.cuda.synchronize()
+    ores = orc.indexer_kl(inp.q, inp.k, inp.idx_q, inp.idx_k, bidx, B)
+    assert all(v == 0.0 for v in ores["kl"][(0, 0)]) and not np.any(ores["d_idx_q"][(0, 0)])
+    R = Hq // G
+    c = np.log2(np.e) / np.sqrt(128)
+    q64, k64 = inp.q[0, 0].double().numpy(), inp.k[0, 0].double().numpy()
+    iq64, ik64 = inp.idx_q[0, 0].double().numpy(), inp.idx_k[0, 0].double().numpy()
+    kl_got, dq_got, dk_got = kl.cpu().double().numpy(), dq.cpu().double().numpy(), dk.cpu().double().numpy()
+    assert np.isfinite(kl_got).all() and np.isfinite(dq_got).all() and np.isfinite(dk_got).all()
+    dk_bound = np.zeros(di)
+    for g in range(G):
+        xc = np.abs(q64[g * R:(g + 1) * R] @ k64[g]) * c
+        ds = 8 * 2.0 ** -24 * (1 + xc.max())
+        assert abs(kl_got[0, 0, g]) <= 2 * ds, g
+        assert (np.abs(dq_got[0, 0, g]) <= ds * (1 + 2.0 ** -8) * np.abs(ik64)).all(), g
+        dk_bound += ds * (1 + 2.0 ** -8) * np.abs(iq64[g])
+    assert (np.abs(dk_got[0, 0]) <= dk_bound * (1 + 1e-6)).all()
+    say(f"  |kl| {np.abs(kl_got).max():.2e}, d idx_q {np.abs(dq_got).max():.2e}, d idx_k {np.abs(dk_got).max():.2e}")
+
+
 def test_indexer_kl_several_list_windows():
     """T beyond two 8192-token list windows: d idx_k summed over the lists of
     one key block in several windows."""
