@@ -290,3 +290,26 @@ def test_one_pass_index_flag(lib):
         bd.MSA_ERR_INVALID_ARG
     assert lib.msa_decode_noalloc(ctypes.byref(fused), fake, fake, fake, fake, fake, fake, fake, None, None,
                                   None) == bd.MSA_ERR_INVALID_ARG
+
+
+def test_host_validation_from_many_threads(lib):
+    """The host side is thread-safe: 16 threads sizing workspaces and having
+    invalid calls rejected at the same time get the answers one thread gets."""
+    from concurrent.futures import ThreadPoolExecutor
+    shapes = [_dims(), _dims(topk=16, flags=bd.MSA_ONE_PASS_INDEX), _dims(seqlen=131072, num_q_heads=64,
+              num_kv_heads=8, index_dim=128, topk=16), _dims(flags=bd.MSA_DENSE), _dims(query_chunk=256)]
+    ops = (bd.MSA_OP_INDEX_TOPK, bd.MSA_OP_PREFILL, bd.MSA_OP_DECODE, bd.MSA_OP_INDEXER_KL, bd.MSA_OP_BACKWARD)
+    want = [[_ws(lib, op, d) for op in ops] for d in shapes]
+    bad = _dims(num_q_heads=10)
+    fake = 0x10000
+
+    def work(i):
+        out = []
+        for _ in range(200):
+            out.append([[_ws(lib, op, d) for op in ops] for d in shapes] == want)
+            out.append(lib.msa_prefill(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None, None, fake,
+                                       1 << 40, None) == bd.MSA_ERR_INVALID_ARG)
+        return all(out)
+
+    with ThreadPoolExecutor(16) as ex:
+        assert all(ex.map(work, range(16)))
