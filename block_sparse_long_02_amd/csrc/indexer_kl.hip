@@ -254,11 +254,16 @@ __global__ __launch_bounds__(256, MSA_KL_ENTRY_MINB) void kl_entry_kernel(Indexe
       for (int kt = 0; kt < KC; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) pm[kt][i] = 0.f;
-      // head r's q rows are in qop while head r + 1's are fetched into qnx
+      // The heads' logit tiles in sequence (head, key tile): the products of
+      // the next step are issued before the exps of the current one, so the
+      // matrix unit has work while the vector unit sums exp(x - lse).  Head
+      // r's q rows are in qop while head r + 1's are fetched into qnx; after
+      // the last head the next step recomputes its first tile, unused.
       bf16x8 qop[D / 16], qnx[D / 16];
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) qop[ks] = load_bf16x8(l.q + qrow * D + 16 * ks + 8 * half);
       float lse_nx = a.lse[qrow];
+      f32x16 xcur = logit_tile<D>(Ks, KROW, k0 * 32, qop, col, half);
 #pragma unroll 1
       for (int r = 0; r < R; ++r) {
         const float lse2 = lse_nx * kLog2e;
@@ -268,9 +273,12 @@ __global__ __launch_bounds__(256, MSA_KL_ENTRY_MINB) void kl_entry_kernel(Indexe
         lse_nx = a.lse[rn];
 #pragma unroll
         for (int kt = 0; kt < KC; ++kt) {
-          const f32x16 x = logit_tile<D>(Ks, KROW, (k0 + kt) * 32, qop, col, half);
+          // the next step: this head's next key tile, or the next head's first
+          const f32x16 xnxt = kt + 1 < KC ? logit_tile<D>(Ks, KROW, (k0 + kt + 1) * 32, qop, col, half)
+                                          : logit_tile<D>(Ks, KROW, k0 * 32, qnx, col, half);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) pm[kt][i] += __builtin_amdgcn_exp2f(x[i] * c - lse2);
+          for (int i = 0; i < 16; ++i) pm[kt][i] += __builtin_amdgcn_exp2f(xcur[i] * c - lse2);
+          xcur = xnxt;
         }
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) qop[ks] = qnx[ks];
