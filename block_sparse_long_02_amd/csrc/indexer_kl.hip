@@ -342,7 +342,13 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
   const int kb = b * l.B;
   const int nkey = min(BS, l.T - kb);
 
-
+  // Transposed rows (IkT and QT: index dim, DT: key) hold 16-byte chunks,
+  // chunk ch of row r at position ch ^ ((r / 16) % 4): the 32 lanes of a
+  // transposing write pass, rows 4 apart, then fall on at most two lanes per
+  // bank (eight without the swizzle), and the operand reads (16 consecutive
+  // rows, one chunk) stay conflict-free.
+  auto tchunk = [](int r, int ch) { return ((ch ^ ((r >> 4) & 3)) * 8); };
+  auto tcol = [&](int r, int u) { return tchunk(r, u >> 1) + 4 * (u & 1); };  // 8-byte unit u of row r
   // idx_k block, transposed: IkT[c][key], in 4 keys x 4 c units
   for (int u = tid; u < (BS / 4) * (DI / 4); u += 256) {
     const int k4 = u / (DI / 4), c4 = u % (DI / 4);
@@ -355,7 +361,8 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
     }
     transpose4x4(r, o);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(IkT + (4 * c4 + j) * IKR + 4 * k4) = o[j];
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x2*>(IkT + (4 * c4 + j) * IKR + tcol(4 * c4 + j, k4)) = o[j];
   }
   f32x16 dk[TPW];
 #pragma unroll
@@ -398,12 +405,14 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
       for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x2*>(Dr + (4 * de4 + i) * DRR + 4 * dk4) = dsr[i];
       transpose4x4(dsr, o);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(DT + (4 * dk4 + j) * ER + 4 * de4) = o[j];
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<u32x2*>(DT + (4 * dk4 + j) * ER + tcol(4 * dk4 + j, de4)) = o[j];
     }
     if (has_q) {
       transpose4x4(qsr, o);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(QT + (4 * qc4 + j) * ER + 4 * qe4) = o[j];
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<u32x2*>(QT + (4 * qc4 + j) * ER + tcol(4 * qc4 + j, qe4)) = o[j];
     }
   };
 
@@ -425,7 +434,8 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
 #pragma unroll
       for (int ks = 0; ks < BS / 16; ++ks) {
         const bf16x8 av = *reinterpret_cast<const bf16x8*>(Dr + col * DRR + 16 * ks + 8 * half);
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(IkT + (32 * wave + col) * IKR + 16 * ks + 8 * half);
+        const bf16x8 bv =
+            *reinterpret_cast<const bf16x8*>(IkT + (32 * wave + col) * IKR + tchunk(32 * wave + col, 2 * ks + half));
         acc = mfma32x32x16(av, bv, acc);
       }
 #pragma unroll
@@ -442,8 +452,10 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
         const int kt = tix / (DI / 32), dt = tix % (DI / 32);
 #pragma unroll
         for (int ks = 0; ks < EC / 16; ++ks) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(DT + (32 * kt + col) * ER + 16 * ks + 8 * half);
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(QT + (32 * dt + col) * ER + 16 * ks + 8 * half);
+          const bf16x8 av =
+              *reinterpret_cast<const bf16x8*>(DT + (32 * kt + col) * ER + tchunk(32 * kt + col, 2 * ks + half));
+          const bf16x8 bv =
+              *reinterpret_cast<const bf16x8*>(QT + (32 * dt + col) * ER + tchunk(32 * dt + col, 2 * ks + half));
           dk[i] = mfma32x32x16(av, bv, dk[i]);
         }
       }
