@@ -81,13 +81,15 @@ __device__ __forceinline__ void vt_unit(int u, int& k4, int& dq) {
 constexpr int kVtPadQ = 8;
 __device__ __forceinline__ int vt_quad_pos(int k4) { return (k4 & ~3) | ((k4 & 1) << 1) | ((k4 >> 1) & 1); }
 
-// Its staging units: in a half-wave 8 d-quads (64 contiguous bytes of a V
-// row) x 4 key-quads, the key-quads offset by 4 for the upper 4 d-quads, so
-// the 8-byte writes at the 4 (mod 64) dword row stride fall on 32 distinct
-// bank pairs.
+// Its staging units (4 keys x 4 d each, 8-byte V^T row writes): the LDS
+// takes 8-byte writes 16 lanes at a time over 32 banks (128 bytes), so each
+// 16-lane group holds two adjacent d-quads (V^T rows 4 apart: 64 bytes apart
+// mod 128 at the 272-byte row stride) x 8 key-quads (8 bytes apart): 16
+// distinct bank pairs.  The 64 lanes of a load instruction cover 8 d-quads x
+// 8 key-quads: 8 V rows, 64 contiguous bytes each.
 __device__ __forceinline__ void vt_unit_q(int u, int& k4, int& dq) {
-  dq = (u & 7) + 8 * ((u >> 5) & 3);
-  k4 = ((u >> 3) & 3) + 4 * (((u >> 2) ^ (u >> 7)) & 1) + 8 * (u >> 8);
+  dq = (u & 1) + 2 * ((u >> 4) & 3) + 8 * ((u >> 6) & 3);
+  k4 = ((u >> 1) & 7) + 8 * (u >> 8);
 }
 
 // 4x4 transpose of 16-bit lanes: o[j] = (r0[j], r1[j], r2[j], r3[j])
