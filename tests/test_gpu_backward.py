@@ -4,7 +4,7 @@ The forward runs on the GPU (its selection and lse feed the backward, as in
 training); the oracle recomputes the gradients in fp64 from the same bf16
 inputs and the GPU's selection.  Bounds: max-abs <= 1e-2 of the largest
 reference value and mean-relative (sum |diff| / sum |ref|) <= 5e-3 per
-gradient.  P and dS enter the MFMA products rounded to bf16 (2^-9 relative)
+gradient.  P and dS enter the MFMA products rounded to bf16 (at most 2^-8 relative)
 and dq is summed from bf16 partials, one per selected block; over the
 hundreds to thousands of keys of a row these roundings average out to a few
 1e-3 of the values, which is what the bounds allow.
