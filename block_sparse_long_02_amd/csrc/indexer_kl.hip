@@ -198,7 +198,7 @@ __global__ void kl_row_lse_kernel(IndexerKlArgs a) {
 #define MSA_KL_ENTRY_KC 4
 #endif
 #ifndef MSA_KL_ENTRY_MINB
-#define MSA_KL_ENTRY_MINB 1
+#define MSA_KL_ENTRY_MINB 2
 #endif
 
 template <int DI, int BS>
@@ -238,15 +238,12 @@ __global__ __launch_bounds__(256, MSA_KL_ENTRY_MINB) void kl_entry_kernel(Indexe
     const int tl = ent >> l.rank_bits;
     const int t = l.t0 + tl;
     const size_t qrow = ((size_t)s * l.T + t) * l.Hq + (size_t)g * R;  // first head of the group
-    bf16x8 iop[DI / 16];
     const bf16_t* ip = a.idx_q + (((size_t)s * l.T + t) * l.G + g) * DI;
-#pragma unroll
-    for (int ks = 0; ks < DI / 16; ++ks) iop[ks] = load_bf16x8(ip + 16 * ks + 8 * half);
     const float lse2_i = a.lse_i[((size_t)s * l.tc + tl) * l.G + g];
     bf16_t* dsrow = a.ds + (size_t)(off + min(pos, count - 1)) * BS;
     float kl = 0.f;
     // chunks of KC key tiles: the q rows are read once per chunk (all of the
-    // block's tiles by default, one workgroup per CU for the registers)
+    // block's tiles by default)
 #pragma unroll 1
     for (int k0 = 0; k0 < KT; k0 += KC) {
       float pm[KC][16];  // sum over the heads of exp(x - lse): R * p_M
@@ -255,34 +252,52 @@ __global__ __launch_bounds__(256, MSA_KL_ENTRY_MINB) void kl_entry_kernel(Indexe
 #pragma unroll
         for (int i = 0; i < 16; ++i) pm[kt][i] = 0.f;
       // The heads' logit tiles in sequence (head, key tile): the products of
-      // the next step are issued before the exps of the current one, so the
-      // matrix unit has work while the vector unit sums exp(x - lse).  Head
-      // r's q rows are in qop while head r + 1's are fetched into qnx; after
-      // the last head the next step recomputes its first tile, unused.
-      bf16x8 qop[D / 16], qnx[D / 16];
+      // the next step (this head's next key tile, or the next head's first)
+      // are issued before the exps of the current one, so the matrix unit has
+      // work while the vector unit sums exp(x - lse).  Head r's q rows sit in
+      // one register set while head r + 1's are fetched into the other; the
+      // loop is unrolled by two so that no set is copied.  After the last head
+      // the next step is computed and unused.
+      bf16x8 qa[D / 16], qb[D / 16];
+      auto load_q = [&](bf16x8* dst, int r) {
+        const size_t row = qrow + (size_t)min(r, R - 1);
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) qop[ks] = load_bf16x8(l.q + qrow * D + 16 * ks + 8 * half);
-      float lse_nx = a.lse[qrow];
-      f32x16 xcur = logit_tile<D>(Ks, KROW, k0 * 32, qop, col, half);
-#pragma unroll 1
-      for (int r = 0; r < R; ++r) {
-        const float lse2 = lse_nx * kLog2e;
-        const size_t rn = qrow + (r + 1 < R ? r + 1 : r);
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) qnx[ks] = load_bf16x8(l.q + rn * D + 16 * ks + 8 * half);
-        lse_nx = a.lse[rn];
+        for (int ks = 0; ks < D / 16; ++ks) dst[ks] = load_bf16x8(l.q + row * D + 16 * ks + 8 * half);
+      };
+      load_q(qa, 0);
+      float lse_a = a.lse[qrow], lse_b = 0.f;
+      f32x16 xcur = logit_tile<D>(Ks, KROW, k0 * 32, qa, col, half);
+      auto head = [&](const bf16x8* qo, bf16x8* qn, int rn, float lse, float& lse_n) {
+        load_q(qn, rn);
+        lse_n = a.lse[qrow + min(rn, R - 1)];
+        // The key operands are read from LDS in every head through an offset
+        // the compiler cannot see through: held in registers across the heads
+        // (its choice otherwise) they would take 128 registers per lane and
+        // leave room for only one wave per SIMD.
+        int koff = 0;
+        asm volatile("" : "+v"(koff));
+        const bf16_t* Kh = Ks + koff;
+        const float lse2 = lse * kLog2e;
 #pragma unroll
         for (int kt = 0; kt < KC; ++kt) {
-          // the next step: this head's next key tile, or the next head's first
-          const f32x16 xnxt = kt + 1 < KC ? logit_tile<D>(Ks, KROW, (k0 + kt + 1) * 32, qop, col, half)
-                                          : logit_tile<D>(Ks, KROW, k0 * 32, qnx, col, half);
+          const f32x16 xnxt = kt + 1 < KC ? logit_tile<D>(Kh, KROW, (k0 + kt + 1) * 32, qo, col, half)
+                                          : logit_tile<D>(Kh, KROW, k0 * 32, qn, col, half);
 #pragma unroll
           for (int i = 0; i < 16; ++i) pm[kt][i] += __builtin_amdgcn_exp2f(xcur[i] * c - lse2);
           xcur = xnxt;
         }
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) qop[ks] = qnx[ks];
+      };
+#pragma unroll 1
+      for (int r = 0; r < R; r += 2) {
+        head(qa, qb, r + 1, lse_a, lse_b);
+        if (r + 1 >= R) break;
+        head(qb, qa, r + 2, lse_b, lse_a);
       }
+      // the index query, read only now so that it holds no registers in the
+      // head loop
+      bf16x8 iop[DI / 16];
+#pragma unroll
+      for (int ks = 0; ks < DI / 16; ++ks) iop[ks] = load_bf16x8(ip + 16 * ks + 8 * half);
 #pragma unroll
       for (int kt = 0; kt < KC; ++kt) {
         const f32x16 si = logit_tile<DI>(Is, KP, (k0 + kt) * 32, iop, col, half);
@@ -294,7 +309,9 @@ __global__ __launch_bounds__(256, MSA_KL_ENTRY_MINB) void kl_entry_kernel(Indexe
           const float p_m = ok ? pm[kt][i] * invR : 0.f;
           const float l2pi = si[i] * kLog2e - lse2_i;
           const float p_i = ok ? __builtin_amdgcn_exp2f(l2pi) : 0.f;
-          if (ok && p_m > 0.f) kl += p_m * (__log2f(p_m) - l2pi);
+          // branch-free: p_m = 0 adds nothing (the log is taken of at least
+          // the smallest normal, so it stays finite)
+          kl += p_m * (__log2f(fmaxf(p_m, 1.17549435e-38f)) - l2pi);
           ds[i] = p_i - p_m;
         }
         if (valid) {
