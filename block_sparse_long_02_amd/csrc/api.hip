@@ -240,7 +240,6 @@ int make_kl_plan(const msa_dims* d, KlPlan* p) {
   if (d->flags != 0) return MSA_ERR_INVALID_ARG;
   const int T = d->seqlen, B = d->block_size, G = d->num_kv_heads;
   p->R = d->num_q_heads / G;
-  if (p->R > 32 || (p->R & (p->R - 1)) != 0) return MSA_ERR_UNSUPPORTED;  // p_M sums aligned lane groups
   p->nb = (T + B - 1) / B;
   p->KS = d->topk < p->nb ? d->topk : p->nb;
   p->mt = msa::kAttnRows / p->R;

@@ -245,8 +245,8 @@ size_t msa_decode_noalloc_limit(void);
  *   kl        [batch, T, G] fp32 OUTPUT (0 for a row without valid entries)
  *   d_idx_q   [batch, T, G, index_dim] fp32 OUTPUT
  *   d_idx_k   [batch, T, index_dim] fp32 OUTPUT (keys never selected get 0)
- * dims: prefill shapes, flags must be 0; Hq / G must be a power of two <= 32
- * (else MSA_ERR_UNSUPPORTED).  d_idx_q 16-byte aligned, the other fp32 pointers
+ * dims: prefill shapes (any Hq / G up to 128, as for msa_prefill), flags must
+ * be 0.  d_idx_q 16-byte aligned, the other fp32 pointers
  * 4-byte aligned.  dS = p_I - p_M
  * enters the gradient products rounded to bf16 (fp32 accumulation).
  * Deterministic: fixed-order sums, no atomics on values.

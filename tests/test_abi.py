@@ -194,10 +194,13 @@ def test_sink_flag_accepted_with_the_index_branch(lib):
 def test_indexer_kl_shape_limits(lib):
     ok = bd.make_dims(1, 2048, 16, 4, index_dim=64, block_size=64, topk=8)
     assert lib.msa_workspace_bytes(bd.MSA_OP_INDEXER_KL, ctypes.byref(ok)) > 0
-    r3 = bd.make_dims(1, 2048, 12, 4, index_dim=64, block_size=64, topk=8)   # R = 3
-    r64 = bd.make_dims(1, 2048, 64, 1, index_dim=64, block_size=64, topk=8)  # R = 64
+    # any head ratio the prefill takes: the heads are visited in turn per entry
+    for hq, g in ((12, 4), (64, 1), (128, 1)):
+        d = bd.make_dims(1, 2048, hq, g, index_dim=64, block_size=64, topk=8)
+        assert lib.msa_workspace_bytes(bd.MSA_OP_INDEXER_KL, ctypes.byref(d)) > 0, (hq, g)
+    r256 = bd.make_dims(1, 2048, 256, 1, index_dim=64, block_size=64, topk=8)  # beyond the prefill's 128
     fl = bd.make_dims(1, 2048, 16, 4, index_dim=64, block_size=64, topk=8, flags=bd.MSA_DENSE)
-    for d in (r3, r64, fl):
+    for d in (r256, fl):
         assert lib.msa_workspace_bytes(bd.MSA_OP_INDEXER_KL, ctypes.byref(d)) == ctypes.c_size_t(-1).value
 
 

@@ -666,6 +666,8 @@ KL_CASES = [
     (700, 64, 8, 128, 128, 4, 0, 1),    # the 128K workload's heads, index dim and block size
     (520, 32, 2, 128, 64, 4, 0, 1),     # R = 16
     (450, 32, 1, 64, 32, 7, 0, 1),      # R = 32, one group
+    (640, 12, 4, 128, 128, 5, 0, 1),    # R = 3: the head loop's odd tail
+    (300, 128, 1, 64, 64, 4, 0, 1),     # R = 128, the largest the prefill takes
 ]
 
 
