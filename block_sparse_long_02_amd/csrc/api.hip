@@ -227,7 +227,7 @@ size_t kl_chunk_bytes(const msa_dims* d, const KlPlan& p, long tc, KlPlan* out) 
   q.off_lse_i = L.add(rows * 4);
   q.off_ds = L.add(emax * B_ * 2);
   q.off_kl_e = L.add(emax * 4);
-  q.off_dq_e = L.add(emax * di * 4);
+  q.off_dq_e = L.add(emax * di * 2);
   q.off_dk = L.add(nlists * B_ * di * 4);
   q.total = L.total;
   if (out != nullptr) *out = q;
@@ -720,7 +720,7 @@ int msa_indexer_kl(const msa_dims* dims, const void* q, const void* k, const voi
   a.lse_i = at<float>(workspace, p.off_lse_i);
   a.ds = at<uint16_t>(workspace, p.off_ds);
   a.kl_e = at<float>(workspace, p.off_kl_e);
-  a.dq_e = at<float>(workspace, p.off_dq_e);
+  a.dq_e = at<uint16_t>(workspace, p.off_dq_e);
   a.dk_part = at<float>(workspace, p.off_dk);
   msa::prof_mark(s, MSA_STAGE_INDEXER_KL);
   for (int c = 0; c < p.nchunks; ++c) {

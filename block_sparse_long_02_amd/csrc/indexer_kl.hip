@@ -24,8 +24,9 @@
 //  3. kl_entry_kernel: per entry, the R heads' logits (summed in the lane)
 //     and the index logits on MFMA, p_M, p_I, the entry's KL term and dS
 //     (bf16, row-major per entry);
-//  4. kl_list_kernel: per list, d idx_q of each entry (dS . idx_k) and the
-//     list's d idx_k partial (dS^T . idx_q) on MFMA, over the entries in
+//  4. kl_list_kernel: per list, d idx_q of each entry (dS . idx_k, stored in
+//     bf16: 2^-8 relative, well inside what the row sums need) and the list's
+//     d idx_k partial (dS^T . idx_q, fp32) on MFMA, over the entries in
 //     (token, slot) order (the lists are sorted right after they are built);
 //  5. kl_row_out_kernel / kl_dk_reduce_kernel: fixed-order sums per row and
 //     per key block.  No atomic touches a value: results are reproducible.
@@ -458,7 +459,7 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int en = 8 * (i / 4) + 4 * half + (i % 4);
-        if (en < n) a.dq_e[(size_t)(off + c0 + en) * DI + 32 * wave + col] = acc[i];
+        if (en < n) a.dq_e[(size_t)(off + c0 + en) * DI + 32 * wave + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[i]);
       }
     }
     // d idx_k partial: [key][c] += sum_entry dS[entry][key] idx_q[entry][c]
@@ -518,17 +519,18 @@ __global__ void kl_row_out_kernel(IndexerKlArgs a) {
     int pq[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) pq[u] = pos[min(q0 + u, nv - 1)];
-    f32x4 v[8];
+    bf16x4 v[8];
     float ke[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      v[u] = *reinterpret_cast<const f32x4*>(a.dq_e + (size_t)pq[u] * a.di + 4 * c4);
+      v[u] = *reinterpret_cast<const bf16x4*>(a.dq_e + (size_t)pq[u] * a.di + 4 * c4);
       ke[u] = a.kl_e[pq[u]];
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (q0 + u < nv) {
-        dq += v[u];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dq[e] += (float)v[u][e];
         kl += ke[u];
       }
   }

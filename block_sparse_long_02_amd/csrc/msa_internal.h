@@ -143,7 +143,7 @@ struct IndexerKlArgs {
   float* lse_i;           // [batch*tc*G] per row index log2-sum-exp
   uint16_t* ds;           // [E][B] bf16 p_I - p_M per entry and key
   float* kl_e;            // [E] per entry KL term
-  float* dq_e;            // [E][di] per entry d idx_q term
+  uint16_t* dq_e;         // [E][di] per entry d idx_q term, bf16
   float* dk_part;         // [nlists][B][di] per list d idx_k partial
 };
 hipError_t launch_indexer_kl(const IndexerKlArgs& a, hipStream_t st);
