@@ -108,3 +108,57 @@ def test_decode_graph_replays(noalloc):
         torch.cuda.synchronize()
         assert torch.equal(got[2], bidx2), f"selection, lens {ln}"
         assert torch.equal(got[0], out2) and torch.equal(got[1], lse2), f"outputs, lens {ln}"
+
+
+def test_indexer_kl_and_backward_graph_replays():
+    """The indexer KL and the main-branch backward, each over three query
+    chunks (T = 3000, B 64, k 8, chunks of 1024: the later chunks add onto
+    d idx_k, dk and dv), captured into graphs and replayed on four seeds: each
+    replay equals an eager call bit for bit."""
+    T, Hq, G, d, di, B, k = 3000, 16, 4, 128, 64, 64, 8
+    say(f"[graph KL + backward] T={T} B={B} k={k} chunks of 1024")
+    dev = torch.device("cuda")
+    dims = bd.make_dims(1, T, Hq, G, head_dim=d, index_dim=di, block_size=B, topk=k, query_chunk=1024)
+    pdims = bd.make_dims(1, T, Hq, G, head_dim=d, index_dim=di, block_size=B, topk=k)
+
+    def forward(y):
+        out = torch.empty_like(y.q)
+        lse = torch.empty((1, T, Hq), dtype=torch.float32, device=dev)
+        bidx = torch.empty((1, T, G, k), dtype=torch.int32, device=dev)
+        bd.msa_prefill(pdims, y.q, y.k, y.v, y.idx_q, y.idx_k, out, lse=lse, block_idx=bidx)
+        gen = torch.Generator(device=dev).manual_seed(int(y.q[0, 0, 0, 0].float().item() * 1000) % 1000)
+        dout = torch.randn(y.q.shape, generator=gen, device=dev).to(torch.bfloat16)
+        return out, lse, bidx, dout
+
+    x = inputs.make_prefill(T, Hq, G, d, di, seed=0, device=dev)
+    out0, lse0, bidx0, dout0 = forward(x)
+    st = [t.clone() for t in (x.q, x.k, x.v, x.idx_q, x.idx_k, out0, lse0, bidx0, dout0)]
+    q, kk_, v, iq, ik, out, lse, bidx, dout = st
+    kl = torch.empty((1, T, G), dtype=torch.float32, device=dev)
+    diq = torch.empty((1, T, G, di), dtype=torch.float32, device=dev)
+    dik = torch.empty((1, T, di), dtype=torch.float32, device=dev)
+    dq = torch.empty((1, T, Hq, d), dtype=torch.float32, device=dev)
+    dk = torch.empty((1, T, G, d), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    wk = torch.empty(bd.msa_workspace_bytes(bd.MSA_OP_INDEXER_KL, dims), dtype=torch.uint8, device=dev)
+    wb = torch.empty(bd.msa_workspace_bytes(bd.MSA_OP_BACKWARD, dims), dtype=torch.uint8, device=dev)
+
+    def both(ws_k, ws_b, outs):
+        bd.msa_indexer_kl(dims, q, kk_, iq, ik, bidx, lse, outs[0], outs[1], outs[2], workspace=ws_k)
+        bd.msa_prefill_backward(dims, q, kk_, v, out, lse, dout, bidx, outs[3], outs[4], outs[5], workspace=ws_b)
+
+    g = _capture(lambda: both(wk, wb, (kl, diq, dik, dq, dk, dv)))
+    wk2, wb2 = torch.empty_like(wk), torch.empty_like(wb)
+    for seed in (1, 2, 3, 4):
+        y = inputs.make_prefill(T, Hq, G, d, di, seed=seed, device=dev)
+        o, l_, b_, do = forward(y)
+        for dst, src in zip(st, (y.q, y.k, y.v, y.idx_q, y.idx_k, o, l_, b_, do)):
+            dst.copy_(src)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (kl, diq, dik, dq, dk, dv)]
+        ref = [torch.empty_like(t) for t in got]
+        both(wk2, wb2, ref)
+        torch.cuda.synchronize()
+        for name, a_, b2 in zip(("kl", "d idx_q", "d idx_k", "dq", "dk", "dv"), got, ref):
+            assert torch.equal(a_, b2), f"{name}, seed {seed}"
