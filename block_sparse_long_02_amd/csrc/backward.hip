@@ -448,7 +448,8 @@ __global__ __launch_bounds__(256, MSA_BWD_MIN_BLOCKS) void bwd_list_kernel(BwdAr
 #pragma unroll
     for (int ks = 0; ks < BS / 16; ++ks)
       dsb[ks] = *reinterpret_cast<const bf16x8*>(DSr + (rt2 * 32 + col) * DSR + 16 * ks + 8 * half);
-#pragma unroll(RT <= 2 ? RT : 1)
+    constexpr int kPairUnroll = RT <= 2 ? RT : 1;
+#pragma unroll kPairUnroll
     for (int ii = 0; ii < RT; ++ii) {
       const int dt = (wave * RT + ii) & 3;
       bf16x8 ka[BS / 16];

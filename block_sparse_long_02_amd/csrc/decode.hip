@@ -26,7 +26,6 @@ namespace msa {
 namespace {
 
 constexpr int D = 128;
-constexpr int kDecMaxR = 16;     // query heads per group handled by the decode kernels (<= 32 MFMA columns)
 constexpr int kDecBlocksPerWave = 1;
 
 template <int DI, int BS>
