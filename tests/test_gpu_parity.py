@@ -385,6 +385,8 @@ def gpu_decode(dec, B, k, flags=0, block_idx=None):  # flags may carry MSA_FORCE
     (2000, 8, 8, 128, 32, 40, [2000, 33]),
     (700, 32, 2, 64, 64, 3, [700, 129, 1]),   # R = 16, the largest heads per group decode takes
     (1, 8, 2, 64, 128, 4, [1, 1]),            # caches of capacity one token
+    (2500, 12, 4, 128, 64, 6, [2500, 777, 65]),  # R = 3
+    (1800, 12, 2, 64, 128, 5, [1800, 1, 1030]),  # R = 6
 ])
 def test_decode_vs_oracle(mode, L, Hq, G, di, B, k, lens):
     say(f"[decode {mode}] L={L} Hq={Hq} G={G} di={di} B={B} k={k} lens={lens}")
