@@ -166,3 +166,33 @@ def test_backward_several_list_windows():
         check_grad(dq, rq, "dq")
         check_grad(dk, rk, "dk")
         check_grad(dv, rv, "dv")
+
+
+def test_backward_and_indexer_kl_on_a_forced_sink_selection():
+    """The forced-sink prefill's selection (block 0 beside the local block in
+    every row) fed to the backward and to the indexer KL: both against the
+    oracle on that selection."""
+    T, Hq, G, B, k = 900, 16, 4, 64, 5
+    say(f"[backward + KL on a sink selection] T={T} B={B} k={k}")
+    inp = inputs.make_prefill(T, Hq, G, 128, 64, seed=930)
+    out, lse, bidx = gpu_prefill(inp, B, k, flags=bd.MSA_FORCE_SINK)
+    sel = bidx.numpy()
+    assert all(0 in sel[0, t, g] for t in range(B, T) for g in range(G)), "block 0 in every row past the first block"
+    dout = _dout((1, T, Hq, 128), 931)
+    dq, dk, dv = gpu_backward(inp, out, lse, bidx, dout, B, k)
+    rq, rk, rv = orc.attention_backward(inp.q, inp.k, inp.v, dout, bidx, B)
+    check_grad(dq, rq, "dq")
+    check_grad(dk, rk, "dk")
+    check_grad(dv, rv, "dv")
+    dims = bd.make_dims(1, T, Hq, G, index_dim=64, block_size=B, topk=k)
+    kl = torch.empty((1, T, G), device="cuda")
+    diq = torch.empty((1, T, G, 64), device="cuda")
+    dik = torch.empty((1, T, 64), device="cuda")
+    bd.msa_indexer_kl(dims, inp.q.cuda(), inp.k.cuda(), inp.idx_q.cuda(), inp.idx_k.cuda(), bidx.cuda(),
+                      lse.cuda(), kl, diq, dik)
+    torch.cuda.synchronize()
+    ores = orc.indexer_kl(inp.q, inp.k, inp.idx_q, inp.idx_k, bidx, B)
+    kl_ref = np.array([ores["kl"][(0, t)] for t in range(T)])
+    assert (np.abs(kl.cpu().double().numpy()[0] - kl_ref) <= 1e-3 * np.abs(kl_ref) + 1e-4).all()
+    check_grad(diq.cpu().double().numpy(), np.stack([ores["d_idx_q"][(0, t)] for t in range(T)])[None], "d idx_q")
+    check_grad(dik.cpu().double().numpy(), ores["d_idx_k"], "d idx_k")
