@@ -1112,6 +1112,23 @@ __global__ __launch_bounds__(256) void lists_sort_kernel(PrefillMainArgs a) {
   const int s = (int)((lid / a.nbl) / a.nwin / a.G);
   const int off = a.offs[lid];
   const int tid = threadIdx.x;
+  const uint32_t mask = (1u << a.rank_bits) - 1u;
+  if (count <= 256) {
+    // The keys of a list are distinct (a token enters a list once), so each
+    // key's rank among them is its place in ascending order: the result is
+    // the same permutation the sorting network below produces.
+    const uint32_t mine = tid < count ? (uint32_t)a.entries[off + tid] : 0xffffffffu;
+    key[tid] = mine;
+    __syncthreads();
+    if (tid < count) {
+      int rank = 0;
+      for (int i = 0; i < count; ++i) rank += key[i] < mine ? 1 : 0;
+      a.entries[off + rank] = (int32_t)mine;
+      const long row = ((long)s * a.tc + (long)(mine >> a.rank_bits)) * a.G + g;
+      a.epos[(size_t)row * a.KS + (mine & mask)] = off + rank;
+    }
+    return;
+  }
   int n2 = 1;
   while (n2 < count) n2 <<= 1;
   for (int i = tid; i < n2; i += 256) key[i] = i < count ? (uint32_t)a.entries[off + i] : 0xffffffffu;
@@ -1131,7 +1148,6 @@ __global__ __launch_bounds__(256) void lists_sort_kernel(PrefillMainArgs a) {
       }
       __syncthreads();
     }
-  const uint32_t mask = (1u << a.rank_bits) - 1u;
   for (int i = tid; i < count; i += 256) {
     const uint32_t e = key[i];
     a.entries[off + i] = (int32_t)e;
