@@ -1098,35 +1098,95 @@ hipError_t launch_fill_i32(int32_t* p, size_t n, int32_t value, hipStream_t st) 
   return hipGetLastError();
 }
 
-// Sorts each block list's entries (tl << rank_bits | slot, all distinct) in
-// LDS and points every row slot at its entry's new list position, so that
-// sums over a list run in an order that does not depend on how the integer
-// atomics filled it.  A list longer than kListWindow (only possible with
-// duplicate selections, which are invalid input) keeps its order.
+// Sorts each block list's entries (tl << rank_bits | slot, all distinct) and
+// points every row slot at its entry's new list position, so that sums over a
+// list run in an order that does not depend on how the integer atomics filled
+// it.  A token enters a list at most once, so the order is the tokens' order:
+// each entry sets its token's bit in a window-sized bitmap in LDS and its rank
+// is the number of bits below it (a prefix count over the bitmap's words).
+// Lists of at most 64 entries count the smaller keys directly.  A list in
+// which a token occurs twice (only possible with duplicate selections, which
+// are invalid input) is sorted by the bitonic network instead, and a list
+// longer than kListWindow (the same case) keeps its order.
 __global__ __launch_bounds__(256) void lists_sort_kernel(PrefillMainArgs a) {
+  constexpr int kWords = kListWindow / 32;
+  constexpr int kPer = kListWindow / 256;  // entries per thread at most
+  static_assert(kWords <= 256, "one bitmap word per thread");
   __shared__ uint32_t key[kListWindow];
+  __shared__ uint32_t bits[kWords];
+  __shared__ int wsum[4];
+  __shared__ int dup;
   const long lid = blockIdx.x;
   const int count = a.cnt[lid];
   if (count < 2 || count > kListWindow) return;
   const int g = (int)((lid / a.nbl) / a.nwin % a.G);
   const int s = (int)((lid / a.nbl) / a.nwin / a.G);
+  const int w = (int)((lid / a.nbl) % a.nwin);
   const int off = a.offs[lid];
   const int tid = threadIdx.x;
   const uint32_t mask = (1u << a.rank_bits) - 1u;
-  if (count <= 256) {
-    // The keys of a list are distinct (a token enters a list once), so each
-    // key's rank among them is its place in ascending order: the result is
-    // the same permutation the sorting network below produces.
+  auto place = [&](uint32_t e, int pos) {
+    a.entries[off + pos] = (int32_t)e;
+    const long row = ((long)s * a.tc + (long)(e >> a.rank_bits)) * a.G + g;
+    a.epos[(size_t)row * a.KS + (e & mask)] = off + pos;
+  };
+  if (count <= 64) {
     const uint32_t mine = tid < count ? (uint32_t)a.entries[off + tid] : 0xffffffffu;
     key[tid] = mine;
     __syncthreads();
     if (tid < count) {
       int rank = 0;
       for (int i = 0; i < count; ++i) rank += key[i] < mine ? 1 : 0;
-      a.entries[off + rank] = (int32_t)mine;
-      const long row = ((long)s * a.tc + (long)(mine >> a.rank_bits)) * a.G + g;
-      a.epos[(size_t)row * a.KS + (mine & mask)] = off + rank;
+      place(mine, rank);
     }
+    return;
+  }
+  // every entry is read (into registers) before any is written back
+  const int wbase = w * a.window;
+  const int nwords = (a.window + 31) / 32;
+  uint32_t mine[kPer];
+  if (tid < kWords) bits[tid] = 0u;
+  if (tid == 0) dup = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = tid + 256 * j;
+    mine[j] = i < count ? (uint32_t)a.entries[off + i] : 0u;
+  }
+  __syncthreads();
+  int seen = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (tid + 256 * j < count) {
+      const int loc = (int)(mine[j] >> a.rank_bits) - wbase;
+      const uint32_t bit = 1u << (loc & 31);
+      seen |= (atomicOr(&bits[loc >> 5], bit) & bit) != 0u;
+    }
+  if (seen) dup = 1;
+  __syncthreads();
+  if (dup == 0) {
+    // exclusive prefix of the words' popcounts, one word per thread
+    const int lane = tid & 63, wave = tid >> 6;
+    const int c = tid < nwords ? __builtin_popcount(bits[tid]) : 0;
+    int x = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, kWave);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int before = x - c;
+    for (int v = 0; v < wave; ++v) before += wsum[v];
+    __syncthreads();  // every thread has read wsum before key[] is reused
+    if (tid < kWords) key[tid] = (uint32_t)before;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (tid + 256 * j < count) {
+        const int loc = (int)(mine[j] >> a.rank_bits) - wbase;
+        const int rank = (int)key[loc >> 5] + __builtin_popcount(bits[loc >> 5] & ((1u << (loc & 31)) - 1u));
+        place(mine[j], rank);
+      }
     return;
   }
   int n2 = 1;
@@ -1148,12 +1208,7 @@ __global__ __launch_bounds__(256) void lists_sort_kernel(PrefillMainArgs a) {
       }
       __syncthreads();
     }
-  for (int i = tid; i < count; i += 256) {
-    const uint32_t e = key[i];
-    a.entries[off + i] = (int32_t)e;
-    const long row = ((long)s * a.tc + (long)(e >> a.rank_bits)) * a.G + g;
-    a.epos[(size_t)row * a.KS + (e & mask)] = off + i;
-  }
+  for (int i = tid; i < count; i += 256) place(key[i], i);
 }
 
 hipError_t launch_sort_lists(const PrefillMainArgs& a, hipStream_t st) {

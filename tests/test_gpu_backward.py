@@ -196,3 +196,36 @@ def test_backward_and_indexer_kl_on_a_forced_sink_selection():
     assert (np.abs(kl.cpu().double().numpy()[0] - kl_ref) <= 1e-3 * np.abs(kl_ref) + 1e-4).all()
     check_grad(diq.cpu().double().numpy(), np.stack([ores["d_idx_q"][(0, t)] for t in range(T)])[None], "d idx_q")
     check_grad(dik.cpu().double().numpy(), ores["d_idx_k"], "d idx_k")
+
+
+def test_duplicate_blocks_in_a_selection_keep_the_fallback_sort():
+    """A selection that repeats a block within a row is invalid input; the
+    list sort detects the repeated token and falls back to its sorting
+    network.  The calls must stay finite and bitwise repeatable."""
+    T, Hq, G, B, k = 700, 8, 2, 64, 4
+    say("[duplicate blocks in a given selection]")
+    inp = inputs.make_prefill(T, Hq, G, 128, 64, seed=940)
+    _, _, bidx = gpu_prefill(inp, B, k)
+    sel = bidx.numpy().copy()
+    for t in range(2 * B, T, 7):
+        for g in range(G):
+            if sel[0, t, g, 1] >= 0:
+                sel[0, t, g, 2] = sel[0, t, g, 1]          # the same block twice
+    bsel = torch.from_numpy(sel)
+    out, lse, _ = gpu_prefill(inp, B, k, flags=bd.MSA_GIVEN_INDICES, block_idx=bsel)
+    dout = _dout((1, T, Hq, 128), 941)
+    runs = [gpu_backward(inp, out, lse, bsel, dout, B, k) for _ in range(2)]
+    for a_, b_ in zip(*runs):
+        assert np.isfinite(a_).all() and np.array_equal(a_, b_)
+    dims = bd.make_dims(1, T, Hq, G, index_dim=64, block_size=B, topk=k)
+    res = []
+    for _ in range(2):
+        kl = torch.empty((1, T, G), device="cuda")
+        diq = torch.empty((1, T, G, 64), device="cuda")
+        dik = torch.empty((1, T, 64), device="cuda")
+        bd.msa_indexer_kl(dims, inp.q.cuda(), inp.k.cuda(), inp.idx_q.cuda(), inp.idx_k.cuda(), bsel.cuda(),
+                          lse.cuda(), kl, diq, dik)
+        torch.cuda.synchronize()
+        res.append([x.cpu().numpy() for x in (kl, diq, dik)])
+    for a_, b_ in zip(*res):
+        assert np.isfinite(a_).all() and np.array_equal(a_, b_)
