@@ -336,18 +336,29 @@ __global__ __launch_bounds__(256, MSA_KL_ENTRY_MINB) void kl_entry_kernel(Indexe
 //    list's d idx_k partial (dS^T . idx_q over its entries), both on MFMA,
 //    over chunks of 32 entries.
 // ---------------------------------------------------------------------------
+// Element offset of 16-byte chunk c of row r in an unpadded tile of rows of
+// NC chunks: the chunk sits at c ^ s(r), with s chosen so that 16 consecutive
+// rows read one chunk each (row-per-lane operand reads) and 4 consecutive
+// rows read 64 bytes each (transposing reads, 32 lanes) both fall on 16
+// distinct 16-byte positions of a 256-byte bank window.
+template <int NC>
+__device__ __forceinline__ int kl_swz(int r, int c) {
+  int sw;
+  if constexpr (NC >= 16) sw = 4 * (r & 3) + ((r >> 2) & 3);
+  else if constexpr (NC == 8) sw = 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  else sw = (r >> 2) & 3;
+  return r * (NC * 8) + ((c ^ sw) * 8);
+}
+
 template <int DI, int BS>
 __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
   constexpr int EC = 32;                  // entries per chunk
-  constexpr int IKR = BS + 8;             // idx_k^T row stride (keys)
-  constexpr int DRR = BS + 8;             // dS row stride (keys)
-  constexpr int ER = EC + 8;              // transposed rows (entries)
+  constexpr int KC = BS / 8, QC = DI / 8;  // 16-byte chunks per key row / per index row
   constexpr int NT = (BS / 32) * (DI / 32);  // d idx_k output tiles of the list
   constexpr int TPW = (NT + 3) / 4;          // tiles per wave
-  __shared__ __attribute__((aligned(16))) bf16_t IkT[DI * IKR];
-  __shared__ __attribute__((aligned(16))) bf16_t Dr[EC * DRR];
-  __shared__ __attribute__((aligned(16))) bf16_t DT[BS * ER];
-  __shared__ __attribute__((aligned(16))) bf16_t QT[DI * ER];
+  __shared__ __attribute__((aligned(16))) bf16_t IkT[DI * BS];  // [c][key]
+  __shared__ __attribute__((aligned(16))) bf16_t Dr[EC * BS];   // [entry][key]
+  __shared__ __attribute__((aligned(16))) bf16_t Qr[EC * DI];   // [entry][c]
   const PrefillMainArgs& l = a.l;
   const long lid = blockIdx.x;
   const int count = l.cnt[lid];
@@ -360,14 +371,8 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
   const int kb = b * l.B;
   const int nkey = min(BS, l.T - kb);
 
-  // Transposed rows (IkT and QT: index dim, DT: key) hold 16-byte chunks,
-  // chunk ch of row r at position ch ^ ((r / 16) % 4): the 32 lanes of a
-  // transposing write pass, rows 4 apart, then fall on at most two lanes per
-  // bank (eight without the swizzle), and the operand reads (16 consecutive
-  // rows, one chunk) stay conflict-free.
-  auto tchunk = [](int r, int ch) { return ((ch ^ ((r >> 4) & 3)) * 8); };
-  auto tcol = [&](int r, int u) { return tchunk(r, u >> 1) + 4 * (u & 1); };  // 8-byte unit u of row r
-  // idx_k block, transposed: IkT[c][key], in 4 keys x 4 c units
+  // idx_k block, transposed through registers in 4 keys x 4 c units:
+  // IkT[c][key], read row-per-lane by the d idx_q product.
   for (int u = tid; u < (BS / 4) * (DI / 4); u += 256) {
     const int k4 = u / (DI / 4), c4 = u % (DI / 4);
     u32x2 r[4], o[4];
@@ -380,16 +385,18 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
     transpose4x4(r, o);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x2*>(IkT + (4 * c4 + j) * IKR + tcol(4 * c4 + j, k4)) = o[j];
+      *reinterpret_cast<u32x2*>(IkT + kl_swz<KC>(4 * c4 + j, k4 >> 1) + 4 * (k4 & 1)) = o[j];
   }
   f32x16 dk[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) dk[i] = f32x16{};
 
   // Each thread stages one 4 entries x 4 keys unit of the chunk's dS rows and
-  // one 4 entries x 4 dims unit of its idx_q rows.  The next chunk's units
-  // are fetched into registers while the current chunk computes, and the
-  // entries that address its idx_q rows one chunk earlier still.
+  // one 4 entries x 4 dims unit of its idx_q rows, both row-major: the d idx_q
+  // product reads dS rows per lane, the d idx_k product reads dS and idx_q
+  // with entries as the contraction index through the transposing LDS read.
+  // The next chunk's units are fetched into registers while the current chunk
+  // computes, and the entries that address its idx_q rows one chunk earlier.
   constexpr int NUD = (EC / 4) * (BS / 4), NUQ = (EC / 4) * (DI / 4);
   static_assert(NUD <= 256 && NUQ <= 256, "one unit per thread");
   const bool has_d = tid < NUD, has_q = tid < NUQ;
@@ -417,22 +424,25 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
     }
   };
   auto store = [&]() {
-    u32x2 o[4];
     if (has_d) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x2*>(Dr + (4 * de4 + i) * DRR + 4 * dk4) = dsr[i];
-      transpose4x4(dsr, o);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<u32x2*>(DT + (4 * dk4 + j) * ER + tcol(4 * dk4 + j, de4)) = o[j];
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x2*>(Dr + kl_swz<KC>(4 * de4 + i, dk4 >> 1) + 4 * (dk4 & 1)) = dsr[i];
     }
     if (has_q) {
-      transpose4x4(qsr, o);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<u32x2*>(QT + (4 * qc4 + j) * ER + tcol(4 * qc4 + j, qe4)) = o[j];
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x2*>(Qr + kl_swz<QC>(4 * qe4 + i, qc4 >> 1) + 4 * (qc4 & 1)) = qsr[i];
     }
   };
+  // Transposing read (ds_read_b64_tr_b16) of a row-major swizzled tile: in
+  // each 16-lane group, lane 4a + c addresses the 8-byte word of row
+  // r0 + c of the group's 4 rows at column 4a, so that lane l receives rows
+  // r0 .. r0 + 3 at column c0 + l % 32, with r0 = rb + 4 (l / 32).
+  const int tr_row = 4 * half + ((lane >> 2) & 3);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto tr_d = [&](int rb, int c0) { return kl_swz<KC>(rb + tr_row, (c0 + tr_col) >> 3) + (tr_col & 7); };
+  auto tr_q = [&](int rb, int c0) { return kl_swz<QC>(rb + tr_row, (c0 + tr_col) >> 3) + (tr_col & 7); };
 
   load_ent(0);
   load_data(0);
@@ -451,9 +461,8 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
       f32x16 acc = {};
 #pragma unroll
       for (int ks = 0; ks < BS / 16; ++ks) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(Dr + col * DRR + 16 * ks + 8 * half);
-        const bf16x8 bv =
-            *reinterpret_cast<const bf16x8*>(IkT + (32 * wave + col) * IKR + tchunk(32 * wave + col, 2 * ks + half));
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(Dr + kl_swz<KC>(col, 2 * ks + half));
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(IkT + kl_swz<KC>(32 * wave + col, 2 * ks + half));
         acc = mfma32x32x16(av, bv, acc);
       }
 #pragma unroll
@@ -462,7 +471,9 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
         if (en < n) a.dq_e[(size_t)(off + c0 + en) * DI + 32 * wave + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[i]);
       }
     }
-    // d idx_k partial: [key][c] += sum_entry dS[entry][key] idx_q[entry][c]
+    // d idx_k partial: [key][c] += sum_entry dS[entry][key] idx_q[entry][c].
+    // Both operands come from the transposing read, rows (entries) 16 ks + 4 h
+    // .. + 3 and 8 further for lane half h, the same k-slot order on both sides.
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int tix = wave + 4 * i;
@@ -470,10 +481,10 @@ __global__ __launch_bounds__(256) void kl_list_kernel(IndexerKlArgs a) {
         const int kt = tix / (DI / 32), dt = tix % (DI / 32);
 #pragma unroll
         for (int ks = 0; ks < EC / 16; ++ks) {
-          const bf16x8 av =
-              *reinterpret_cast<const bf16x8*>(DT + (32 * kt + col) * ER + tchunk(32 * kt + col, 2 * ks + half));
-          const bf16x8 bv =
-              *reinterpret_cast<const bf16x8*>(QT + (32 * dt + col) * ER + tchunk(32 * dt + col, 2 * ks + half));
+          const bf16x8 av = join_bf16x4(lds_read_tr16(Dr + tr_d(16 * ks, 32 * kt)),
+                                        lds_read_tr16(Dr + tr_d(16 * ks + 8, 32 * kt)));
+          const bf16x8 bv = join_bf16x4(lds_read_tr16(Qr + tr_q(16 * ks, 32 * dt)),
+                                        lds_read_tr16(Qr + tr_q(16 * ks + 8, 32 * dt)));
           dk[i] = mfma32x32x16(av, bv, dk[i]);
         }
       }
